@@ -1,0 +1,298 @@
+"""Zero-copy decode attention for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over the C ABI in ``include/dkv.h`` (``libdkv.so``, built
+in-tree by :func:`build`). Functions keep the C names; device buffers are
+passed as torch tensors (only their addresses and the current HIP stream are
+used), host buffers as numpy arrays. Every step of the decode path runs in the
+library's HIP kernels; there is no fallback -- without the built library the
+functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from ._build import LIBRARY, build_library
+
+__all__ = [
+    "DkvError", "Shape", "Pool", "Layout", "build", "lib", "kv_page_bytes", "kv_page_offset",
+    "kv_placement", "kv_alloc_host", "kv_alloc_hbm", "kv_layout_create", "kv_append", "kv_read",
+    "decode_step", "decode_step_f32", "probe_stream_read", "PAGE_TOKENS",
+]
+
+PAGE_TOKENS = 16
+HOST_COHERENT = 0
+HOST_NONCOHERENT = 1
+
+_STATUS = {0: "DKV_OK", -1: "DKV_E_INVALID_ARG", -2: "DKV_E_OUT_OF_MEMORY", -3: "DKV_E_CAPACITY",
+           -4: "DKV_E_HIP", -5: "DKV_E_UNSUPPORTED"}
+
+
+class DkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (_STATUS.get(status, str(status)), message))
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("page_tokens", ctypes.c_int32)]
+
+    @classmethod
+    def of(cls, hidden, n_q_heads, n_kv_heads, head_dim, n_layers=1):
+        return cls(hidden, n_q_heads, n_kv_heads, head_dim, n_layers, PAGE_TOKENS)
+
+
+_lib = None
+
+
+def build() -> str:
+    """Compiles the HIP library for gfx950 (always) and returns its path."""
+    global _lib
+    _lib = None
+    return build_library()
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError("libdkv.so is not built; run __graft_entry__.build() "
+                               "(decode_attention_zero_amd.build()) first")
+        L = ctypes.CDLL(LIBRARY)
+        P, I32, I64, U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+        SP = ctypes.POINTER(Shape)
+        sig = {
+            "dkv_last_error": ([], ctypes.c_char_p),
+            "kv_page_bytes": ([SP], I64),
+            "kv_page_offset": ([SP, I32, I32, I32, I32], I64),
+            "kv_placement": ([I32, I32, P, P], I32),
+            "kv_alloc_host": ([SP, I64, U32, P], I32),
+            "kv_alloc_hbm": ([SP, I64, P], I32),
+            "kv_pool_free_pages": ([P, P], I32),
+            "kv_pool_info": ([P, P, P, P], I32),
+            "kv_pool_free": ([P], I32),
+            "kv_layout_create": ([SP, I32, P, P, P, P, P], I32),
+            "kv_layout_free": ([P], I32),
+            "kv_layout_page_tier": ([P, I32, I32, P], I32),
+            "kv_layout_split_tokens": ([P], I32),
+            "kv_layout_check_status": ([P], I32),
+            "kv_append": ([P, I32, I32, I32, I32, P, P, P], I32),
+            "kv_read": ([P, I32, I32, I32, I32, P, P], I32),
+            "decode_step": ([P, I32, P, P, P, P, P], I32),
+            "decode_step_f32": ([P, I32, P, P, P, P, P], I32),
+            "dkv_probe_stream_read": ([P, ctypes.c_uint64, I32, I32, I32, P], I32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement", "kv_alloc_host",
+            "kv_alloc_hbm", "kv_pool_free_pages", "kv_pool_info", "kv_pool_free",
+            "kv_layout_create", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
+            "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
+            "dkv_probe_stream_read"]
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DkvError(status, lib().dkv_last_error().decode(errors="replace"))
+
+
+def _np_ptr(a: np.ndarray) -> int:
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("host buffers must be C-contiguous")
+    return a.ctypes.data
+
+
+def _stream_ptr(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+# ----------------------------------------------------------------------------- pure host
+def kv_page_bytes(shape: Shape) -> int:
+    return lib().kv_page_bytes(ctypes.byref(shape))
+
+
+def kv_page_offset(shape: Shape, token_in_page: int, kv_head: int, kv_select: int, dim: int) -> int:
+    return lib().kv_page_offset(ctypes.byref(shape), token_in_page, kv_head, kv_select, dim)
+
+
+def kv_placement(capacity_tokens: int, hbm_tail_tokens: int) -> tuple[int, int]:
+    n = ctypes.c_int32()
+    f = ctypes.c_int32()
+    _check(lib().kv_placement(capacity_tokens, hbm_tail_tokens, ctypes.byref(n), ctypes.byref(f)))
+    return n.value, f.value
+
+
+# ----------------------------------------------------------------------------- pools, layouts
+class Pool:
+    def __init__(self, handle: int, shape: Shape, tier: int):
+        self.handle = handle
+        self.shape = shape
+        self.tier = tier
+
+    def free_pages(self) -> int:
+        n = ctypes.c_int64()
+        _check(lib().kv_pool_free_pages(self.handle, ctypes.byref(n)))
+        return n.value
+
+    def info(self) -> tuple[int, int, int]:
+        base = ctypes.c_void_p()
+        nbytes = ctypes.c_int64()
+        tier = ctypes.c_int32()
+        _check(lib().kv_pool_info(self.handle, ctypes.byref(base), ctypes.byref(nbytes),
+                                  ctypes.byref(tier)))
+        return base.value or 0, nbytes.value, tier.value
+
+    def free(self) -> None:
+        if self.handle:
+            _check(lib().kv_pool_free(self.handle))
+            self.handle = None
+
+
+def kv_alloc_host(shape: Shape, n_pages: int, flags: int = HOST_COHERENT) -> Pool:
+    h = ctypes.c_void_p()
+    _check(lib().kv_alloc_host(ctypes.byref(shape), n_pages, flags, ctypes.byref(h)))
+    return Pool(h.value, shape, 0)
+
+
+def kv_alloc_hbm(shape: Shape, n_pages: int) -> Pool:
+    h = ctypes.c_void_p()
+    _check(lib().kv_alloc_hbm(ctypes.byref(shape), n_pages, ctypes.byref(h)))
+    return Pool(h.value, shape, 1)
+
+
+class Layout:
+    def __init__(self, handle: int, shape: Shape, batch: int, capacity: np.ndarray):
+        self.handle = handle
+        self.shape = shape
+        self.batch = batch
+        self.capacity = capacity
+
+    @property
+    def split_tokens(self) -> int:
+        return lib().kv_layout_split_tokens(self.handle)
+
+    def page_tier(self, seq: int, page: int) -> int:
+        t = ctypes.c_int32()
+        _check(lib().kv_layout_page_tier(self.handle, seq, page, ctypes.byref(t)))
+        return t.value
+
+    def check_status(self) -> None:
+        _check(lib().kv_layout_check_status(self.handle))
+
+    def free(self) -> None:
+        if self.handle:
+            _check(lib().kv_layout_free(self.handle))
+            self.handle = None
+
+
+def kv_layout_create(shape: Shape, capacity_tokens, hbm_tail_tokens=None,
+                     host_pool: Pool | None = None, hbm_pool: Pool | None = None) -> Layout:
+    cap = np.ascontiguousarray(capacity_tokens, dtype=np.int32)
+    tail = None if hbm_tail_tokens is None else np.ascontiguousarray(hbm_tail_tokens, dtype=np.int32)
+    if tail is not None and tail.shape != cap.shape:
+        raise ValueError("hbm_tail_tokens must have one entry per sequence")
+    h = ctypes.c_void_p()
+    _check(lib().kv_layout_create(ctypes.byref(shape), len(cap), _np_ptr(cap),
+                                  None if tail is None else _np_ptr(tail),
+                                  host_pool.handle if host_pool else None,
+                                  hbm_pool.handle if hbm_pool else None, ctypes.byref(h)))
+    return Layout(h.value, shape, len(cap), cap)
+
+
+def kv_append(layout: Layout, layer: int, seq: int, start_token: int, k: np.ndarray,
+              v: np.ndarray, stream=0) -> None:
+    """k, v: host uint16 arrays [n][Hkv][d] (bf16 bits) in logical order."""
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    s = layout.shape
+    n = k.shape[0] if k.ndim > 0 else 0
+    if k.shape != (n, s.n_kv_heads, s.head_dim) or v.shape != k.shape:
+        raise ValueError("k and v must be [n][n_kv_heads][head_dim]")
+    _check(lib().kv_append(layout.handle, layer, seq, start_token, n, _np_ptr(k), _np_ptr(v),
+                           _stream_ptr(stream) if stream else None))
+
+
+def kv_read(layout: Layout, layer: int, seq: int, start_token: int, n_tokens: int):
+    s = layout.shape
+    k = np.empty((n_tokens, s.n_kv_heads, s.head_dim), dtype=np.uint16)
+    v = np.empty_like(k)
+    _check(lib().kv_read(layout.handle, layer, seq, start_token, n_tokens, _np_ptr(k), _np_ptr(v)))
+    return k, v
+
+
+# ----------------------------------------------------------------------------- decode step
+def _dev_ptr(t, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _step(fn, layout, layer, q_in, W_qkv, ctx_lens, attn_out, stream):
+    import torch
+    for t, name, dt in ((q_in, "q_in", torch.bfloat16), (W_qkv, "W_qkv", torch.bfloat16),
+                        (ctx_lens, "ctx_lens", torch.int32)):
+        if t.dtype != dt:
+            raise ValueError("%s must be %s" % (name, dt))
+    s = layout.shape
+    n_qkv = (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim
+    if tuple(q_in.shape) != (layout.batch, s.hidden):
+        raise ValueError("q_in must be [batch][hidden]")
+    if tuple(W_qkv.shape) != (n_qkv, s.hidden):
+        raise ValueError("W_qkv must be [(Hq + 2 Hkv) d][hidden]")
+    if tuple(ctx_lens.shape) != (layout.batch,):
+        raise ValueError("ctx_lens must be [batch]")
+    if tuple(attn_out.shape) != (layout.batch, s.n_q_heads * s.head_dim):
+        raise ValueError("attn_out must be [batch][Hq d]")
+    _check(fn(layout.handle, layer, _dev_ptr(q_in, "q_in"), _dev_ptr(W_qkv, "W_qkv"),
+              _dev_ptr(ctx_lens, "ctx_lens"), _dev_ptr(attn_out, "attn_out"), _stream_ptr(stream)))
+    return attn_out
+
+
+def decode_step(layout: Layout, layer: int, q_in, W_qkv, ctx_lens, attn_out=None, stream=None):
+    """One decode step of `layer`; returns attn_out [batch][Hq*d] bf16 (device)."""
+    import torch
+    if attn_out is None:
+        s = layout.shape
+        attn_out = torch.empty((layout.batch, s.n_q_heads * s.head_dim), dtype=torch.bfloat16,
+                               device=q_in.device)
+    if attn_out.dtype != torch.bfloat16:
+        raise ValueError("attn_out must be bfloat16")
+    return _step(lib().decode_step, layout, layer, q_in, W_qkv, ctx_lens, attn_out, stream)
+
+
+def decode_step_f32(layout: Layout, layer: int, q_in, W_qkv, ctx_lens, attn_out=None,
+                    stream=None):
+    """decode_step with an fp32 attn_out (no output rounding)."""
+    import torch
+    if attn_out is None:
+        s = layout.shape
+        attn_out = torch.empty((layout.batch, s.n_q_heads * s.head_dim), dtype=torch.float32,
+                               device=q_in.device)
+    if attn_out.dtype != torch.float32:
+        raise ValueError("attn_out must be float32")
+    return _step(lib().decode_step_f32, layout, layer, q_in, W_qkv, ctx_lens, attn_out, stream)
+
+
+def probe_stream_read(device_ptr: int, nbytes: int, grid: int = 256, unroll: int = 2,
+                      reps: int = 3) -> float:
+    """Median milliseconds of a kernel streaming-read of nbytes at device_ptr."""
+    ms = ctypes.c_float()
+    _check(lib().dkv_probe_stream_read(device_ptr, nbytes, grid, unroll, reps, ctypes.byref(ms)))
+    return ms.value

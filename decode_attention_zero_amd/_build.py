@@ -1,0 +1,45 @@
+"""Builds the HIP library ``libdkv.so`` in-tree with hipcc for gfx950."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIBRARY = os.path.join(PKG, "libdkv.so")
+SOURCES = ["kernels.hip", "runtime.hip"]
+HEADERS = [os.path.join(CSRC, "dkv_internal.h"), os.path.join(INCLUDE, "dkv.h"),
+           os.path.join(INCLUDE, "dkv_probe.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+# Packed fp32 instructions are switched off for every HIP source.
+COMMON_FLAGS = ["-O3", "-std=c++17", "--offload-arch=" + ARCH, "-fPIC",
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
+
+
+def sources() -> list[str]:
+    return [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def build_library(out: str = LIBRARY, verbose: bool = False) -> str:
+    """Compiles every HIP source into one shared library (always recompiles)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + COMMON_FLAGS + ["-shared", "-o", tmp] + sources()
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+    if verbose:
+        print(res.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+def device_assembly(source: str = "kernels.hip") -> str:
+    """gfx950 assembly of one source (for inspecting this library's own code)."""
+    cmd = [HIPCC] + COMMON_FLAGS + ["--cuda-device-only", "-S", "-o", "-",
+                                    os.path.join(CSRC, source)]
+    return subprocess.run(cmd, capture_output=True, text=True, check=True).stdout

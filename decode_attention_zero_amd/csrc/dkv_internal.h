@@ -1,0 +1,52 @@
+// Internal declarations shared by the runtime and the kernels of the
+// zero-copy decode-attention library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dkv.h"
+
+namespace dkv {
+
+constexpr int kPageTokens = DKV_PAGE_TOKENS;
+
+// Everything one decode step's kernels read or write. Built on the host by
+// decode_step from the layout and the caller's pointers; passed by value.
+struct StepArgs {
+    // shape
+    int32_t batch;
+    int32_t hidden;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t n_qkv;          // (Hq + 2 Hkv) * d
+    int32_t max_pages;      // page-table row length
+    int32_t split_tokens;   // tokens per attention work item (multiple of 16)
+    int32_t max_splits;     // partial slots per (sequence, query head)
+    float qscale;           // log2(e) / sqrt(head_dim): scores come out in log2 units
+    // this layer's page table [batch][max_pages] of device addresses
+    const uint64_t *page_table;
+    const int32_t *capacity;  // [batch] slots per sequence (device)
+    // caller's buffers
+    const uint16_t *x;        // [batch][hidden] bf16
+    const uint16_t *w;        // [n_qkv][hidden] bf16
+    const int32_t *ctx_lens;  // [batch]
+    void *out;                // [batch][Hq * d] bf16 or fp32
+    int32_t out_f32;
+    // layout-owned scratch
+    float *q;                 // [batch][Hq][d] fp32, scaled by log2(e) / sqrt(d)
+    uint16_t *kv_new;         // [batch][Hkv][2][d] bf16 (fresh K then V)
+    float *part_o;            // [batch][Hq][max_splits][d] unnormalised outputs
+    float2 *part_ml;          // [batch][Hq][max_splits] (running max, sum of weights)
+    uint32_t *status;         // range flag (bit 0: a ctx_lens entry out of range)
+};
+
+// Enqueues the decode step's kernels on `stream`.
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream);
+
+// Streaming-read probe (grid-stride, 16 B per lane per load).
+hipError_t launch_stream_read(const void *ptr, uint64_t bytes, int grid, int unroll,
+                              uint32_t *sink, hipStream_t stream);
+
+}  // namespace dkv

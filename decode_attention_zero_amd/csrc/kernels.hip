@@ -1,0 +1,478 @@
+// Kernels of one zero-copy decode step on gfx950 (MI355X).
+//
+// Three stream-ordered launches per layer:
+//   1. qkv_proj_kernel     y = W x for the batch (HBM-bound on W): q kept in
+//                          fp32 scratch (pre-scaled for exp2), fresh K/V
+//                          rounded once to bf16 into a small HBM scratch.
+//   2. attn_split_kernel   one wavefront per work item (sequence b, KV head g,
+//                          token split s): streams the split's KV pages in
+//                          place -- host pages over the host link, HBM pages
+//                          from HBM, chosen only by the page's address -- and
+//                          keeps an online-softmax state for the G query heads
+//                          that share the KV head, so each remote byte is read
+//                          once for all of them. Writes an unnormalised
+//                          partial (m, l, o).
+//   3. attn_combine_kernel one wavefront per (b, query head): scores the fresh
+//                          token from the scratch (it never travels to host
+//                          memory and back), merges the partials and the fresh
+//                          token in a fixed order, writes attn_out, and writes
+//                          the fresh K/V once into slot ctx_lens[b] of the
+//                          sequence's last page.
+//
+// Method (pages): "长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）" (DirectKV
+// digest), 核心方法: the kernel reads CPU-resident KV directly with a layout
+// arranged for coalesced remote reads, and the fresh K/V stay on chip instead
+// of being written to CPU memory and read back. The split/merge of the
+// softmax state is the standard flash-decoding decomposition (not on the
+// pages); the split boundaries depend only on token indices, never on where a
+// page lives, so host and HBM placements give bit-identical results.
+#include "dkv_internal.h"
+
+namespace dkv {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void unpack8(const uint4 &v, float f[8]) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Cross-lane move inside a 16-lane row (DPP). CTRL: 0xB1 = quad_perm
+// [1,0,3,2] (lane ^ 1), 0x4E = quad_perm [2,3,0,1] (lane ^ 2),
+// 0x141 = row_half_mirror (i <-> 7 - i in each 8-lane half), 0x140 =
+// row_mirror (i <-> 15 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the LPT consecutive lanes that hold one token (LPT = 8 or 16);
+// every lane of the group gets the total.
+template <int LPT>
+__device__ __forceinline__ float token_sum(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    if constexpr (LPT == 16) v += dpp<0x140>(v);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// exp2(x - M) weight of a softmax state whose max is x, under a common max M;
+// a state that has seen no token (x = -inf) weighs 0.
+__device__ __forceinline__ float rescale(float x, float M) {
+    return x == kNegInf ? 0.0f : exp2f(x - M);
+}
+
+// ------------------------------------------------------------------------------
+// 1. QKV projection. One wavefront computes 4 output rows for BT sequences;
+// lanes split the hidden dimension in 16-byte (8 x bf16) chunks, so each W
+// row is read as contiguous 1 KiB wave loads. Rows >= Hq*d are the fresh K
+// then V heads.
+template <int BT>
+__global__ __launch_bounds__(256) void qkv_proj_kernel(StepArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row0 = (blockIdx.x * 4 + wave) * 4;
+    const int b0 = blockIdx.y * BT;
+    const int nb = min(BT, a.batch - b0);
+
+    if (blockIdx.x == 0 && threadIdx.x < BT && threadIdx.x < nb) {
+        const int b = b0 + threadIdx.x;
+        const int L = a.ctx_lens[b];
+        if (L < 0 || L >= a.capacity[b]) atomicOr(a.status, 1u);
+    }
+    if (row0 >= a.n_qkv) return;
+
+    float acc[4][BT];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int bb = 0; bb < BT; ++bb) acc[r][bb] = 0.0f;
+
+    for (int k = lane * 8; k < a.hidden; k += 512) {
+        float wf[4][8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(a.w + (size_t)(row0 + r) * a.hidden + k);
+            unpack8(w, wf[r]);
+        }
+#pragma unroll
+        for (int bb = 0; bb < BT; ++bb) {
+            if (bb < nb) {
+                float xf[8];
+                unpack8(*reinterpret_cast<const uint4 *>(a.x + (size_t)(b0 + bb) * a.hidden + k), xf);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[r][bb] = fmaf(wf[r][e], xf[e], acc[r][bb]);
+            }
+        }
+    }
+
+    float y = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int bb = 0; bb < BT; ++bb) {
+            const float v = wave_sum(acc[r][bb]);
+            if (lane == r * BT + bb) y = v;
+        }
+
+    if (lane < 4 * BT) {
+        const int r = lane / BT, bb = lane % BT;
+        if (bb < nb) {
+            const int n = row0 + r;
+            const int b = b0 + bb;
+            const int D = a.head_dim;
+            const int nq = a.n_q_heads * D;
+            if (n < nq) {
+                a.q[(size_t)b * nq + n] = y * a.qscale;
+            } else {
+                const int n2 = n - nq;
+                const int c = n2 / (a.n_kv_heads * D);
+                const int rem = n2 - c * (a.n_kv_heads * D);
+                const int g = rem / D, i = rem - g * D;
+                a.kv_new[(((size_t)b * a.n_kv_heads + g) * 2 + c) * D + i] = f32_to_bf16(y);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------
+// 2. Split attention. Work item (s, g, b) = blockIdx (x, y, z); one wavefront.
+//
+// Lane mapping inside a page run (K tile then V tile, each [16 tok][D] bf16):
+// wave load j reads bytes [j*1024, (j+1)*1024) of a tile, lane l the 16 bytes
+// at l*16, i.e. token j*TPL + l/LPT, dims 8*(l%LPT) .. +7. Every wave load is
+// one fully used, contiguous 1 KiB -- the coalesced remote access the layout is
+// arranged for. A token's score is summed over its LPT lanes with DPP; each
+// group of lanes holding the same token slot across loads (a "row") keeps its
+// own online-softmax state, merged across rows at the end of the item.
+template <int D, int G>
+__global__ __launch_bounds__(64) void attn_split_kernel(StepArgs a) {
+    constexpr int LPT = D / 8;               // lanes per token
+    constexpr int TPL = 64 / LPT;            // tokens per wave load
+    constexpr int NLD = kPageTokens / TPL;   // wave loads per 16-token tile
+    constexpr int TILE = kPageTokens * D * 2;
+    constexpr int RUN = 2 * TILE;
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int L = a.ctx_lens[b];
+    if (L < 0 || L >= a.capacity[b]) return;
+    const int t0 = s * a.split_tokens;
+    if (t0 >= L) return;
+    const int t1 = min(t0 + a.split_tokens, L);
+
+    const int lane = threadIdx.x;
+    const int sub = lane / LPT;
+    const int dl = lane % LPT;
+
+    float q[G][8];
+    {
+        const float *qb = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + dl * 8;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float4 lo = *reinterpret_cast<const float4 *>(qb + h * D);
+            const float4 hi = *reinterpret_cast<const float4 *>(qb + h * D + 4);
+            q[h][0] = lo.x; q[h][1] = lo.y; q[h][2] = lo.z; q[h][3] = lo.w;
+            q[h][4] = hi.x; q[h][5] = hi.y; q[h][6] = hi.z; q[h][7] = hi.w;
+        }
+    }
+
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = kNegInf;
+        l[h] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    }
+
+    const uint64_t *pt = a.page_table + (size_t)b * a.max_pages;
+    const int p0 = t0 / kPageTokens;
+    const int p1 = (t1 + kPageTokens - 1) / kPageTokens;
+    const size_t run_off = (size_t)g * RUN + (size_t)lane * 16;
+
+    uint4 kc[NLD], vc[NLD];
+    {
+        const char *run = reinterpret_cast<const char *>(pt[p0]) + run_off;
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            kc[j] = *reinterpret_cast<const uint4 *>(run + j * 1024);
+            vc[j] = *reinterpret_cast<const uint4 *>(run + TILE + j * 1024);
+        }
+    }
+
+    for (int p = p0; p < p1; ++p) {
+        uint4 kn[NLD], vn[NLD];
+        const bool more = p + 1 < p1;
+        if (more) {
+            const char *run = reinterpret_cast<const char *>(pt[p + 1]) + run_off;
+#pragma unroll
+            for (int j = 0; j < NLD; ++j) {
+                kn[j] = *reinterpret_cast<const uint4 *>(run + j * 1024);
+                vn[j] = *reinterpret_cast<const uint4 *>(run + TILE + j * 1024);
+            }
+        }
+
+        const int tok0 = p * kPageTokens;
+        const bool full = tok0 + kPageTokens <= t1;
+        bool valid[NLD];
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) valid[j] = full || (tok0 + j * TPL + sub < t1);
+
+        float sc[NLD][G];
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            float kf[8];
+            unpack8(kc[j], kf);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float d0 = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d0 = fmaf(q[h][e], kf[e], d0);
+                sc[j][h] = token_sum<LPT>(d0);
+            }
+        }
+
+        float vf[NLD][8];
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            unpack8(vc[j], vf[j]);
+            if (!valid[j]) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vf[j][e] = 0.0f;   // stale slots may hold any bits
+            }
+        }
+
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mx = m[h];
+#pragma unroll
+            for (int j = 0; j < NLD; ++j)
+                if (valid[j]) mx = fmaxf(mx, sc[j][h]);
+            const float alpha = (mx == m[h]) ? 1.0f : rescale(m[h], mx);
+            float pj[NLD];
+            float psum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NLD; ++j) {
+                pj[j] = valid[j] ? exp2f(sc[j][h] - mx) : 0.0f;
+                psum += pj[j];
+            }
+            l[h] = fmaf(l[h], alpha, psum);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float o = acc[h][e] * alpha;
+#pragma unroll
+                for (int j = 0; j < NLD; ++j) o = fmaf(pj[j], vf[j][e], o);
+                acc[h][e] = o;
+            }
+            m[h] = mx;
+        }
+
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < NLD; ++j) {
+                kc[j] = kn[j];
+                vc[j] = vn[j];
+            }
+        }
+    }
+
+    // Merge the row states (lanes l and l ^ off, off >= LPT) in a fixed order.
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float mo = __shfl_xor(m[h], off);
+            const float lo = __shfl_xor(l[h], off);
+            const float M = fmaxf(m[h], mo);
+            const float c1 = rescale(m[h], M);
+            const float c2 = rescale(mo, M);
+            l[h] = fmaf(l[h], c1, lo * c2);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float ao = __shfl_xor(acc[h][e], off);
+                acc[h][e] = fmaf(acc[h][e], c1, ao * c2);
+            }
+            m[h] = M;
+        }
+    }
+
+    if (sub == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const size_t slot = ((size_t)b * a.n_q_heads + (size_t)g * G + h) * a.max_splits + s;
+            float *po = a.part_o + slot * D + dl * 8;
+            *reinterpret_cast<float4 *>(po) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+            *reinterpret_cast<float4 *>(po + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+            if (dl == 0) a.part_ml[slot] = make_float2(m[h], l[h]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------
+// 3. Combine + fresh token + write-back. One wavefront per (b, query head).
+template <int D, int G>
+__global__ __launch_bounds__(64) void attn_combine_kernel(StepArgs a) {
+    constexpr int DPL = D / 64;    // dims per lane
+    const int b = blockIdx.x / a.n_q_heads;
+    const int h = blockIdx.x - b * a.n_q_heads;
+    const int g = h / G;
+    const int lane = threadIdx.x;
+    const int L = a.ctx_lens[b];
+    const size_t obase = ((size_t)b * a.n_q_heads + h) * D + (size_t)lane * DPL;
+
+    float o[DPL];
+    if (L < 0 || L >= a.capacity[b]) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] = __builtin_nanf("");
+    } else {
+        const float *qh = a.q + ((size_t)b * a.n_q_heads + h) * D;
+        const uint16_t *kn = a.kv_new + ((size_t)b * a.n_kv_heads + g) * 2 * D;
+        const uint16_t *vn = kn + D;
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+            part = fmaf(qh[lane * DPL + e], __uint_as_float((uint32_t)kn[lane * DPL + e] << 16), part);
+        const float s_new = wave_sum(part);
+
+        const int S = (L + a.split_tokens - 1) / a.split_tokens;
+        const size_t slot0 = ((size_t)b * a.n_q_heads + h) * a.max_splits;
+        const float2 *ml = a.part_ml + slot0;
+        const float *po = a.part_o + slot0 * D + (size_t)lane * DPL;
+
+        float M = s_new;
+        for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s].x);
+        float den = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
+        for (int s = 0; s < S; ++s) {
+            const float2 st = ml[s];
+            const float c = exp2f(st.x - M);
+            den = fmaf(c, st.y, den);
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) o[e] = fmaf(c, po[(size_t)s * D + e], o[e]);
+        }
+        const float cn = exp2f(s_new - M);
+        den += cn;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+            o[e] = fmaf(cn, __uint_as_float((uint32_t)vn[lane * DPL + e] << 16), o[e]) / den;
+
+        // The fresh K and V rows go to slot L once: lanes 0-31 the K row,
+        // lanes 32-63 the V row (one query head per KV group does it).
+        if (h % G == 0) {
+            const int c = lane >> 5;
+            char *page = reinterpret_cast<char *>(a.page_table[(size_t)b * a.max_pages + L / kPageTokens]);
+            char *dst = page + ((size_t)((g * 2 + c) * kPageTokens + (L % kPageTokens)) * D) * 2;
+            const char *src = reinterpret_cast<const char *>(kn + c * D);
+            constexpr int BPL = D * 2 / 32;    // bytes per lane
+            const int li = lane & 31;
+            if constexpr (BPL == 8) {
+                *reinterpret_cast<uint2 *>(dst + li * 8) = *reinterpret_cast<const uint2 *>(src + li * 8);
+            } else {
+                *reinterpret_cast<uint32_t *>(dst + li * 4) = *reinterpret_cast<const uint32_t *>(src + li * 4);
+            }
+        }
+    }
+
+    if (a.out_f32) {
+        float *out = reinterpret_cast<float *>(a.out) + obase;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) out[e] = o[e];
+    } else {
+        uint16_t *out = reinterpret_cast<uint16_t *>(a.out) + obase;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) out[e] = f32_to_bf16(o[e]);
+    }
+}
+
+template <int D, int G>
+void launch_attention(const StepArgs &a, hipStream_t st) {
+    dim3 grid_split(a.max_splits, a.n_kv_heads, a.batch);
+    attn_split_kernel<D, G><<<grid_split, 64, 0, st>>>(a);
+    attn_combine_kernel<D, G><<<a.batch * a.n_q_heads, 64, 0, st>>>(a);
+}
+
+template <int D>
+bool dispatch_group(const StepArgs &a, int G, hipStream_t st) {
+    switch (G) {
+        case 1: launch_attention<D, 1>(a, st); return true;
+        case 2: launch_attention<D, 2>(a, st); return true;
+        case 4: launch_attention<D, 4>(a, st); return true;
+        case 8: launch_attention<D, 8>(a, st); return true;
+        default: return false;
+    }
+}
+
+// ------------------------------------------------------------------------------
+// Streaming-read probe: grid-stride 16-byte loads, U in flight per lane.
+template <int U>
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restrict__ p, uint64_t nvec,
+                                                          uint32_t *sink) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    uint32_t x = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride * U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t j = i + (uint64_t)u * stride;
+            v[u] = j < nvec ? p[j] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (x == 0x9E3779B9u) sink[0] = x;   // keeps the loads alive
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t st) {
+    constexpr int BT = 8;
+    dim3 grid_proj((a.n_qkv + 15) / 16, (a.batch + BT - 1) / BT);
+    qkv_proj_kernel<BT><<<grid_proj, 256, 0, st>>>(a);
+    const int G = a.n_q_heads / a.n_kv_heads;
+    bool ok = false;
+    if (a.head_dim == 128) ok = dispatch_group<128>(a, G, st);
+    else if (a.head_dim == 64) ok = dispatch_group<64>(a, G, st);
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void *ptr, uint64_t bytes, int grid, int unroll, uint32_t *sink,
+                              hipStream_t st) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(ptr);
+    const uint64_t nvec = bytes / 16;
+    switch (unroll) {
+        case 1: stream_read_kernel<1><<<grid, 256, 0, st>>>(p, nvec, sink); break;
+        case 2: stream_read_kernel<2><<<grid, 256, 0, st>>>(p, nvec, sink); break;
+        case 4: stream_read_kernel<4><<<grid, 256, 0, st>>>(p, nvec, sink); break;
+        case 8: stream_read_kernel<8><<<grid, 256, 0, st>>>(p, nvec, sink); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dkv

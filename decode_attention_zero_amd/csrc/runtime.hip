@@ -1,0 +1,649 @@
+// Host runtime and C ABI of the zero-copy decode-attention library:
+// KV page pools (host-pinned or HBM), per-batch layouts (page tables,
+// placement, scratch), set-up copies, validation and the decode-step launch.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "dkv_internal.h"
+#include "dkv_probe.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dkv_status fail(dkv_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+dkv_status hip_fail(hipError_t e, const char *what) {
+    return fail(DKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(call)                                        \
+    do {                                                     \
+        hipError_t e_ = (call);                              \
+        if (e_ != hipSuccess) return hip_fail(e_, #call);    \
+    } while (0)
+
+bool shape_ok(const dkv_shape *s) {
+    if (!s) return false;
+    if (s->hidden <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 ||
+        s->n_layers <= 0)
+        return false;
+    if (s->page_tokens != DKV_PAGE_TOKENS) return false;
+    if (s->n_q_heads % s->n_kv_heads != 0) return false;
+    return true;
+}
+
+bool shape_supported(const dkv_shape *s) {
+    const int G = s->n_q_heads / s->n_kv_heads;
+    return (s->head_dim == 64 || s->head_dim == 128) && (G == 1 || G == 2 || G == 4 || G == 8) &&
+           s->hidden % 512 == 0;
+}
+
+int64_t page_bytes_of(const dkv_shape *s) {
+    return (int64_t)s->n_kv_heads * 2 * DKV_PAGE_TOKENS * s->head_dim * 2;
+}
+
+int64_t row_offset(const dkv_shape *s, int t, int g, int c) {
+    return ((int64_t)(g * 2 + c) * DKV_PAGE_TOKENS + t) * s->head_dim * 2;
+}
+
+}  // namespace
+
+struct dkv_pool {
+    dkv_shape shape;
+    int32_t tier;            // 0 host, 1 HBM
+    int64_t n_pages;
+    int64_t page_bytes;
+    char *host_base;         // CPU address (host tier), else nullptr
+    char *dev_base;          // GPU address of page 0
+    std::vector<uint8_t> used;
+    int64_t n_free;
+    int64_t scan;            // allocation cursor
+    int64_t n_layouts;       // layouts holding pages of this pool
+};
+
+struct dkv_layout {
+    dkv_shape shape;
+    int32_t batch;
+    std::vector<int32_t> capacity;
+    std::vector<int32_t> n_pages;
+    std::vector<int32_t> first_hbm;
+    int32_t max_pages;
+    int32_t split_tokens;
+    int32_t max_splits;
+    dkv_pool *host_pool;
+    dkv_pool *hbm_pool;
+    std::vector<int64_t> page_index;   // [n_layers][batch][max_pages] index in its pool, -1 = none
+    uint64_t *d_page_table;            // same shape, device addresses
+    int32_t *d_capacity;
+    float *d_q;
+    uint16_t *d_kv_new;
+    float *d_part_o;
+    float2 *d_part_ml;
+    uint32_t *d_status;
+};
+
+namespace {
+
+size_t pt_index(const dkv_layout *L, int layer, int b, int p) {
+    return ((size_t)layer * L->batch + b) * L->max_pages + p;
+}
+
+dkv_pool *pool_of(const dkv_layout *L, int b, int p) {
+    return p >= L->first_hbm[b] ? L->hbm_pool : L->host_pool;
+}
+
+bool take_pages(dkv_pool *pool, int64_t n, std::vector<int64_t> &out) {
+    if (pool->n_free < n) return false;
+    out.clear();
+    out.reserve(n);
+    int64_t i = pool->scan;
+    for (int64_t cnt = 0; cnt < pool->n_pages && (int64_t)out.size() < n; ++cnt) {
+        if (!pool->used[i]) out.push_back(i);
+        i = (i + 1) % pool->n_pages;
+    }
+    if ((int64_t)out.size() < n) return false;
+    for (int64_t idx : out) pool->used[idx] = 1;
+    pool->n_free -= n;
+    pool->scan = i;
+    return true;
+}
+
+void give_back(dkv_pool *pool, int64_t idx) {
+    if (pool && idx >= 0 && pool->used[idx]) {
+        pool->used[idx] = 0;
+        ++pool->n_free;
+    }
+}
+
+void free_device(dkv_layout *L) {
+    if (L->d_page_table) (void)hipFree(L->d_page_table);
+    if (L->d_capacity) (void)hipFree(L->d_capacity);
+    if (L->d_q) (void)hipFree(L->d_q);
+    if (L->d_kv_new) (void)hipFree(L->d_kv_new);
+    if (L->d_part_o) (void)hipFree(L->d_part_o);
+    if (L->d_part_ml) (void)hipFree(L->d_part_ml);
+    if (L->d_status) (void)hipFree(L->d_status);
+}
+
+void release_pages(dkv_layout *L) {
+    for (int layer = 0; layer < L->shape.n_layers; ++layer)
+        for (int b = 0; b < L->batch; ++b)
+            for (int p = 0; p < L->n_pages[b]; ++p)
+                give_back(pool_of(L, b, p), L->page_index[pt_index(L, layer, b, p)]);
+}
+
+char *host_page_ptr(const dkv_layout *L, int layer, int b, int p) {
+    const dkv_pool *pool = pool_of(L, b, p);
+    return pool->host_base + L->page_index[pt_index(L, layer, b, p)] * pool->page_bytes;
+}
+
+char *dev_page_ptr(const dkv_layout *L, int layer, int b, int p) {
+    const dkv_pool *pool = pool_of(L, b, p);
+    return pool->dev_base + L->page_index[pt_index(L, layer, b, p)] * pool->page_bytes;
+}
+
+int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, int32_t max_cap) {
+    if (const char *env = getenv("DKV_SPLIT_TOKENS")) {
+        const int v = atoi(env);
+        if (v >= DKV_PAGE_TOKENS && v % DKV_PAGE_TOKENS == 0) return v;
+    }
+    // Enough work items to spread over 256 CUs, each at most 512 tokens.
+    const int64_t max_cached = std::max(1, max_cap - 1);
+    int32_t t = 512;
+    while (t > DKV_PAGE_TOKENS &&
+           (int64_t)batch * n_kv_heads * ((max_cached + t - 1) / t) < 2048)
+        t /= 2;
+    return t;
+}
+
+// Parallel copy helper for host pages: runs f(first, last) over [0, n) in
+// contiguous chunks on up to 16 threads.
+template <class F>
+void parallel_for(int64_t n, F f) {
+    const int64_t nthreads = std::min<int64_t>(16, std::max<int64_t>(1, n / 64));
+    if (nthreads <= 1) {
+        f(0, n);
+        return;
+    }
+    std::vector<std::thread> ts;
+    const int64_t chunk = (n + nthreads - 1) / nthreads;
+    for (int64_t i = 0; i < nthreads; ++i) {
+        const int64_t a = i * chunk, e = std::min(n, a + chunk);
+        if (a < e) ts.emplace_back([=] { f(a, e); });
+    }
+    for (auto &t : ts) t.join();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dkv_last_error(void) { return g_last_error.c_str(); }
+
+int64_t kv_page_bytes(const dkv_shape *shape) {
+    return shape_ok(shape) ? page_bytes_of(shape) : 0;
+}
+
+int64_t kv_page_offset(const dkv_shape *shape, int32_t t, int32_t g, int32_t c, int32_t i) {
+    if (!shape_ok(shape)) return -1;
+    if (t < 0 || t >= DKV_PAGE_TOKENS || g < 0 || g >= shape->n_kv_heads || c < 0 || c > 1 || i < 0 ||
+        i >= shape->head_dim)
+        return -1;
+    return row_offset(shape, t, g, c) + (int64_t)i * 2;
+}
+
+dkv_status kv_placement(int32_t capacity_tokens, int32_t hbm_tail_tokens, int32_t *n_pages,
+                        int32_t *first_hbm_page) {
+    if (capacity_tokens <= 0 || hbm_tail_tokens < 0 || !n_pages || !first_hbm_page)
+        return fail(DKV_E_INVALID_ARG, "kv_placement: capacity must be > 0, tail >= 0, outputs non-null");
+    const int32_t P = (int32_t)(((int64_t)capacity_tokens + DKV_PAGE_TOKENS - 1) / DKV_PAGE_TOKENS);
+    const int32_t w = (int32_t)std::min<int64_t>(P, ((int64_t)hbm_tail_tokens + DKV_PAGE_TOKENS - 1) /
+                                                        DKV_PAGE_TOKENS);
+    *n_pages = P;
+    *first_hbm_page = P - w;
+    return DKV_OK;
+}
+
+dkv_status kv_alloc_host(const dkv_shape *shape, int64_t n_pages, uint32_t flags, dkv_pool **out) {
+    if (!out || !shape_ok(shape) || n_pages <= 0 || flags > DKV_HOST_NONCOHERENT)
+        return fail(DKV_E_INVALID_ARG, "kv_alloc_host: bad shape, n_pages, flags or null output");
+    const int64_t pb = page_bytes_of(shape);
+    const size_t bytes = (size_t)pb * (size_t)n_pages;
+    void *h = nullptr;
+    unsigned hflags = hipHostMallocMapped | hipHostMallocPortable |
+                      (flags == DKV_HOST_NONCOHERENT ? hipHostMallocNonCoherent : hipHostMallocCoherent);
+    hipError_t e = hipHostMalloc(&h, bytes, hflags);
+    if (e != hipSuccess || !h) {
+        (void)hipGetLastError();
+        return fail(DKV_E_OUT_OF_MEMORY, "kv_alloc_host: hipHostMalloc of %zu bytes failed: %s", bytes,
+                    hipGetErrorString(e));
+    }
+    void *d = nullptr;
+    e = hipHostGetDevicePointer(&d, h, 0);
+    if (e != hipSuccess || !d) {
+        (void)hipHostFree(h);
+        return hip_fail(e, "kv_alloc_host: hipHostGetDevicePointer");
+    }
+    dkv_pool *p = new dkv_pool();
+    p->shape = *shape;
+    p->tier = 0;
+    p->n_pages = n_pages;
+    p->page_bytes = pb;
+    p->host_base = static_cast<char *>(h);
+    p->dev_base = static_cast<char *>(d);
+    p->used.assign((size_t)n_pages, 0);
+    p->n_free = n_pages;
+    p->scan = 0;
+    p->n_layouts = 0;
+    *out = p;
+    return DKV_OK;
+}
+
+dkv_status kv_alloc_hbm(const dkv_shape *shape, int64_t n_pages, dkv_pool **out) {
+    if (!out || !shape_ok(shape) || n_pages <= 0)
+        return fail(DKV_E_INVALID_ARG, "kv_alloc_hbm: bad shape, n_pages or null output");
+    const int64_t pb = page_bytes_of(shape);
+    const size_t bytes = (size_t)pb * (size_t)n_pages;
+    void *d = nullptr;
+    hipError_t e = hipMalloc(&d, bytes);
+    if (e != hipSuccess || !d) {
+        (void)hipGetLastError();
+        return fail(DKV_E_OUT_OF_MEMORY, "kv_alloc_hbm: hipMalloc of %zu bytes failed: %s", bytes,
+                    hipGetErrorString(e));
+    }
+    dkv_pool *p = new dkv_pool();
+    p->shape = *shape;
+    p->tier = 1;
+    p->n_pages = n_pages;
+    p->page_bytes = pb;
+    p->host_base = nullptr;
+    p->dev_base = static_cast<char *>(d);
+    p->used.assign((size_t)n_pages, 0);
+    p->n_free = n_pages;
+    p->scan = 0;
+    p->n_layouts = 0;
+    *out = p;
+    return DKV_OK;
+}
+
+dkv_status kv_pool_free_pages(const dkv_pool *pool, int64_t *n_free) {
+    if (!pool || !n_free) return fail(DKV_E_INVALID_ARG, "kv_pool_free_pages: null argument");
+    *n_free = pool->n_free;
+    return DKV_OK;
+}
+
+dkv_status kv_pool_info(const dkv_pool *pool, void **device_base, int64_t *bytes, int32_t *tier) {
+    if (!pool) return fail(DKV_E_INVALID_ARG, "kv_pool_info: null pool");
+    if (device_base) *device_base = pool->dev_base;
+    if (bytes) *bytes = pool->n_pages * pool->page_bytes;
+    if (tier) *tier = pool->tier;
+    return DKV_OK;
+}
+
+dkv_status kv_pool_free(dkv_pool *pool) {
+    if (!pool) return DKV_OK;
+    if (pool->n_layouts > 0)
+        return fail(DKV_E_INVALID_ARG, "kv_pool_free: %lld layout(s) still use this pool",
+                    (long long)pool->n_layouts);
+    hipError_t e = pool->tier == 0 ? hipHostFree(pool->host_base) : hipFree(pool->dev_base);
+    delete pool;
+    if (e != hipSuccess) return hip_fail(e, "kv_pool_free");
+    return DKV_OK;
+}
+
+dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t *capacity_tokens,
+                            const int32_t *hbm_tail_tokens, dkv_pool *host_pool, dkv_pool *hbm_pool,
+                            dkv_layout **out) {
+    if (!out || !shape_ok(shape) || batch <= 0 || !capacity_tokens)
+        return fail(DKV_E_INVALID_ARG, "kv_layout_create: bad shape, batch or null argument");
+    if (!shape_supported(shape))
+        return fail(DKV_E_UNSUPPORTED,
+                    "kv_layout_create: head_dim must be 64/128, group 1/2/4/8, hidden a multiple of 512");
+    if (batch > 65535) return fail(DKV_E_INVALID_ARG, "kv_layout_create: batch > 65535");
+    for (dkv_pool *p : {host_pool, hbm_pool}) {
+        if (p && (p->shape.n_kv_heads != shape->n_kv_heads || p->shape.head_dim != shape->head_dim))
+            return fail(DKV_E_INVALID_ARG, "kv_layout_create: pool page shape differs from the layout's");
+    }
+    if (host_pool && host_pool->tier != 0) return fail(DKV_E_INVALID_ARG, "kv_layout_create: host_pool is HBM");
+    if (hbm_pool && hbm_pool->tier != 1) return fail(DKV_E_INVALID_ARG, "kv_layout_create: hbm_pool is host");
+
+    dkv_layout *L = new dkv_layout();
+    L->shape = *shape;
+    L->batch = batch;
+    L->capacity.assign(capacity_tokens, capacity_tokens + batch);
+    L->n_pages.resize(batch);
+    L->first_hbm.resize(batch);
+    L->host_pool = host_pool;
+    L->hbm_pool = hbm_pool;
+    int64_t need_host = 0, need_hbm = 0;
+    int32_t max_pages = 0, max_cap = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int32_t tail = hbm_tail_tokens ? hbm_tail_tokens[b] : 0;
+        if (kv_placement(capacity_tokens[b], tail, &L->n_pages[b], &L->first_hbm[b]) != DKV_OK) {
+            delete L;
+            return fail(DKV_E_INVALID_ARG, "kv_layout_create: sequence %d: capacity %d / hbm tail %d invalid",
+                        b, capacity_tokens[b], tail);
+        }
+        need_host += L->first_hbm[b];
+        need_hbm += L->n_pages[b] - L->first_hbm[b];
+        max_pages = std::max(max_pages, L->n_pages[b]);
+        max_cap = std::max(max_cap, capacity_tokens[b]);
+    }
+    need_host *= shape->n_layers;
+    need_hbm *= shape->n_layers;
+    if ((need_host > 0 && !host_pool) || (need_hbm > 0 && !hbm_pool)) {
+        delete L;
+        return fail(DKV_E_INVALID_ARG, "kv_layout_create: placement needs %lld host and %lld HBM pages but a pool is missing",
+                    (long long)need_host, (long long)need_hbm);
+    }
+    if ((host_pool && host_pool->n_free < need_host) || (hbm_pool && hbm_pool->n_free < need_hbm)) {
+        delete L;
+        return fail(DKV_E_CAPACITY, "kv_layout_create: needs %lld host / %lld HBM pages, pools have %lld / %lld free",
+                    (long long)need_host, (long long)need_hbm, (long long)(host_pool ? host_pool->n_free : 0),
+                    (long long)(hbm_pool ? hbm_pool->n_free : 0));
+    }
+    L->max_pages = max_pages;
+    L->split_tokens = choose_split_tokens(batch, shape->n_kv_heads, max_cap);
+    L->max_splits = std::max(1, (std::max(1, max_cap - 1) + L->split_tokens - 1) / L->split_tokens);
+
+    // Pages are taken in (layer, sequence, page) order, so each sequence's
+    // pages of a tier are consecutive in their pool when it is fresh.
+    const size_t n_entries = (size_t)shape->n_layers * batch * max_pages;
+    L->page_index.assign(n_entries, -1);
+    std::vector<uint64_t> table(n_entries, 0);
+    std::vector<int64_t> got;
+    for (int layer = 0; layer < shape->n_layers; ++layer) {
+        for (int b = 0; b < batch; ++b) {
+            for (int tier = 0; tier < 2; ++tier) {
+                const int p_lo = tier == 0 ? 0 : L->first_hbm[b];
+                const int p_hi = tier == 0 ? L->first_hbm[b] : L->n_pages[b];
+                if (p_hi <= p_lo) continue;
+                dkv_pool *pool = tier == 0 ? host_pool : hbm_pool;
+                take_pages(pool, p_hi - p_lo, got);   // counts were checked above
+                for (int p = p_lo; p < p_hi; ++p) {
+                    const int64_t idx = got[p - p_lo];
+                    L->page_index[pt_index(L, layer, b, p)] = idx;
+                    table[pt_index(L, layer, b, p)] = (uint64_t)(uintptr_t)(pool->dev_base + idx * pool->page_bytes);
+                }
+            }
+        }
+    }
+    if (host_pool) ++host_pool->n_layouts;
+    if (hbm_pool) ++hbm_pool->n_layouts;
+
+    auto cleanup = [&](dkv_status st) {
+        free_device(L);
+        release_pages(L);
+        if (host_pool) --host_pool->n_layouts;
+        if (hbm_pool) --hbm_pool->n_layouts;
+        delete L;
+        return st;
+    };
+    const int D = shape->head_dim, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads;
+    const size_t bytes_q = (size_t)batch * Hq * D * sizeof(float);
+    const size_t bytes_kv = (size_t)batch * Hkv * 2 * D * sizeof(uint16_t);
+    const size_t bytes_po = (size_t)batch * Hq * L->max_splits * D * sizeof(float);
+    const size_t bytes_ml = (size_t)batch * Hq * L->max_splits * sizeof(float2);
+    struct {
+        void **ptr;
+        size_t bytes;
+    } allocs[] = {{(void **)&L->d_page_table, n_entries * sizeof(uint64_t)},
+                  {(void **)&L->d_capacity, (size_t)batch * sizeof(int32_t)},
+                  {(void **)&L->d_q, bytes_q},
+                  {(void **)&L->d_kv_new, bytes_kv},
+                  {(void **)&L->d_part_o, bytes_po},
+                  {(void **)&L->d_part_ml, bytes_ml},
+                  {(void **)&L->d_status, 256}};
+    for (auto &a : allocs) {
+        if (hipMalloc(a.ptr, a.bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            *a.ptr = nullptr;
+            fail(DKV_E_OUT_OF_MEMORY, "kv_layout_create: hipMalloc of %zu bytes failed", a.bytes);
+            return cleanup(DKV_E_OUT_OF_MEMORY);
+        }
+    }
+    hipError_t e = hipMemcpy(L->d_page_table, table.data(), n_entries * sizeof(uint64_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(L->d_capacity, capacity_tokens, (size_t)batch * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(L->d_status, 0, 256);
+    if (e == hipSuccess) e = hipMemset(L->d_kv_new, 0, bytes_kv);
+    if (e != hipSuccess) {
+        hip_fail(e, "kv_layout_create: initialising device tables");
+        return cleanup(DKV_E_HIP);
+    }
+    *out = L;
+    return DKV_OK;
+}
+
+dkv_status kv_layout_free(dkv_layout *L) {
+    if (!L) return DKV_OK;
+    (void)hipDeviceSynchronize();
+    free_device(L);
+    release_pages(L);
+    if (L->host_pool) --L->host_pool->n_layouts;
+    if (L->hbm_pool) --L->hbm_pool->n_layouts;
+    delete L;
+    return DKV_OK;
+}
+
+dkv_status kv_layout_page_tier(const dkv_layout *L, int32_t seq, int32_t page, int32_t *tier) {
+    if (!L || !tier || seq < 0 || seq >= L->batch || page < 0 || page >= L->n_pages[seq])
+        return fail(DKV_E_INVALID_ARG, "kv_layout_page_tier: index out of range");
+    *tier = page >= L->first_hbm[seq] ? 1 : 0;
+    return DKV_OK;
+}
+
+int32_t kv_layout_split_tokens(const dkv_layout *L) { return L ? L->split_tokens : 0; }
+
+static dkv_status check_range(const dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n,
+                              const char *who) {
+    if (!L) return fail(DKV_E_INVALID_ARG, "%s: null layout", who);
+    if (layer < 0 || layer >= L->shape.n_layers || seq < 0 || seq >= L->batch || start < 0 || n < 0)
+        return fail(DKV_E_INVALID_ARG, "%s: layer/seq/start/n out of range", who);
+    if ((int64_t)start + n > L->capacity[seq])
+        return fail(DKV_E_CAPACITY, "%s: slots [%d, %lld) exceed capacity %d", who, start,
+                    (long long)start + n, L->capacity[seq]);
+    return DKV_OK;
+}
+
+dkv_status kv_append(dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n, const uint16_t *k,
+                     const uint16_t *v, dkv_stream_t stream) {
+    dkv_status st = check_range(L, layer, seq, start, n, "kv_append");
+    if (st != DKV_OK) return st;
+    if (n == 0) return DKV_OK;
+    if (!k || !v) return fail(DKV_E_INVALID_ARG, "kv_append: null k or v");
+    const dkv_shape *s = &L->shape;
+    const int D = s->head_dim, Hkv = s->n_kv_heads;
+    const size_t row = (size_t)D * 2;
+    const size_t tok_elems = (size_t)Hkv * D;
+    const int p_first = start / DKV_PAGE_TOKENS, p_last = (start + n - 1) / DKV_PAGE_TOKENS;
+
+    // Host pages: the CPU writes them in place, page by page, in parallel.
+    parallel_for(p_last - p_first + 1, [&](int64_t i0, int64_t i1) {
+        for (int64_t i = i0; i < i1; ++i) {
+            const int p = p_first + (int)i;
+            if (pool_of(L, seq, p)->tier != 0) continue;
+            char *page = host_page_ptr(L, layer, seq, p);
+            const int t_lo = std::max(start, p * DKV_PAGE_TOKENS);
+            const int t_hi = std::min(start + n, (p + 1) * DKV_PAGE_TOKENS);
+            for (int t = t_lo; t < t_hi; ++t)
+                for (int g = 0; g < Hkv; ++g) {
+                    const size_t src = (size_t)(t - start) * tok_elems + (size_t)g * D;
+                    memcpy(page + row_offset(s, t % DKV_PAGE_TOKENS, g, 0), k + src, row);
+                    memcpy(page + row_offset(s, t % DKV_PAGE_TOKENS, g, 1), v + src, row);
+                }
+        }
+    });
+
+    // HBM pages: assemble each touched page on the host (reading it back
+    // first when only part of it is written) and copy it in.
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    std::vector<char> img;
+    for (int p = std::max(p_first, L->first_hbm[seq]); p <= p_last; ++p) {
+        const size_t pb = (size_t)L->hbm_pool->page_bytes;
+        img.resize(pb);
+        char *dpage = dev_page_ptr(L, layer, seq, p);
+        const int t_lo = std::max(start, p * DKV_PAGE_TOKENS);
+        const int t_hi = std::min(start + n, (p + 1) * DKV_PAGE_TOKENS);
+        if (t_hi - t_lo < DKV_PAGE_TOKENS) {
+            HIP_TRY(hipMemcpyAsync(img.data(), dpage, pb, hipMemcpyDeviceToHost, hs));
+            HIP_TRY(hipStreamSynchronize(hs));
+        }
+        for (int t = t_lo; t < t_hi; ++t)
+            for (int g = 0; g < Hkv; ++g) {
+                const size_t src = (size_t)(t - start) * tok_elems + (size_t)g * D;
+                memcpy(img.data() + row_offset(s, t % DKV_PAGE_TOKENS, g, 0), k + src, row);
+                memcpy(img.data() + row_offset(s, t % DKV_PAGE_TOKENS, g, 1), v + src, row);
+            }
+        HIP_TRY(hipMemcpyAsync(dpage, img.data(), pb, hipMemcpyHostToDevice, hs));
+        HIP_TRY(hipStreamSynchronize(hs));
+    }
+    return DKV_OK;
+}
+
+dkv_status kv_read(const dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n, uint16_t *k_out,
+                   uint16_t *v_out) {
+    dkv_status st = check_range(L, layer, seq, start, n, "kv_read");
+    if (st != DKV_OK) return st;
+    if (n == 0) return DKV_OK;
+    if (!k_out || !v_out) return fail(DKV_E_INVALID_ARG, "kv_read: null output");
+    HIP_TRY(hipDeviceSynchronize());
+    const dkv_shape *s = &L->shape;
+    const int D = s->head_dim, Hkv = s->n_kv_heads;
+    const size_t row = (size_t)D * 2;
+    const size_t tok_elems = (size_t)Hkv * D;
+    std::vector<char> img;
+    const int p_first = start / DKV_PAGE_TOKENS, p_last = (start + n - 1) / DKV_PAGE_TOKENS;
+    for (int p = p_first; p <= p_last; ++p) {
+        const dkv_pool *pool = pool_of(L, seq, p);
+        const char *page;
+        if (pool->tier == 0) {
+            page = host_page_ptr(L, layer, seq, p);
+        } else {
+            img.resize((size_t)pool->page_bytes);
+            HIP_TRY(hipMemcpy(img.data(), dev_page_ptr(L, layer, seq, p), img.size(), hipMemcpyDeviceToHost));
+            page = img.data();
+        }
+        const int t_lo = std::max(start, p * DKV_PAGE_TOKENS);
+        const int t_hi = std::min(start + n, (p + 1) * DKV_PAGE_TOKENS);
+        for (int t = t_lo; t < t_hi; ++t)
+            for (int g = 0; g < Hkv; ++g) {
+                const size_t dst = (size_t)(t - start) * tok_elems + (size_t)g * D;
+                memcpy(k_out + dst, page + row_offset(s, t % DKV_PAGE_TOKENS, g, 0), row);
+                memcpy(v_out + dst, page + row_offset(s, t % DKV_PAGE_TOKENS, g, 1), row);
+            }
+    }
+    return DKV_OK;
+}
+
+static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, const uint16_t *W,
+                            const int32_t *ctx_lens, void *out, int out_f32, dkv_stream_t stream,
+                            const char *who) {
+    if (!L) return fail(DKV_E_INVALID_ARG, "%s: null layout", who);
+    if (layer < 0 || layer >= L->shape.n_layers) return fail(DKV_E_INVALID_ARG, "%s: layer %d out of range", who, layer);
+    if (!q_in || !W || !ctx_lens || !out) return fail(DKV_E_INVALID_ARG, "%s: null pointer argument", who);
+    if (((uintptr_t)q_in | (uintptr_t)W) & 15u)
+        return fail(DKV_E_INVALID_ARG, "%s: q_in and W_qkv must be 16-byte aligned", who);
+    if (((uintptr_t)ctx_lens & 3u) || ((uintptr_t)out & (out_f32 ? 3u : 1u)))
+        return fail(DKV_E_INVALID_ARG, "%s: misaligned ctx_lens or attn_out", who);
+    const dkv_shape *s = &L->shape;
+    dkv::StepArgs a{};
+    a.batch = L->batch;
+    a.hidden = s->hidden;
+    a.n_q_heads = s->n_q_heads;
+    a.n_kv_heads = s->n_kv_heads;
+    a.head_dim = s->head_dim;
+    a.n_qkv = (s->n_q_heads + 2 * s->n_kv_heads) * s->head_dim;
+    a.max_pages = L->max_pages;
+    a.split_tokens = L->split_tokens;
+    a.max_splits = L->max_splits;
+    a.qscale = (float)(1.4426950408889634074 / std::sqrt((double)s->head_dim));
+    a.page_table = L->d_page_table + (size_t)layer * L->batch * L->max_pages;
+    a.capacity = L->d_capacity;
+    a.x = q_in;
+    a.w = W;
+    a.ctx_lens = ctx_lens;
+    a.out = out;
+    a.out_f32 = out_f32;
+    a.q = L->d_q;
+    a.kv_new = L->d_kv_new;
+    a.part_o = L->d_part_o;
+    a.part_ml = L->d_part_ml;
+    a.status = L->d_status;
+    hipError_t e = dkv::launch_decode_step(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, who);
+    return DKV_OK;
+}
+
+dkv_status decode_step(dkv_layout *L, int32_t layer, const uint16_t *q_in, const uint16_t *W_qkv,
+                       const int32_t *ctx_lens, uint16_t *attn_out, dkv_stream_t stream) {
+    return step_impl(L, layer, q_in, W_qkv, ctx_lens, attn_out, 0, stream, "decode_step");
+}
+
+dkv_status decode_step_f32(dkv_layout *L, int32_t layer, const uint16_t *q_in, const uint16_t *W_qkv,
+                           const int32_t *ctx_lens, float *attn_out, dkv_stream_t stream) {
+    return step_impl(L, layer, q_in, W_qkv, ctx_lens, attn_out, 1, stream, "decode_step_f32");
+}
+
+dkv_status kv_layout_check_status(dkv_layout *L) {
+    if (!L) return fail(DKV_E_INVALID_ARG, "kv_layout_check_status: null layout");
+    HIP_TRY(hipDeviceSynchronize());
+    uint32_t flag = 0;
+    HIP_TRY(hipMemcpy(&flag, L->d_status, sizeof flag, hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemset(L->d_status, 0, sizeof flag));
+    if (flag & 1u)
+        return fail(DKV_E_CAPACITY, "decode_step: a ctx_lens entry was outside [0, capacity - 1]");
+    return DKV_OK;
+}
+
+dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid, int32_t unroll, int32_t reps,
+                                 float *ms_median) {
+    if (!ptr || !ms_median || bytes == 0 || bytes % 16 || ((uintptr_t)ptr & 15u) || grid <= 0 || reps <= 0 ||
+        !(unroll == 1 || unroll == 2 || unroll == 4 || unroll == 8))
+        return fail(DKV_E_INVALID_ARG, "dkv_probe_stream_read: bad argument");
+    hipStream_t st;
+    HIP_TRY(hipStreamCreate(&st));
+    uint32_t *sink = nullptr;
+    hipEvent_t e0, e1;
+    std::vector<float> ts;
+    hipError_t e = hipMalloc(&sink, 64);
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    if (e == hipSuccess) e = dkv::launch_stream_read(ptr, bytes, grid, unroll, sink, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    for (int r = 0; r < reps && e == hipSuccess; ++r) {
+        e = hipEventRecord(e0, st);
+        if (e == hipSuccess) e = dkv::launch_stream_read(ptr, bytes, grid, unroll, sink, st);
+        if (e == hipSuccess) e = hipEventRecord(e1, st);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+        ts.push_back(ms);
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    (void)hipFree(sink);
+    (void)hipStreamDestroy(st);
+    if (e != hipSuccess) return hip_fail(e, "dkv_probe_stream_read");
+    std::sort(ts.begin(), ts.end());
+    *ms_median = ts[ts.size() / 2];
+    return DKV_OK;
+}
+
+}  // extern "C"

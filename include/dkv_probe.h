@@ -1,0 +1,41 @@
+/*
+ * dkv_probe.h -- measurement helpers of the zero-copy decode-attention
+ * library: the streaming-read ceiling of a memory region as seen by a GPU
+ * kernel, used as the denominator of the host-link roofline.
+ *
+ * The pages put the bottleneck of direct CPU-memory access on sustained link
+ * bandwidth ("KV Cache 内存层级" overview, 2.1 去搬运：DirectKV: on a fast
+ * link the deciding factor becomes sustained bandwidth, not single-access
+ * latency) and warn that on PCIe-only platforms the kernel cannot beat the
+ * physical link (DirectKV digest, 核心方法). This probe measures that link.
+ */
+#ifndef DKV_PROBE_H
+#define DKV_PROBE_H
+
+#include <stdint.h>
+
+#include "dkv.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Device address, size in bytes and tier (0 host, 1 HBM) of a pool's
+ * memory. Any output pointer may be NULL. */
+dkv_status kv_pool_info(const dkv_pool *pool, void **device_base, int64_t *bytes,
+                        int32_t *tier);
+
+/* Times a streaming read of `bytes` bytes at device address `ptr` (host
+ * mapped memory or HBM): a grid-stride kernel of `grid` x 256 threads,
+ * 16-byte loads, `unroll` (1, 2, 4 or 8) loads in flight per thread. One
+ * warm-up run, then `reps` timed runs on a private stream; *ms_median gets
+ * the median in milliseconds. Synchronous. bytes must be a multiple of 16
+ * and ptr 16-byte aligned. */
+dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid,
+                                 int32_t unroll, int32_t reps, float *ms_median);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DKV_PROBE_H */

@@ -25,3 +25,10 @@ def gpu_available() -> bool:
 def oracle():
     import oracle as oracle_pkg
     return oracle_pkg.default()
+
+
+@pytest.fixture(scope="session")
+def golden():
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "page_facts.json")) as f:
+        return json.load(f)
