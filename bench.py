@@ -1,0 +1,269 @@
+"""Decode-step benchmark: effective KV bandwidth of one zero-copy decode step.
+
+Workload (default): Llama-3-8B-shaped layer (hidden 4096, 32 query / 8 KV
+heads, head_dim 128), batch 8, 32768 cached tokens per sequence, KV 100 % in
+host-pinned memory read in place over the host link; synthetic bf16 inputs
+from the seeded generator (W ~ N(0, 0.02^2), x and K/V ~ N(0, 1)).
+
+A step is one decode_step call: QKV projection, attention over every cached
+token plus the fresh one, fresh K/V write-back, split combine. Inputs are
+resident (KV in its pool, x/W in HBM) before the timed region starts.
+
+Prints one JSON line: metric/value (effective KV GB/s = algorithmic KV bytes
+per step / step time), ms_per_step, roofline (dominant kernel = split
+attention, against the host link), the measured host-link streaming-read
+ceiling, the same step with every page in HBM (against 8 TB/s), and the fp64
+oracle timed on the host cores on the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PCIE_GEN5_X16_GBPS = 64.0     # published per-direction rate of the MI355X host interface
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+
+
+def log(msg):
+    print("[bench %s] %s" % (time.strftime("%H:%M:%S"), msg), file=sys.stderr, flush=True)
+
+
+class Resident:
+    """One workload's KV in a pool (host or HBM), plus x, W, ctx_lens in HBM."""
+
+    def __init__(self, dkv, wl, K_all, V_all, ctx, hbm_tail):
+        import torch
+        self.dkv = dkv
+        self.shape = dkv.Shape.of(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, 1)
+        cap = (ctx + 1).astype(np.int32)
+        tail = np.full(len(ctx), hbm_tail, np.int32)
+        n_host = n_hbm = 0
+        for b in range(len(ctx)):
+            n, first = dkv.kv_placement(int(cap[b]), int(tail[b]))
+            n_host += first
+            n_hbm += n - first
+        self.host_pool = dkv.kv_alloc_host(self.shape, n_host) if n_host else None
+        self.hbm_pool = dkv.kv_alloc_hbm(self.shape, n_hbm) if n_hbm else None
+        self.n_host, self.n_hbm = n_host, n_hbm
+        self.layout = dkv.kv_layout_create(self.shape, cap, tail, self.host_pool, self.hbm_pool)
+        for b in range(len(ctx)):
+            dkv.kv_append(self.layout, 0, b, 0, K_all[b, :ctx[b]], V_all[b, :ctx[b]])
+        dev = torch.device("cuda", 0)
+        self.x = torch.from_numpy(wl.x(0).view(np.int16)).to(dev).view(torch.bfloat16)
+        self.W = torch.from_numpy(wl.W(0).view(np.int16)).to(dev).view(torch.bfloat16)
+        self.ctx = torch.from_numpy(ctx.copy()).to(dev)
+        self.out = torch.empty((len(ctx), wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16,
+                               device=dev)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self):
+        self.dkv.decode_step(self.layout, 0, self.x, self.W, self.ctx, self.out, self.stream)
+
+    def timed(self, steps, warmup):
+        """Milliseconds per step over `steps` steps (HIP events on the step's stream)."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(steps):
+            self.step()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def kernel_times(self, steps):
+        """Average per-kernel milliseconds from events the library records
+        around each kernel on the step's stream."""
+        import torch
+        self.layout.timing_enable(True, steps)
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        t = self.layout.timing_read()
+        self.layout.timing_enable(False)
+        n = max(1, t["steps"])
+        return {k: t[k] / n for k in ("projection", "split", "combine")}
+
+    def free(self):
+        import torch
+        torch.cuda.synchronize()
+        self.layout.free()
+        for p in (self.host_pool, self.hbm_pool):
+            if p:
+                p.free()
+
+
+def probe_ceiling(dkv, pool, configs_):
+    base, nbytes, _ = pool.info()
+    nbytes -= nbytes % (1 << 20)
+    best = 0.0
+    rows = []
+    for grid, unroll in configs_:
+        ms = dkv.probe_stream_read(base, nbytes, grid, unroll, reps=3)
+        gbps = nbytes / ms / 1e6
+        rows.append({"grid": grid, "unroll": unroll, "GBps": round(gbps, 2)})
+        best = max(best, gbps)
+    return best, rows, nbytes
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3-8b-b8-ctx32768-host")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm-leg", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="only the timed host-placement leg (for rocprofv3 runs)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the decode path runs on one MI355X and this build "
+              "launches nothing on a second GPU (--gpus %d is not supported)." % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import decode_attention_zero_amd as dkv
+    from synth import configs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = configs.BY_NAME[args.workload]
+    if wl.n_layers != 1:
+        raise SystemExit("the bench workload must be a single layer")
+    ctx = wl.ctx_lens()
+    B, Hkv, d = wl.batch, wl.n_kv_heads, wl.head_dim
+    Lmax = int(ctx.max())
+    log("generating inputs for %s" % wl.name)
+    K_all = np.zeros((B, Lmax, Hkv, d), np.uint16)
+    V_all = np.zeros_like(K_all)
+    for b in range(B):
+        wl.kv("k", 0, b, 0, int(ctx[b]), out=K_all[b, :ctx[b]])
+        wl.kv("v", 0, b, 0, int(ctx[b]), out=V_all[b, :ctx[b]])
+
+    kv_bytes = int(ctx.astype(np.int64).sum()) * wl.kv_bytes_per_token
+    w_bytes = wl.n_qkv * wl.hidden * 2
+    step_bytes = kv_bytes + w_bytes + B * wl.hidden * 2 + B * Hkv * d * 4 + B * wl.n_q_heads * d * 2
+
+    result = {}
+    # ------------------------------------------------------------------ host placement
+    log("host-placement leg")
+    r = Resident(dkv, wl, K_all, V_all, ctx, wl.hbm_tail_tokens if wl.hbm_fraction is None else 0)
+    host_kv = r.n_host * dkv.kv_page_bytes(r.shape)
+    ms = r.timed(args.steps, args.warmup)
+    kt = r.kernel_times(args.steps)
+    out_host = r.out.view(torch.int16).cpu().numpy().view(np.uint16)
+    ceiling = ceiling_rows = None
+    if not args.profile_run and r.host_pool is not None:
+        ceiling, ceiling_rows, probe_bytes = probe_ceiling(
+            dkv, r.host_pool, [(64, 1), (256, 1), (512, 1), (1024, 2), (2048, 2)])
+    r.free()
+    log("host leg: %.3f ms/step, split kernel %.3f ms" % (ms, kt["split"]))
+
+    value = kv_bytes / (ms * 1e-3) / 1e9
+    split_gbps = kv_bytes / (kt["split"] * 1e-3) / 1e9
+    if args.profile_run:
+        print(json.dumps({"profile_run": True, "ms_per_step": ms, "kernel_ms": kt}), flush=True)
+        return 0
+
+    # ------------------------------------------------------------------ HBM placement
+    hbm = None
+    out_hbm = None
+    if not args.no_hbm_leg:
+        log("HBM-placement leg")
+        r = Resident(dkv, wl, K_all, V_all, ctx, 1 << 30)
+        ms_h = r.timed(max(args.steps, 50), args.warmup)
+        kt_h = r.kernel_times(max(args.steps, 50))
+        hbm_ceiling, _, _ = probe_ceiling(dkv, r.hbm_pool, [(2048, 4), (4096, 4), (8192, 8)])
+        out_hbm = r.out.view(torch.int16).cpu().numpy().view(np.uint16)
+        r.free()
+        hbm = {
+            "ms_per_step": round(ms_h, 4),
+            "kv_GBps": round(kv_bytes / (ms_h * 1e-3) / 1e9, 1),
+            "split_kernel_ms": round(kt_h["split"], 4),
+            "split_kernel_GBps": round(kv_bytes / (kt_h["split"] * 1e-3) / 1e9, 1),
+            "split_kernel_frac_of_8TBps": round(kv_bytes / (kt_h["split"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "kernel_ms": {k: round(v, 4) for k, v in kt_h.items()},
+            "measured_hbm_read_GBps": round(hbm_ceiling, 1),
+            "bit_identical_to_host_placement": bool(np.array_equal(out_host, out_hbm)),
+        }
+        log("HBM leg: %.4f ms/step, split kernel %.1f GB/s" % (ms_h, hbm["split_kernel_GBps"]))
+
+    # ------------------------------------------------------------------ CPU oracle
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.default()
+        threads = oracle.DEFAULT_THREADS
+        log("oracle on %d threads (full step)" % threads)
+        x = wl.x(0)
+        W = wl.W(0)
+        t0 = time.perf_counter()
+        ref = orc.decode_step(x, W, ctx, K_all, V_all, wl.n_q_heads, Hkv, d, threads=threads)
+        t_cpu = time.perf_counter() - t0
+        cpu = {"value": round(kv_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": threads,
+               "kind": "oracle", "seconds": round(t_cpu, 2),
+               "sample": "one full step of the bench workload (all %d sequences x %d query heads, "
+                         "%d KV bytes), fp64, plain C + OpenMP" % (B, wl.n_q_heads, kv_bytes)}
+        got = (out_host.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        err = np.abs(got - ref["attn_out"])
+        parity = {"max_abs": float(err.max()),
+                  "rel_l2": float(np.linalg.norm(got - ref["attn_out"]) /
+                                  np.linalg.norm(ref["attn_out"])),
+                  "gates": {"max_abs": 2e-2, "rel_l2": 5e-3}}
+
+    t_star = max(host_kv / (ceiling * 1e9) if ceiling else 0.0,
+                 (kv_bytes - min(kv_bytes, host_kv)) / (HBM_PEAK_GBPS * 1e9))
+    result = {
+        "metric": "effective KV GB/s per decode step (% of host-link+HBM roofline); step latency",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "ctx_tokens": int(ctx[0]),
+                   "hidden": wl.hidden, "q_heads": wl.n_q_heads, "kv_heads": Hkv,
+                   "head_dim": d, "kv_placement": "100% host-pinned, read in place",
+                   "kv_bytes_per_step": kv_bytes, "algorithmic_bytes_per_step": step_bytes},
+        "roofline": {"bound": "host_link", "kernel": "attn_split_kernel",
+                     "achieved": round(split_gbps, 3), "peak": PCIE_GEN5_X16_GBPS,
+                     "unit": "GB/s", "frac": round(split_gbps / PCIE_GEN5_X16_GBPS, 4),
+                     "traffic": None,
+                     "measured_ceiling_GBps": round(ceiling, 3) if ceiling else None,
+                     "frac_of_measured_ceiling": round(split_gbps / ceiling, 4) if ceiling else None,
+                     "split_kernel_ms": round(kt["split"], 4)},
+        "combined_roofline": {"t_star_ms": round(t_star * 1e3, 4),
+                              "frac": round(t_star * 1e3 / ms, 4) if t_star else None},
+        "kernel_ms": {k: round(v, 4) for k, v in kt.items()},
+        "host_link_probe": ceiling_rows,
+        "hbm_placement": hbm,
+        "parity": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

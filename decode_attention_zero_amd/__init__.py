@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
             "decode_step": ([P, I32, P, P, P, P, P], I32),
             "decode_step_f32": ([P, I32, P, P, P, P, P], I32),
             "dkv_probe_stream_read": ([P, ctypes.c_uint64, I32, I32, I32, P], I32),
+            "kv_layout_timing_enable": ([P, I32, I32], I32),
+            "kv_layout_timing_read": ([P, P, P, P, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -98,7 +100,7 @@ EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement",
             "kv_alloc_hbm", "kv_pool_free_pages", "kv_pool_info", "kv_pool_free",
             "kv_layout_create", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
             "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
-            "dkv_probe_stream_read"]
+            "dkv_probe_stream_read", "kv_layout_timing_enable", "kv_layout_timing_read"]
 
 
 def _check(status: int) -> None:
@@ -193,6 +195,17 @@ class Layout:
 
     def check_status(self) -> None:
         _check(lib().kv_layout_check_status(self.handle))
+
+    def timing_enable(self, enable: bool = True, max_steps: int = 1024) -> None:
+        _check(lib().kv_layout_timing_enable(self.handle, 1 if enable else 0, max_steps))
+
+    def timing_read(self) -> dict:
+        """Summed per-kernel milliseconds and the step count since the last read."""
+        p, s, c = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        n = ctypes.c_int32()
+        _check(lib().kv_layout_timing_read(self.handle, ctypes.byref(p), ctypes.byref(s),
+                                           ctypes.byref(c), ctypes.byref(n)))
+        return {"projection": p.value, "split": s.value, "combine": c.value, "steps": n.value}
 
     def free(self) -> None:
         if self.handle:

@@ -42,8 +42,10 @@ struct StepArgs {
     uint32_t *status;         // range flag (bit 0: a ctx_lens entry out of range)
 };
 
-// Enqueues the decode step's kernels on `stream`.
-hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream);
+// Enqueues the decode step's kernels on `stream`. With `events` non-null,
+// records events[0] before the projection, events[1] after it, events[2]
+// after the split attention and events[3] after the combine.
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream, hipEvent_t *events);
 
 // Streaming-read probe (grid-stride, 16 B per lane per load).
 hipError_t launch_stream_read(const void *ptr, uint64_t bytes, int grid, int unroll,

@@ -410,20 +410,21 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(StepArgs a) {
 }
 
 template <int D, int G>
-void launch_attention(const StepArgs &a, hipStream_t st) {
+void launch_attention(const StepArgs &a, hipStream_t st, hipEvent_t *ev) {
     dim3 grid_split(a.max_splits, a.n_kv_heads, a.batch);
     attn_split_kernel<D, G><<<grid_split, 64, 0, st>>>(a);
+    if (ev) (void)hipEventRecord(ev[2], st);
     attn_combine_kernel<D, G><<<a.batch * a.n_q_heads, 64, 0, st>>>(a);
+    if (ev) (void)hipEventRecord(ev[3], st);
 }
 
 template <int D>
-bool dispatch_group(const StepArgs &a, int G, hipStream_t st) {
+void dispatch_group(const StepArgs &a, int G, hipStream_t st, hipEvent_t *ev) {
     switch (G) {
-        case 1: launch_attention<D, 1>(a, st); return true;
-        case 2: launch_attention<D, 2>(a, st); return true;
-        case 4: launch_attention<D, 4>(a, st); return true;
-        case 8: launch_attention<D, 8>(a, st); return true;
-        default: return false;
+        case 1: launch_attention<D, 1>(a, st, ev); break;
+        case 2: launch_attention<D, 2>(a, st, ev); break;
+        case 4: launch_attention<D, 4>(a, st, ev); break;
+        default: launch_attention<D, 8>(a, st, ev); break;
     }
 }
 
@@ -449,15 +450,17 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
 
 }  // namespace
 
-hipError_t launch_decode_step(const StepArgs &a, hipStream_t st) {
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t st, hipEvent_t *ev) {
     constexpr int BT = 8;
+    const int G = a.n_q_heads / a.n_kv_heads;
+    if (!((a.head_dim == 128 || a.head_dim == 64) && (G == 1 || G == 2 || G == 4 || G == 8)))
+        return hipErrorInvalidValue;
+    if (ev) (void)hipEventRecord(ev[0], st);
     dim3 grid_proj((a.n_qkv + 15) / 16, (a.batch + BT - 1) / BT);
     qkv_proj_kernel<BT><<<grid_proj, 256, 0, st>>>(a);
-    const int G = a.n_q_heads / a.n_kv_heads;
-    bool ok = false;
-    if (a.head_dim == 128) ok = dispatch_group<128>(a, G, st);
-    else if (a.head_dim == 64) ok = dispatch_group<64>(a, G, st);
-    if (!ok) return hipErrorInvalidValue;
+    if (ev) (void)hipEventRecord(ev[1], st);
+    if (a.head_dim == 128) dispatch_group<128>(a, G, st, ev);
+    else dispatch_group<64>(a, G, st, ev);
     return hipGetLastError();
 }
 

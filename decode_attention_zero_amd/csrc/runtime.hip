@@ -96,6 +96,9 @@ struct dkv_layout {
     float *d_part_o;
     float2 *d_part_ml;
     uint32_t *d_status;
+    // per-kernel timing (measurement mode only)
+    std::vector<hipEvent_t> timing_events;   // 4 per recorded step
+    int32_t timing_recorded = 0;
 };
 
 namespace {
@@ -431,9 +434,43 @@ dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t
     return DKV_OK;
 }
 
+dkv_status kv_layout_timing_enable(dkv_layout *L, int32_t enable, int32_t max_steps) {
+    if (!L || (enable && max_steps <= 0)) return fail(DKV_E_INVALID_ARG, "kv_layout_timing_enable: bad argument");
+    HIP_TRY(hipDeviceSynchronize());
+    for (hipEvent_t e : L->timing_events) (void)hipEventDestroy(e);
+    L->timing_events.clear();
+    L->timing_recorded = 0;
+    if (!enable) return DKV_OK;
+    L->timing_events.resize((size_t)max_steps * 4);
+    for (auto &e : L->timing_events) HIP_TRY(hipEventCreate(&e));
+    return DKV_OK;
+}
+
+dkv_status kv_layout_timing_read(dkv_layout *L, double *ms_proj, double *ms_split, double *ms_combine,
+                                 int32_t *n_steps) {
+    if (!L) return fail(DKV_E_INVALID_ARG, "kv_layout_timing_read: null layout");
+    HIP_TRY(hipDeviceSynchronize());
+    double sum[3] = {0.0, 0.0, 0.0};
+    for (int32_t i = 0; i < L->timing_recorded; ++i) {
+        hipEvent_t *ev = &L->timing_events[(size_t)i * 4];
+        for (int k = 0; k < 3; ++k) {
+            float ms = 0.0f;
+            HIP_TRY(hipEventElapsedTime(&ms, ev[k], ev[k + 1]));
+            sum[k] += ms;
+        }
+    }
+    if (ms_proj) *ms_proj = sum[0];
+    if (ms_split) *ms_split = sum[1];
+    if (ms_combine) *ms_combine = sum[2];
+    if (n_steps) *n_steps = L->timing_recorded;
+    L->timing_recorded = 0;
+    return DKV_OK;
+}
+
 dkv_status kv_layout_free(dkv_layout *L) {
     if (!L) return DKV_OK;
     (void)hipDeviceSynchronize();
+    for (hipEvent_t e : L->timing_events) (void)hipEventDestroy(e);
     free_device(L);
     release_pages(L);
     if (L->host_pool) --L->host_pool->n_layouts;
@@ -586,7 +623,10 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     a.part_o = L->d_part_o;
     a.part_ml = L->d_part_ml;
     a.status = L->d_status;
-    hipError_t e = dkv::launch_decode_step(a, reinterpret_cast<hipStream_t>(stream));
+    hipEvent_t *ev = nullptr;
+    if (!L->timing_events.empty() && (size_t)(L->timing_recorded + 1) * 4 <= L->timing_events.size())
+        ev = &L->timing_events[(size_t)L->timing_recorded++ * 4];
+    hipError_t e = dkv::launch_decode_step(a, reinterpret_cast<hipStream_t>(stream), ev);
     if (e != hipSuccess) return hip_fail(e, who);
     return DKV_OK;
 }

@@ -34,6 +34,19 @@ dkv_status kv_pool_info(const dkv_pool *pool, void **device_base, int64_t *bytes
 dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid,
                                  int32_t unroll, int32_t reps, float *ms_median);
 
+/* Per-kernel timing of a layout's decode steps. While enabled, decode_step
+ * records HIP events on its stream before and after each of its kernels
+ * (projection, split attention, combine) for up to max_steps steps; enabling
+ * creates those events, so do it outside graph capture. Disabling (enable =
+ * 0) destroys them. */
+dkv_status kv_layout_timing_enable(dkv_layout *layout, int32_t enable, int32_t max_steps);
+
+/* Synchronises, then returns the milliseconds each kernel took summed over
+ * the steps recorded since the last read (*n_steps of them), and restarts
+ * the count. Any output pointer may be NULL. */
+dkv_status kv_layout_timing_read(dkv_layout *layout, double *ms_projection, double *ms_split,
+                                 double *ms_combine, int32_t *n_steps);
+
 #ifdef __cplusplus
 }
 #endif
