@@ -119,6 +119,43 @@ def probe_ceiling(dkv, pool, configs_):
     return best, rows, nbytes
 
 
+def counter_traffic(workload: str):
+    """HBM + host-link bytes per split-kernel launch from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a copy kernel of known
+    size); None when the summary is missing or the kernel source has changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_split_%s_traffic.json" % workload)
+    src = os.path.join(ROOT, "decode_attention_zero_amd", "csrc", "kernels.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("kernels_hip_sha256") != sha:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def calibrate(dkv, r):
+    """Kernels whose HBM / host traffic is known exactly, for counter scaling."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)                    # reads 256 MiB, writes 256 MiB of HBM
+    torch.cuda.synchronize()
+    base, nbytes, _ = r.host_pool.info()
+    dkv.probe_stream_read(base, 1 << 30, 256, 1, reps=1)        # 2 x 1 GiB host reads
+    dkv.probe_stream_read(dst.data_ptr(), n, 2048, 4, reps=1)   # 2 x 256 MiB HBM reads
+    torch.cuda.synchronize()
+    log("calibration kernels done")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +166,10 @@ def main(argv=None):
     ap.add_argument("--no-hbm-leg", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the timed host-placement leg (for rocprofv3 runs)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="with --profile-run: also run kernels of known traffic (a 256 MiB "
+                         "HBM-to-HBM copy, 1 GiB streaming reads of the host pool and of HBM) "
+                         "to scale counter readings")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the decode path runs on one MI355X and this build "
@@ -166,6 +207,8 @@ def main(argv=None):
     host_kv = r.n_host * dkv.kv_page_bytes(r.shape)
     ms = r.timed(args.steps, args.warmup)
     kt = r.kernel_times(args.steps)
+    if args.profile_run and args.calibrate:
+        calibrate(dkv, r)
     out_host = r.out.view(torch.int16).cpu().numpy().view(np.uint16)
     ceiling = ceiling_rows = None
     if not args.profile_run and r.host_pool is not None:
@@ -249,7 +292,7 @@ def main(argv=None):
         "roofline": {"bound": "host_link", "kernel": "attn_split_kernel",
                      "achieved": round(split_gbps, 3), "peak": PCIE_GEN5_X16_GBPS,
                      "unit": "GB/s", "frac": round(split_gbps / PCIE_GEN5_X16_GBPS, 4),
-                     "traffic": None,
+                     "traffic": counter_traffic(wl.name),
                      "measured_ceiling_GBps": round(ceiling, 3) if ceiling else None,
                      "frac_of_measured_ceiling": round(split_gbps / ceiling, 4) if ceiling else None,
                      "split_kernel_ms": round(kt["split"], 4)},
