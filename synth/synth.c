@@ -53,22 +53,35 @@ static void block_words(uint64_t seed, uint32_t tensor, uint32_t stream,
     synth_philox4x32_10(ctr, key, w);
 }
 
+/* The four standard normals of Philox block blk: Box-Muller of word pairs
+ * (0, 1) -> elements 0 (cos) and 1 (sin), (2, 3) -> elements 2 and 3. */
+static void normal_block(uint64_t seed, uint32_t tensor, uint32_t stream, uint64_t blk,
+                         double z[4])
+{
+    uint32_t w[4];
+    block_words(seed, tensor, stream, blk, w);
+    for (int pair = 0; pair < 2; ++pair) {
+        const double u1 = ((double)w[2 * pair] + 1.0) * (1.0 / 4294967296.0);  /* (0, 1] */
+        const double u2 = (double)w[2 * pair + 1] * (1.0 / 4294967296.0);      /* [0, 1) */
+        const double r = sqrt(-2.0 * log(u1));
+        const double t = 6.283185307179586476925286766559 * u2;
+        z[2 * pair] = r * cos(t);
+        z[2 * pair + 1] = r * sin(t);
+    }
+}
+
 /* Standard normal for element idx of (seed, tensor, stream). */
 static double normal_at(uint64_t seed, uint32_t tensor, uint32_t stream, uint64_t idx)
 {
-    uint32_t w[4];
-    block_words(seed, tensor, stream, idx >> 2, w);
-    const int j = (int)(idx & 3);
-    const int pair = j >> 1;
-    const double u1 = ((double)w[2 * pair] + 1.0) * (1.0 / 4294967296.0);  /* (0, 1] */
-    const double u2 = (double)w[2 * pair + 1] * (1.0 / 4294967296.0);      /* [0, 1) */
-    const double r = sqrt(-2.0 * log(u1));
-    const double t = 6.283185307179586476925286766559 * u2;
-    return (j & 1) ? r * sin(t) : r * cos(t);
+    double z[4];
+    normal_block(seed, tensor, stream, idx >> 2, z);
+    return z[idx & 3];
 }
 
-/* fp64 -> bf16, round to nearest even, no double rounding through fp32. */
-static uint16_t to_bf16(double x)
+/* fp64 -> bf16, round to nearest even straight from the 53-bit significand
+ * (no double rounding through fp32). Finite inputs of normal bf16 range
+ * (|x| >= 2^-126) take the bit path; others the exact slow path. */
+static uint16_t to_bf16_slow(double x)
 {
     if (x == 0.0) return signbit(x) ? 0x8000u : 0u;
     int e;
@@ -82,15 +95,57 @@ static uint16_t to_bf16(double x)
     return (uint16_t)(u >> 16);
 }
 
+static uint16_t to_bf16(double x)
+{
+    uint64_t b;
+    memcpy(&b, &x, sizeof b);
+    const int bexp = (int)((b >> 52) & 0x7FF);
+    if (bexp < 1023 - 126 || bexp > 1023 + 126) return to_bf16_slow(x);
+    /* keep 7 fraction bits: drop 45, round half to even on the dropped bits */
+    const uint64_t drop = 45;
+    const uint64_t half = (uint64_t)1 << (drop - 1);
+    const uint64_t low = b & (((uint64_t)1 << drop) - 1);
+    uint64_t keep = b >> drop;                      /* sign | exp(11) | frac(7) */
+    if (low > half || (low == half && (keep & 1))) keep += 1;   /* may carry into exp */
+    const uint64_t sign = keep >> 18;
+    const int64_t e11 = (int64_t)((keep >> 7) & 0x7FF);
+    const uint64_t frac7 = keep & 0x7F;
+    const uint64_t e8 = (uint64_t)(e11 - 1023 + 127);
+    if (e8 >= 255) return to_bf16_slow(x);
+    return (uint16_t)((sign << 15) | (e8 << 7) | frac7);
+}
+
+/* Elements [offset, offset + n) of one stream, block by block, on the
+ * calling thread. */
+static void fill_range(uint64_t seed, uint32_t tensor, uint32_t stream, uint64_t offset,
+                       uint64_t n, double sigma, uint16_t *out)
+{
+    if (n == 0) return;
+    const uint64_t end = offset + n;
+    for (uint64_t bi = offset >> 2; (bi << 2) < end; ++bi) {
+        double z[4];
+        normal_block(seed, tensor, stream, bi, z);
+        for (int j = 0; j < 4; ++j) {
+            const uint64_t idx = (bi << 2) + (uint64_t)j;
+            if (idx >= offset && idx < end) out[idx - offset] = to_bf16(sigma * z[j]);
+        }
+    }
+}
+
 /* out[i] = bf16(sigma * N(seed, tensor, stream, offset + i)), i < n. */
 void synth_normal_bf16(uint64_t seed, uint32_t tensor, uint32_t stream,
                        uint64_t offset, uint64_t n, double sigma,
                        uint16_t *out, int n_threads)
 {
     if (n_threads < 1) n_threads = 1;
-    #pragma omp parallel for num_threads(n_threads) schedule(static, 65536)
-    for (int64_t i = 0; i < (int64_t)n; ++i)
-        out[i] = to_bf16(sigma * normal_at(seed, tensor, stream, offset + (uint64_t)i));
+    const uint64_t chunk = 1u << 16;
+    const int64_t n_chunks = (int64_t)((n + chunk - 1) / chunk);
+    #pragma omp parallel for num_threads(n_threads) schedule(dynamic, 1)
+    for (int64_t c = 0; c < n_chunks; ++c) {
+        const uint64_t a = (uint64_t)c * chunk;
+        const uint64_t m = n - a < chunk ? n - a : chunk;
+        fill_range(seed, tensor, stream, offset + a, m, sigma, out + a);
+    }
 }
 
 /* Row-strided variant: n_rows rows of row_len elements; row r starts at
@@ -105,10 +160,8 @@ void synth_normal_bf16_rows(uint64_t seed, uint32_t tensor, uint32_t stream,
     if (n_threads < 1) n_threads = 1;
     #pragma omp parallel for num_threads(n_threads) schedule(static, 256)
     for (int64_t r = 0; r < (int64_t)n_rows; ++r)
-        for (uint64_t i = 0; i < row_len; ++i)
-            out[(uint64_t)r * dst_stride + i] =
-                to_bf16(sigma * normal_at(seed, tensor, stream,
-                                          offset + (uint64_t)r * src_stride + i));
+        fill_range(seed, tensor, stream, offset + (uint64_t)r * src_stride, row_len, sigma,
+                   out + (uint64_t)r * dst_stride);
 }
 
 /* fp64 normals (for distribution tests of the generator itself). */

@@ -73,3 +73,16 @@ def test_workload_shapes():
     d = configs.LLAMA8B_DENSE
     tail = d.hbm_tail(d.ctx_lens())
     assert np.all(tail == 8193)          # first 8192 tokens host, the rest + new slot HBM
+
+
+def test_bf16_values_are_rne_of_the_fp64_normals(oracle):
+    """The generator's bulk bf16 path equals the oracle's independent fp64 ->
+    bf16 round-to-nearest-even of the generator's fp64 normals."""
+    for sigma, off in ((1.0, 0), (0.02, 12345), (0.015, 7)):
+        z = synth.normal_f64(3, synth.TENSOR_W, 2, 3001, offset=off)
+        bits = synth.normal_bf16(3, synth.TENSOR_W, 2, 3001, sigma, offset=off)
+        assert np.array_equal(bits, oracle.f64_to_bf16(sigma * z))
+    rows = synth.normal_bf16_rows(3, synth.TENSOR_K, 9, 6, 5, 7, 13, 1.0)
+    for r in range(5):
+        assert np.array_equal(rows[r], synth.normal_bf16(3, synth.TENSOR_K, 9, 7, 1.0,
+                                                        offset=6 + 13 * r))
