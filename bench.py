@@ -114,7 +114,8 @@ def probe_ceiling(dkv, pool, configs_):
     for grid, unroll in configs_:
         ms = dkv.probe_stream_read(base, nbytes, grid, unroll, reps=3)
         gbps = nbytes / ms / 1e6
-        rows.append({"grid": grid, "unroll": unroll, "GBps": round(gbps, 2)})
+        rows.append({"grid": grid, "in_flight": abs(unroll), "nontemporal": unroll < 0,
+                     "GBps": round(gbps, 2)})
         best = max(best, gbps)
     return best, rows, nbytes
 
@@ -213,7 +214,7 @@ def main(argv=None):
     ceiling = ceiling_rows = None
     if not args.profile_run and r.host_pool is not None:
         ceiling, ceiling_rows, probe_bytes = probe_ceiling(
-            dkv, r.host_pool, [(64, 1), (256, 1), (512, 1), (1024, 2), (2048, 2)])
+            dkv, r.host_pool, [(64, 1), (256, 1), (512, 1), (1024, 2), (256, -1), (1024, -2)])
     r.free()
     log("host leg: %.3f ms/step, split kernel %.3f ms" % (ms, kt["split"]))
 
@@ -231,7 +232,8 @@ def main(argv=None):
         r = Resident(dkv, wl, K_all, V_all, ctx, 1 << 30)
         ms_h = r.timed(max(args.steps, 50), args.warmup)
         kt_h = r.kernel_times(max(args.steps, 50))
-        hbm_ceiling, _, _ = probe_ceiling(dkv, r.hbm_pool, [(2048, 4), (4096, 4), (8192, 8)])
+        hbm_ceiling, hbm_rows, _ = probe_ceiling(
+            dkv, r.hbm_pool, [(1024, -2), (2048, -2), (4096, -4), (8192, -8), (2048, 4)])
         out_hbm = r.out.view(torch.int16).cpu().numpy().view(np.uint16)
         r.free()
         hbm = {
@@ -242,6 +244,7 @@ def main(argv=None):
             "split_kernel_frac_of_8TBps": round(kv_bytes / (kt_h["split"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "kernel_ms": {k: round(v, 4) for k, v in kt_h.items()},
             "measured_hbm_read_GBps": round(hbm_ceiling, 1),
+            "hbm_probe": hbm_rows,
             "bit_identical_to_host_placement": bool(np.array_equal(out_host, out_hbm)),
         }
         log("HBM leg: %.4f ms/step, split kernel %.1f GB/s" % (ms_h, hbm["split_kernel_GBps"]))

@@ -47,8 +47,9 @@ struct StepArgs {
 // after the split attention and events[3] after the combine.
 hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream, hipEvent_t *events);
 
-// Streaming-read probe (grid-stride, 16 B per lane per load).
+// Streaming-read probe (grid-stride, 16 B per lane per load, optionally
+// nontemporal).
 hipError_t launch_stream_read(const void *ptr, uint64_t bytes, int grid, int unroll,
-                              uint32_t *sink, hipStream_t stream);
+                              bool nontemporal, uint32_t *sink, hipStream_t stream);
 
 }  // namespace dkv

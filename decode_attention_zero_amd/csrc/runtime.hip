@@ -654,6 +654,9 @@ dkv_status kv_layout_check_status(dkv_layout *L) {
 
 dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid, int32_t unroll, int32_t reps,
                                  float *ms_median) {
+    // unroll < 0 selects nontemporal loads with |unroll| in flight
+    const bool nt = unroll < 0;
+    if (nt) unroll = -unroll;
     if (!ptr || !ms_median || bytes == 0 || bytes % 16 || ((uintptr_t)ptr & 15u) || grid <= 0 || reps <= 0 ||
         !(unroll == 1 || unroll == 2 || unroll == 4 || unroll == 8))
         return fail(DKV_E_INVALID_ARG, "dkv_probe_stream_read: bad argument");
@@ -665,11 +668,11 @@ dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid, 
     hipError_t e = hipMalloc(&sink, 64);
     if (e == hipSuccess) e = hipEventCreate(&e0);
     if (e == hipSuccess) e = hipEventCreate(&e1);
-    if (e == hipSuccess) e = dkv::launch_stream_read(ptr, bytes, grid, unroll, sink, st);
+    if (e == hipSuccess) e = dkv::launch_stream_read(ptr, bytes, grid, unroll, nt, sink, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     for (int r = 0; r < reps && e == hipSuccess; ++r) {
         e = hipEventRecord(e0, st);
-        if (e == hipSuccess) e = dkv::launch_stream_read(ptr, bytes, grid, unroll, sink, st);
+        if (e == hipSuccess) e = dkv::launch_stream_read(ptr, bytes, grid, unroll, nt, sink, st);
         if (e == hipSuccess) e = hipEventRecord(e1, st);
         if (e == hipSuccess) e = hipEventSynchronize(e1);
         float ms = 0.0f;

@@ -27,7 +27,8 @@ dkv_status kv_pool_info(const dkv_pool *pool, void **device_base, int64_t *bytes
 
 /* Times a streaming read of `bytes` bytes at device address `ptr` (host
  * mapped memory or HBM): a grid-stride kernel of `grid` x 256 threads,
- * 16-byte loads, `unroll` (1, 2, 4 or 8) loads in flight per thread. One
+ * 16-byte loads, `unroll` (1, 2, 4 or 8) loads in flight per thread; a
+ * negative `unroll` (-1, -2, -4, -8) uses nontemporal loads instead. One
  * warm-up run, then `reps` timed runs on a private stream; *ms_median gets
  * the median in milliseconds. Synchronous. bytes must be a multiple of 16
  * and ptr 16-byte aligned. */
