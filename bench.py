@@ -4,10 +4,13 @@ Workload (default): Llama-3-8B-shaped layer (hidden 4096, 32 query / 8 KV
 heads, head_dim 128), batch 8, 32768 cached tokens per sequence, KV 100 % in
 host-pinned memory read in place over the host link; synthetic bf16 inputs
 from the seeded generator (W ~ N(0, 0.02^2), x and K/V ~ N(0, 1)).
+``--workload`` selects any of the five workloads (see synth/configs.py); for
+a multi-layer workload a step runs every layer in order.
 
-A step is one decode_step call: QKV projection, attention over every cached
-token plus the fresh one, fresh K/V write-back, split combine. Inputs are
-resident (KV in its pool, x/W in HBM) before the timed region starts.
+A step is one decode_step call per layer: QKV projection, attention over
+every cached token plus the fresh one, fresh K/V write-back, split combine.
+Inputs are resident (KV in its pool, x/W in HBM) before the timed region
+starts.
 
 Prints one JSON line: metric/value (effective KV GB/s = algorithmic KV bytes
 per step / step time), ms_per_step, roofline (dominant kernel = split
@@ -15,7 +18,7 @@ attention, against the host link), the measured host-link streaming-read
 ceiling, the same step with every page in HBM (against 8 TB/s), and the fp64
 oracle timed on the host cores on the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -32,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PCIE_GEN5_X16_GBPS = 64.0     # published per-direction rate of the MI355X host interface
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+CHUNK = 8192                  # tokens per set-up append
 
 
 def log(msg):
@@ -39,35 +43,51 @@ def log(msg):
 
 
 class Resident:
-    """One workload's KV in a pool (host or HBM), plus x, W, ctx_lens in HBM."""
+    """One workload's KV in its pools (placed by `tail`), plus x, W, ctx_lens
+    in HBM, for every layer."""
 
-    def __init__(self, dkv, wl, K_all, V_all, ctx, hbm_tail):
+    def __init__(self, dkv, wl, ctx, tail, kv_source):
         import torch
         self.dkv = dkv
-        self.shape = dkv.Shape.of(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, 1)
+        self.wl = wl
+        self.n_layers = wl.n_layers
+        self.shape = dkv.Shape.of(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                                  wl.n_layers)
         cap = (ctx + 1).astype(np.int32)
-        tail = np.full(len(ctx), hbm_tail, np.int32)
+        tail = np.asarray(tail, np.int32)
         n_host = n_hbm = 0
         for b in range(len(ctx)):
             n, first = dkv.kv_placement(int(cap[b]), int(tail[b]))
             n_host += first
             n_hbm += n - first
+        n_host *= wl.n_layers
+        n_hbm *= wl.n_layers
         self.host_pool = dkv.kv_alloc_host(self.shape, n_host) if n_host else None
         self.hbm_pool = dkv.kv_alloc_hbm(self.shape, n_hbm) if n_hbm else None
+        self.page_bytes = dkv.kv_page_bytes(self.shape)
         self.n_host, self.n_hbm = n_host, n_hbm
         self.layout = dkv.kv_layout_create(self.shape, cap, tail, self.host_pool, self.hbm_pool)
-        for b in range(len(ctx)):
-            dkv.kv_append(self.layout, 0, b, 0, K_all[b, :ctx[b]], V_all[b, :ctx[b]])
         dev = torch.device("cuda", 0)
-        self.x = torch.from_numpy(wl.x(0).view(np.int16)).to(dev).view(torch.bfloat16)
-        self.W = torch.from_numpy(wl.W(0).view(np.int16)).to(dev).view(torch.bfloat16)
+        self.x, self.W = [], []
+        for layer in range(wl.n_layers):
+            for b in range(len(ctx)):
+                for t0 in range(0, int(ctx[b]), CHUNK):
+                    t1 = min(int(ctx[b]), t0 + CHUNK)
+                    k, v = kv_source(layer, b, t0, t1)
+                    dkv.kv_append(self.layout, layer, b, t0, k, v)
+            self.x.append(torch.from_numpy(wl.x(layer).view(np.int16)).to(dev).view(torch.bfloat16))
+            self.W.append(torch.from_numpy(wl.W(layer).view(np.int16)).to(dev).view(torch.bfloat16))
+            if wl.n_layers > 1:
+                log("layer %d resident" % layer)
         self.ctx = torch.from_numpy(ctx.copy()).to(dev)
-        self.out = torch.empty((len(ctx), wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16,
-                               device=dev)
+        self.out = [torch.empty((len(ctx), wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16,
+                                device=dev) for _ in range(wl.n_layers)]
         self.stream = torch.cuda.current_stream()
 
     def step(self):
-        self.dkv.decode_step(self.layout, 0, self.x, self.W, self.ctx, self.out, self.stream)
+        for layer in range(self.n_layers):
+            self.dkv.decode_step(self.layout, layer, self.x[layer], self.W[layer], self.ctx,
+                                 self.out[layer], self.stream)
 
     def timed(self, steps, warmup):
         """Milliseconds per step over `steps` steps (HIP events on the step's stream)."""
@@ -85,17 +105,21 @@ class Resident:
         return e0.elapsed_time(e1) / steps
 
     def kernel_times(self, steps):
-        """Average per-kernel milliseconds from events the library records
-        around each kernel on the step's stream."""
+        """Per-step kernel milliseconds (summed over layers) from events the
+        library records around each kernel on the step's stream."""
         import torch
-        self.layout.timing_enable(True, steps)
+        self.layout.timing_enable(True, steps * self.n_layers)
         for _ in range(steps):
             self.step()
         torch.cuda.synchronize()
         t = self.layout.timing_read()
         self.layout.timing_enable(False)
-        n = max(1, t["steps"])
+        n = max(1, t["steps"]) / self.n_layers
         return {k: t[k] / n for k in ("projection", "split", "combine")}
+
+    def out_bits(self, layer=0):
+        import torch
+        return self.out[layer].view(torch.int16).cpu().numpy().view(np.uint16)
 
     def free(self):
         import torch
@@ -106,8 +130,9 @@ class Resident:
                 p.free()
 
 
-def probe_ceiling(dkv, pool, configs_):
+def probe_ceiling(dkv, pool, configs_, max_bytes=4 << 30):
     base, nbytes, _ = pool.info()
+    nbytes = min(nbytes, max_bytes)
     nbytes -= nbytes % (1 << 20)
     best = 0.0
     rows = []
@@ -118,6 +143,10 @@ def probe_ceiling(dkv, pool, configs_):
                      "GBps": round(gbps, 2)})
         best = max(best, gbps)
     return best, rows, nbytes
+
+
+HOST_PROBES = [(64, 1), (256, 1), (512, 1), (1024, 2), (256, -1), (1024, -2)]
+HBM_PROBES = [(1024, -2), (2048, -2), (4096, -4), (8192, -8), (2048, 4)]
 
 
 def counter_traffic(workload: str):
@@ -166,7 +195,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-leg", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
-                    help="only the timed host-placement leg (for rocprofv3 runs)")
+                    help="only the timed leg in the workload's own placement (for rocprofv3)")
     ap.add_argument("--calibrate", action="store_true",
                     help="with --profile-run: also run kernels of known traffic (a 256 MiB "
                          "HBM-to-HBM copy, 1 GiB streaming reads of the host pool and of HBM) "
@@ -185,74 +214,91 @@ def main(argv=None):
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = configs.BY_NAME[args.workload]
-    if wl.n_layers != 1:
-        raise SystemExit("the bench workload must be a single layer")
     ctx = wl.ctx_lens()
     B, Hkv, d = wl.batch, wl.n_kv_heads, wl.head_dim
-    Lmax = int(ctx.max())
-    log("generating inputs for %s" % wl.name)
-    K_all = np.zeros((B, Lmax, Hkv, d), np.uint16)
-    V_all = np.zeros_like(K_all)
-    for b in range(B):
-        wl.kv("k", 0, b, 0, int(ctx[b]), out=K_all[b, :ctx[b]])
-        wl.kv("v", 0, b, 0, int(ctx[b]), out=V_all[b, :ctx[b]])
+    tail = wl.hbm_tail(ctx)
+    # The oracle baseline needs the logical-order KV; keep it for single-layer
+    # workloads (the default one is 1 GiB), otherwise draw chunks on demand.
+    keep = wl.n_layers == 1 and not args.no_cpu_baseline and not args.profile_run
+    K_all = V_all = None
+    if keep:
+        log("generating inputs for %s" % wl.name)
+        Lmax = int(ctx.max())
+        K_all = np.zeros((B, Lmax, Hkv, d), np.uint16)
+        V_all = np.zeros_like(K_all)
+        for b in range(B):
+            wl.kv("k", 0, b, 0, int(ctx[b]), out=K_all[b, :ctx[b]])
+            wl.kv("v", 0, b, 0, int(ctx[b]), out=V_all[b, :ctx[b]])
 
-    kv_bytes = int(ctx.astype(np.int64).sum()) * wl.kv_bytes_per_token
+    def kv_source(layer, b, t0, t1):
+        if K_all is not None:
+            return K_all[b, t0:t1], V_all[b, t0:t1]
+        return wl.kv("k", layer, b, t0, t1), wl.kv("v", layer, b, t0, t1)
+
+    kv_layer_bytes = int(ctx.astype(np.int64).sum()) * wl.kv_bytes_per_token
+    kv_bytes = kv_layer_bytes * wl.n_layers
     w_bytes = wl.n_qkv * wl.hidden * 2
-    step_bytes = kv_bytes + w_bytes + B * wl.hidden * 2 + B * Hkv * d * 4 + B * wl.n_q_heads * d * 2
+    step_bytes = wl.n_layers * (kv_layer_bytes + w_bytes + B * wl.hidden * 2 + B * Hkv * d * 4
+                                + B * wl.n_q_heads * d * 2)
 
-    result = {}
-    # ------------------------------------------------------------------ host placement
-    log("host-placement leg")
-    r = Resident(dkv, wl, K_all, V_all, ctx, wl.hbm_tail_tokens if wl.hbm_fraction is None else 0)
-    host_kv = r.n_host * dkv.kv_page_bytes(r.shape)
+    # ------------------------------------------------------------------ the workload's placement
+    log("%s: own placement leg" % wl.name)
+    r = Resident(dkv, wl, ctx, tail, kv_source)
+    host_kv_layer = 0
+    for b in range(B):
+        n, first = dkv.kv_placement(int(ctx[b]) + 1, int(tail[b]))
+        host_tokens = min(int(ctx[b]), first * dkv.PAGE_TOKENS)
+        host_kv_layer += host_tokens * wl.kv_bytes_per_token
+    host_kv = host_kv_layer * wl.n_layers
+    hbm_kv = kv_bytes - host_kv
     ms = r.timed(args.steps, args.warmup)
     kt = r.kernel_times(args.steps)
-    if args.profile_run and args.calibrate:
-        calibrate(dkv, r)
-    out_host = r.out.view(torch.int16).cpu().numpy().view(np.uint16)
+    if args.profile_run:
+        if args.calibrate:
+            calibrate(dkv, r)
+        r.free()
+        print(json.dumps({"profile_run": True, "workload": wl.name, "ms_per_step": ms,
+                          "kernel_ms": kt}), flush=True)
+        return 0
+    out_own = r.out_bits(0)
     ceiling = ceiling_rows = None
-    if not args.profile_run and r.host_pool is not None:
-        ceiling, ceiling_rows, probe_bytes = probe_ceiling(
-            dkv, r.host_pool, [(64, 1), (256, 1), (512, 1), (1024, 2), (256, -1), (1024, -2)])
+    if r.host_pool is not None:
+        ceiling, ceiling_rows, _ = probe_ceiling(dkv, r.host_pool, HOST_PROBES)
     r.free()
-    log("host leg: %.3f ms/step, split kernel %.3f ms" % (ms, kt["split"]))
+    log("own placement: %.3f ms/step, split kernel %.3f ms" % (ms, kt["split"]))
 
     value = kv_bytes / (ms * 1e-3) / 1e9
     split_gbps = kv_bytes / (kt["split"] * 1e-3) / 1e9
-    if args.profile_run:
-        print(json.dumps({"profile_run": True, "ms_per_step": ms, "kernel_ms": kt}), flush=True)
-        return 0
 
-    # ------------------------------------------------------------------ HBM placement
+    # ------------------------------------------------------------------ every page in HBM
     hbm = None
-    out_hbm = None
     if not args.no_hbm_leg:
         log("HBM-placement leg")
-        r = Resident(dkv, wl, K_all, V_all, ctx, 1 << 30)
-        ms_h = r.timed(max(args.steps, 50), args.warmup)
-        kt_h = r.kernel_times(max(args.steps, 50))
-        hbm_ceiling, hbm_rows, _ = probe_ceiling(
-            dkv, r.hbm_pool, [(1024, -2), (2048, -2), (4096, -4), (8192, -8), (2048, 4)])
-        out_hbm = r.out.view(torch.int16).cpu().numpy().view(np.uint16)
+        r = Resident(dkv, wl, ctx, np.full(B, 1 << 30, np.int32), kv_source)
+        n_hbm_steps = max(args.steps, 50) if wl.n_layers == 1 else args.steps
+        ms_h = r.timed(n_hbm_steps, args.warmup)
+        kt_h = r.kernel_times(n_hbm_steps)
+        hbm_ceiling, hbm_rows, _ = probe_ceiling(dkv, r.hbm_pool, HBM_PROBES)
+        out_hbm = r.out_bits(0)
         r.free()
         hbm = {
             "ms_per_step": round(ms_h, 4),
             "kv_GBps": round(kv_bytes / (ms_h * 1e-3) / 1e9, 1),
             "split_kernel_ms": round(kt_h["split"], 4),
             "split_kernel_GBps": round(kv_bytes / (kt_h["split"] * 1e-3) / 1e9, 1),
-            "split_kernel_frac_of_8TBps": round(kv_bytes / (kt_h["split"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "split_kernel_frac_of_8TBps": round(kv_bytes / (kt_h["split"] * 1e-3) / 1e9
+                                                / HBM_PEAK_GBPS, 4),
             "kernel_ms": {k: round(v, 4) for k, v in kt_h.items()},
             "measured_hbm_read_GBps": round(hbm_ceiling, 1),
             "hbm_probe": hbm_rows,
-            "bit_identical_to_host_placement": bool(np.array_equal(out_host, out_hbm)),
+            "bit_identical_to_own_placement": bool(np.array_equal(out_own, out_hbm)),
         }
         log("HBM leg: %.4f ms/step, split kernel %.1f GB/s" % (ms_h, hbm["split_kernel_GBps"]))
 
     # ------------------------------------------------------------------ CPU oracle
     cpu = None
     parity = None
-    if not args.no_cpu_baseline:
+    if K_all is not None:
         import oracle
         orc = oracle.default()
         threads = oracle.DEFAULT_THREADS
@@ -266,15 +312,17 @@ def main(argv=None):
                "kind": "oracle", "seconds": round(t_cpu, 2),
                "sample": "one full step of the bench workload (all %d sequences x %d query heads, "
                          "%d KV bytes), fp64, plain C + OpenMP" % (B, wl.n_q_heads, kv_bytes)}
-        got = (out_host.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        got = (out_own.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         err = np.abs(got - ref["attn_out"])
         parity = {"max_abs": float(err.max()),
                   "rel_l2": float(np.linalg.norm(got - ref["attn_out"]) /
                                   np.linalg.norm(ref["attn_out"])),
                   "gates": {"max_abs": 2e-2, "rel_l2": 5e-3}}
 
-    t_star = max(host_kv / (ceiling * 1e9) if ceiling else 0.0,
-                 (kv_bytes - min(kv_bytes, host_kv)) / (HBM_PEAK_GBPS * 1e9))
+    t_star = max(host_kv / (ceiling * 1e9) if ceiling else 0.0, hbm_kv / (HBM_PEAK_GBPS * 1e9))
+    placement = ("100% host-pinned, read in place" if hbm_kv == 0 else
+                 "%.1f%% host-pinned (read in place) / %.1f%% HBM" %
+                 (100.0 * host_kv / kv_bytes, 100.0 * hbm_kv / kv_bytes))
     result = {
         "metric": "effective KV GB/s per decode step (% of host-link+HBM roofline); step latency",
         "value": round(value, 3),
@@ -288,16 +336,20 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": B, "ctx_tokens": int(ctx[0]),
+        "config": {"workload": wl.name, "batch": B, "layers": wl.n_layers,
+                   "ctx_tokens": int(ctx[0]) if wl.ctx_range is None else list(wl.ctx_range),
                    "hidden": wl.hidden, "q_heads": wl.n_q_heads, "kv_heads": Hkv,
-                   "head_dim": d, "kv_placement": "100% host-pinned, read in place",
-                   "kv_bytes_per_step": kv_bytes, "algorithmic_bytes_per_step": step_bytes},
+                   "head_dim": d, "kv_placement": placement,
+                   "kv_bytes_per_step": kv_bytes, "host_kv_bytes_per_step": host_kv,
+                   "algorithmic_bytes_per_step": step_bytes},
         "roofline": {"bound": "host_link", "kernel": "attn_split_kernel",
                      "achieved": round(split_gbps, 3), "peak": PCIE_GEN5_X16_GBPS,
                      "unit": "GB/s", "frac": round(split_gbps / PCIE_GEN5_X16_GBPS, 4),
                      "traffic": counter_traffic(wl.name),
                      "measured_ceiling_GBps": round(ceiling, 3) if ceiling else None,
                      "frac_of_measured_ceiling": round(split_gbps / ceiling, 4) if ceiling else None,
+                     "host_GBps_vs_ceiling": round(host_kv / (kt["split"] * 1e-3) / 1e9 / ceiling, 4)
+                     if ceiling else None,
                      "split_kernel_ms": round(kt["split"], 4)},
         "combined_roofline": {"t_star_ms": round(t_star * 1e3, 4),
                               "frac": round(t_star * 1e3 / ms, 4) if t_star else None},

@@ -33,6 +33,10 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// From this batch size on, y = W x has enough columns (sequences) to be a
+// real contraction and runs on MFMA; below it W is read by a VALU GEMV.
+constexpr int kMfmaMinBatch = 32;
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -99,10 +103,32 @@ __device__ __forceinline__ float rescale(float x, float M) {
 }
 
 // ------------------------------------------------------------------------------
-// 1. QKV projection. One wavefront computes 4 output rows for BT sequences;
-// lanes split the hidden dimension in 16-byte (8 x bf16) chunks, so each W
-// row is read as contiguous 1 KiB wave loads. Rows >= Hq*d are the fresh K
-// then V heads.
+// 1. QKV projection: y_b = W x_b with fp32 accumulation. Rows < Hq*d are q
+// (kept fp32, pre-scaled for exp2); the rest are the fresh K then V heads,
+// rounded once to bf16.
+__device__ __forceinline__ void store_projection(const StepArgs &a, int n, int b, float y) {
+    const int D = a.head_dim;
+    const int nq = a.n_q_heads * D;
+    if (n < nq) {
+        a.q[(size_t)b * nq + n] = y * a.qscale;
+    } else {
+        const int n2 = n - nq;
+        const int c = n2 / (a.n_kv_heads * D);
+        const int rem = n2 - c * (a.n_kv_heads * D);
+        const int g = rem / D, i = rem - g * D;
+        a.kv_new[(((size_t)b * a.n_kv_heads + g) * 2 + c) * D + i] = f32_to_bf16(y);
+    }
+}
+
+// Sequences whose ctx_lens entry is out of range raise the layout's flag.
+__device__ __forceinline__ void check_context_range(const StepArgs &a, int b) {
+    const int L = a.ctx_lens[b];
+    if (L < 0 || L >= a.capacity[b]) atomicOr(a.status, 1u);
+}
+
+// 1a. Small batches (B < 32): a GEMV on VALU. One wavefront computes 4 output
+// rows for BT sequences; lanes split the hidden dimension in 16-byte
+// (8 x bf16) chunks, so each W row is read as contiguous 1 KiB wave loads.
 template <int BT>
 __global__ __launch_bounds__(256) void qkv_proj_kernel(StepArgs a) {
     const int lane = threadIdx.x & 63;
@@ -111,11 +137,7 @@ __global__ __launch_bounds__(256) void qkv_proj_kernel(StepArgs a) {
     const int b0 = blockIdx.y * BT;
     const int nb = min(BT, a.batch - b0);
 
-    if (blockIdx.x == 0 && threadIdx.x < BT && threadIdx.x < nb) {
-        const int b = b0 + threadIdx.x;
-        const int L = a.ctx_lens[b];
-        if (L < 0 || L >= a.capacity[b]) atomicOr(a.status, 1u);
-    }
+    if (blockIdx.x == 0 && threadIdx.x < nb) check_context_range(a, b0 + threadIdx.x);
     if (row0 >= a.n_qkv) return;
 
     float acc[4][BT];
@@ -155,20 +177,112 @@ __global__ __launch_bounds__(256) void qkv_proj_kernel(StepArgs a) {
 
     if (lane < 4 * BT) {
         const int r = lane / BT, bb = lane % BT;
-        if (bb < nb) {
-            const int n = row0 + r;
-            const int b = b0 + bb;
-            const int D = a.head_dim;
-            const int nq = a.n_q_heads * D;
-            if (n < nq) {
-                a.q[(size_t)b * nq + n] = y * a.qscale;
-            } else {
-                const int n2 = n - nq;
-                const int c = n2 / (a.n_kv_heads * D);
-                const int rem = n2 - c * (a.n_kv_heads * D);
-                const int g = rem / D, i = rem - g * D;
-                a.kv_new[(((size_t)b * a.n_kv_heads + g) * 2 + c) * D + i] = f32_to_bf16(y);
-            }
+        if (bb < nb) store_projection(a, row0 + r, b0 + bb, y);
+    }
+}
+
+// 1b. Batches of 32 or more: the projection is a dense [N_qkv x hidden] x
+// [hidden x B] contraction, done on the matrix cores with
+// v_mfma_f32_16x16x32_bf16 (bf16 in, fp32 accumulate). One wavefront owns 16
+// W rows and 16*NB sequences, so every W byte is read once per step.
+// Operand layout of the 16x16x32 MFMA: lane l supplies A[i = l%16][k = 8*(l/16)
+// .. +7] and B[k = 8*(l/16) .. +7][j = l%16], and receives
+// D[i = 4*(l/16) + r][j = l%16], r < 4. A is the W tile (rows of W are
+// contiguous in k), B is x^T (rows of x are contiguous in k), so both operands
+// are plain 16-byte loads from row-major memory.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int NB>
+struct MfmaChunk {
+    static constexpr int UK = 4;   // 32-wide k steps per chunk (128 k)
+    uint4 w[UK];
+    uint4 x[UK][NB];
+};
+
+template <int NB>
+__device__ __forceinline__ void mfma_load(MfmaChunk<NB> &c, const uint16_t *wrow,
+                                          const uint16_t *const (&xrow)[NB], int k0) {
+#pragma unroll
+    for (int u = 0; u < MfmaChunk<NB>::UK; ++u) {
+        c.w[u] = *reinterpret_cast<const uint4 *>(wrow + k0 + 32 * u);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) c.x[u][nb] = *reinterpret_cast<const uint4 *>(xrow[nb] + k0 + 32 * u);
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void mfma_step(const MfmaChunk<NB> &c, f32x4 (&acc)[NB]) {
+#pragma unroll
+    for (int u = 0; u < MfmaChunk<NB>::UK; ++u) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, c.w[u]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, c.x[u][nb]),
+                                                              acc[nb], 0, 0, 0);
+    }
+}
+
+// Split-k: the workgroup's KS wavefronts (blockDim.x / 64, 2 or 4) take equal
+// k ranges of the same 16-row x 16*NB-sequence tile; their partial tiles are
+// added through LDS in wave order, so the result does not depend on timing.
+template <int NB>
+__global__ __launch_bounds__(256) void qkv_proj_mfma_kernel(StepArgs a) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int ks = blockDim.x >> 6;
+    const int row0 = blockIdx.x * 16;
+    const int b0 = blockIdx.y * 16 * NB;
+    const int i = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int krange = a.hidden / ks;      // a multiple of 256 (checked at launch)
+    const int kbeg = wave * krange;
+
+    if (blockIdx.x == 0 && wave == 0) {
+        for (int b = b0 + lane; b < min(a.batch, b0 + 16 * NB); b += 64) check_context_range(a, b);
+    }
+
+    // Columns past the batch read a valid row (the last sequence's) and are
+    // never stored, so the k loop has no per-lane branches.
+    const uint16_t *wrow = a.w + (size_t)(row0 + i) * a.hidden + kbeg + kq;
+    const uint16_t *xrow[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        xrow[nb] = a.x + (size_t)min(b0 + nb * 16 + i, a.batch - 1) * a.hidden + kbeg + kq;
+    f32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // The 128-wide chunks of a wave's k range come in pairs: ping-pong between
+    // two register sets, the next chunk's loads in flight while the current
+    // one feeds the matrix cores.
+    constexpr int KC = 32 * MfmaChunk<NB>::UK;
+    MfmaChunk<NB> c0, c1;
+    mfma_load(c0, wrow, xrow, 0);
+    for (int k0 = 0; k0 < krange; k0 += 2 * KC) {
+        mfma_load(c1, wrow, xrow, k0 + KC);
+        mfma_step(c0, acc);
+        if (k0 + 2 * KC < krange) mfma_load(c0, wrow, xrow, k0 + 2 * KC);
+        mfma_step(c1, acc);
+    }
+
+    __shared__ f32x4 partial[3][NB][64];
+    if (wave > 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) partial[wave - 1][nb][lane] = acc[nb];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 1; w < ks; ++w) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] += partial[w - 1][nb][lane];
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int b = b0 + nb * 16 + i;
+        if (b < a.batch) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) store_projection(a, row0 + 4 * (lane >> 4) + r, b, acc[nb][r]);
         }
     }
 }
@@ -488,8 +602,19 @@ hipError_t launch_decode_step(const StepArgs &a, hipStream_t st, hipEvent_t *ev)
     if (!((a.head_dim == 128 || a.head_dim == 64) && (G == 1 || G == 2 || G == 4 || G == 8)))
         return hipErrorInvalidValue;
     if (ev) (void)hipEventRecord(ev[0], st);
-    dim3 grid_proj((a.n_qkv + 15) / 16, (a.batch + BT - 1) / BT);
-    qkv_proj_kernel<BT><<<grid_proj, 256, 0, st>>>(a);
+    if (a.batch >= kMfmaMinBatch) {
+        // 16 W rows x 64 sequences per workgroup (32 for batches up to 32),
+        // k split over 4 wavefronts (2 when hidden is not a multiple of 1024)
+        const int threads = (a.hidden % 1024 == 0) ? 256 : 128;
+        if (a.batch <= 32) {
+            qkv_proj_mfma_kernel<2><<<dim3(a.n_qkv / 16, (a.batch + 31) / 32), threads, 0, st>>>(a);
+        } else {
+            qkv_proj_mfma_kernel<4><<<dim3(a.n_qkv / 16, (a.batch + 63) / 64), threads, 0, st>>>(a);
+        }
+    } else {
+        dim3 grid_proj((a.n_qkv + 15) / 16, (a.batch + BT - 1) / BT);
+        qkv_proj_kernel<BT><<<grid_proj, 256, 0, st>>>(a);
+    }
     if (ev) (void)hipEventRecord(ev[1], st);
     if (a.head_dim == 128) dispatch_group<128>(a, G, st, ev);
     else dispatch_group<64>(a, G, st, ev);

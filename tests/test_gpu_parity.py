@@ -91,7 +91,9 @@ def test_tiny_workload(oracle):
         s.free()
 
 
-@pytest.mark.parametrize("ctx", [[0, 1, 17, 1000], [33, 512, 513, 2049]])
+@pytest.mark.parametrize("ctx", [[0, 1, 17, 1000], [33, 512, 513, 2049],
+                                 [(37 * i) % 700 for i in range(40)]],
+                         ids=["b4-short", "b4-mid", "b40-mfma-projection"])
 def test_llama8b_shape_ragged(oracle, ctx):
     wl = configs.LLAMA8B_HOST.replace(batch=len(ctx))
     s = H.Setup(wl, ctx_lens=ctx, hbm_tail=0)
@@ -136,13 +138,16 @@ def test_split_and_page_edges(oracle, monkeypatch, split):
 
 
 # --------------------------------------------------------------------------- exactness
-def test_projection_integer_exact(oracle):
+@pytest.mark.parametrize("batch", [3, 32, 40, 64])
+def test_projection_integer_exact(oracle, batch):
     """Small-integer x and W make every product and fp32 sum exact, so the
     written-back K/V must equal the oracle's fp64 values rounded to bf16, bit
-    for bit; with an empty history attn_out is exactly bf16(v_new)."""
+    for bit; with an empty history attn_out is exactly bf16(v_new). Batches
+    below 32 take the VALU projection, 32 and up the MFMA one (40: a partly
+    filled 64-sequence tile)."""
     import synth
-    wl = configs.LLAMA8B_HOST.replace(batch=3)
-    ctx = np.array([0, 5, 16], np.int32)
+    wl = configs.LLAMA8B_HOST.replace(batch=batch)
+    ctx = np.array([[0, 5, 16][b % 3] for b in range(batch)], np.int32)
     xi = synth.int_bf16(99, 20, 0, wl.batch * wl.hidden, -4, 4).reshape(wl.batch, wl.hidden)
     Wi = synth.int_bf16(99, 21, 0, wl.n_qkv * wl.hidden, -4, 4).reshape(wl.n_qkv, wl.hidden)
     s = H.Setup(wl, ctx_lens=ctx, hbm_tail=0)
@@ -160,9 +165,9 @@ def test_projection_integer_exact(oracle):
             assert np.array_equal(k_slot[0], kn), b
             assert np.array_equal(v_slot[0], vn), b
         # empty history: the output is the fresh value, exactly
+        y = oracle.qkv_projection(xi[0], Wi)
         for h in range(Hq):
             g = oracle.kv_head_of(h, Hq, Hkv)
-            y = oracle.qkv_projection(xi[0], Wi)
             vn = oracle.f64_to_bf16(y[(Hq + Hkv) * d + g * d:(Hq + Hkv) * d + (g + 1) * d])
             assert np.array_equal(out[0, h * d:(h + 1) * d], vn), h
     finally:
