@@ -149,22 +149,32 @@ HOST_PROBES = [(64, 1), (256, 1), (512, 1), (1024, 2), (256, -1), (1024, -2)]
 HBM_PROBES = [(1024, -2), (2048, -2), (4096, -4), (8192, -8), (2048, 4)]
 
 
+SPLIT_KERNEL_SOURCES = ("attn_split.hip", "device_common.h", "dkv_internal.h")
+
+
+def split_kernel_sha256() -> str:
+    """sha256 over the sources the split-attention kernel is compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in SPLIT_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_zero_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def counter_traffic(workload: str):
     """HBM + host-link bytes per split-kernel launch from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a copy kernel of known
-    size); None when the summary is missing or the kernel source has changed
-    since the counters were taken."""
-    import hashlib
+    size); None when the summary is missing or the kernel's sources have
+    changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "attn_split_%s_traffic.json" % workload)
-    src = os.path.join(ROOT, "decode_attention_zero_amd", "csrc", "kernels.hip")
     try:
         with open(path) as f:
             rec = json.load(f)
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = split_kernel_sha256()
     except OSError:
         return None
-    if rec.get("kernels_hip_sha256") != sha:
+    if rec.get("split_kernel_sources_sha256") != sha:
         return None
     return int(rec["traffic_bytes_per_launch"])
 

@@ -9,8 +9,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libdkv.so")
-SOURCES = ["kernels.hip", "runtime.hip"]
-HEADERS = [os.path.join(CSRC, "dkv_internal.h"), os.path.join(INCLUDE, "dkv.h"),
+SOURCES = ["proj.hip", "attn_split.hip", "attn_combine.hip", "probe.hip", "runtime.hip"]
+HEADERS = [os.path.join(CSRC, "dkv_internal.h"), os.path.join(CSRC, "device_common.h"), os.path.join(INCLUDE, "dkv.h"),
            os.path.join(INCLUDE, "dkv_probe.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -38,7 +38,7 @@ def build_library(out: str = LIBRARY, verbose: bool = False) -> str:
     return out
 
 
-def device_assembly(source: str = "kernels.hip") -> str:
+def device_assembly(source: str = "attn_split.hip") -> str:
     """gfx950 assembly of one source (for inspecting this library's own code)."""
     cmd = [HIPCC] + COMMON_FLAGS + ["--cuda-device-only", "-S", "-o", "-",
                                     os.path.join(CSRC, source)]

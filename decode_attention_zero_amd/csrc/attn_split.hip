@@ -1,0 +1,242 @@
+// Split attention of one zero-copy decode step on gfx950 (MI355X): one
+// wavefront per work item (sequence b, KV head g, token split s) streams the
+// split's KV pages in place -- host pages over the host link, HBM pages from
+// HBM, chosen only by the page's address -- and keeps an online-softmax state
+// for the G query heads that share the KV head, so each remote byte is read
+// once for all of them. Writes an unnormalised partial (m, l, o) per query
+// head and split.
+//
+// Method (pages): "长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）" (DirectKV
+// digest), 核心方法: the attention kernel reads CPU-resident KV directly, with a
+// layout arranged for coalesced remote reads. The split/merge of the softmax
+// state is the standard flash-decoding decomposition (not on the pages); the
+// split boundaries depend only on token indices, never on where a page lives,
+// so host and HBM placements give bit-identical results.
+#include "device_common.h"
+
+namespace dkv {
+namespace {
+
+// Split attention. Work item (s, g, b) = blockIdx (x, y, z); one wavefront.
+//
+// Lane mapping inside a page run (K tile then V tile, each [16 tok][D] bf16):
+// wave load j reads bytes [j*1024, (j+1)*1024) of a tile, lane l the 16 bytes
+// at l*16, i.e. token j*TPL + l/LPT, dims 8*(l%LPT) .. +7. Every wave load is
+// one fully used, contiguous 1 KiB -- the coalesced remote access the layout is
+// arranged for. A token's score is summed over its LPT lanes with DPP; each
+// group of lanes holding the same token slot across loads (a "row") keeps its
+// own online-softmax state, merged across rows at the end of the item.
+//
+// Pages are double-buffered in registers (ping-pong, so no copies): the next
+// page's loads are in flight while the current one is computed. Full pages
+// take a mask-free path; only the split's last page can be partial.
+template <int D, int G>
+struct SplitState {
+    static constexpr int LPT = D / 8;               // lanes per token
+    static constexpr int TPL = 64 / LPT;            // tokens per wave load
+    static constexpr int NLD = kPageTokens / TPL;   // wave loads per 16-token tile
+    static constexpr int TILE = kPageTokens * D * 2;
+    static constexpr int RUN = 2 * TILE;
+
+    float q[G][8];
+    float m[G], l[G], acc[G][8];
+
+    __device__ __forceinline__ void load(const char *run, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) const {
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) kr[j] = load_stream(run + j * 1024);
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) vr[j] = load_stream(run + TILE + j * 1024);
+    }
+
+    // One page. PARTIAL: only the first n_valid tokens of the page count.
+    template <bool PARTIAL>
+    __device__ __forceinline__ void page(const uint4 (&kr)[NLD], const uint4 (&vr)[NLD], int sub,
+                                         int n_valid) {
+        float sc[NLD][G];
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            float kf[8];
+            unpack8(kr[j], kf);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float d0 = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d0 = fmaf(q[h][e], kf[e], d0);
+                sc[j][h] = token_sum<LPT>(d0);
+            }
+        }
+        bool valid[NLD];
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) valid[j] = !PARTIAL || (j * TPL + sub < n_valid);
+
+        // New running max per head; the rescale runs only when some row's max
+        // grew (otherwise its factor would be exactly 1).
+        float mx[G];
+        bool grow = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            mx[h] = m[h];
+#pragma unroll
+            for (int j = 0; j < NLD; ++j)
+                if (valid[j]) mx[h] = fmaxf(mx[h], sc[j][h]);
+            grow |= mx[h] > m[h];
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float alpha = (mx[h] == m[h]) ? 1.0f : rescale(m[h], mx[h]);
+                l[h] *= alpha;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+                m[h] = mx[h];
+            }
+        }
+
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            float vf[8];
+            unpack8(vr[j], vf);
+            if (PARTIAL && !valid[j]) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vf[e] = 0.0f;   // stale slots may hold any bits
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float p = fast_exp2(sc[j][h] - m[h]);
+                if (PARTIAL && !valid[j]) p = 0.0f;
+                l[h] += p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+            }
+        }
+    }
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(64) void attn_split_kernel(StepArgs a) {
+    using S = SplitState<D, G>;
+    constexpr int NLD = S::NLD;
+    constexpr int LPT = S::LPT;
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int L = a.ctx_lens[b];
+    if (L < 0 || L >= a.capacity[b]) return;
+    const int t0 = s * a.split_tokens;
+    if (t0 >= L) return;
+    const int t1 = min(t0 + a.split_tokens, L);
+
+    const int lane = threadIdx.x;
+    const int sub = lane / LPT;
+    const int dl = lane % LPT;
+
+    S st;
+    {
+        const float *qb = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + dl * 8;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float4 lo = *reinterpret_cast<const float4 *>(qb + h * D);
+            const float4 hi = *reinterpret_cast<const float4 *>(qb + h * D + 4);
+            st.q[h][0] = lo.x; st.q[h][1] = lo.y; st.q[h][2] = lo.z; st.q[h][3] = lo.w;
+            st.q[h][4] = hi.x; st.q[h][5] = hi.y; st.q[h][6] = hi.z; st.q[h][7] = hi.w;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        st.m[h] = kNegInf;
+        st.l[h] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.0f;
+    }
+
+    const uint64_t *pt = a.page_table + (size_t)b * a.max_pages;
+    const size_t run_off = (size_t)g * S::RUN + (size_t)lane * 16;
+    auto run_of = [&](int p) { return reinterpret_cast<const char *>(pt[p]) + run_off; };
+
+    const int p0 = t0 / kPageTokens;
+    const int p1 = (t1 + kPageTokens - 1) / kPageTokens;   // pages [p0, p1)
+    const int pf = t1 / kPageTokens;                        // pages [p0, pf) are full
+    uint4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
+    int p = p0;
+    st.load(run_of(p), ka, va);
+    while (p + 1 < pf) {                 // pages p (in a) and p + 1 are full
+        st.load(run_of(p + 1), kb, vb);
+        st.template page<false>(ka, va, sub, kPageTokens);
+        if (p + 2 < p1) st.load(run_of(p + 2), ka, va);
+        st.template page<false>(kb, vb, sub, kPageTokens);
+        p += 2;
+    }
+    if (p < pf) {                        // one last full page (in a), maybe a partial one after
+        if (p + 1 < p1) st.load(run_of(p + 1), kb, vb);
+        st.template page<false>(ka, va, sub, kPageTokens);
+        if (p + 1 < p1) st.template page<true>(kb, vb, sub, t1 - (p + 1) * kPageTokens);
+    } else if (p < p1) {                 // the partial page (in a)
+        st.template page<true>(ka, va, sub, t1 - p * kPageTokens);
+    }
+
+    // Merge the row states (lanes l and l ^ off, off >= LPT) in a fixed order.
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float mo = __shfl_xor(st.m[h], off);
+            const float lo = __shfl_xor(st.l[h], off);
+            const float M = fmaxf(st.m[h], mo);
+            const float c1 = rescale(st.m[h], M);
+            const float c2 = rescale(mo, M);
+            st.l[h] = fmaf(st.l[h], c1, lo * c2);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float ao = __shfl_xor(st.acc[h][e], off);
+                st.acc[h][e] = fmaf(st.acc[h][e], c1, ao * c2);
+            }
+            st.m[h] = M;
+        }
+    }
+
+    if (sub == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const size_t slot = ((size_t)b * a.n_q_heads + (size_t)g * G + h) * a.max_splits + s;
+            float *po = a.part_o + slot * D + dl * 8;
+            *reinterpret_cast<float4 *>(po) =
+                make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
+            *reinterpret_cast<float4 *>(po + 4) =
+                make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
+            if (dl == 0) a.part_ml[slot] = make_float2(st.m[h], st.l[h]);
+        }
+    }
+}
+
+template <int D, int G>
+void launch(const StepArgs &a, hipStream_t st) {
+    dim3 grid(a.max_splits, a.n_kv_heads, a.batch);
+    attn_split_kernel<D, G><<<grid, 64, 0, st>>>(a);
+}
+
+}  // namespace
+
+hipError_t launch_split(const StepArgs &a, hipStream_t st) {
+    const int G = a.n_q_heads / a.n_kv_heads;
+    if (a.head_dim == 128) {
+        switch (G) {
+            case 1: launch<128, 1>(a, st); break;
+            case 2: launch<128, 2>(a, st); break;
+            case 4: launch<128, 4>(a, st); break;
+            case 8: launch<128, 8>(a, st); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else if (a.head_dim == 64) {
+        switch (G) {
+            case 1: launch<64, 1>(a, st); break;
+            case 2: launch<64, 2>(a, st); break;
+            case 4: launch<64, 4>(a, st); break;
+            case 8: launch<64, 8>(a, st); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dkv

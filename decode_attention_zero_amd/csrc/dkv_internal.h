@@ -47,6 +47,12 @@ struct StepArgs {
 // after the split attention and events[3] after the combine.
 hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream, hipEvent_t *events);
 
+// The three kernels of a step (each returns hipErrorInvalidValue for a shape
+// outside its compiled variants, before launching anything).
+hipError_t launch_projection(const StepArgs &a, hipStream_t stream);
+hipError_t launch_split(const StepArgs &a, hipStream_t stream);
+hipError_t launch_combine(const StepArgs &a, hipStream_t stream);
+
 // Streaming-read probe (grid-stride, 16 B per lane per load, optionally
 // nontemporal).
 hipError_t launch_stream_read(const void *ptr, uint64_t bytes, int grid, int unroll,

@@ -1,0 +1,272 @@
+// Fused QKV projection of one decode step on gfx950: y_b = W_qkv x_b for
+// every sequence b, fp32 accumulation of exact bf16 products. Rows below
+// Hq*d are the query (kept in fp32, pre-scaled by log2(e)/sqrt(d) so that
+// scores come out in log2 units); the rest are the fresh K then V heads,
+// rounded once to bf16. The projection that produces the new token's K/V is
+// part of the decode step, as in the core-method section of the DirectKV
+// digest ("长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）"); the step is bound
+// by reading W from HBM at every batch size here, so both variants are built
+// to stream W once at full bandwidth.
+#include "device_common.h"
+
+namespace dkv {
+namespace {
+
+// From this batch size on, y = W x has enough columns (sequences) to be a
+// real contraction and runs on MFMA; below it W is read by a VALU GEMV.
+constexpr int kMfmaMinBatch = 32;
+
+__device__ __forceinline__ void store_projection(const StepArgs &a, int n, int b, float y) {
+    const int D = a.head_dim;
+    const int nq = a.n_q_heads * D;
+    if (n < nq) {
+        a.q[(size_t)b * nq + n] = y * a.qscale;
+    } else {
+        const int n2 = n - nq;
+        const int c = n2 / (a.n_kv_heads * D);
+        const int rem = n2 - c * (a.n_kv_heads * D);
+        const int g = rem / D, i = rem - g * D;
+        a.kv_new[(((size_t)b * a.n_kv_heads + g) * 2 + c) * D + i] = f32_to_bf16(y);
+    }
+}
+
+// Sums each of the N values (N a power of two <= 64) over the 64 lanes of
+// the wave, leaving the total of value i in the lanes whose top log2(N)
+// lane-id bits equal i. One butterfly halves the value count per step
+// (N - 1 shuffles in all instead of 6 N), then plain butterflies finish the
+// lanes that still share an index. The order of additions is fixed.
+template <int N, int TOTAL>
+__device__ __forceinline__ void halve(float (&v)[TOTAL], int lane) {
+    if constexpr (N > 1) {
+        constexpr int off = 32 * N / TOTAL;    // 32 on the first step, then 16, 8, ...
+        const bool upper = (lane & off) != 0;
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const float send = upper ? v[i] : v[i + N / 2];
+            const float keep = upper ? v[i + N / 2] : v[i];
+            v[i] = keep + __shfl_xor(send, off);
+        }
+        halve<N / 2, TOTAL>(v, lane);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ float reduce_scatter(float (&v)[N], int lane) {
+    static_assert(N >= 2 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
+    halve<N, N>(v, lane);
+    float r = v[0];
+#pragma unroll
+    for (int off = 32 / N; off >= 1; off >>= 1) r += __shfl_xor(r, off);
+    return r;
+}
+
+// 1a. Batches below 32: a GEMV on VALU. A workgroup owns 4 W rows and BT
+// sequences; its KS wavefronts split the hidden dimension into equal ranges,
+// and each lane reads 16-byte (8 x bf16) chunks, so every W row is read as
+// contiguous 1 KiB wave loads, all of a wave's loads issued before its
+// FMAs (short k ranges, unrolled). The wave's 4*BT partial sums are reduced
+// with a reduce-scatter butterfly and the KS waves' sums added through LDS in
+// wave order, so the result does not depend on timing.
+template <int BT, int KS>
+__global__ __launch_bounds__(64 * KS) void qkv_proj_gemv_kernel(StepArgs a) {
+    constexpr int NV = 4 * BT;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row0 = blockIdx.x * 4;
+    const int b0 = blockIdx.y * BT;
+    const int nb = min(BT, a.batch - b0);
+    const int krange = a.hidden / KS;     // a multiple of 512 (checked at launch)
+    const int kbeg = wave * krange;
+
+    if (blockIdx.x == 0 && threadIdx.x < nb) check_context_range(a, b0 + threadIdx.x);
+
+    float acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
+
+    const uint16_t *w0 = a.w + (size_t)row0 * a.hidden;
+#pragma unroll 2
+    for (int k = kbeg + lane * 8; k < kbeg + krange; k += 512) {
+        float wf[4][8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) unpack8(*reinterpret_cast<const uint4 *>(w0 + (size_t)r * a.hidden + k), wf[r]);
+#pragma unroll
+        for (int bb = 0; bb < BT; ++bb) {
+            if (bb < nb) {
+                float xf[8];
+                unpack8(*reinterpret_cast<const uint4 *>(a.x + (size_t)(b0 + bb) * a.hidden + k), xf);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[r * BT + bb] = fmaf(wf[r][e], xf[e], acc[r * BT + bb]);
+            }
+        }
+    }
+
+    const float y = reduce_scatter<NV>(acc, lane);
+    constexpr int SHIFT = NV == 64 ? 0 : NV == 32 ? 1 : NV == 16 ? 2 : 3;
+    const int idx = lane >> SHIFT;            // value index this lane holds
+    const bool owner = (lane & ((1 << SHIFT) - 1)) == 0;
+
+    float total = y;
+    if constexpr (KS > 1) {
+        __shared__ float part[KS][NV];
+        if (owner) part[wave][idx] = y;
+        __syncthreads();
+        if (wave != 0) return;
+        total = part[0][idx];
+#pragma unroll
+        for (int w = 1; w < KS; ++w) total += part[w][idx];
+    }
+    if (owner) {
+        const int r = idx / BT, bb = idx % BT;
+        if (bb < nb) store_projection(a, row0 + r, b0 + bb, total);
+    }
+}
+
+// 1b. Batches of 32 or more: the projection is a dense [N_qkv x hidden] x
+// [hidden x B] contraction, done on the matrix cores with
+// v_mfma_f32_16x16x32_bf16 (bf16 in, fp32 accumulate). One wavefront owns 16
+// W rows and 16*NB sequences, so every W byte is read once per step.
+// Operand layout of the 16x16x32 MFMA: lane l supplies A[i = l%16][k = 8*(l/16)
+// .. +7] and B[k = 8*(l/16) .. +7][j = l%16], and receives
+// D[i = 4*(l/16) + r][j = l%16], r < 4. A is the W tile (rows of W are
+// contiguous in k), B is x^T (rows of x are contiguous in k), so both operands
+// are plain 16-byte loads from row-major memory.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int NB>
+struct MfmaChunk {
+    static constexpr int UK = 4;   // 32-wide k steps per chunk (128 k)
+    uint4 w[UK];
+    uint4 x[UK][NB];
+};
+
+template <int NB>
+__device__ __forceinline__ void mfma_load(MfmaChunk<NB> &c, const uint16_t *wrow,
+                                          const uint16_t *const (&xrow)[NB], int k0) {
+#pragma unroll
+    for (int u = 0; u < MfmaChunk<NB>::UK; ++u) {
+        c.w[u] = *reinterpret_cast<const uint4 *>(wrow + k0 + 32 * u);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) c.x[u][nb] = *reinterpret_cast<const uint4 *>(xrow[nb] + k0 + 32 * u);
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void mfma_step(const MfmaChunk<NB> &c, f32x4 (&acc)[NB]) {
+#pragma unroll
+    for (int u = 0; u < MfmaChunk<NB>::UK; ++u) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, c.w[u]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, c.x[u][nb]),
+                                                              acc[nb], 0, 0, 0);
+    }
+}
+
+// Split-k: the workgroup's KS wavefronts (blockDim.x / 64, 2 or 4) take equal
+// k ranges of the same 16-row x 16*NB-sequence tile; their partial tiles are
+// added through LDS in wave order, so the result does not depend on timing.
+template <int NB>
+__global__ __launch_bounds__(256) void qkv_proj_mfma_kernel(StepArgs a) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int ks = blockDim.x >> 6;
+    const int row0 = blockIdx.x * 16;
+    const int b0 = blockIdx.y * 16 * NB;
+    const int i = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int krange = a.hidden / ks;      // a multiple of 256 (checked at launch)
+    const int kbeg = wave * krange;
+
+    if (blockIdx.x == 0 && wave == 0) {
+        for (int b = b0 + lane; b < min(a.batch, b0 + 16 * NB); b += 64) check_context_range(a, b);
+    }
+
+    // Columns past the batch read a valid row (the last sequence's) and are
+    // never stored, so the k loop has no per-lane branches.
+    const uint16_t *wrow = a.w + (size_t)(row0 + i) * a.hidden + kbeg + kq;
+    const uint16_t *xrow[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        xrow[nb] = a.x + (size_t)min(b0 + nb * 16 + i, a.batch - 1) * a.hidden + kbeg + kq;
+    f32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // The 128-wide chunks of a wave's k range come in pairs: ping-pong between
+    // two register sets, the next chunk's loads in flight while the current
+    // one feeds the matrix cores.
+    constexpr int KC = 32 * MfmaChunk<NB>::UK;
+    MfmaChunk<NB> c0, c1;
+    mfma_load(c0, wrow, xrow, 0);
+    for (int k0 = 0; k0 < krange; k0 += 2 * KC) {
+        mfma_load(c1, wrow, xrow, k0 + KC);
+        mfma_step(c0, acc);
+        if (k0 + 2 * KC < krange) mfma_load(c0, wrow, xrow, k0 + 2 * KC);
+        mfma_step(c1, acc);
+    }
+
+    __shared__ f32x4 partial[3][NB][64];
+    if (wave > 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) partial[wave - 1][nb][lane] = acc[nb];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 1; w < ks; ++w) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] += partial[w - 1][nb][lane];
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int b = b0 + nb * 16 + i;
+        if (b < a.batch) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) store_projection(a, row0 + 4 * (lane >> 4) + r, b, acc[nb][r]);
+        }
+    }
+}
+
+template <int BT>
+hipError_t launch_gemv(const StepArgs &a, hipStream_t st) {
+    // Largest split of the hidden dimension (up to 8 waves) that leaves each
+    // wave a range of at least two 512-wide steps; 1 for short rows.
+    int ks = 8;
+    while (ks > 1 && (a.hidden % (512 * ks) != 0 || a.hidden / (512 * ks) < 2)) ks >>= 1;
+    const dim3 grid(a.n_qkv / 4, (a.batch + BT - 1) / BT);
+    switch (ks) {
+        case 1: qkv_proj_gemv_kernel<BT, 1><<<grid, 64, 0, st>>>(a); break;
+        case 2: qkv_proj_gemv_kernel<BT, 2><<<grid, 128, 0, st>>>(a); break;
+        case 4: qkv_proj_gemv_kernel<BT, 4><<<grid, 256, 0, st>>>(a); break;
+        default: qkv_proj_gemv_kernel<BT, 8><<<grid, 512, 0, st>>>(a); break;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_projection(const StepArgs &a, hipStream_t st) {
+    if (a.hidden % 512 != 0 || a.n_qkv % 16 != 0) return hipErrorInvalidValue;
+    if (a.batch >= kMfmaMinBatch) {
+        // 16 W rows x 64 sequences per workgroup (32 for batches up to 32),
+        // k split over 4 wavefronts (2 when hidden is not a multiple of 1024)
+        const int threads = (a.hidden % 1024 == 0) ? 256 : 128;
+        if (a.batch <= 32) {
+            qkv_proj_mfma_kernel<2><<<dim3(a.n_qkv / 16, (a.batch + 31) / 32), threads, 0, st>>>(a);
+        } else {
+            qkv_proj_mfma_kernel<4><<<dim3(a.n_qkv / 16, (a.batch + 63) / 64), threads, 0, st>>>(a);
+        }
+    } else if (a.batch <= 4) {
+        launch_gemv<4>(a, st);
+    } else if (a.batch <= 8) {
+        launch_gemv<8>(a, st);
+    } else {
+        launch_gemv<16>(a, st);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dkv

@@ -195,6 +195,25 @@ void parallel_for(int64_t n, F f) {
 
 }  // namespace
 
+namespace dkv {
+
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t st, hipEvent_t *ev) {
+    const int G = a.n_q_heads / a.n_kv_heads;
+    if (!((a.head_dim == 128 || a.head_dim == 64) && (G == 1 || G == 2 || G == 4 || G == 8)))
+        return hipErrorInvalidValue;
+    hipError_t e;
+    if (ev) (void)hipEventRecord(ev[0], st);
+    if ((e = launch_projection(a, st)) != hipSuccess) return e;
+    if (ev) (void)hipEventRecord(ev[1], st);
+    if ((e = launch_split(a, st)) != hipSuccess) return e;
+    if (ev) (void)hipEventRecord(ev[2], st);
+    if ((e = launch_combine(a, st)) != hipSuccess) return e;
+    if (ev) (void)hipEventRecord(ev[3], st);
+    return hipSuccess;
+}
+
+}  // namespace dkv
+
 extern "C" {
 
 const char *dkv_last_error(void) { return g_last_error.c_str(); }
