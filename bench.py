@@ -189,8 +189,10 @@ def calibrate(dkv, r):
     torch.cuda.synchronize()
     dst.copy_(src)                    # reads 256 MiB, writes 256 MiB of HBM
     torch.cuda.synchronize()
-    base, nbytes, _ = r.host_pool.info()
-    dkv.probe_stream_read(base, 1 << 30, 256, 1, reps=1)        # 2 x 1 GiB host reads
+    if r.host_pool is not None:
+        base, nbytes, _ = r.host_pool.info()
+        dkv.probe_stream_read(base, min(1 << 30, nbytes - nbytes % (1 << 20)), 256, 1,
+                              reps=1)                       # 2 x (up to) 1 GiB host reads
     dkv.probe_stream_read(dst.data_ptr(), n, 2048, 4, reps=1)   # 2 x 256 MiB HBM reads
     torch.cuda.synchronize()
     log("calibration kernels done")
@@ -206,6 +208,9 @@ def main(argv=None):
     ap.add_argument("--no-hbm-leg", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the timed leg in the workload's own placement (for rocprofv3)")
+    ap.add_argument("--all-hbm", action="store_true",
+                    help="with --profile-run: place every page in HBM instead of the "
+                         "workload's own placement")
     ap.add_argument("--calibrate", action="store_true",
                     help="with --profile-run: also run kernels of known traffic (a 256 MiB "
                          "HBM-to-HBM copy, 1 GiB streaming reads of the host pool and of HBM) "
@@ -252,7 +257,9 @@ def main(argv=None):
                                 + B * wl.n_q_heads * d * 2)
 
     # ------------------------------------------------------------------ the workload's placement
-    log("%s: own placement leg" % wl.name)
+    if args.profile_run and args.all_hbm:
+        tail = np.full(B, 1 << 30, np.int32)
+    log("%s: %s placement leg" % (wl.name, "all-HBM" if args.profile_run and args.all_hbm else "own"))
     r = Resident(dkv, wl, ctx, tail, kv_source)
     host_kv_layer = 0
     for b in range(B):
@@ -267,7 +274,8 @@ def main(argv=None):
         if args.calibrate:
             calibrate(dkv, r)
         r.free()
-        print(json.dumps({"profile_run": True, "workload": wl.name, "ms_per_step": ms,
+        print(json.dumps({"profile_run": True, "workload": wl.name, "all_hbm": bool(args.all_hbm),
+                          "ms_per_step": ms,
                           "kernel_ms": kt}), flush=True)
         return 0
     out_own = r.out_bits(0)
