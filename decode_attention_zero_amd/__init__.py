@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "kv_layout_free": ([P], I32),
             "kv_layout_page_tier": ([P, I32, I32, P], I32),
             "kv_layout_split_tokens": ([P], I32),
+            "kv_layout_split_kernel": ([P], I32),
             "kv_layout_check_status": ([P], I32),
             "kv_append": ([P, I32, I32, I32, I32, P, P, P], I32),
             "kv_read": ([P, I32, I32, I32, I32, P, P], I32),
@@ -99,7 +100,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement", "kv_alloc_host",
             "kv_alloc_hbm", "kv_pool_free_pages", "kv_pool_info", "kv_pool_free",
             "kv_layout_create", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
-            "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
+            "kv_layout_split_kernel", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
             "dkv_probe_stream_read", "kv_layout_timing_enable", "kv_layout_timing_read"]
 
 
@@ -187,6 +188,11 @@ class Layout:
     @property
     def split_tokens(self) -> int:
         return lib().kv_layout_split_tokens(self.handle)
+
+    @property
+    def split_kernel(self) -> str:
+        """'regs' (register double buffer) or 'lds' (producer/consumer LDS ring)."""
+        return {0: "regs", 1: "lds"}[lib().kv_layout_split_kernel(self.handle)]
 
     def page_tier(self, seq: int, page: int) -> int:
         t = ctypes.c_int32()

@@ -110,6 +110,59 @@ struct SplitState {
             }
         }
     }
+
+    // Query rows of heads h0 .. h0 + G - 1 (this lane's 8 dims) and an empty
+    // softmax state.
+    __device__ __forceinline__ void init(const StepArgs &a, int b, int h0, int dl) {
+        const float *qb = a.q + ((size_t)b * a.n_q_heads + (size_t)h0) * D + dl * 8;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float4 lo = *reinterpret_cast<const float4 *>(qb + h * D);
+            const float4 hi = *reinterpret_cast<const float4 *>(qb + h * D + 4);
+            q[h][0] = lo.x; q[h][1] = lo.y; q[h][2] = lo.z; q[h][3] = lo.w;
+            q[h][4] = hi.x; q[h][5] = hi.y; q[h][6] = hi.z; q[h][7] = hi.w;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            m[h] = kNegInf;
+            l[h] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+        }
+    }
+
+    // Merges the row states (lanes l and l ^ off, off >= LPT) in a fixed order
+    // and writes the partial (m, l, o) of heads h0 .. h0 + G - 1 for split s.
+    __device__ __forceinline__ void finish(const StepArgs &a, int b, int h0, int s, int sub, int dl) {
+#pragma unroll
+        for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float mo = __shfl_xor(m[h], off);
+                const float lo = __shfl_xor(l[h], off);
+                const float M = fmaxf(m[h], mo);
+                const float c1 = rescale(m[h], M);
+                const float c2 = rescale(mo, M);
+                l[h] = fmaf(l[h], c1, lo * c2);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float ao = __shfl_xor(acc[h][e], off);
+                    acc[h][e] = fmaf(acc[h][e], c1, ao * c2);
+                }
+                m[h] = M;
+            }
+        }
+        if (sub == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const size_t slot = ((size_t)b * a.n_q_heads + (size_t)h0 + h) * a.max_splits + s;
+                float *po = a.part_o + slot * D + dl * 8;
+                *reinterpret_cast<float4 *>(po) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+                *reinterpret_cast<float4 *>(po + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+                if (dl == 0) a.part_ml[slot] = make_float2(m[h], l[h]);
+            }
+        }
+    }
 };
 
 template <int D, int G>
@@ -130,23 +183,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(StepArgs a) {
     const int dl = lane % LPT;
 
     S st;
-    {
-        const float *qb = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D + dl * 8;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float4 lo = *reinterpret_cast<const float4 *>(qb + h * D);
-            const float4 hi = *reinterpret_cast<const float4 *>(qb + h * D + 4);
-            st.q[h][0] = lo.x; st.q[h][1] = lo.y; st.q[h][2] = lo.z; st.q[h][3] = lo.w;
-            st.q[h][4] = hi.x; st.q[h][5] = hi.y; st.q[h][6] = hi.z; st.q[h][7] = hi.w;
-        }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        st.m[h] = kNegInf;
-        st.l[h] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.0f;
-    }
+    st.init(a, b, g * G, dl);
 
     const uint64_t *pt = a.page_table + (size_t)b * a.max_pages;
     const size_t run_off = (size_t)g * S::RUN + (size_t)lane * 16;
@@ -173,44 +210,119 @@ __global__ __launch_bounds__(64) void attn_split_kernel(StepArgs a) {
         st.template page<true>(ka, va, sub, t1 - p * kPageTokens);
     }
 
-    // Merge the row states (lanes l and l ^ off, off >= LPT) in a fixed order.
+    st.finish(a, b, g * G, s, sub, dl);
+}
+
+// ------------------------------------------------------------------------------
+// Producer/consumer variant. One workgroup per work item: wavefront 0 is the
+// producer and streams the item's page runs with LDS DMA
+// (global_load_lds_dwordx4: 16 bytes per lane straight into LDS, no
+// registers) into an NS-slot ring, keeping NS - 1 runs in flight;
+// wavefronts 1 .. NC are consumers, each owning G / NC of the group's query
+// heads, reading every run from LDS once it has landed. The run is fetched
+// from host memory or HBM once for all NC consumers. Per page the workgroup
+// meets at one barrier: the producer has waited for that run's loads
+// (s_waitcnt vmcnt, so the ring slot is complete) and the consumers have
+// finished the previous run (so its slot may be refilled). Every head's
+// arithmetic is the same as in attn_split_kernel, in the same order, so both
+// variants give identical bits.
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0],
+// expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding DMA load); the compiler may not move memory
+// accesses across it.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+constexpr int kAuxNontemporal = 2;   // cache-policy bits of the DMA load: nt
+
+template <int D, int G, int NC, int NS>
+__global__ __launch_bounds__(64 * (NC + 1)) void attn_split_lds_kernel(StepArgs a) {
+    static_assert(G % NC == 0 && NS >= 2, "bad variant");
+    constexpr int HW = G / NC;                 // query heads per consumer
+    using S = SplitState<D, HW>;
+    constexpr int NLD = S::NLD;
+    constexpr int LPT = S::LPT;
+    constexpr int LPP = 2 * NLD;               // DMA loads per page run
+    __shared__ __attribute__((aligned(16))) char ring[NS][S::RUN];
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int L = a.ctx_lens[b];
+    if (L < 0 || L >= a.capacity[b]) return;
+    const int t0 = s * a.split_tokens;
+    if (t0 >= L) return;
+    const int t1 = min(t0 + a.split_tokens, L);
+    const int p0 = t0 / kPageTokens;
+    const int np = (t1 + kPageTokens - 1) / kPageTokens - p0;   // pages p0 .. p0 + np - 1
+    const int pf = t1 / kPageTokens;                              // pages below pf are full
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+
+    if (wave == 0) {
+        // Producer. Page addresses come 64 at a time into one VGPR pair per
+        // lane and are broadcast with readlane, so no vector load of the page
+        // table sits between the DMA loads (its wait would drain them).
+        const uint64_t *pt = a.page_table + (size_t)b * a.max_pages + p0;
+        const size_t run_off = (size_t)g * S::RUN + (size_t)lane * 16;
+        uint64_t window = 0;
+        auto issue = [&](int i) {
+            if ((i & 63) == 0) window = (i + lane < np) ? pt[i + lane] : 0;
+            const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)window, i & 63);
+            const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(window >> 32), i & 63);
+            const char *src = reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo) + run_off;
+            char *dst = ring[i % NS];
 #pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float mo = __shfl_xor(st.m[h], off);
-            const float lo = __shfl_xor(st.l[h], off);
-            const float M = fmaxf(st.m[h], mo);
-            const float c1 = rescale(st.m[h], M);
-            const float c2 = rescale(mo, M);
-            st.l[h] = fmaf(st.l[h], c1, lo * c2);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float ao = __shfl_xor(st.acc[h][e], off);
-                st.acc[h][e] = fmaf(st.acc[h][e], c1, ao * c2);
-            }
-            st.m[h] = M;
+            for (int j = 0; j < LPP; ++j)
+                __builtin_amdgcn_global_load_lds(src + j * 1024, (__attribute__((address_space(3))) void *)(dst + j * 1024),
+                                                 16, 0, kAuxNontemporal);
+        };
+        for (int i = 0; i < NS - 1 && i < np; ++i) issue(i);
+        for (int i = 0; i < np; ++i) {
+            if (i + NS - 2 < np) wait_vmcnt<LPP * (NS - 2)>();   // runs i + 1 .. i + NS - 2 may still fly
+            else wait_vmcnt<0>();
+            ring_barrier();
+            if (i + NS - 1 < np) issue(i + NS - 1);              // refills the slot of run i - 1
         }
+        return;
     }
 
-    if (sub == 0) {
+    // Consumer wave c = wave - 1: query heads h0 .. h0 + HW - 1.
+    const int sub = lane / LPT;
+    const int dl = lane % LPT;
+    const int h0 = g * G + (wave - 1) * HW;
+    S st;
+    st.init(a, b, h0, dl);
+    for (int i = 0; i < np; ++i) {
+        ring_barrier();
+        const char *slot = ring[i % NS] + lane * 16;
+        uint4 kr[NLD], vr[NLD];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const size_t slot = ((size_t)b * a.n_q_heads + (size_t)g * G + h) * a.max_splits + s;
-            float *po = a.part_o + slot * D + dl * 8;
-            *reinterpret_cast<float4 *>(po) =
-                make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
-            *reinterpret_cast<float4 *>(po + 4) =
-                make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
-            if (dl == 0) a.part_ml[slot] = make_float2(st.m[h], st.l[h]);
-        }
+        for (int j = 0; j < NLD; ++j) kr[j] = *reinterpret_cast<const uint4 *>(slot + j * 1024);
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) vr[j] = *reinterpret_cast<const uint4 *>(slot + S::TILE + j * 1024);
+        if (p0 + i < pf) st.template page<false>(kr, vr, sub, kPageTokens);
+        else st.template page<true>(kr, vr, sub, t1 - (p0 + i) * kPageTokens);
     }
+    st.finish(a, b, h0, s, sub, dl);
 }
 
 template <int D, int G>
 void launch(const StepArgs &a, hipStream_t st) {
     dim3 grid(a.max_splits, a.n_kv_heads, a.batch);
-    attn_split_kernel<D, G><<<grid, 64, 0, st>>>(a);
+    if (a.split_variant == kSplitLds) {
+        // Consumers own at most 4 query heads each; 4 ring slots (3 runs in flight).
+        constexpr int NC = G > 4 ? G / 4 : 1;
+        attn_split_lds_kernel<D, G, NC, 4><<<grid, 64 * (NC + 1), 0, st>>>(a);
+    } else {
+        attn_split_kernel<D, G><<<grid, 64, 0, st>>>(a);
+    }
 }
 
 }  // namespace

@@ -11,6 +11,12 @@ namespace dkv {
 
 constexpr int kPageTokens = DKV_PAGE_TOKENS;
 
+// Split-attention kernel variants: one wavefront per work item with a
+// register double buffer, or a producer wavefront streaming page runs into an
+// LDS ring for consumer wavefronts.
+constexpr int kSplitRegisters = 0;
+constexpr int kSplitLds = 1;
+
 // Everything one decode step's kernels read or write. Built on the host by
 // decode_step from the layout and the caller's pointers; passed by value.
 struct StepArgs {
@@ -25,6 +31,7 @@ struct StepArgs {
     int32_t split_tokens;   // tokens per attention work item (multiple of 16)
     int32_t max_splits;     // partial slots per (sequence, query head)
     float qscale;           // log2(e) / sqrt(head_dim): scores come out in log2 units
+    int32_t split_variant;  // kSplitRegisters or kSplitLds
     // this layer's page table [batch][max_pages] of device addresses
     const uint64_t *page_table;
     const int32_t *capacity;  // [batch] slots per sequence (device)

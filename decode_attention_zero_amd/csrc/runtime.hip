@@ -86,6 +86,7 @@ struct dkv_layout {
     int32_t max_pages;
     int32_t split_tokens;
     int32_t max_splits;
+    int32_t split_variant;             // dkv::kSplitRegisters or dkv::kSplitLds
     dkv_pool *host_pool;
     dkv_pool *hbm_pool;
     std::vector<int64_t> page_index;   // [n_layers][batch][max_pages] index in its pool, -1 = none
@@ -173,6 +174,19 @@ int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, int32_t max_cap) 
            (int64_t)batch * n_kv_heads * ((max_cached + t - 1) / t) < 2048)
         t /= 2;
     return t;
+}
+
+// Split-attention kernel variant. The register double buffer is the default
+// for every group size: on MI355X it measured faster than the LDS
+// producer/consumer ring in the all-HBM placement (1 GiB of KV at group 4:
+// 189 us vs 258 us; group 8: 18.8 ms vs 27.6 ms for 64 GiB) and the same on
+// the host link. DKV_SPLIT_KERNEL=regs|lds overrides it.
+int32_t choose_split_variant(int32_t /*group*/) {
+    if (const char *env = getenv("DKV_SPLIT_KERNEL")) {
+        if (!strcmp(env, "lds")) return dkv::kSplitLds;
+        if (!strcmp(env, "regs")) return dkv::kSplitRegisters;
+    }
+    return dkv::kSplitRegisters;
 }
 
 // Parallel copy helper for host pages: runs f(first, last) over [0, n) in
@@ -383,6 +397,7 @@ dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t
     L->max_pages = max_pages;
     L->split_tokens = choose_split_tokens(batch, shape->n_kv_heads, max_cap);
     L->max_splits = std::max(1, (std::max(1, max_cap - 1) + L->split_tokens - 1) / L->split_tokens);
+    L->split_variant = choose_split_variant(shape->n_q_heads / shape->n_kv_heads);
 
     // Pages are taken in (layer, sequence, page) order, so each sequence's
     // pages of a tier are consecutive in their pool when it is fresh.
@@ -507,6 +522,8 @@ dkv_status kv_layout_page_tier(const dkv_layout *L, int32_t seq, int32_t page, i
 
 int32_t kv_layout_split_tokens(const dkv_layout *L) { return L ? L->split_tokens : 0; }
 
+int32_t kv_layout_split_kernel(const dkv_layout *L) { return L ? L->split_variant : -1; }
+
 static dkv_status check_range(const dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n,
                               const char *who) {
     if (!L) return fail(DKV_E_INVALID_ARG, "%s: null layout", who);
@@ -628,6 +645,7 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     a.n_qkv = (s->n_q_heads + 2 * s->n_kv_heads) * s->head_dim;
     a.max_pages = L->max_pages;
     a.split_tokens = L->split_tokens;
+    a.split_variant = L->split_variant;
     a.max_splits = L->max_splits;
     a.qscale = (float)(1.4426950408889634074 / std::sqrt((double)s->head_dim));
     a.page_table = L->d_page_table + (size_t)layer * L->batch * L->max_pages;

@@ -229,6 +229,15 @@ dkv_status kv_layout_check_status(dkv_layout *kv_layout);
  * of 16 fixed at creation, independent of placement. */
 int32_t kv_layout_split_tokens(const dkv_layout *kv_layout);
 
+/* Split-attention kernel the layout's decode steps use: 0 = one wavefront
+ * per work item with a register double buffer (the default), 1 = a producer
+ * wavefront that streams page runs with LDS DMA into a ring for consumer
+ * wavefronts that own the group's query heads. Both compute every head in
+ * the same order and give identical bits. Chosen at creation; the
+ * environment variable DKV_SPLIT_KERNEL=regs|lds, read by kv_layout_create,
+ * selects one. -1 for a NULL layout. */
+int32_t kv_layout_split_kernel(const dkv_layout *kv_layout);
+
 /* Thread-local message of the last failing call on this thread. */
 const char *dkv_last_error(void);
 

@@ -299,3 +299,46 @@ def test_out_of_range_context_is_flagged():
             s.layout.check_status()
     finally:
         s.free()
+
+
+# --------------------------------------------------------------------------- kernel variants
+@pytest.mark.parametrize("wl_name,ctx", [
+    ("tiny-h512-b1-ctx1024", [1024]),
+    ("llama3-8b-b8-ctx32768-host", [0, 1, 17, 700, 2049]),
+    ("llama3-70b-b16-ctx131072-8layers-host", [300, 47, 1025]),
+], ids=["g1-d64", "g4-d128", "g8-d128"])
+def test_split_kernel_variants_bit_identical(oracle, monkeypatch, wl_name, ctx):
+    """The register-double-buffer and the LDS producer/consumer split kernels
+    compute every head in the same order: identical bits, and the oracle's
+    gates, with host and HBM pages mixed."""
+    wl = configs.BY_NAME[wl_name].replace(batch=len(ctx), n_layers=1)
+    outs, outs32 = {}, {}
+    for variant in ("regs", "lds"):
+        monkeypatch.setenv("DKV_SPLIT_KERNEL", variant)
+        s = H.Setup(wl, ctx_lens=ctx, hbm_tail=[0, 40, 1 << 20, 16, 0][:len(ctx)])
+        try:
+            assert s.layout.split_kernel == variant
+            outs[variant] = bits(s.run())
+            outs32[variant] = s.run(f32=True).cpu().numpy()
+        finally:
+            s.free()
+    assert np.array_equal(outs["regs"], outs["lds"])
+    assert np.array_equal(outs32["regs"].view(np.uint32), outs32["lds"].view(np.uint32))
+    ref = H.oracle_full(oracle, wl, 0, np.asarray(ctx, np.int32))["attn_out"]
+    assert_gates(H.bf16_to_f64(outs["lds"]), ref, "%s lds" % wl_name)
+    check_tight(outs32["lds"].astype(np.float64),
+                tight_reference(oracle, wl, 0, np.asarray(ctx, np.int32)), "%s lds" % wl_name)
+
+
+def test_lds_split_kernel_split_edges(oracle, monkeypatch):
+    """Ring wrap-around and partial last pages: splits of 1..9 pages."""
+    monkeypatch.setenv("DKV_SPLIT_KERNEL", "lds")
+    monkeypatch.setenv("DKV_SPLIT_TOKENS", "144")
+    ctx = [1, 15, 16, 17, 63, 64, 65, 143, 144, 145, 300]
+    wl = configs.LLAMA8B_HOST.replace(batch=len(ctx))
+    s = H.Setup(wl, ctx_lens=ctx, hbm_tail=0)
+    try:
+        assert s.layout.split_kernel == "lds" and s.layout.split_tokens == 144
+        check_tight(f32(s.run(f32=True)), tight_reference(oracle, wl, 0, s.ctx), "lds split 144 edges")
+    finally:
+        s.free()
