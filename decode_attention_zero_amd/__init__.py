@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
             "kv_pool_info": ([P, P, P, P], I32),
             "kv_pool_free": ([P], I32),
             "kv_layout_create": ([SP, I32, P, P, P, P, P], I32),
+            "kv_layout_create_windowed": ([SP, I32, P, P, P, P, P, P], I32),
+            "kv_advance": ([P, P, P], I32),
             "kv_layout_free": ([P], I32),
             "kv_layout_page_tier": ([P, I32, I32, P], I32),
             "kv_layout_split_tokens": ([P], I32),
@@ -99,7 +101,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement", "kv_alloc_host",
             "kv_alloc_hbm", "kv_pool_free_pages", "kv_pool_info", "kv_pool_free",
-            "kv_layout_create", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
+            "kv_layout_create", "kv_layout_create_windowed", "kv_advance", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
             "kv_layout_split_kernel", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
             "dkv_probe_stream_read", "kv_layout_timing_enable", "kv_layout_timing_read"]
 
@@ -231,6 +233,30 @@ def kv_layout_create(shape: Shape, capacity_tokens, hbm_tail_tokens=None,
                                   host_pool.handle if host_pool else None,
                                   hbm_pool.handle if hbm_pool else None, ctypes.byref(h)))
     return Layout(h.value, shape, len(cap), cap)
+
+
+def kv_layout_create_windowed(shape: Shape, capacity_tokens, window_tokens, ctx_lens,
+                              host_pool: Pool, hbm_pool: Pool) -> Layout:
+    """Layout whose HBM part is a window of the most recent pages, slid by kv_advance."""
+    cap = np.ascontiguousarray(capacity_tokens, dtype=np.int32)
+    win = np.ascontiguousarray(np.broadcast_to(np.asarray(window_tokens, dtype=np.int32), cap.shape))
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    if ctx.shape != cap.shape:
+        raise ValueError("ctx_lens must have one entry per sequence")
+    h = ctypes.c_void_p()
+    _check(lib().kv_layout_create_windowed(ctypes.byref(shape), len(cap), _np_ptr(cap), _np_ptr(win),
+                                           _np_ptr(ctx), host_pool.handle, hbm_pool.handle,
+                                           ctypes.byref(h)))
+    return Layout(h.value, shape, len(cap), cap)
+
+
+def kv_advance(layout: Layout, ctx_lens, stream=None) -> None:
+    """ctx_lens[b] += 1 on the device (int32 device tensor, in place), sliding a
+    windowed layout's HBM window; enqueued on `stream` (default: current)."""
+    import torch
+    if ctx_lens.dtype != torch.int32 or tuple(ctx_lens.shape) != (layout.batch,):
+        raise ValueError("ctx_lens must be an int32 [batch] device tensor")
+    _check(lib().kv_advance(layout.handle, _dev_ptr(ctx_lens, "ctx_lens"), _stream_ptr(stream)))
 
 
 def kv_append(layout: Layout, layer: int, seq: int, start_token: int, k: np.ndarray,

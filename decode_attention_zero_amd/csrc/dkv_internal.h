@@ -49,6 +49,25 @@ struct StepArgs {
     uint32_t *status;         // range flag (bit 0: a ctx_lens entry out of range)
 };
 
+// What kv_advance's kernel reads and writes (see kv_advance in dkv.h).
+struct AdvanceArgs {
+    int32_t batch;
+    int32_t n_layers;
+    int32_t max_pages;
+    int32_t max_window;
+    int64_t page_bytes;
+    int32_t windowed;            // 0: only advance ctx_lens
+    uint64_t *page_table;        // [n_layers][batch][max_pages]
+    const uint64_t *host_pages;  // [n_layers][batch][max_pages] (windowed)
+    const uint64_t *ring;        // [n_layers][batch][max_window] (windowed)
+    const int32_t *window;       // [batch] (windowed)
+    const int32_t *capacity;     // [batch]
+    int32_t *ctx_lens;           // [batch], advanced in place
+    uint32_t *status;
+};
+
+hipError_t launch_advance(const AdvanceArgs &a, hipStream_t stream);
+
 // Enqueues the decode step's kernels on `stream`. With `events` non-null,
 // records events[0] before the projection, events[1] after it, events[2]
 // after the split attention and events[3] after the combine.

@@ -82,21 +82,28 @@ struct dkv_layout {
     int32_t batch;
     std::vector<int32_t> capacity;
     std::vector<int32_t> n_pages;
-    std::vector<int32_t> first_hbm;
+    std::vector<int32_t> first_hbm;    // static placement: pages [first_hbm, n_pages) are HBM
     int32_t max_pages;
     int32_t split_tokens;
     int32_t max_splits;
     int32_t split_variant;             // dkv::kSplitRegisters or dkv::kSplitLds
     dkv_pool *host_pool;
     dkv_pool *hbm_pool;
-    std::vector<int64_t> page_index;   // [n_layers][batch][max_pages] index in its pool, -1 = none
-    uint64_t *d_page_table;            // same shape, device addresses
+    std::vector<std::pair<dkv_pool *, int64_t>> owned;   // every page the layout holds
+    uint64_t *d_page_table;            // [n_layers][batch][max_pages] current device address of each page
     int32_t *d_capacity;
     float *d_q;
     uint16_t *d_kv_new;
     float *d_part_o;
     float2 *d_part_ml;
     uint32_t *d_status;
+    // sliding hot window (kv_layout_create_windowed); windowed == 0 otherwise
+    int32_t windowed = 0;
+    std::vector<int32_t> window;       // HBM window pages per sequence
+    int32_t max_window = 0;
+    uint64_t *d_host_pages = nullptr;  // [n_layers][batch][max_pages] host page of every page
+    uint64_t *d_ring = nullptr;        // [n_layers][batch][max_window] HBM pages of the window
+    int32_t *d_window = nullptr;       // [batch] window pages per sequence
     // per-kernel timing (measurement mode only)
     std::vector<hipEvent_t> timing_events;   // 4 per recorded step
     int32_t timing_recorded = 0;
@@ -106,10 +113,6 @@ namespace {
 
 size_t pt_index(const dkv_layout *L, int layer, int b, int p) {
     return ((size_t)layer * L->batch + b) * L->max_pages + p;
-}
-
-dkv_pool *pool_of(const dkv_layout *L, int b, int p) {
-    return p >= L->first_hbm[b] ? L->hbm_pool : L->host_pool;
 }
 
 bool take_pages(dkv_pool *pool, int64_t n, std::vector<int64_t> &out) {
@@ -135,31 +138,37 @@ void give_back(dkv_pool *pool, int64_t idx) {
     }
 }
 
+uint64_t page_addr(const dkv_pool *pool, int64_t idx) {
+    return (uint64_t)(uintptr_t)(pool->dev_base + idx * pool->page_bytes);
+}
+
 void free_device(dkv_layout *L) {
-    if (L->d_page_table) (void)hipFree(L->d_page_table);
-    if (L->d_capacity) (void)hipFree(L->d_capacity);
-    if (L->d_q) (void)hipFree(L->d_q);
-    if (L->d_kv_new) (void)hipFree(L->d_kv_new);
-    if (L->d_part_o) (void)hipFree(L->d_part_o);
-    if (L->d_part_ml) (void)hipFree(L->d_part_ml);
-    if (L->d_status) (void)hipFree(L->d_status);
+    for (void *p : {(void *)L->d_page_table, (void *)L->d_capacity, (void *)L->d_q, (void *)L->d_kv_new,
+                    (void *)L->d_part_o, (void *)L->d_part_ml, (void *)L->d_status, (void *)L->d_host_pages,
+                    (void *)L->d_ring, (void *)L->d_window})
+        if (p) (void)hipFree(p);
 }
 
 void release_pages(dkv_layout *L) {
-    for (int layer = 0; layer < L->shape.n_layers; ++layer)
-        for (int b = 0; b < L->batch; ++b)
-            for (int p = 0; p < L->n_pages[b]; ++p)
-                give_back(pool_of(L, b, p), L->page_index[pt_index(L, layer, b, p)]);
+    for (auto &pi : L->owned) give_back(pi.first, pi.second);
+    L->owned.clear();
 }
 
-char *host_page_ptr(const dkv_layout *L, int layer, int b, int p) {
-    const dkv_pool *pool = pool_of(L, b, p);
-    return pool->host_base + L->page_index[pt_index(L, layer, b, p)] * pool->page_bytes;
+// Current device addresses of pages [p_first, p_last] of (layer, seq), read
+// from the device page table (the authority: kv_advance moves pages there).
+hipError_t table_row(const dkv_layout *L, int layer, int b, int p_first, int p_last, std::vector<uint64_t> &row) {
+    row.resize((size_t)(p_last - p_first + 1));
+    return hipMemcpy(row.data(), L->d_page_table + pt_index(L, layer, b, p_first), row.size() * sizeof(uint64_t),
+                     hipMemcpyDeviceToHost);
 }
 
-char *dev_page_ptr(const dkv_layout *L, int layer, int b, int p) {
-    const dkv_pool *pool = pool_of(L, b, p);
-    return pool->dev_base + L->page_index[pt_index(L, layer, b, p)] * pool->page_bytes;
+// CPU address of a page that lives in the host pool, nullptr for an HBM page.
+char *host_view(const dkv_layout *L, uint64_t addr) {
+    const dkv_pool *hp = L->host_pool;
+    if (!hp) return nullptr;
+    const uint64_t base = (uint64_t)(uintptr_t)hp->dev_base;
+    if (addr < base || addr >= base + (uint64_t)(hp->n_pages * hp->page_bytes)) return nullptr;
+    return hp->host_base + (addr - base);
 }
 
 int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, int32_t max_cap) {
@@ -343,22 +352,102 @@ dkv_status kv_pool_free(dkv_pool *pool) {
     return DKV_OK;
 }
 
+static dkv_status check_pools(const dkv_shape *shape, int32_t batch, const int32_t *capacity_tokens,
+                              dkv_pool *host_pool, dkv_pool *hbm_pool, dkv_layout **out, const char *who) {
+    if (!out || !shape_ok(shape) || batch <= 0 || !capacity_tokens)
+        return fail(DKV_E_INVALID_ARG, "%s: bad shape, batch or null argument", who);
+    if (!shape_supported(shape))
+        return fail(DKV_E_UNSUPPORTED, "%s: head_dim must be 64/128, group 1/2/4/8, hidden a multiple of 512", who);
+    if (batch > 65535) return fail(DKV_E_INVALID_ARG, "%s: batch > 65535", who);
+    for (dkv_pool *p : {host_pool, hbm_pool}) {
+        if (p && (p->shape.n_kv_heads != shape->n_kv_heads || p->shape.head_dim != shape->head_dim))
+            return fail(DKV_E_INVALID_ARG, "%s: pool page shape differs from the layout's", who);
+    }
+    if (host_pool && host_pool->tier != 0) return fail(DKV_E_INVALID_ARG, "%s: host_pool is HBM", who);
+    if (hbm_pool && hbm_pool->tier != 1) return fail(DKV_E_INVALID_ARG, "%s: hbm_pool is host", who);
+    for (int b = 0; b < batch; ++b)
+        if (capacity_tokens[b] <= 0) return fail(DKV_E_INVALID_ARG, "%s: capacity of sequence %d is not positive", who, b);
+    return DKV_OK;
+}
+
+// Allocates the layout's device tables and scratch, uploads the page table
+// (and the window tables), and hands the layout out; frees everything on
+// failure.
+static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &table,
+                                const std::vector<uint64_t> *host_pages, const std::vector<uint64_t> *ring,
+                                dkv_layout **out) {
+    const dkv_shape *shape = &L->shape;
+    const int batch = L->batch;
+    int32_t max_cap = 0;
+    for (int b = 0; b < batch; ++b) max_cap = std::max(max_cap, L->capacity[b]);
+    L->split_tokens = choose_split_tokens(batch, shape->n_kv_heads, max_cap);
+    L->max_splits = std::max(1, (std::max(1, max_cap - 1) + L->split_tokens - 1) / L->split_tokens);
+    L->split_variant = choose_split_variant(shape->n_q_heads / shape->n_kv_heads);
+    if (L->host_pool) ++L->host_pool->n_layouts;
+    if (L->hbm_pool) ++L->hbm_pool->n_layouts;
+
+    auto cleanup = [&](dkv_status st) {
+        free_device(L);
+        release_pages(L);
+        if (L->host_pool) --L->host_pool->n_layouts;
+        if (L->hbm_pool) --L->hbm_pool->n_layouts;
+        delete L;
+        return st;
+    };
+    const int D = shape->head_dim, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads;
+    const size_t n_entries = table.size();
+    const size_t bytes_q = (size_t)batch * Hq * D * sizeof(float);
+    const size_t bytes_kv = (size_t)batch * Hkv * 2 * D * sizeof(uint16_t);
+    const size_t bytes_po = (size_t)batch * Hq * L->max_splits * D * sizeof(float);
+    const size_t bytes_ml = (size_t)batch * Hq * L->max_splits * sizeof(float2);
+    struct {
+        void **ptr;
+        size_t bytes;
+    } allocs[] = {{(void **)&L->d_page_table, n_entries * sizeof(uint64_t)},
+                  {(void **)&L->d_capacity, (size_t)batch * sizeof(int32_t)},
+                  {(void **)&L->d_q, bytes_q},
+                  {(void **)&L->d_kv_new, bytes_kv},
+                  {(void **)&L->d_part_o, bytes_po},
+                  {(void **)&L->d_part_ml, bytes_ml},
+                  {(void **)&L->d_status, 256},
+                  {(void **)&L->d_host_pages, host_pages ? host_pages->size() * sizeof(uint64_t) : 0},
+                  {(void **)&L->d_ring, ring ? ring->size() * sizeof(uint64_t) : 0},
+                  {(void **)&L->d_window, L->windowed ? (size_t)batch * sizeof(int32_t) : 0}};
+    for (auto &a : allocs) {
+        if (a.bytes == 0) continue;
+        if (hipMalloc(a.ptr, a.bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            *a.ptr = nullptr;
+            fail(DKV_E_OUT_OF_MEMORY, "kv_layout_create: hipMalloc of %zu bytes failed", a.bytes);
+            return cleanup(DKV_E_OUT_OF_MEMORY);
+        }
+    }
+    hipError_t e = hipMemcpy(L->d_page_table, table.data(), n_entries * sizeof(uint64_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(L->d_capacity, L->capacity.data(), (size_t)batch * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess && host_pages)
+        e = hipMemcpy(L->d_host_pages, host_pages->data(), host_pages->size() * sizeof(uint64_t),
+                      hipMemcpyHostToDevice);
+    if (e == hipSuccess && ring)
+        e = hipMemcpy(L->d_ring, ring->data(), ring->size() * sizeof(uint64_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess && L->windowed) {
+        e = hipMemcpy(L->d_window, L->window.data(), (size_t)batch * sizeof(int32_t), hipMemcpyHostToDevice);
+    }
+    if (e == hipSuccess) e = hipMemset(L->d_status, 0, 256);
+    if (e == hipSuccess) e = hipMemset(L->d_kv_new, 0, bytes_kv);
+    if (e != hipSuccess) {
+        hip_fail(e, "kv_layout_create: initialising device tables");
+        return cleanup(DKV_E_HIP);
+    }
+    *out = L;
+    return DKV_OK;
+}
+
 dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t *capacity_tokens,
                             const int32_t *hbm_tail_tokens, dkv_pool *host_pool, dkv_pool *hbm_pool,
                             dkv_layout **out) {
-    if (!out || !shape_ok(shape) || batch <= 0 || !capacity_tokens)
-        return fail(DKV_E_INVALID_ARG, "kv_layout_create: bad shape, batch or null argument");
-    if (!shape_supported(shape))
-        return fail(DKV_E_UNSUPPORTED,
-                    "kv_layout_create: head_dim must be 64/128, group 1/2/4/8, hidden a multiple of 512");
-    if (batch > 65535) return fail(DKV_E_INVALID_ARG, "kv_layout_create: batch > 65535");
-    for (dkv_pool *p : {host_pool, hbm_pool}) {
-        if (p && (p->shape.n_kv_heads != shape->n_kv_heads || p->shape.head_dim != shape->head_dim))
-            return fail(DKV_E_INVALID_ARG, "kv_layout_create: pool page shape differs from the layout's");
-    }
-    if (host_pool && host_pool->tier != 0) return fail(DKV_E_INVALID_ARG, "kv_layout_create: host_pool is HBM");
-    if (hbm_pool && hbm_pool->tier != 1) return fail(DKV_E_INVALID_ARG, "kv_layout_create: hbm_pool is host");
-
+    dkv_status st = check_pools(shape, batch, capacity_tokens, host_pool, hbm_pool, out, "kv_layout_create");
+    if (st != DKV_OK) return st;
     dkv_layout *L = new dkv_layout();
     L->shape = *shape;
     L->batch = batch;
@@ -368,7 +457,7 @@ dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t
     L->host_pool = host_pool;
     L->hbm_pool = hbm_pool;
     int64_t need_host = 0, need_hbm = 0;
-    int32_t max_pages = 0, max_cap = 0;
+    int32_t max_pages = 0;
     for (int b = 0; b < batch; ++b) {
         const int32_t tail = hbm_tail_tokens ? hbm_tail_tokens[b] : 0;
         if (kv_placement(capacity_tokens[b], tail, &L->n_pages[b], &L->first_hbm[b]) != DKV_OK) {
@@ -379,7 +468,6 @@ dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t
         need_host += L->first_hbm[b];
         need_hbm += L->n_pages[b] - L->first_hbm[b];
         max_pages = std::max(max_pages, L->n_pages[b]);
-        max_cap = std::max(max_cap, capacity_tokens[b]);
     }
     need_host *= shape->n_layers;
     need_hbm *= shape->n_layers;
@@ -395,15 +483,10 @@ dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t
                     (long long)(hbm_pool ? hbm_pool->n_free : 0));
     }
     L->max_pages = max_pages;
-    L->split_tokens = choose_split_tokens(batch, shape->n_kv_heads, max_cap);
-    L->max_splits = std::max(1, (std::max(1, max_cap - 1) + L->split_tokens - 1) / L->split_tokens);
-    L->split_variant = choose_split_variant(shape->n_q_heads / shape->n_kv_heads);
 
     // Pages are taken in (layer, sequence, page) order, so each sequence's
     // pages of a tier are consecutive in their pool when it is fresh.
-    const size_t n_entries = (size_t)shape->n_layers * batch * max_pages;
-    L->page_index.assign(n_entries, -1);
-    std::vector<uint64_t> table(n_entries, 0);
+    std::vector<uint64_t> table((size_t)shape->n_layers * batch * max_pages, 0);
     std::vector<int64_t> got;
     for (int layer = 0; layer < shape->n_layers; ++layer) {
         for (int b = 0; b < batch; ++b) {
@@ -415,57 +498,86 @@ dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t
                 take_pages(pool, p_hi - p_lo, got);   // counts were checked above
                 for (int p = p_lo; p < p_hi; ++p) {
                     const int64_t idx = got[p - p_lo];
-                    L->page_index[pt_index(L, layer, b, p)] = idx;
-                    table[pt_index(L, layer, b, p)] = (uint64_t)(uintptr_t)(pool->dev_base + idx * pool->page_bytes);
+                    L->owned.emplace_back(pool, idx);
+                    table[pt_index(L, layer, b, p)] = page_addr(pool, idx);
                 }
             }
         }
     }
-    if (host_pool) ++host_pool->n_layouts;
-    if (hbm_pool) ++hbm_pool->n_layouts;
+    return finish_layout(L, table, nullptr, nullptr, out);
+}
 
-    auto cleanup = [&](dkv_status st) {
-        free_device(L);
-        release_pages(L);
-        if (host_pool) --host_pool->n_layouts;
-        if (hbm_pool) --hbm_pool->n_layouts;
+dkv_status kv_layout_create_windowed(const dkv_shape *shape, int32_t batch, const int32_t *capacity_tokens,
+                                     const int32_t *window_tokens, const int32_t *ctx_lens, dkv_pool *host_pool,
+                                     dkv_pool *hbm_pool, dkv_layout **out) {
+    const char *who = "kv_layout_create_windowed";
+    dkv_status st = check_pools(shape, batch, capacity_tokens, host_pool, hbm_pool, out, who);
+    if (st != DKV_OK) return st;
+    if (!window_tokens || !ctx_lens || !host_pool || !hbm_pool)
+        return fail(DKV_E_INVALID_ARG, "%s: window_tokens, ctx_lens and both pools are required", who);
+    dkv_layout *L = new dkv_layout();
+    L->shape = *shape;
+    L->batch = batch;
+    L->windowed = 1;
+    L->capacity.assign(capacity_tokens, capacity_tokens + batch);
+    L->n_pages.resize(batch);
+    L->first_hbm.resize(batch);
+    L->window.resize(batch);
+    L->host_pool = host_pool;
+    L->hbm_pool = hbm_pool;
+    int64_t need_host = 0, need_hbm = 0;
+    int32_t max_pages = 0, max_window = 0;
+    for (int b = 0; b < batch; ++b) {
+        if (window_tokens[b] <= 0 || ctx_lens[b] < 0 || ctx_lens[b] >= capacity_tokens[b]) {
+            delete L;
+            return fail(DKV_E_INVALID_ARG, "%s: sequence %d: window %d must be > 0 and ctx_lens %d in [0, capacity %d)",
+                        who, b, window_tokens[b], ctx_lens[b], capacity_tokens[b]);
+        }
+        L->n_pages[b] = (int32_t)(((int64_t)capacity_tokens[b] + DKV_PAGE_TOKENS - 1) / DKV_PAGE_TOKENS);
+        L->window[b] = std::min<int32_t>(L->n_pages[b], (window_tokens[b] + DKV_PAGE_TOKENS - 1) / DKV_PAGE_TOKENS);
+        L->first_hbm[b] = L->n_pages[b];
+        need_host += L->n_pages[b];
+        need_hbm += L->window[b];
+        max_pages = std::max(max_pages, L->n_pages[b]);
+        max_window = std::max(max_window, L->window[b]);
+    }
+    need_host *= shape->n_layers;
+    need_hbm *= shape->n_layers;
+    if (host_pool->n_free < need_host || hbm_pool->n_free < need_hbm) {
         delete L;
-        return st;
-    };
-    const int D = shape->head_dim, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads;
-    const size_t bytes_q = (size_t)batch * Hq * D * sizeof(float);
-    const size_t bytes_kv = (size_t)batch * Hkv * 2 * D * sizeof(uint16_t);
-    const size_t bytes_po = (size_t)batch * Hq * L->max_splits * D * sizeof(float);
-    const size_t bytes_ml = (size_t)batch * Hq * L->max_splits * sizeof(float2);
-    struct {
-        void **ptr;
-        size_t bytes;
-    } allocs[] = {{(void **)&L->d_page_table, n_entries * sizeof(uint64_t)},
-                  {(void **)&L->d_capacity, (size_t)batch * sizeof(int32_t)},
-                  {(void **)&L->d_q, bytes_q},
-                  {(void **)&L->d_kv_new, bytes_kv},
-                  {(void **)&L->d_part_o, bytes_po},
-                  {(void **)&L->d_part_ml, bytes_ml},
-                  {(void **)&L->d_status, 256}};
-    for (auto &a : allocs) {
-        if (hipMalloc(a.ptr, a.bytes) != hipSuccess) {
-            (void)hipGetLastError();
-            *a.ptr = nullptr;
-            fail(DKV_E_OUT_OF_MEMORY, "kv_layout_create: hipMalloc of %zu bytes failed", a.bytes);
-            return cleanup(DKV_E_OUT_OF_MEMORY);
+        return fail(DKV_E_CAPACITY, "%s: needs %lld host / %lld HBM pages, pools have %lld / %lld free", who,
+                    (long long)need_host, (long long)need_hbm, (long long)host_pool->n_free,
+                    (long long)hbm_pool->n_free);
+    }
+    L->max_pages = max_pages;
+    L->max_window = max_window;
+
+    // Every page has a host page; page p of the window uses HBM ring slot
+    // p % W. The pages [P - W + 1, P] up to the one holding slot ctx_lens[b]
+    // start in HBM.
+    const size_t n_entries = (size_t)shape->n_layers * batch * max_pages;
+    std::vector<uint64_t> table(n_entries, 0), host_pages(n_entries, 0);
+    std::vector<uint64_t> ring((size_t)shape->n_layers * batch * max_window, 0);
+    std::vector<int64_t> got;
+    for (int layer = 0; layer < shape->n_layers; ++layer) {
+        for (int b = 0; b < batch; ++b) {
+            const int W = L->window[b];
+            take_pages(host_pool, L->n_pages[b], got);
+            for (int p = 0; p < L->n_pages[b]; ++p) {
+                L->owned.emplace_back(host_pool, got[p]);
+                host_pages[pt_index(L, layer, b, p)] = table[pt_index(L, layer, b, p)] = page_addr(host_pool, got[p]);
+            }
+            take_pages(hbm_pool, W, got);
+            for (int k = 0; k < W; ++k) {
+                L->owned.emplace_back(hbm_pool, got[k]);
+                ring[((size_t)layer * batch + b) * max_window + k] = page_addr(hbm_pool, got[k]);
+            }
+            const int P = ctx_lens[b] / DKV_PAGE_TOKENS;
+            for (int p = std::max(0, P - W + 1); p <= P; ++p)
+                table[pt_index(L, layer, b, p)] = ring[((size_t)layer * batch + b) * max_window + p % W];
         }
     }
-    hipError_t e = hipMemcpy(L->d_page_table, table.data(), n_entries * sizeof(uint64_t), hipMemcpyHostToDevice);
-    if (e == hipSuccess)
-        e = hipMemcpy(L->d_capacity, capacity_tokens, (size_t)batch * sizeof(int32_t), hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = hipMemset(L->d_status, 0, 256);
-    if (e == hipSuccess) e = hipMemset(L->d_kv_new, 0, bytes_kv);
-    if (e != hipSuccess) {
-        hip_fail(e, "kv_layout_create: initialising device tables");
-        return cleanup(DKV_E_HIP);
-    }
-    *out = L;
-    return DKV_OK;
+    return finish_layout(L, table, &host_pages, &ring, out);
 }
 
 dkv_status kv_layout_timing_enable(dkv_layout *L, int32_t enable, int32_t max_steps) {
@@ -516,7 +628,10 @@ dkv_status kv_layout_free(dkv_layout *L) {
 dkv_status kv_layout_page_tier(const dkv_layout *L, int32_t seq, int32_t page, int32_t *tier) {
     if (!L || !tier || seq < 0 || seq >= L->batch || page < 0 || page >= L->n_pages[seq])
         return fail(DKV_E_INVALID_ARG, "kv_layout_page_tier: index out of range");
-    *tier = page >= L->first_hbm[seq] ? 1 : 0;
+    std::vector<uint64_t> row;
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(table_row(L, 0, seq, page, page, row));
+    *tier = host_view(L, row[0]) ? 0 : 1;
     return DKV_OK;
 }
 
@@ -546,44 +661,43 @@ dkv_status kv_append(dkv_layout *L, int32_t layer, int32_t seq, int32_t start, i
     const size_t row = (size_t)D * 2;
     const size_t tok_elems = (size_t)Hkv * D;
     const int p_first = start / DKV_PAGE_TOKENS, p_last = (start + n - 1) / DKV_PAGE_TOKENS;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    HIP_TRY(hipStreamSynchronize(hs));            // earlier work may still move or write pages
+    std::vector<uint64_t> addr;
+    HIP_TRY(table_row(L, layer, seq, p_first, p_last, addr));
+
+    auto fill = [&](char *page, int p) {
+        const int t_lo = std::max(start, p * DKV_PAGE_TOKENS);
+        const int t_hi = std::min(start + n, (p + 1) * DKV_PAGE_TOKENS);
+        for (int t = t_lo; t < t_hi; ++t)
+            for (int g = 0; g < Hkv; ++g) {
+                const size_t src = (size_t)(t - start) * tok_elems + (size_t)g * D;
+                memcpy(page + row_offset(s, t % DKV_PAGE_TOKENS, g, 0), k + src, row);
+                memcpy(page + row_offset(s, t % DKV_PAGE_TOKENS, g, 1), v + src, row);
+            }
+    };
 
     // Host pages: the CPU writes them in place, page by page, in parallel.
     parallel_for(p_last - p_first + 1, [&](int64_t i0, int64_t i1) {
-        for (int64_t i = i0; i < i1; ++i) {
-            const int p = p_first + (int)i;
-            if (pool_of(L, seq, p)->tier != 0) continue;
-            char *page = host_page_ptr(L, layer, seq, p);
-            const int t_lo = std::max(start, p * DKV_PAGE_TOKENS);
-            const int t_hi = std::min(start + n, (p + 1) * DKV_PAGE_TOKENS);
-            for (int t = t_lo; t < t_hi; ++t)
-                for (int g = 0; g < Hkv; ++g) {
-                    const size_t src = (size_t)(t - start) * tok_elems + (size_t)g * D;
-                    memcpy(page + row_offset(s, t % DKV_PAGE_TOKENS, g, 0), k + src, row);
-                    memcpy(page + row_offset(s, t % DKV_PAGE_TOKENS, g, 1), v + src, row);
-                }
-        }
+        for (int64_t i = i0; i < i1; ++i)
+            if (char *page = host_view(L, addr[i])) fill(page, p_first + (int)i);
     });
 
     // HBM pages: assemble each touched page on the host (reading it back
     // first when only part of it is written) and copy it in.
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    std::vector<char> img;
-    for (int p = std::max(p_first, L->first_hbm[seq]); p <= p_last; ++p) {
-        const size_t pb = (size_t)L->hbm_pool->page_bytes;
-        img.resize(pb);
-        char *dpage = dev_page_ptr(L, layer, seq, p);
+    const size_t pb = (size_t)page_bytes_of(s);
+    std::vector<char> img(pb);
+    for (int p = p_first; p <= p_last; ++p) {
+        const uint64_t a = addr[p - p_first];
+        if (host_view(L, a)) continue;
+        void *dpage = reinterpret_cast<void *>((uintptr_t)a);
         const int t_lo = std::max(start, p * DKV_PAGE_TOKENS);
         const int t_hi = std::min(start + n, (p + 1) * DKV_PAGE_TOKENS);
         if (t_hi - t_lo < DKV_PAGE_TOKENS) {
             HIP_TRY(hipMemcpyAsync(img.data(), dpage, pb, hipMemcpyDeviceToHost, hs));
             HIP_TRY(hipStreamSynchronize(hs));
         }
-        for (int t = t_lo; t < t_hi; ++t)
-            for (int g = 0; g < Hkv; ++g) {
-                const size_t src = (size_t)(t - start) * tok_elems + (size_t)g * D;
-                memcpy(img.data() + row_offset(s, t % DKV_PAGE_TOKENS, g, 0), k + src, row);
-                memcpy(img.data() + row_offset(s, t % DKV_PAGE_TOKENS, g, 1), v + src, row);
-            }
+        fill(img.data(), p);
         HIP_TRY(hipMemcpyAsync(dpage, img.data(), pb, hipMemcpyHostToDevice, hs));
         HIP_TRY(hipStreamSynchronize(hs));
     }
@@ -601,16 +715,15 @@ dkv_status kv_read(const dkv_layout *L, int32_t layer, int32_t seq, int32_t star
     const int D = s->head_dim, Hkv = s->n_kv_heads;
     const size_t row = (size_t)D * 2;
     const size_t tok_elems = (size_t)Hkv * D;
-    std::vector<char> img;
     const int p_first = start / DKV_PAGE_TOKENS, p_last = (start + n - 1) / DKV_PAGE_TOKENS;
+    std::vector<uint64_t> addr;
+    HIP_TRY(table_row(L, layer, seq, p_first, p_last, addr));
+    std::vector<char> img((size_t)page_bytes_of(s));
     for (int p = p_first; p <= p_last; ++p) {
-        const dkv_pool *pool = pool_of(L, seq, p);
-        const char *page;
-        if (pool->tier == 0) {
-            page = host_page_ptr(L, layer, seq, p);
-        } else {
-            img.resize((size_t)pool->page_bytes);
-            HIP_TRY(hipMemcpy(img.data(), dev_page_ptr(L, layer, seq, p), img.size(), hipMemcpyDeviceToHost));
+        const char *page = host_view(L, addr[p - p_first]);
+        if (!page) {
+            HIP_TRY(hipMemcpy(img.data(), reinterpret_cast<const void *>((uintptr_t)addr[p - p_first]), img.size(),
+                              hipMemcpyDeviceToHost));
             page = img.data();
         }
         const int t_lo = std::max(start, p * DKV_PAGE_TOKENS);
@@ -676,6 +789,28 @@ dkv_status decode_step(dkv_layout *L, int32_t layer, const uint16_t *q_in, const
 dkv_status decode_step_f32(dkv_layout *L, int32_t layer, const uint16_t *q_in, const uint16_t *W_qkv,
                            const int32_t *ctx_lens, float *attn_out, dkv_stream_t stream) {
     return step_impl(L, layer, q_in, W_qkv, ctx_lens, attn_out, 1, stream, "decode_step_f32");
+}
+
+dkv_status kv_advance(dkv_layout *L, int32_t *ctx_lens, dkv_stream_t stream) {
+    if (!L || !ctx_lens) return fail(DKV_E_INVALID_ARG, "kv_advance: null argument");
+    if ((uintptr_t)ctx_lens & 3u) return fail(DKV_E_INVALID_ARG, "kv_advance: misaligned ctx_lens");
+    dkv::AdvanceArgs a{};
+    a.batch = L->batch;
+    a.n_layers = L->shape.n_layers;
+    a.max_pages = L->max_pages;
+    a.max_window = L->max_window;
+    a.page_bytes = page_bytes_of(&L->shape);
+    a.windowed = L->windowed;
+    a.page_table = L->d_page_table;
+    a.host_pages = L->d_host_pages;
+    a.ring = L->d_ring;
+    a.window = L->d_window;
+    a.capacity = L->d_capacity;
+    a.ctx_lens = ctx_lens;
+    a.status = L->d_status;
+    hipError_t e = dkv::launch_advance(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kv_advance");
+    return DKV_OK;
 }
 
 dkv_status kv_layout_check_status(dkv_layout *L) {

@@ -151,12 +151,31 @@ dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch,
                             dkv_pool *host_pool, dkv_pool *hbm_pool,
                             dkv_layout **out);
 
+/* A layout whose HBM part is a sliding hot window instead of a fixed tail
+ * (DirectKV digest, 局限与后续工作: hot KV in HBM, cold KV read in place from
+ * host memory). Sequence b gets room for capacity_tokens[b] slots in every
+ * layer, a host page for every one of its ceil(capacity / 16) pages, and
+ * W_b = min(pages, ceil(window_tokens[b] / 16)) HBM pages. The W_b pages up
+ * to and including the one holding slot ctx_lens[b] (the slot the next
+ * decode_step writes) are HBM-resident; page p always uses HBM page p % W_b
+ * of the sequence's window. kv_advance slides the window as the sequence
+ * grows. Host arrays of length `batch`: capacity_tokens (> 0), window_tokens
+ * (> 0), ctx_lens (in [0, capacity)). Both pools are required. Allocation,
+ * ownership and errors as kv_layout_create. */
+dkv_status kv_layout_create_windowed(const dkv_shape *shape, int32_t batch,
+                                     const int32_t *capacity_tokens,
+                                     const int32_t *window_tokens,
+                                     const int32_t *ctx_lens,
+                                     dkv_pool *host_pool, dkv_pool *hbm_pool,
+                                     dkv_layout **out);
+
 /* Returns the layout's pages to their pools and frees its device memory.
  * Synchronises the device first. NULL is accepted and ignored. */
 dkv_status kv_layout_free(dkv_layout *layout);
 
-/* Tier of page `page` of sequence `seq` (same in every layer): 0 = host,
- * 1 = HBM. Errors: DKV_E_INVALID_ARG for out-of-range indices. */
+/* Tier of page `page` of sequence `seq` (same in every layer) as the page
+ * table holds it now (synchronises the device first): 0 = host, 1 = HBM.
+ * Errors: DKV_E_INVALID_ARG for out-of-range indices. */
 dkv_status kv_layout_page_tier(const dkv_layout *layout, int32_t seq, int32_t page,
                                int32_t *tier);
 
@@ -219,6 +238,21 @@ dkv_status decode_step_f32(dkv_layout *kv_layout, int32_t layer,
                            const uint16_t *q_in, const uint16_t *W_qkv,
                            const int32_t *ctx_lens, float *attn_out,
                            dkv_stream_t stream);
+
+/* Advances every sequence by one decoded token, on the device: for each b
+ * with ctx_lens[b] + 1 < capacity, ctx_lens[b] += 1 (in place; ctx_lens is
+ * the device array decode_step reads). In a windowed layout, when the new
+ * value starts a page (a multiple of 16), that page takes the HBM page of
+ * the window's oldest page, whose contents are first copied to its own host
+ * page (every layer), and the page table is repointed; the slots from the
+ * new ctx_lens[b] on are assumed to hold nothing yet. A sequence that has no
+ * room for another slot is left as it is and raises the flag that
+ * kv_layout_check_status reports. Enqueued on `stream` after the step that
+ * wrote slot ctx_lens[b]; it allocates nothing, copies nothing from the host
+ * and does not synchronise, so a decode step and kv_advance can be captured
+ * together in one HIP graph and replayed step after step. Host-side checks:
+ * DKV_E_INVALID_ARG for a null or misaligned pointer. */
+dkv_status kv_advance(dkv_layout *kv_layout, int32_t *ctx_lens, dkv_stream_t stream);
 
 /* Synchronises the device and reports (then clears) the in-kernel range
  * flag: DKV_OK, or DKV_E_CAPACITY if some decode_step since the last check

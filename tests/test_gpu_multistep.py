@@ -1,0 +1,217 @@
+"""Multi-step decode through the C ABI: decode_step followed by kv_advance,
+step after step, eagerly and replayed from one captured HIP graph, on a
+layout whose HBM part is a sliding window of the most recent pages.
+
+Inputs are chosen so that every fresh K/V value is computed exactly: x holds
+small integers and W_qkv multiples of 1/16, so the projection is exact in
+fp32 and fp64 and both sides round the same value to bf16. The oracle then
+rebuilds each step's context itself (the seeded initial cache plus the K/V
+it projected for the earlier steps) and never sees a GPU output.
+
+Checked: every step's attn_out against the oracle (bf16 gates and the tight
+fp32 gate); graph replays bit-identical to the eager run; after the run, the
+written-back slots (host pages demoted by the window and HBM pages still in
+it) equal the oracle's bf16 K/V bit for bit, the seeded cache is untouched,
+and each page sits in the tier the window puts it in."""
+import numpy as np
+import pytest
+
+import synth
+from synth import configs
+from tests import harness as H
+from tests.conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
+
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+TIGHT_REL_L2 = 1e-4
+WL = configs.TINY.replace(batch=3)
+CTX0 = np.array([5, 30, 47], np.int32)
+STEPS = 40
+WINDOW = 32                     # tokens: 2 HBM pages per sequence
+
+
+def bf16_bits(values: np.ndarray) -> np.ndarray:
+    """Exact bf16 bit patterns of values that bf16 represents exactly."""
+    f = np.asarray(values, np.float32)
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(H.bf16_to_f64(bits), f.astype(np.float64))
+    return bits
+
+
+def step_inputs():
+    """x_t: integers in [-2, 2]; W_qkv: multiples of 1/16 in [-1/8, 1/8] (bf16 bits)."""
+    xs = [synth.int_bf16(7, 30, t, WL.batch * WL.hidden, -2, 2).reshape(WL.batch, WL.hidden)
+          for t in range(STEPS)]
+    Wk = H.bf16_to_f64(synth.int_bf16(7, 31, 0, WL.n_qkv * WL.hidden, -2, 2)).reshape(WL.n_qkv, WL.hidden)
+    return xs, bf16_bits(Wk / 16.0)
+
+
+def oracle_run(orc, xs, W):
+    """Per step: the oracle's [B][Hq*d] output and each sequence's fresh bf16 K/V."""
+    d, Hq, Hkv = WL.head_dim, WL.n_q_heads, WL.n_kv_heads
+    Kc = [[wl_kv("k", b)] for b in range(WL.batch)]
+    Vc = [[wl_kv("v", b)] for b in range(WL.batch)]
+    outs, fresh = [], []
+    for t in range(STEPS):
+        out = np.zeros((WL.batch, Hq * d))
+        fk = []
+        for b in range(WL.batch):
+            y = orc.qkv_projection(xs[t][b], W)
+            kn = orc.f64_to_bf16(y[Hq * d:(Hq + Hkv) * d]).reshape(Hkv, d)
+            vn = orc.f64_to_bf16(y[(Hq + Hkv) * d:]).reshape(Hkv, d)
+            K = np.concatenate(Kc[b])
+            V = np.concatenate(Vc[b])
+            for h in range(Hq):
+                g = orc.kv_head_of(h, Hq, Hkv)
+                out[b, h * d:(h + 1) * d] = orc.attention_head(
+                    y[h * d:(h + 1) * d], K[:, g, :], V[:, g, :], H.bf16_to_f64(kn[g]), H.bf16_to_f64(vn[g]))
+            Kc[b].append(kn[None])
+            Vc[b].append(vn[None])
+            fk.append((kn, vn))
+        outs.append(out)
+        fresh.append(fk)
+    return outs, fresh
+
+
+def wl_kv(which, b):
+    return WL.kv(which, 0, b, 0, int(CTX0[b]))
+
+
+def make_layout(windowed: bool):
+    import torch
+    import decode_attention_zero_amd as dkv
+    shape = dkv.Shape.of(WL.hidden, WL.n_q_heads, WL.n_kv_heads, WL.head_dim, 1)
+    cap = CTX0 + STEPS + 1
+    pages = [int(dkv.kv_placement(int(c), 0)[0]) for c in cap]
+    if windowed:
+        host = dkv.kv_alloc_host(shape, sum(pages))
+        hbm = dkv.kv_alloc_hbm(shape, sum(min(p, WINDOW // 16) for p in pages))
+        layout = dkv.kv_layout_create_windowed(shape, cap, WINDOW, CTX0, host, hbm)
+    else:
+        host = dkv.kv_alloc_host(shape, sum(pages))
+        hbm = None
+        layout = dkv.kv_layout_create(shape, cap, None, host, None)
+    for b in range(WL.batch):
+        dkv.kv_append(layout, 0, b, 0, wl_kv("k", b), wl_kv("v", b))
+    ctx = torch.from_numpy(CTX0.copy()).cuda()
+    return dkv, layout, host, hbm, ctx
+
+
+def free_all(layout, host, hbm):
+    import torch
+    torch.cuda.synchronize()
+    layout.free()
+    host.free()
+    if hbm:
+        hbm.free()
+
+
+def run_eager(windowed, xs, W):
+    import torch
+    dkv, layout, host, hbm, ctx = make_layout(windowed)
+    Wd = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
+    outs = []
+    try:
+        for t in range(STEPS):
+            x = torch.from_numpy(xs[t].view(np.int16)).cuda().view(torch.bfloat16)
+            out = dkv.decode_step_f32(layout, 0, x, Wd, ctx)
+            dkv.kv_advance(layout, ctx)
+            outs.append(out.cpu().numpy())
+        assert np.array_equal(ctx.cpu().numpy(), CTX0 + STEPS)
+        layout.check_status()
+        return outs, dkv, layout, host, hbm
+    except Exception:
+        free_all(layout, host, hbm)
+        raise
+
+
+@pytest.mark.parametrize("windowed", [True, False], ids=["window", "static-host"])
+def test_multistep_eager_against_oracle(oracle, windowed):
+    xs, W = step_inputs()
+    ref, fresh = oracle_run(oracle, xs, W)
+    outs, dkv, layout, host, hbm = run_eager(windowed, xs, W)
+    try:
+        for t in range(STEPS):
+            got = outs[t].astype(np.float64)
+            rel = H.rel_l2(got, ref[t])
+            assert np.all(np.isfinite(got)), t
+            assert rel <= TIGHT_REL_L2, (t, rel)
+            assert np.abs(got - ref[t]).max() <= MAX_ABS, t
+        H.log("multistep %s: %d steps, worst tight rel-L2 %.3e" % (
+            "window" if windowed else "static", STEPS,
+            max(H.rel_l2(outs[t].astype(np.float64), ref[t]) for t in range(STEPS))))
+        for b in range(WL.batch):
+            L0 = int(CTX0[b])
+            k_all, v_all = dkv.kv_read(layout, 0, b, 0, L0 + STEPS)
+            assert np.array_equal(k_all[:L0], wl_kv("k", b)), b
+            assert np.array_equal(v_all[:L0], wl_kv("v", b)), b
+            for t in range(STEPS):
+                assert np.array_equal(k_all[L0 + t], fresh[t][b][0]), (b, t)
+                assert np.array_equal(v_all[L0 + t], fresh[t][b][1]), (b, t)
+            if windowed:
+                P = (L0 + STEPS) // 16
+                Wp = WINDOW // 16
+                for p in range((L0 + STEPS + 1 + 15) // 16):
+                    want = 1 if P - Wp < p <= P else 0
+                    assert layout.page_tier(b, p) == want, (b, p, P)
+    finally:
+        free_all(layout, host, hbm)
+
+
+def test_multistep_graph_replay_matches_eager(oracle):
+    """One captured graph (decode_step + kv_advance) replayed STEPS times,
+    with the next step's x copied in and a synchronisation between replays;
+    every replay equals the eager run bit for bit."""
+    import torch
+    xs, W = step_inputs()
+    eager, dkv, layout, host, hbm = run_eager(True, xs, W)
+    free_all(layout, host, hbm)
+    dkv, layout, host, hbm, ctx = make_layout(True)
+    try:
+        Wd = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
+        x_buf = torch.empty((WL.batch, WL.hidden), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((WL.batch, WL.n_q_heads * WL.head_dim), dtype=torch.float32, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            dkv.decode_step_f32(layout, 0, x_buf, Wd, ctx, out)
+            dkv.kv_advance(layout, ctx)
+        torch.cuda.synchronize()
+        assert np.array_equal(ctx.cpu().numpy(), CTX0)     # capture ran nothing
+        for t in range(STEPS):
+            x_buf.copy_(torch.from_numpy(xs[t].view(np.int16)).cuda().view(torch.bfloat16))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy().view(np.uint32), eager[t].view(np.uint32)), t
+        assert np.array_equal(ctx.cpu().numpy(), CTX0 + STEPS)
+        layout.check_status()
+    finally:
+        free_all(layout, host, hbm)
+
+
+def test_advance_stops_at_capacity():
+    import torch
+    import decode_attention_zero_amd as dkv
+    shape = dkv.Shape.of(WL.hidden, WL.n_q_heads, WL.n_kv_heads, WL.head_dim, 1)
+    cap = np.array([4, 40], np.int32)
+    host = dkv.kv_alloc_host(shape, 1 + 3)
+    layout = dkv.kv_layout_create(shape, cap, None, host, None)
+    try:
+        ctx = torch.tensor([2, 5], dtype=torch.int32, device="cuda")
+        dkv.kv_advance(layout, ctx)                     # 3 < 4: fine
+        torch.cuda.synchronize()
+        layout.check_status()
+        dkv.kv_advance(layout, ctx)                     # 4 would leave no slot: stays, flagged
+        torch.cuda.synchronize()
+        assert ctx.cpu().tolist() == [3, 7]
+        with pytest.raises(dkv.DkvError):
+            layout.check_status()
+    finally:
+        torch.cuda.synchronize()
+        layout.free()
+        host.free()
