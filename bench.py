@@ -198,6 +198,45 @@ def calibrate(dkv, r):
     log("calibration kernels done")
 
 
+SWEEP_HOST_FRACTIONS = (0.0, 0.01, 0.03, 0.1, 0.25, 0.5, 0.75, 1.0)
+
+
+def sweep(dkv, wl, ctx, kv_source, kv_bytes, args):
+    """Step time as the host-resident share of the same KV goes from 0 to 1:
+    the first round(f * L_b) cached tokens of each sequence on the host, the
+    rest (and the new slot) in HBM. Prints one JSON line with a row per share
+    and the roofline model T* = max(host bytes / C_host, HBM bytes / 8 TB/s)."""
+    B = len(ctx)
+    rows = []
+    ceiling = None
+    for f in SWEEP_HOST_FRACTIONS:
+        host_tokens = np.floor(ctx.astype(np.float64) * f).astype(np.int64)
+        tail = (ctx.astype(np.int64) + 1 - host_tokens).astype(np.int32)
+        r = Resident(dkv, wl, ctx, tail, kv_source)
+        host_kv = 0
+        for b in range(B):
+            n, first = dkv.kv_placement(int(ctx[b]) + 1, int(tail[b]))
+            host_kv += min(int(ctx[b]), first * dkv.PAGE_TOKENS) * wl.kv_bytes_per_token
+        host_kv *= wl.n_layers
+        steps = max(args.steps, 50) if f < 0.05 else args.steps
+        ms = r.timed(steps, args.warmup)
+        if ceiling is None and r.host_pool is not None:
+            ceiling, _, _ = probe_ceiling(dkv, r.host_pool, HOST_PROBES[:3])
+        r.free()
+        rows.append({"host_fraction": f, "host_kv_bytes": host_kv, "ms_per_step": round(ms, 4),
+                     "effective_kv_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2)})
+        log("sweep f=%.2f: %.4f ms/step" % (f, ms))
+    for row in rows:
+        hb = row["host_kv_bytes"]
+        t_star = max(hb / (ceiling * 1e9) if ceiling else 0.0, (kv_bytes - hb) / (HBM_PEAK_GBPS * 1e9))
+        row["t_star_ms"] = round(t_star * 1e3, 4)
+        row["frac_of_roofline"] = round(t_star * 1e3 / row["ms_per_step"], 4)
+    print(json.dumps({"sweep": "host_fraction", "workload": wl.name, "kv_bytes_per_step": kv_bytes,
+                      "host_link_ceiling_GBps": round(ceiling, 3) if ceiling else None,
+                      "hbm_peak_GBps": HBM_PEAK_GBPS, "rows": rows}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +245,11 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama3-8b-b8-ctx32768-host")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-leg", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="crossover sweep instead of the bench line: the workload's KV with the "
+                         "host-resident share stepped from 0 to 100 %% (rest in HBM)")
+    ap.add_argument("--no-comparators", action="store_true",
+                    help="skip the naive zero-copy and staging comparator legs")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the timed leg in the workload's own placement (for rocprofv3)")
     ap.add_argument("--all-hbm", action="store_true",
@@ -256,6 +300,9 @@ def main(argv=None):
     step_bytes = wl.n_layers * (kv_layer_bytes + w_bytes + B * wl.hidden * 2 + B * Hkv * d * 4
                                 + B * wl.n_q_heads * d * 2)
 
+    if args.sweep:
+        return sweep(dkv, wl, ctx, kv_source, kv_bytes, args)
+
     # ------------------------------------------------------------------ the workload's placement
     if args.profile_run and args.all_hbm:
         tail = np.full(B, 1 << 30, np.int32)
@@ -279,26 +326,46 @@ def main(argv=None):
                           "kernel_ms": kt}), flush=True)
         return 0
     out_own = r.out_bits(0)
+    split_kernel_name = ("attn_split_persistent_kernel (%d wavefronts)" % r.layout.split_waves
+                         if r.layout.split_waves > 0 else "attn_split_kernel")
     ceiling = ceiling_rows = None
     if r.host_pool is not None:
         ceiling, ceiling_rows, _ = probe_ceiling(dkv, r.host_pool, HOST_PROBES)
-    r.free()
     log("own placement: %.3f ms/step, split kernel %.3f ms" % (ms, kt["split"]))
 
     value = kv_bytes / (ms * 1e-3) / 1e9
     split_gbps = kv_bytes / (kt["split"] * 1e-3) / 1e9
 
+    # ------------------------------------------------------------------ comparator: naive zero-copy
+    comparators = {}
+    if r.host_pool is not None and not args.no_comparators:
+        default_kernel = r.layout.split_kernel
+        r.layout.split_kernel = "naive"
+        n_cmp = max(1, min(args.steps, 5))
+        ms_n = r.timed(n_cmp, 1)
+        out_naive = r.out_bits(0)
+        r.layout.split_kernel = default_kernel
+        comparators["naive_zero_copy"] = {
+            "what": "one work item per query head: each KV head's pages read once per query "
+                    "head of its group (%dx the link bytes of the grouped kernel)" % wl.group,
+            "ms_per_step": round(ms_n, 4),
+            "effective_kv_GBps": round(kv_bytes / (ms_n * 1e-3) / 1e9, 3),
+            "host_link_bytes_per_step": host_kv * wl.group,
+            "step_time_vs_method": round(ms_n / ms, 3),
+            "bit_identical_to_method": bool(np.array_equal(out_own, out_naive)),
+        }
+        log("naive zero-copy: %.3f ms/step" % ms_n)
+
     # ------------------------------------------------------------------ every page in HBM
     hbm = None
     if not args.no_hbm_leg:
         log("HBM-placement leg")
-        r = Resident(dkv, wl, ctx, np.full(B, 1 << 30, np.int32), kv_source)
+        rh = Resident(dkv, wl, ctx, np.full(B, 1 << 30, np.int32), kv_source)
         n_hbm_steps = max(args.steps, 50) if wl.n_layers == 1 else args.steps
-        ms_h = r.timed(n_hbm_steps, args.warmup)
-        kt_h = r.kernel_times(n_hbm_steps)
-        hbm_ceiling, hbm_rows, _ = probe_ceiling(dkv, r.hbm_pool, HBM_PROBES)
-        out_hbm = r.out_bits(0)
-        r.free()
+        ms_h = rh.timed(n_hbm_steps, args.warmup)
+        kt_h = rh.kernel_times(n_hbm_steps)
+        hbm_ceiling, hbm_rows, _ = probe_ceiling(dkv, rh.hbm_pool, HBM_PROBES)
+        out_hbm = rh.out_bits(0)
         hbm = {
             "ms_per_step": round(ms_h, 4),
             "kv_GBps": round(kv_bytes / (ms_h * 1e-3) / 1e9, 1),
@@ -312,6 +379,41 @@ def main(argv=None):
             "bit_identical_to_own_placement": bool(np.array_equal(out_own, out_hbm)),
         }
         log("HBM leg: %.4f ms/step, split kernel %.1f GB/s" % (ms_h, hbm["split_kernel_GBps"]))
+
+        # -------------------------------------------------------------- comparator: staging
+        if r.hbm_pool is None and r.host_pool is not None and not args.no_comparators:
+            import torch
+            stream = torch.cuda.current_stream()
+            host_bytes = r.host_pool.info()[1]
+            n_cmp = max(1, min(args.steps, 5))
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            copy_ms = step_ms = 0.0
+            for i in range(n_cmp + 1):
+                e0.record(stream)
+                dkv.kv_pool_copy(rh.hbm_pool, r.host_pool, host_bytes, stream)
+                e1.record(stream)
+                rh.step()
+                e2.record(stream)
+                torch.cuda.synchronize()
+                if i:      # the first round warms up
+                    copy_ms += e0.elapsed_time(e1) / n_cmp
+                    step_ms += e1.elapsed_time(e2) / n_cmp
+            out_staged = rh.out_bits(0)
+            comparators["staging"] = {
+                "what": "copy-engine copy of the host pool into an HBM buffer of the same size "
+                        "(hipMemcpyAsync), then the decode step on the HBM copy",
+                "ms_per_step": round(copy_ms + step_ms, 4),
+                "copy_ms": round(copy_ms, 4),
+                "copy_GBps": round(host_bytes / (copy_ms * 1e-3) / 1e9, 2),
+                "decode_ms": round(step_ms, 4),
+                "effective_kv_GBps": round(kv_bytes / ((copy_ms + step_ms) * 1e-3) / 1e9, 3),
+                "extra_hbm_bytes": host_bytes,
+                "step_time_vs_method": round((copy_ms + step_ms) / ms, 3),
+                "bit_identical_to_method": bool(np.array_equal(out_own, out_staged)),
+            }
+            log("staging: copy %.3f ms + step %.3f ms" % (copy_ms, step_ms))
+        rh.free()
+    r.free()
 
     # ------------------------------------------------------------------ CPU oracle
     cpu = None
@@ -360,7 +462,7 @@ def main(argv=None):
                    "head_dim": d, "kv_placement": placement,
                    "kv_bytes_per_step": kv_bytes, "host_kv_bytes_per_step": host_kv,
                    "algorithmic_bytes_per_step": step_bytes},
-        "roofline": {"bound": "host_link", "kernel": "attn_split_kernel",
+        "roofline": {"bound": "host_link", "kernel": split_kernel_name,
                      "achieved": round(split_gbps, 3), "peak": PCIE_GEN5_X16_GBPS,
                      "unit": "GB/s", "frac": round(split_gbps / PCIE_GEN5_X16_GBPS, 4),
                      "traffic": counter_traffic(wl.name),
@@ -374,6 +476,7 @@ def main(argv=None):
         "kernel_ms": {k: round(v, 4) for k, v in kt.items()},
         "host_link_probe": ceiling_rows,
         "hbm_placement": hbm,
+        "comparators": comparators,
         "parity": parity,
         "cpu_baseline": cpu,
     }

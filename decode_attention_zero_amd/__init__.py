@@ -82,12 +82,15 @@ def lib() -> ctypes.CDLL:
             "kv_layout_page_tier": ([P, I32, I32, P], I32),
             "kv_layout_split_tokens": ([P], I32),
             "kv_layout_split_kernel": ([P], I32),
+            "kv_layout_set_split_kernel": ([P, I32], I32),
+            "kv_layout_split_waves": ([P], I32),
             "kv_layout_check_status": ([P], I32),
             "kv_append": ([P, I32, I32, I32, I32, P, P, P], I32),
             "kv_read": ([P, I32, I32, I32, I32, P, P], I32),
             "decode_step": ([P, I32, P, P, P, P, P], I32),
             "decode_step_f32": ([P, I32, P, P, P, P, P], I32),
             "dkv_probe_stream_read": ([P, ctypes.c_uint64, I32, I32, I32, P], I32),
+            "kv_pool_copy": ([P, P, I64, P], I32),
             "kv_layout_timing_enable": ([P, I32, I32], I32),
             "kv_layout_timing_read": ([P, P, P, P, P], I32),
         }
@@ -102,8 +105,8 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement", "kv_alloc_host",
             "kv_alloc_hbm", "kv_pool_free_pages", "kv_pool_info", "kv_pool_free",
             "kv_layout_create", "kv_layout_create_windowed", "kv_advance", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
-            "kv_layout_split_kernel", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
-            "dkv_probe_stream_read", "kv_layout_timing_enable", "kv_layout_timing_read"]
+            "kv_layout_split_kernel", "kv_layout_set_split_kernel", "kv_layout_split_waves", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
+            "dkv_probe_stream_read", "kv_pool_copy", "kv_layout_timing_enable", "kv_layout_timing_read"]
 
 
 def _check(status: int) -> None:
@@ -168,6 +171,11 @@ class Pool:
             self.handle = None
 
 
+def kv_pool_copy(dst: Pool, src: Pool, nbytes: int, stream=None) -> None:
+    """Staging comparator: copy-engine copy of src's first nbytes into dst."""
+    _check(lib().kv_pool_copy(dst.handle, src.handle, nbytes, _stream_ptr(stream)))
+
+
 def kv_alloc_host(shape: Shape, n_pages: int, flags: int = HOST_COHERENT) -> Pool:
     h = ctypes.c_void_p()
     _check(lib().kv_alloc_host(ctypes.byref(shape), n_pages, flags, ctypes.byref(h)))
@@ -193,8 +201,18 @@ class Layout:
 
     @property
     def split_kernel(self) -> str:
-        """'regs' (register double buffer) or 'lds' (producer/consumer LDS ring)."""
-        return {0: "regs", 1: "lds"}[lib().kv_layout_split_kernel(self.handle)]
+        """'regs' (register double buffer), 'lds' (producer/consumer LDS ring) or
+        'naive' (comparator: one work item per query head)."""
+        return {0: "regs", 1: "lds", 2: "naive"}[lib().kv_layout_split_kernel(self.handle)]
+
+    @property
+    def split_waves(self) -> int:
+        """Wavefronts of the register split kernel (0: one per work item)."""
+        return lib().kv_layout_split_waves(self.handle)
+
+    @split_kernel.setter
+    def split_kernel(self, name: str) -> None:
+        _check(lib().kv_layout_set_split_kernel(self.handle, {"regs": 0, "lds": 1, "naive": 2}[name]))
 
     def page_tier(self, seq: int, page: int) -> int:
         t = ctypes.c_int32()

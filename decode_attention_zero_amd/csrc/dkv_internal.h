@@ -16,6 +16,8 @@ constexpr int kPageTokens = DKV_PAGE_TOKENS;
 // LDS ring for consumer wavefronts.
 constexpr int kSplitRegisters = 0;
 constexpr int kSplitLds = 1;
+// Comparator: one wavefront per query head, each KV head fetched G times.
+constexpr int kSplitNaive = 2;
 
 // Everything one decode step's kernels read or write. Built on the host by
 // decode_step from the layout and the caller's pointers; passed by value.
@@ -31,7 +33,8 @@ struct StepArgs {
     int32_t split_tokens;   // tokens per attention work item (multiple of 16)
     int32_t max_splits;     // partial slots per (sequence, query head)
     float qscale;           // log2(e) / sqrt(head_dim): scores come out in log2 units
-    int32_t split_variant;  // kSplitRegisters or kSplitLds
+    int32_t split_variant;  // kSplitRegisters, kSplitLds or kSplitNaive
+    int32_t split_waves;    // register kernel: > 0 = that many wavefronts loop over the items
     // this layer's page table [batch][max_pages] of device addresses
     const uint64_t *page_table;
     const int32_t *capacity;  // [batch] slots per sequence (device)

@@ -260,11 +260,11 @@ hipError_t launch_projection(const StepArgs &a, hipStream_t st) {
             qkv_proj_mfma_kernel<4><<<dim3(a.n_qkv / 16, (a.batch + 63) / 64), threads, 0, st>>>(a);
         }
     } else if (a.batch <= 4) {
-        launch_gemv<4>(a, st);
+        (void)launch_gemv<4>(a, st);
     } else if (a.batch <= 8) {
-        launch_gemv<8>(a, st);
+        (void)launch_gemv<8>(a, st);
     } else {
-        launch_gemv<16>(a, st);
+        (void)launch_gemv<16>(a, st);
     }
     return hipGetLastError();
 }

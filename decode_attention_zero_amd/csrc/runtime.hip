@@ -86,7 +86,8 @@ struct dkv_layout {
     int32_t max_pages;
     int32_t split_tokens;
     int32_t max_splits;
-    int32_t split_variant;             // dkv::kSplitRegisters or dkv::kSplitLds
+    int32_t split_variant;             // dkv::kSplitRegisters, kSplitLds or kSplitNaive
+    int32_t split_waves;               // > 0: the register kernel runs on that many looping wavefronts
     dkv_pool *host_pool;
     dkv_pool *hbm_pool;
     std::vector<std::pair<dkv_pool *, int64_t>> owned;   // every page the layout holds
@@ -189,13 +190,34 @@ int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, int32_t max_cap) 
 // for every group size: on MI355X it measured faster than the LDS
 // producer/consumer ring in the all-HBM placement (1 GiB of KV at group 4:
 // 189 us vs 258 us; group 8: 18.8 ms vs 27.6 ms for 64 GiB) and the same on
-// the host link. DKV_SPLIT_KERNEL=regs|lds overrides it.
+// the host link. DKV_SPLIT_KERNEL=regs|lds overrides it; DKV_SPLIT_KERNEL=naive
+// selects the naive zero-copy comparator (one work item per query head).
 int32_t choose_split_variant(int32_t /*group*/) {
     if (const char *env = getenv("DKV_SPLIT_KERNEL")) {
         if (!strcmp(env, "lds")) return dkv::kSplitLds;
         if (!strcmp(env, "regs")) return dkv::kSplitRegisters;
+        if (!strcmp(env, "naive")) return dkv::kSplitNaive;
     }
     return dkv::kSplitRegisters;
+}
+
+// Wavefronts of the split kernel. A layout with host pages runs a fixed,
+// small number of looping wavefronts, enough to cover the host link's
+// latency with a few MiB in flight but not so many that its request queue
+// overflows; an all-HBM layout runs one wavefront per work item (HBM needs
+// ~16 MiB in flight). Measured on MI355X, 1 GiB host-resident at batch 8:
+// 19.13 ms with one wave per item (4096), 18.69 ms with 128-384, 18.74 ms
+// with 512, 19.1 ms from 768 up; 4 GiB half host / half HBM at batch 64:
+// 38.2 ms vs 37.3-37.5 ms with 256-512. DKV_SPLIT_WAVES=<n> overrides
+// (0: one wavefront per item).
+constexpr int32_t kHostSplitWaves = 256;
+
+int32_t choose_split_waves(bool host_pages) {
+    if (const char *env = getenv("DKV_SPLIT_WAVES")) {
+        const int v = atoi(env);
+        if (v >= 0) return v;
+    }
+    return host_pages ? kHostSplitWaves : 0;
 }
 
 // Parallel copy helper for host pages: runs f(first, last) over [0, n) in
@@ -383,6 +405,9 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
     L->split_tokens = choose_split_tokens(batch, shape->n_kv_heads, max_cap);
     L->max_splits = std::max(1, (std::max(1, max_cap - 1) + L->split_tokens - 1) / L->split_tokens);
     L->split_variant = choose_split_variant(shape->n_q_heads / shape->n_kv_heads);
+    bool any_host = L->windowed != 0;
+    for (int b = 0; b < batch; ++b) any_host |= L->first_hbm[b] > 0;
+    L->split_waves = choose_split_waves(any_host);
     if (L->host_pool) ++L->host_pool->n_layouts;
     if (L->hbm_pool) ++L->hbm_pool->n_layouts;
 
@@ -639,6 +664,15 @@ int32_t kv_layout_split_tokens(const dkv_layout *L) { return L ? L->split_tokens
 
 int32_t kv_layout_split_kernel(const dkv_layout *L) { return L ? L->split_variant : -1; }
 
+int32_t kv_layout_split_waves(const dkv_layout *L) { return L ? L->split_waves : -1; }
+
+dkv_status kv_layout_set_split_kernel(dkv_layout *L, int32_t kernel) {
+    if (!L || (kernel != dkv::kSplitRegisters && kernel != dkv::kSplitLds && kernel != dkv::kSplitNaive))
+        return fail(DKV_E_INVALID_ARG, "kv_layout_set_split_kernel: null layout or unknown kernel %d", kernel);
+    L->split_variant = kernel;
+    return DKV_OK;
+}
+
 static dkv_status check_range(const dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n,
                               const char *who) {
     if (!L) return fail(DKV_E_INVALID_ARG, "%s: null layout", who);
@@ -759,6 +793,7 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     a.max_pages = L->max_pages;
     a.split_tokens = L->split_tokens;
     a.split_variant = L->split_variant;
+    a.split_waves = L->split_waves;
     a.max_splits = L->max_splits;
     a.qscale = (float)(1.4426950408889634074 / std::sqrt((double)s->head_dim));
     a.page_table = L->d_page_table + (size_t)layer * L->batch * L->max_pages;
@@ -821,6 +856,17 @@ dkv_status kv_layout_check_status(dkv_layout *L) {
     HIP_TRY(hipMemset(L->d_status, 0, sizeof flag));
     if (flag & 1u)
         return fail(DKV_E_CAPACITY, "decode_step: a ctx_lens entry was outside [0, capacity - 1]");
+    return DKV_OK;
+}
+
+dkv_status kv_pool_copy(dkv_pool *dst, const dkv_pool *src, int64_t bytes, dkv_stream_t stream) {
+    if (!dst || !src || bytes < 0 || dst->page_bytes != src->page_bytes ||
+        bytes > dst->n_pages * dst->page_bytes || bytes > src->n_pages * src->page_bytes)
+        return fail(DKV_E_INVALID_ARG, "kv_pool_copy: null pool, page sizes differ or bytes out of range");
+    if (bytes == 0) return DKV_OK;
+    const void *from = src->tier == 0 ? (const void *)src->host_base : (const void *)src->dev_base;
+    void *to = dst->tier == 0 ? (void *)dst->host_base : (void *)dst->dev_base;
+    HIP_TRY(hipMemcpyAsync(to, from, (size_t)bytes, hipMemcpyDefault, reinterpret_cast<hipStream_t>(stream)));
     return DKV_OK;
 }
 

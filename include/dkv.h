@@ -267,10 +267,27 @@ int32_t kv_layout_split_tokens(const dkv_layout *kv_layout);
  * per work item with a register double buffer (the default), 1 = a producer
  * wavefront that streams page runs with LDS DMA into a ring for consumer
  * wavefronts that own the group's query heads. Both compute every head in
- * the same order and give identical bits. Chosen at creation; the
- * environment variable DKV_SPLIT_KERNEL=regs|lds, read by kv_layout_create,
- * selects one. -1 for a NULL layout. */
+ * the same order and give identical bits. 2 = the naive zero-copy
+ * comparator (one wavefront per query head, so each KV head's pages are read
+ * once per query head of its group), for measurement only; same bits too.
+ * Chosen at creation; the environment variable
+ * DKV_SPLIT_KERNEL=regs|lds|naive, read by kv_layout_create, selects one.
+ * -1 for a NULL layout. */
 int32_t kv_layout_split_kernel(const dkv_layout *kv_layout);
+
+/* Wavefronts the register split kernel runs on: 0 = one per work item
+ * (sequence, KV head, token split); n > 0 = n wavefronts, each looping over
+ * every n-th item. Layouts that hold host pages default to 256, which keeps
+ * the host link's request queue short (more outstanding reads lower its
+ * bandwidth); all-HBM layouts default to 0. The environment variable
+ * DKV_SPLIT_WAVES=<n>, read by kv_layout_create, overrides it. Same bits
+ * either way. -1 for a NULL layout. */
+int32_t kv_layout_split_waves(const dkv_layout *kv_layout);
+
+/* Switches the layout's split-attention kernel (0, 1 or 2 as above) for the
+ * decode steps enqueued after the call. Errors: DKV_E_INVALID_ARG for a NULL
+ * layout or an unknown kernel. */
+dkv_status kv_layout_set_split_kernel(dkv_layout *kv_layout, int32_t kernel);
 
 /* Thread-local message of the last failing call on this thread. */
 const char *dkv_last_error(void);

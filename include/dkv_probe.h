@@ -35,6 +35,18 @@ dkv_status kv_pool_info(const dkv_pool *pool, void **device_base, int64_t *bytes
 dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid,
                                  int32_t unroll, int32_t reps, float *ms_median);
 
+/* Comparator for measurement: the staging design the pages set against
+ * zero-copy (KV Offload wiki, Offload 的基本机制: swap-in copies KV into a GPU
+ * buffer before attention runs; KV-hierarchy overview, 2.1: staging costs a
+ * reserved GPU buffer and doubled link traffic). Copies the first `bytes`
+ * bytes of pool `src` into pool `dst` with hipMemcpyAsync (the copy engines)
+ * on `stream`. Two fresh pools of the same page shape, handed to layouts of
+ * the same capacities created in the same order, hold every page at the same
+ * offset, so staging a host-placed layout's pool into the HBM-placed layout's
+ * pool gives the latter the same KV. Errors: DKV_E_INVALID_ARG (null pool,
+ * different page sizes, or bytes < 0 or beyond either pool). */
+dkv_status kv_pool_copy(dkv_pool *dst, const dkv_pool *src, int64_t bytes, dkv_stream_t stream);
+
 /* Per-kernel timing of a layout's decode steps. While enabled, decode_step
  * records HIP events on its stream before and after each of its kernels
  * (projection, split attention, combine) for up to max_steps steps; enabling

@@ -342,3 +342,57 @@ def test_lds_split_kernel_split_edges(oracle, monkeypatch):
         check_tight(f32(s.run(f32=True)), tight_reference(oracle, wl, 0, s.ctx), "lds split 144 edges")
     finally:
         s.free()
+
+
+# --------------------------------------------------------------------------- comparators
+def test_comparators_are_bit_identical(oracle):
+    """The naive zero-copy comparator (one work item per query head) and the
+    staging comparator (copy-engine copy of the host pool into an HBM pool,
+    then the step on the HBM copy) compute the same bits as the method."""
+    wl = configs.LLAMA8B_HOST.replace(batch=3)
+    ctx = [700, 1030, 64]
+    host = H.Setup(wl, ctx_lens=ctx, hbm_tail=0)
+    zeros = lambda layer, b, t0, t1: (np.zeros((t1 - t0, wl.n_kv_heads, wl.head_dim), np.uint16),) * 2
+    staged = H.Setup(wl, ctx_lens=ctx, hbm_tail=1 << 20, kv_writer=zeros)
+    try:
+        want = bits(host.run())
+        assert host.layout.split_kernel == "regs"
+        host.layout.split_kernel = "naive"
+        assert host.layout.split_kernel == "naive"
+        assert np.array_equal(bits(host.run()), want)
+        host.layout.split_kernel = "regs"
+        assert staged.n_host_pages == 0 and staged.n_hbm_pages == host.n_host_pages
+        assert not np.array_equal(bits(staged.run()), want)      # zeros before staging
+        H.dkv.kv_pool_copy(staged.hbm_pool, host.host_pool, host.host_pool.info()[1])
+        assert np.array_equal(bits(staged.run()), want)
+        ref = H.oracle_full(oracle, wl, 0, np.asarray(ctx, np.int32))["attn_out"]
+        assert_gates(H.bf16_to_f64(want), ref, "comparators")
+    finally:
+        host.free()
+        staged.free()
+
+
+def test_wave_count_does_not_change_bits(monkeypatch):
+    """The register split kernel on one wavefront per item or on a few looping
+    wavefronts (the default when host pages exist) gives the same bits."""
+    wl = configs.LLAMA8B_HOST.replace(batch=3)
+    ctx = [700, 1030, 64]
+    outs = {}
+    for waves in ("0", "7", None):
+        if waves is None:
+            monkeypatch.delenv("DKV_SPLIT_WAVES", raising=False)
+        else:
+            monkeypatch.setenv("DKV_SPLIT_WAVES", waves)
+        s = H.Setup(wl, ctx_lens=ctx, hbm_tail=[0, 300, 0])
+        try:
+            assert s.layout.split_waves == (256 if waves is None else int(waves))
+            outs[waves] = s.run(f32=True).cpu().numpy().view(np.uint32)
+        finally:
+            s.free()
+    assert np.array_equal(outs["0"], outs["7"]) and np.array_equal(outs["0"], outs[None])
+    monkeypatch.delenv("DKV_SPLIT_WAVES", raising=False)
+    s = H.Setup(wl, ctx_lens=ctx, hbm_tail=1 << 20)
+    try:
+        assert s.layout.split_waves == 0          # all-HBM: one wavefront per item
+    finally:
+        s.free()
