@@ -30,28 +30,39 @@ namespace {
 // Pages are double-buffered in registers (ping-pong, so no copies): the next
 // page's loads are in flight while the current one is computed. Full pages
 // take a mask-free path; only the split's last page can be partial.
-template <int D, int G>
+//
+// WPI wavefronts share a work item by splitting each tile's wave loads (WPI
+// = 2: wave 0 takes tokens 0-7 of every page, wave 1 tokens 8-15), so every
+// byte is still read once; their softmax states are merged through LDS at
+// the end of the item, in a fixed order. Used for groups of 8 query heads,
+// whose single-wave state would need 367 registers (one wave per SIMD).
+template <int D, int G, int WPI = 1>
 struct SplitState {
     static constexpr int LPT = D / 8;               // lanes per token
     static constexpr int TPL = 64 / LPT;            // tokens per wave load
     static constexpr int NLD = kPageTokens / TPL;   // wave loads per 16-token tile
+    static constexpr int NLDW = NLD / WPI;          // of those, loads per wavefront
     static constexpr int TILE = kPageTokens * D * 2;
     static constexpr int RUN = 2 * TILE;
+    static_assert(NLD % WPI == 0, "tile loads must split evenly over the wavefronts");
 
     float q[G][8];
     float m[G], l[G], acc[G][8];
 
-    __device__ __forceinline__ void load(const char *run, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) const {
+    // `run` points at this lane's 16 bytes of the wave's first load of the run.
+    __device__ __forceinline__ void load(const char *run, uint4 (&kr)[NLDW], uint4 (&vr)[NLDW]) const {
 #pragma unroll
-        for (int j = 0; j < NLD; ++j) kr[j] = load_stream(run + j * 1024);
+        for (int j = 0; j < NLDW; ++j) kr[j] = load_stream(run + j * 1024);
 #pragma unroll
-        for (int j = 0; j < NLD; ++j) vr[j] = load_stream(run + TILE + j * 1024);
+        for (int j = 0; j < NLDW; ++j) vr[j] = load_stream(run + TILE + j * 1024);
     }
 
-    // One page. PARTIAL: only the first n_valid tokens of the page count.
+    // One page. PARTIAL: only the first n_valid tokens of the page count;
+    // `sub` is the page token this lane holds in the wave's first load.
     template <bool PARTIAL>
-    __device__ __forceinline__ void page(const uint4 (&kr)[NLD], const uint4 (&vr)[NLD], int sub,
+    __device__ __forceinline__ void page(const uint4 (&kr)[NLDW], const uint4 (&vr)[NLDW], int sub,
                                          int n_valid) {
+        constexpr int NLD = NLDW;
         float sc[NLD][G];
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
@@ -133,7 +144,8 @@ struct SplitState {
 
     // Merges the row states (lanes l and l ^ off, off >= LPT) in a fixed order
     // and writes the partial (m, l, o) of heads h0 .. h0 + G - 1 for split s.
-    __device__ __forceinline__ void finish(const StepArgs &a, int b, int h0, int s, int sub, int dl) {
+    __device__ __forceinline__ void finish(const StepArgs &a, int b, int h0, int s, int dl) {
+        const bool row0 = (threadIdx.x & 63) < LPT;     // lanes of the wave's first row
 #pragma unroll
         for (int off = LPT; off < 64; off <<= 1) {
 #pragma unroll
@@ -152,7 +164,40 @@ struct SplitState {
                 m[h] = M;
             }
         }
-        if (sub == 0) {
+        if constexpr (WPI == 2) {
+            // Wave 1 hands its merged state to wave 0 through LDS.
+            __shared__ float xw[G][2 + LPT * 8];
+            const int w = threadIdx.x >> 6;
+            if (w == 1 && row0) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    if (dl == 0) {
+                        xw[h][0] = m[h];
+                        xw[h][1] = l[h];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xw[h][2 + dl * 8 + e] = acc[h][e];
+                }
+            }
+            __syncthreads();
+            if (w == 0) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float mo = xw[h][0];
+                    const float lo = xw[h][1];
+                    const float M = fmaxf(m[h], mo);
+                    const float c1 = rescale(m[h], M);
+                    const float c2 = rescale(mo, M);
+                    l[h] = fmaf(l[h], c1, lo * c2);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], c1, xw[h][2 + dl * 8 + e] * c2);
+                    m[h] = M;
+                }
+            }
+            __syncthreads();     // the buffer is free again before the next item
+            if (w != 0) return;
+        }
+        if (row0) {
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 const size_t slot = ((size_t)b * a.n_q_heads + (size_t)h0 + h) * a.max_splits + s;
@@ -165,11 +210,12 @@ struct SplitState {
     }
 };
 
-// One work item: split s of sequence b, KV head g, query heads h0 .. h0 + G - 1.
-template <int D, int G>
+// One work item: split s of sequence b, KV head g, query heads h0 .. h0 + G - 1,
+// on the WPI wavefronts of the workgroup.
+template <int D, int G, int WPI>
 __device__ __forceinline__ void split_item(const StepArgs &a, int s, int g, int h0, int b) {
-    using S = SplitState<D, G>;
-    constexpr int NLD = S::NLD;
+    using S = SplitState<D, G, WPI>;
+    constexpr int NLD = S::NLDW;
     constexpr int LPT = S::LPT;
 
     const int L = a.ctx_lens[b];
@@ -178,15 +224,16 @@ __device__ __forceinline__ void split_item(const StepArgs &a, int s, int g, int 
     if (t0 >= L) return;
     const int t1 = min(t0 + a.split_tokens, L);
 
-    const int lane = threadIdx.x;
-    const int sub = lane / LPT;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int sub = lane / LPT + w * S::NLDW * S::TPL;   // page token of the wave's first load
     const int dl = lane % LPT;
 
     S st;
     st.init(a, b, h0, dl);
 
     const uint64_t *pt = a.page_table + (size_t)b * a.max_pages;
-    const size_t run_off = (size_t)g * S::RUN + (size_t)lane * 16;
+    const size_t run_off = (size_t)g * S::RUN + (size_t)w * S::NLDW * 1024 + (size_t)lane * 16;
     auto run_of = [&](int p) { return reinterpret_cast<const char *>(pt[p]) + run_off; };
 
     const int p0 = t0 / kPageTokens;
@@ -209,7 +256,7 @@ __device__ __forceinline__ void split_item(const StepArgs &a, int s, int g, int 
     } else if (p < p1) {                 // the partial page (in a)
         st.template page<true>(ka, va, sub, t1 - p * kPageTokens);
     }
-    st.finish(a, b, h0, s, sub, dl);
+    st.finish(a, b, h0, s, dl);
 }
 
 // One wavefront per work item (s, g, b) = blockIdx (x, y, z).
@@ -217,11 +264,11 @@ __device__ __forceinline__ void split_item(const StepArgs &a, int s, int g, int 
 // method: one work item per query head (blockIdx.y), so each KV head's pages
 // cross the link once per query head of its group (G times per step) instead
 // of once. Each head's arithmetic is the same as in the grouped kernel.
-template <int D, int G, bool PER_QUERY_HEAD = false>
-__global__ __launch_bounds__(64) void attn_split_kernel(StepArgs a) {
+template <int D, int G, int WPI, bool PER_QUERY_HEAD = false>
+__global__ __launch_bounds__(64 * WPI, WPI) void attn_split_kernel(StepArgs a) {
     const int g = PER_QUERY_HEAD ? blockIdx.y / (a.n_q_heads / a.n_kv_heads) : blockIdx.y;
     const int h0 = PER_QUERY_HEAD ? blockIdx.y : blockIdx.y * G;
-    split_item<D, G>(a, blockIdx.x, g, h0, blockIdx.z);
+    split_item<D, G, WPI>(a, blockIdx.x, g, h0, blockIdx.z);
 }
 
 // The same work items on a fixed number of wavefronts (gridDim.x), each
@@ -231,15 +278,15 @@ __global__ __launch_bounds__(64) void attn_split_kernel(StepArgs a) {
 // the host link, where too many outstanding reads lower its bandwidth (the
 // streaming-read probe drops from 57.5 to 56.0 GB/s when it keeps 8 MiB in
 // flight instead of 1 MiB). Each item is computed exactly as above.
-template <int D, int G>
-__global__ __launch_bounds__(64) void attn_split_persistent_kernel(StepArgs a) {
+template <int D, int G, int WPI>
+__global__ __launch_bounds__(64 * WPI, WPI) void attn_split_persistent_kernel(StepArgs a) {
     const int n_items = a.n_kv_heads * a.max_splits * a.batch;
     for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
         const int g = i % a.n_kv_heads;
         const int rest = i / a.n_kv_heads;
         const int s = rest % a.max_splits;
         const int b = rest / a.max_splits;
-        split_item<D, G>(a, s, g, g * G, b);
+        split_item<D, G, WPI>(a, s, g, g * G, b);
     }
 }
 
@@ -340,22 +387,24 @@ __global__ __launch_bounds__(64 * (NC + 1)) void attn_split_lds_kernel(StepArgs 
         if (p0 + i < pf) st.template page<false>(kr, vr, sub, kPageTokens);
         else st.template page<true>(kr, vr, sub, t1 - (p0 + i) * kPageTokens);
     }
-    st.finish(a, b, h0, s, sub, dl);
+    st.finish(a, b, h0, s, dl);
 }
 
 template <int D, int G>
 void launch(const StepArgs &a, hipStream_t st) {
+    // Groups of 8 query heads share each work item between two wavefronts.
+    constexpr int WPI = G >= 8 ? 2 : 1;
     dim3 grid(a.max_splits, a.n_kv_heads, a.batch);
     if (a.split_variant == kSplitNaive) {
-        attn_split_kernel<D, 1, true><<<dim3(a.max_splits, a.n_q_heads, a.batch), 64, 0, st>>>(a);
+        attn_split_kernel<D, 1, WPI, true><<<dim3(a.max_splits, a.n_q_heads, a.batch), 64 * WPI, 0, st>>>(a);
     } else if (a.split_variant == kSplitLds) {
         // Consumers own at most 4 query heads each; 4 ring slots (3 runs in flight).
         constexpr int NC = G > 4 ? G / 4 : 1;
         attn_split_lds_kernel<D, G, NC, 4><<<grid, 64 * (NC + 1), 0, st>>>(a);
     } else if (a.split_waves > 0) {
-        attn_split_persistent_kernel<D, G><<<a.split_waves, 64, 0, st>>>(a);
+        attn_split_persistent_kernel<D, G, WPI><<<a.split_waves, 64 * WPI, 0, st>>>(a);
     } else {
-        attn_split_kernel<D, G><<<grid, 64, 0, st>>>(a);
+        attn_split_kernel<D, G, WPI><<<grid, 64 * WPI, 0, st>>>(a);
     }
 }
 

@@ -309,8 +309,10 @@ def test_out_of_range_context_is_flagged():
 ], ids=["g1-d64", "g4-d128", "g8-d128"])
 def test_split_kernel_variants_bit_identical(oracle, monkeypatch, wl_name, ctx):
     """The register-double-buffer and the LDS producer/consumer split kernels
-    compute every head in the same order: identical bits, and the oracle's
-    gates, with host and HBM pages mixed."""
+    meet the oracle's gates with host and HBM pages mixed. Up to groups of 4
+    they compute every head in the same order (identical bits); at group 8
+    the register kernel splits each page's tokens over two wavefronts, which
+    changes the order of the fp32 sums."""
     wl = configs.BY_NAME[wl_name].replace(batch=len(ctx), n_layers=1)
     outs, outs32 = {}, {}
     for variant in ("regs", "lds"):
@@ -322,12 +324,14 @@ def test_split_kernel_variants_bit_identical(oracle, monkeypatch, wl_name, ctx):
             outs32[variant] = s.run(f32=True).cpu().numpy()
         finally:
             s.free()
-    assert np.array_equal(outs["regs"], outs["lds"])
-    assert np.array_equal(outs32["regs"].view(np.uint32), outs32["lds"].view(np.uint32))
+    if wl.group < 8:
+        assert np.array_equal(outs["regs"], outs["lds"])
+        assert np.array_equal(outs32["regs"].view(np.uint32), outs32["lds"].view(np.uint32))
     ref = H.oracle_full(oracle, wl, 0, np.asarray(ctx, np.int32))["attn_out"]
-    assert_gates(H.bf16_to_f64(outs["lds"]), ref, "%s lds" % wl_name)
-    check_tight(outs32["lds"].astype(np.float64),
-                tight_reference(oracle, wl, 0, np.asarray(ctx, np.int32)), "%s lds" % wl_name)
+    tight = tight_reference(oracle, wl, 0, np.asarray(ctx, np.int32))
+    for variant in ("regs", "lds"):
+        assert_gates(H.bf16_to_f64(outs[variant]), ref, "%s %s" % (wl_name, variant))
+        check_tight(outs32[variant].astype(np.float64), tight, "%s %s" % (wl_name, variant))
 
 
 def test_lds_split_kernel_split_edges(oracle, monkeypatch):
