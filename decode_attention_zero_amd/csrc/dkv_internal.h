@@ -35,6 +35,7 @@ struct StepArgs {
     float qscale;           // log2(e) / sqrt(head_dim): scores come out in log2 units
     int32_t split_variant;  // kSplitRegisters, kSplitLds or kSplitNaive
     int32_t split_waves;    // register kernel: > 0 = that many wavefronts loop over the items
+    int32_t proj_mfma_min_batch;  // batches from this size on project on MFMA, below on VALU
     // this layer's page table [batch][max_pages] of device addresses
     const uint64_t *page_table;
     const int32_t *capacity;  // [batch] slots per sequence (device)

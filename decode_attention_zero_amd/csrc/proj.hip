@@ -12,9 +12,6 @@
 namespace dkv {
 namespace {
 
-// From this batch size on, y = W x has enough columns (sequences) to be a
-// real contraction and runs on MFMA; below it W is read by a VALU GEMV.
-constexpr int kMfmaMinBatch = 32;
 
 __device__ __forceinline__ void store_projection(const StepArgs &a, int n, int b, float y) {
     const int D = a.head_dim;
@@ -124,109 +121,112 @@ __global__ __launch_bounds__(64 * KS) void qkv_proj_gemv_kernel(StepArgs a) {
     }
 }
 
-// 1b. Batches of 32 or more: the projection is a dense [N_qkv x hidden] x
-// [hidden x B] contraction, done on the matrix cores with
-// v_mfma_f32_16x16x32_bf16 (bf16 in, fp32 accumulate). One wavefront owns 16
-// W rows and 16*NB sequences, so every W byte is read once per step.
-// Operand layout of the 16x16x32 MFMA: lane l supplies A[i = l%16][k = 8*(l/16)
-// .. +7] and B[k = 8*(l/16) .. +7][j = l%16], and receives
-// D[i = 4*(l/16) + r][j = l%16], r < 4. A is the W tile (rows of W are
-// contiguous in k), B is x^T (rows of x are contiguous in k), so both operands
+// 1b. Larger batches: the projection is a dense [N_qkv x hidden] x [hidden x B]
+// contraction, done on the matrix cores with v_mfma_f32_16x16x32_bf16 (bf16
+// in, fp32 accumulate). Operand layout of the 16x16x32 MFMA: lane l supplies
+// A[i = l%16][k = 8*(l/16) .. +7] and B[k = 8*(l/16) .. +7][j = l%16], and
+// receives D[i = 4*(l/16) + r][j = l%16], r < 4. A is a W tile (W rows are
+// contiguous in k), B is x^T (x rows are contiguous in k), so both operands
 // are plain 16-byte loads from row-major memory.
+//
+// One wavefront owns 16 W rows x a 512-wide slice of k x up to 64 sequences
+// (NBT tiles of 16): it loads its W slice once (16 KiB, issued together with
+// the first sequence tile's x slice, all before the first MFMA) and keeps it
+// in registers while it walks the sequence tiles, the next tile's x slice
+// in flight during the current tile's 16 MFMAs. x is small and shared by
+// every workgroup, so it comes from L2; W crosses HBM once. The KS
+// wavefronts of a workgroup cover the hidden dimension (CH slices each) and
+// add their partial tiles through LDS in wave order, so the result does not
+// depend on timing. Batches above 64 take more workgroup columns.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int NB>
-struct MfmaChunk {
-    static constexpr int UK = 4;   // 32-wide k steps per chunk (128 k)
-    uint4 w[UK];
-    uint4 x[UK][NB];
-};
-
-template <int NB>
-__device__ __forceinline__ void mfma_load(MfmaChunk<NB> &c, const uint16_t *wrow,
-                                          const uint16_t *const (&xrow)[NB], int k0) {
+template <int NK>
+__device__ __forceinline__ void load_slice(uint4 (&v)[NK], const uint16_t *row, int k0) {
 #pragma unroll
-    for (int u = 0; u < MfmaChunk<NB>::UK; ++u) {
-        c.w[u] = *reinterpret_cast<const uint4 *>(wrow + k0 + 32 * u);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) c.x[u][nb] = *reinterpret_cast<const uint4 *>(xrow[nb] + k0 + 32 * u);
-    }
+    for (int u = 0; u < NK; ++u) v[u] = *reinterpret_cast<const uint4 *>(row + k0 + 32 * u);
 }
 
-template <int NB>
-__device__ __forceinline__ void mfma_step(const MfmaChunk<NB> &c, f32x4 (&acc)[NB]) {
+template <int NK>
+__device__ __forceinline__ void mfma_slice(f32x4 &acc, const uint4 (&w)[NK], const uint4 (&x)[NK]) {
 #pragma unroll
-    for (int u = 0; u < MfmaChunk<NB>::UK; ++u) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, c.w[u]);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, c.x[u][nb]),
-                                                              acc[nb], 0, 0, 0);
-    }
+    for (int u = 0; u < NK; ++u)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[u]),
+                                                      __builtin_bit_cast(bf16x8, x[u]), acc, 0, 0, 0);
 }
 
-// Split-k: the workgroup's KS wavefronts (blockDim.x / 64, 2 or 4) take equal
-// k ranges of the same 16-row x 16*NB-sequence tile; their partial tiles are
-// added through LDS in wave order, so the result does not depend on timing.
-template <int NB>
-__global__ __launch_bounds__(256) void qkv_proj_mfma_kernel(StepArgs a) {
+template <int KS, int NBT>
+__global__ __launch_bounds__(64 * KS) void qkv_proj_mfma_kernel(StepArgs a, int ch) {
+    constexpr int KSL = 512;            // k per slice
+    constexpr int NK = KSL / 32;        // MFMA k steps per slice
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int ks = blockDim.x >> 6;
-    const int row0 = blockIdx.x * 16;
-    const int b0 = blockIdx.y * 16 * NB;
     const int i = lane & 15;
     const int kq = (lane >> 4) * 8;
-    const int krange = a.hidden / ks;      // a multiple of 256 (checked at launch)
-    const int kbeg = wave * krange;
+    const int row0 = blockIdx.x * 16;
+    const int b0 = blockIdx.y * 16 * NBT;
 
-    if (blockIdx.x == 0 && wave == 0) {
-        for (int b = b0 + lane; b < min(a.batch, b0 + 16 * NB); b += 64) check_context_range(a, b);
+    if (blockIdx.x == 0 && wave == 0)
+        for (int b = b0 + lane; b < min(a.batch, b0 + 16 * NBT); b += 64) check_context_range(a, b);
+
+    // Sequences past the batch read a valid row (the last one) and are never stored.
+    const uint16_t *wrow = a.w + (size_t)(row0 + i) * a.hidden + kq;
+    const uint16_t *xrow[NBT];
+#pragma unroll
+    for (int t = 0; t < NBT; ++t) xrow[t] = a.x + (size_t)min(b0 + 16 * t + i, a.batch - 1) * a.hidden + kq;
+
+    f32x4 acc[NBT];
+#pragma unroll
+    for (int t = 0; t < NBT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < ch; ++c) {
+        const int k0 = (wave * ch + c) * KSL;
+        uint4 wv[NK], xa[NK], xb[NK];
+        load_slice(wv, wrow, k0);
+        load_slice(xa, xrow[0], k0);
+        __builtin_amdgcn_sched_barrier(0);     // the slice's loads go out before the first MFMA
+#pragma unroll
+        for (int t = 0; t < NBT; t += 2) {
+            if (t + 1 < NBT) load_slice(xb, xrow[t + 1], k0);
+            mfma_slice(acc[t], wv, xa);
+            if (t + 1 < NBT) {
+                if (t + 2 < NBT) load_slice(xa, xrow[t + 2], k0);
+                mfma_slice(acc[t + 1], wv, xb);
+            }
+        }
     }
 
-    // Columns past the batch read a valid row (the last sequence's) and are
-    // never stored, so the k loop has no per-lane branches.
-    const uint16_t *wrow = a.w + (size_t)(row0 + i) * a.hidden + kbeg + kq;
-    const uint16_t *xrow[NB];
+    if constexpr (KS > 1) {
+        __shared__ f32x4 partial[KS - 1][NBT][64];
+        if (wave > 0) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-        xrow[nb] = a.x + (size_t)min(b0 + nb * 16 + i, a.batch - 1) * a.hidden + kbeg + kq;
-    f32x4 acc[NB];
+            for (int t = 0; t < NBT; ++t) partial[wave - 1][t][lane] = acc[t];
+        }
+        __syncthreads();
+        if (wave != 0) return;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // The 128-wide chunks of a wave's k range come in pairs: ping-pong between
-    // two register sets, the next chunk's loads in flight while the current
-    // one feeds the matrix cores.
-    constexpr int KC = 32 * MfmaChunk<NB>::UK;
-    MfmaChunk<NB> c0, c1;
-    mfma_load(c0, wrow, xrow, 0);
-    for (int k0 = 0; k0 < krange; k0 += 2 * KC) {
-        mfma_load(c1, wrow, xrow, k0 + KC);
-        mfma_step(c0, acc);
-        if (k0 + 2 * KC < krange) mfma_load(c0, wrow, xrow, k0 + 2 * KC);
-        mfma_step(c1, acc);
-    }
-
-    __shared__ f32x4 partial[3][NB][64];
-    if (wave > 0) {
+        for (int w = 1; w < KS; ++w)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) partial[wave - 1][nb][lane] = acc[nb];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    for (int w = 1; w < ks; ++w) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] += partial[w - 1][nb][lane];
+            for (int t = 0; t < NBT; ++t) acc[t] += partial[w - 1][t][lane];
     }
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int b = b0 + nb * 16 + i;
+    for (int t = 0; t < NBT; ++t) {
+        const int b = b0 + 16 * t + i;
         if (b < a.batch) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) store_projection(a, row0 + 4 * (lane >> 4) + r, b, acc[nb][r]);
+            for (int r = 0; r < 4; ++r) store_projection(a, row0 + 4 * (lane >> 4) + r, b, acc[t][r]);
         }
+    }
+}
+
+template <int KS>
+void launch_mfma(const StepArgs &a, int ch, hipStream_t st) {
+    const int nbt = (a.batch + 15) / 16;
+    if (nbt == 1) {
+        qkv_proj_mfma_kernel<KS, 1><<<dim3(a.n_qkv / 16, 1), 64 * KS, 0, st>>>(a, ch);
+    } else if (nbt == 2) {
+        qkv_proj_mfma_kernel<KS, 2><<<dim3(a.n_qkv / 16, 1), 64 * KS, 0, st>>>(a, ch);
+    } else {
+        qkv_proj_mfma_kernel<KS, 4><<<dim3(a.n_qkv / 16, (nbt + 3) / 4), 64 * KS, 0, st>>>(a, ch);
     }
 }
 
@@ -250,14 +250,17 @@ hipError_t launch_gemv(const StepArgs &a, hipStream_t st) {
 
 hipError_t launch_projection(const StepArgs &a, hipStream_t st) {
     if (a.hidden % 512 != 0 || a.n_qkv % 16 != 0) return hipErrorInvalidValue;
-    if (a.batch >= kMfmaMinBatch) {
-        // 16 W rows x 64 sequences per workgroup (32 for batches up to 32),
-        // k split over 4 wavefronts (2 when hidden is not a multiple of 1024)
-        const int threads = (a.hidden % 1024 == 0) ? 256 : 128;
-        if (a.batch <= 32) {
-            qkv_proj_mfma_kernel<2><<<dim3(a.n_qkv / 16, (a.batch + 31) / 32), threads, 0, st>>>(a);
-        } else {
-            qkv_proj_mfma_kernel<4><<<dim3(a.n_qkv / 16, (a.batch + 63) / 64), threads, 0, st>>>(a);
+    if (a.batch >= a.proj_mfma_min_batch) {
+        // Up to 8 wavefronts per workgroup over the 512-wide k slices.
+        const int n_slices = a.hidden / 512;
+        int ks = 8;
+        while (ks > 1 && n_slices % ks != 0) ks >>= 1;
+        const int ch = n_slices / ks;
+        switch (ks) {
+            case 1: launch_mfma<1>(a, ch, st); break;
+            case 2: launch_mfma<2>(a, ch, st); break;
+            case 4: launch_mfma<4>(a, ch, st); break;
+            default: launch_mfma<8>(a, ch, st); break;
         }
     } else if (a.batch <= 4) {
         (void)launch_gemv<4>(a, st);

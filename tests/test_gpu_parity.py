@@ -138,13 +138,13 @@ def test_split_and_page_edges(oracle, monkeypatch, split):
 
 
 # --------------------------------------------------------------------------- exactness
-@pytest.mark.parametrize("batch", [3, 32, 40, 64])
+@pytest.mark.parametrize("batch", [3, 16, 17, 32, 40, 64])
 def test_projection_integer_exact(oracle, batch):
     """Small-integer x and W make every product and fp32 sum exact, so the
     written-back K/V must equal the oracle's fp64 values rounded to bf16, bit
     for bit; with an empty history attn_out is exactly bf16(v_new). Batches
-    below 32 take the VALU projection, 32 and up the MFMA one (40: a partly
-    filled 64-sequence tile)."""
+    below 16 take the VALU projection, 16 and up the MFMA one in 16-sequence
+    tiles (17 and 40: a partly filled last tile)."""
     import synth
     wl = configs.LLAMA8B_HOST.replace(batch=batch)
     ctx = np.array([[0, 5, 16][b % 3] for b in range(batch)], np.int32)
