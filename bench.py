@@ -13,10 +13,12 @@ Inputs are resident (KV in its pool, x/W in HBM) before the timed region
 starts.
 
 Prints one JSON line: metric/value (effective KV GB/s = algorithmic KV bytes
-per step / step time), ms_per_step, roofline (dominant kernel = split
-attention, against the host link), the measured host-link streaming-read
-ceiling, the same step with every page in HBM (against 8 TB/s), and the fp64
-oracle timed on the host cores on the same workload.
+per step / step time, steps enqueued eagerly), ms_per_step and
+graph_ms_per_step (the same step replayed from one captured HIP graph),
+roofline (dominant kernel = split attention, against the host link), the
+measured host-link streaming-read ceiling, the same step with every page in
+HBM (against 8 TB/s), the naive zero-copy and staging comparators, and the
+fp64 oracle timed on the host cores on the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -102,6 +104,31 @@ class Resident:
             self.step()
         e1.record(self.stream)
         torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def graph_timed(self, steps):
+        """Milliseconds per step with one step (every layer) captured in a HIP
+        graph and replayed `steps` times (events on the replaying stream)."""
+        import torch
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            for layer in range(self.n_layers):
+                self.dkv.decode_step(self.layout, layer, self.x[layer], self.W[layer], self.ctx,
+                                     self.out[layer])
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del graph
         return e0.elapsed_time(e1) / steps
 
     def kernel_times(self, steps):
@@ -325,6 +352,7 @@ def main(argv=None):
                           "ms_per_step": ms,
                           "kernel_ms": kt}), flush=True)
         return 0
+    ms_graph = r.graph_timed(args.steps)
     out_own = r.out_bits(0)
     split_kernel_name = ("attn_split_persistent_kernel (%d wavefronts)" % r.layout.split_waves
                          if r.layout.split_waves > 0 else "attn_split_kernel")
@@ -364,10 +392,12 @@ def main(argv=None):
         n_hbm_steps = max(args.steps, 50) if wl.n_layers == 1 else args.steps
         ms_h = rh.timed(n_hbm_steps, args.warmup)
         kt_h = rh.kernel_times(n_hbm_steps)
+        ms_h_graph = rh.graph_timed(n_hbm_steps)
         hbm_ceiling, hbm_rows, _ = probe_ceiling(dkv, rh.hbm_pool, HBM_PROBES)
         out_hbm = rh.out_bits(0)
         hbm = {
             "ms_per_step": round(ms_h, 4),
+            "graph_ms_per_step": round(ms_h_graph, 4),
             "kv_GBps": round(kv_bytes / (ms_h * 1e-3) / 1e9, 1),
             "split_kernel_ms": round(kt_h["split"], 4),
             "split_kernel_GBps": round(kv_bytes / (kt_h["split"] * 1e-3) / 1e9, 1),
@@ -451,6 +481,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "graph_ms_per_step": round(ms_graph, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
