@@ -205,23 +205,30 @@ int32_t choose_split_variant(int32_t /*group*/) {
     return dkv::kSplitRegisters;
 }
 
-// Wavefronts of the split kernel. A layout with host pages runs a fixed,
-// small number of looping wavefronts, enough to cover the host link's
-// latency with a few MiB in flight but not so many that its request queue
-// overflows; an all-HBM layout runs one wavefront per work item (HBM needs
-// ~16 MiB in flight). Measured on MI355X, 1 GiB host-resident at batch 8:
-// 19.13 ms with one wave per item (4096), 18.69 ms with 128-384, 18.74 ms
-// with 512, 19.1 ms from 768 up; 4 GiB half host / half HBM at batch 64:
-// 38.2 ms vs 37.3-37.5 ms with 256-512. DKV_SPLIT_WAVES=<n> overrides
-// (0: one wavefront per item).
+// Wavefronts of the split kernel. On the host link the number of reads in
+// flight matters beyond Little's law: 256 looping wavefronts keep it at its
+// ceiling, one wavefront per item (thousands) loses ~2.5 %. HBM needs many
+// more reads in flight (~16 MiB), so 256 waves starve it. Measured on MI355X
+// (1 GiB at batch 8): host-resident 19.13 ms with one wave per item vs 18.69
+// ms with 128-384 waves (18.74 ms with 512, 19.1 ms from 768 up); HBM-resident
+// 0.18 ms per item vs ~0.8 ms on 256 waves (~1.34 TB/s). The layout takes
+// whichever launch its page counts predict to be faster:
+//   looping:  max(host / 57.5 GB/s, HBM / 1.34 TB/s)
+//   per item: max(host / 56.1 GB/s, HBM / 6.0 TB/s)
+// so a layout keeps one wavefront per item below ~4 % host bytes.
+// DKV_SPLIT_WAVES=<n> overrides (0: one wavefront per item).
 constexpr int32_t kHostSplitWaves = 256;
 
-int32_t choose_split_waves(bool host_pages) {
+int32_t choose_split_waves(int64_t host_pages, int64_t hbm_pages) {
     if (const char *env = getenv("DKV_SPLIT_WAVES")) {
         const int v = atoi(env);
         if (v >= 0) return v;
     }
-    return host_pages ? kHostSplitWaves : 0;
+    if (host_pages == 0) return 0;
+    const double h = (double)host_pages, m = (double)hbm_pages;   // page bytes cancel out
+    const double t_looping = std::max(h / 57.5, m / 1340.0);
+    const double t_per_item = std::max(h / 56.1, m / 6000.0);
+    return t_looping < t_per_item ? kHostSplitWaves : 0;
 }
 
 // Batch size from which the QKV projection runs on the matrix cores (one
@@ -425,9 +432,13 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
     L->split_tokens = choose_split_tokens(batch, shape->n_kv_heads, max_cap);
     L->max_splits = std::max(1, (std::max(1, max_cap - 1) + L->split_tokens - 1) / L->split_tokens);
     L->split_variant = choose_split_variant(shape->n_q_heads / shape->n_kv_heads);
-    bool any_host = L->windowed != 0;
-    for (int b = 0; b < batch; ++b) any_host |= L->first_hbm[b] > 0;
-    L->split_waves = choose_split_waves(any_host);
+    int64_t n_host = 0, n_hbm = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int hot = L->windowed ? L->window[b] : L->n_pages[b] - L->first_hbm[b];
+        n_host += L->n_pages[b] - hot;
+        n_hbm += hot;
+    }
+    L->split_waves = choose_split_waves(n_host, n_hbm);
     L->proj_mfma_min_batch = choose_proj_mfma_min_batch();
     if (L->host_pool) ++L->host_pool->n_layouts;
     if (L->hbm_pool) ++L->hbm_pool->n_layouts;

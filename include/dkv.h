@@ -277,9 +277,11 @@ int32_t kv_layout_split_kernel(const dkv_layout *kv_layout);
 
 /* Wavefronts the register split kernel runs on: 0 = one per work item
  * (sequence, KV head, token split); n > 0 = n wavefronts, each looping over
- * every n-th item. Layouts that hold host pages default to 256, which keeps
- * the host link's request queue short (more outstanding reads lower its
- * bandwidth); all-HBM layouts default to 0. The environment variable
+ * every n-th item. Layouts whose host pages dominate the step default to
+ * 256, which keeps the host link's request queue short (more outstanding
+ * reads lower its bandwidth); layouts that are all or nearly all HBM (below
+ * ~4 % host pages) default to 0, since HBM needs far more reads in flight.
+ * The environment variable
  * DKV_SPLIT_WAVES=<n>, read by kv_layout_create, overrides it. Same bits
  * either way. -1 for a NULL layout. */
 int32_t kv_layout_split_waves(const dkv_layout *kv_layout);

@@ -400,3 +400,9 @@ def test_wave_count_does_not_change_bits(monkeypatch):
         assert s.layout.split_waves == 0          # all-HBM: one wavefront per item
     finally:
         s.free()
+    s = H.Setup(wl, ctx_lens=[700, 1030, 10], hbm_tail=[1 << 20, 1 << 20, 0])
+    try:
+        assert s.n_host_pages == 1 and s.n_hbm_pages == 109
+        assert s.layout.split_waves == 0          # 1 host page in 110: HBM decides the step
+    finally:
+        s.free()
