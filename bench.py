@@ -247,8 +247,9 @@ def sweep(dkv, wl, ctx, kv_source, kv_bytes, args):
         host_kv *= wl.n_layers
         steps = max(args.steps, 50) if f < 0.05 else args.steps
         ms = r.timed(steps, args.warmup)
-        if ceiling is None and r.host_pool is not None:
-            ceiling, _, _ = probe_ceiling(dkv, r.host_pool, HOST_PROBES[:3])
+        if r.host_pool is not None and r.host_pool.info()[1] >= (256 << 20):
+            c, _, _ = probe_ceiling(dkv, r.host_pool, HOST_PROBES[:3])
+            ceiling = max(ceiling or 0.0, c)
         r.free()
         rows.append({"host_fraction": f, "host_kv_bytes": host_kv, "ms_per_step": round(ms, 4),
                      "effective_kv_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2)})
