@@ -225,6 +225,92 @@ def calibrate(dkv, r):
     log("calibration kernels done")
 
 
+def gemm_experiment(dkv, args):
+    """C = A x B^T (S x S x S, bf16 in, fp32 out) with B in pinned host memory:
+    swap (copy-engine copy of B into HBM, then the GEMM), naive zero-copy (the
+    GEMM reading B in place in row-major tile order) and CPU-aware zero-copy
+    (the tile order that fetches each B column block over the link once),
+    next to the GEMM with B already in HBM. One JSON line."""
+    import torch
+    import synth
+    S = args.gemm
+    M = N = K = S
+    dev = torch.device("cuda", 0)
+    log("gemm %d^3: generating operands" % S)
+    A = torch.from_numpy(synth.normal_bf16(7, 60, 0, M * K, 1.0).view(np.int16)).to(dev).view(torch.bfloat16)
+    A = A.reshape(M, K)
+    flags = dkv.HOST_NONCOHERENT if args.gemm_noncoherent else dkv.HOST_COHERENT
+    hb = dkv.HostBuffer(N * K * 2, flags)
+    Bh = hb.view(np.uint16, (N, K))
+    synth.normal_bf16(7, 61, 0, N * K, 1.0, out=Bh.reshape(-1))
+    B_hbm = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    flop = 2.0 * M * N * K
+    b_bytes = N * K * 2
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def gemm(ptr, cpu_aware):
+        return lambda: dkv.gemm_bf16_nt(A, ptr, C, M, N, K, cpu_aware, stream)
+
+    def swap():
+        dkv.copy(B_hbm.data_ptr(), hb.device_ptr, b_bytes, stream)
+        dkv.gemm_bf16_nt(A, B_hbm.data_ptr(), C, M, N, K, False, stream)
+
+    results, outs = {}, {}
+    reps = max(1, min(args.steps, 10))
+    variants = [("gemm_B_in_hbm", None, reps), ("swap", swap, reps),
+                ("zero_copy_cpu_aware", gemm(hb.device_ptr, True), reps),
+                ("zero_copy_naive", gemm(hb.device_ptr, False), 1)]
+    dkv.copy(B_hbm.data_ptr(), hb.device_ptr, b_bytes, stream)
+    torch.cuda.synchronize()
+    for name, fn, n in variants:
+        fn = fn or gemm(B_hbm.data_ptr(), False)
+        ms = timed(fn, n)
+        results[name] = {"ms": round(ms, 3), "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 1)}
+        outs[name] = C.view(torch.int32).cpu().numpy()
+        log("gemm %s: %.3f ms" % (name, ms))
+    ms_copy = timed(lambda: dkv.copy(B_hbm.data_ptr(), hb.device_ptr, b_bytes, stream), reps)
+    results["swap"]["copy_ms"] = round(ms_copy, 3)
+    results["swap"]["extra_hbm_bytes"] = b_bytes
+    first = outs["gemm_B_in_hbm"]
+    identical = all(np.array_equal(v, first) for v in outs.values())
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.default()
+        rng = np.random.default_rng(5)
+        rows, cols = rng.integers(0, M, 64), rng.integers(0, N, 64)
+        Ah = A.view(torch.int16).cpu().numpy().view(np.uint16)
+        ref = orc.gemm_nt_entries(Ah, Bh, rows, cols)
+        got = first.view(np.float32)[rows, cols].astype(np.float64)
+        a_abs = np.abs((Ah[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+        b_abs = np.abs((Bh[cols].astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+        g = K * 2.0 ** -24 / (1 - K * 2.0 ** -24)
+        bnd = g * np.einsum("ek,ek->e", a_abs, b_abs)
+        parity = {"sampled_entries": 64, "max_abs_err": float(np.abs(got - ref).max()),
+                  "max_err_over_bound": float((np.abs(got - ref) / bnd).max()),
+                  "within_fp32_summation_bound": bool(np.all(np.abs(got - ref) <= bnd))}
+    hb.free()
+    print(json.dumps({"experiment": "gemm_host_operand", "M": M, "N": N, "K": K,
+                      "dtype": "bf16 in, fp32 accumulate and out",
+                      "B_host_memory": "non-coherent" if args.gemm_noncoherent else "coherent",
+                      "B_bytes": b_bytes, "results": results, "bit_identical": identical,
+                      "parity": parity}), flush=True)
+    return 0
+
+
 SWEEP_HOST_FRACTIONS = (0.0, 0.01, 0.03, 0.1, 0.25, 0.5, 0.75, 1.0)
 
 
@@ -276,6 +362,11 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true",
                     help="crossover sweep instead of the bench line: the workload's KV with the "
                          "host-resident share stepped from 0 to 100 %% (rest in HBM)")
+    ap.add_argument("--gemm", type=int, default=0, metavar="S",
+                    help="host-operand GEMM experiment instead of the bench line: C = A x B^T, "
+                         "S x S x S, B in pinned host memory (the pages use S = 10240)")
+    ap.add_argument("--gemm-noncoherent", action="store_true",
+                    help="with --gemm: allocate B non-coherent (cacheable in the GPU's L2)")
     ap.add_argument("--no-comparators", action="store_true",
                     help="skip the naive zero-copy and staging comparator legs")
     ap.add_argument("--profile-run", action="store_true",
@@ -300,6 +391,8 @@ def main(argv=None):
     from synth import configs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.gemm:
+        return gemm_experiment(dkv, args)
     wl = configs.BY_NAME[args.workload]
     ctx = wl.ctx_lens()
     B, Hkv, d = wl.batch, wl.n_kv_heads, wl.head_dim

@@ -91,6 +91,10 @@ def lib() -> ctypes.CDLL:
             "decode_step_f32": ([P, I32, P, P, P, P, P], I32),
             "dkv_probe_stream_read": ([P, ctypes.c_uint64, I32, I32, I32, P], I32),
             "kv_pool_copy": ([P, P, I64, P], I32),
+            "dkv_host_buffer_alloc": ([ctypes.c_uint64, U32, P, P], I32),
+            "dkv_host_buffer_free": ([P], I32),
+            "dkv_copy": ([P, P, ctypes.c_uint64, P], I32),
+            "dkv_gemm_bf16_nt": ([P, P, P, I32, I32, I32, I32, P], I32),
             "kv_layout_timing_enable": ([P, I32, I32], I32),
             "kv_layout_timing_read": ([P, P, P, P, P], I32),
         }
@@ -106,7 +110,8 @@ EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement",
             "kv_alloc_hbm", "kv_pool_free_pages", "kv_pool_info", "kv_pool_free",
             "kv_layout_create", "kv_layout_create_windowed", "kv_advance", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
             "kv_layout_split_kernel", "kv_layout_set_split_kernel", "kv_layout_split_waves", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
-            "dkv_probe_stream_read", "kv_pool_copy", "kv_layout_timing_enable", "kv_layout_timing_read"]
+            "dkv_probe_stream_read", "kv_pool_copy", "dkv_host_buffer_alloc", "dkv_host_buffer_free",
+            "dkv_copy", "dkv_gemm_bf16_nt", "kv_layout_timing_enable", "kv_layout_timing_read"]
 
 
 def _check(status: int) -> None:
@@ -359,3 +364,43 @@ def probe_stream_read(device_ptr: int, nbytes: int, grid: int = 256, unroll: int
     ms = ctypes.c_float()
     _check(lib().dkv_probe_stream_read(device_ptr, nbytes, grid, unroll, reps, ctypes.byref(ms)))
     return ms.value
+
+
+# ----------------------------------------------------------------------------- host-operand GEMM
+class HostBuffer:
+    """Pinned, mapped host memory: `array` is a numpy view of it, `device_ptr`
+    the address kernels use."""
+
+    def __init__(self, nbytes: int, flags: int = HOST_COHERENT):
+        h, d = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(lib().dkv_host_buffer_alloc(nbytes, flags, ctypes.byref(h), ctypes.byref(d)))
+        self.host_ptr, self.device_ptr, self.nbytes = h.value, d.value, nbytes
+        self.array = np.ctypeslib.as_array((ctypes.c_uint8 * nbytes).from_address(self.host_ptr))
+
+    def view(self, dtype, shape) -> np.ndarray:
+        return self.array.view(dtype)[:int(np.prod(shape))].reshape(shape)
+
+    def free(self) -> None:
+        if self.host_ptr:
+            self.array = None
+            _check(lib().dkv_host_buffer_free(self.host_ptr))
+            self.host_ptr = None
+
+
+def copy(dst_ptr: int, src_ptr: int, nbytes: int, stream=None) -> None:
+    """Copy-engine copy between device-known addresses (the swap-in of staging)."""
+    _check(lib().dkv_copy(dst_ptr, src_ptr, nbytes, _stream_ptr(stream)))
+
+
+def gemm_bf16_nt(A, B_ptr: int, C, M: int, N: int, K: int, cpu_aware: bool, stream=None):
+    """C [M][N] fp32 (device tensor) = A [M][K] bf16 (device tensor) x B^T, with B
+    [N][K] bf16 at device address B_ptr (HBM or a mapped host buffer)."""
+    import torch
+    if A.dtype != torch.bfloat16 or tuple(A.shape) != (M, K):
+        raise ValueError("A must be a bf16 [M][K] device tensor")
+    if C.dtype != torch.float32 or tuple(C.shape) != (M, N):
+        raise ValueError("C must be an fp32 [M][N] device tensor")
+    _check(lib().dkv_gemm_bf16_nt(_dev_ptr(A, "A"), B_ptr, _dev_ptr(C, "C"), M, N, K,
+                                  1 if cpu_aware else 0, _stream_ptr(stream)))
+    return C
+

@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libdkv.so")
-SOURCES = ["proj.hip", "attn_split.hip", "attn_combine.hip", "window.hip", "probe.hip", "runtime.hip"]
+SOURCES = ["proj.hip", "attn_split.hip", "attn_combine.hip", "window.hip", "gemm.hip", "probe.hip", "runtime.hip"]
 HEADERS = [os.path.join(CSRC, "dkv_internal.h"), os.path.join(CSRC, "device_common.h"), os.path.join(INCLUDE, "dkv.h"),
            os.path.join(INCLUDE, "dkv_probe.h")]
 

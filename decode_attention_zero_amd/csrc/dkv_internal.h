@@ -83,6 +83,10 @@ hipError_t launch_projection(const StepArgs &a, hipStream_t stream);
 hipError_t launch_split(const StepArgs &a, hipStream_t stream);
 hipError_t launch_combine(const StepArgs &a, hipStream_t stream);
 
+// GEMM C = A x B^T (bf16 in, fp32 out) with a row-major or CPU-aware tile order.
+hipError_t launch_gemm_nt(const uint16_t *A, const uint16_t *B, float *C, int M, int N, int K,
+                          bool cpu_aware, hipStream_t stream);
+
 // Streaming-read probe (grid-stride, 16 B per lane per load, optionally
 // nontemporal).
 hipError_t launch_stream_read(const void *ptr, uint64_t bytes, int grid, int unroll,

@@ -903,6 +903,54 @@ dkv_status kv_pool_copy(dkv_pool *dst, const dkv_pool *src, int64_t bytes, dkv_s
     return DKV_OK;
 }
 
+dkv_status dkv_host_buffer_alloc(uint64_t bytes, uint32_t flags, void **host_ptr, void **device_ptr) {
+    if (!bytes || !host_ptr || !device_ptr || flags > DKV_HOST_NONCOHERENT)
+        return fail(DKV_E_INVALID_ARG, "dkv_host_buffer_alloc: bad size, flags or null output");
+    void *h = nullptr, *d = nullptr;
+    const unsigned hflags = hipHostMallocMapped | hipHostMallocPortable |
+                            (flags == DKV_HOST_NONCOHERENT ? hipHostMallocNonCoherent : hipHostMallocCoherent);
+    hipError_t e = hipHostMalloc(&h, (size_t)bytes, hflags);
+    if (e != hipSuccess || !h) {
+        (void)hipGetLastError();
+        return fail(DKV_E_OUT_OF_MEMORY, "dkv_host_buffer_alloc: hipHostMalloc of %llu bytes failed: %s",
+                    (unsigned long long)bytes, hipGetErrorString(e));
+    }
+    e = hipHostGetDevicePointer(&d, h, 0);
+    if (e != hipSuccess || !d) {
+        (void)hipHostFree(h);
+        return hip_fail(e, "dkv_host_buffer_alloc: hipHostGetDevicePointer");
+    }
+    *host_ptr = h;
+    *device_ptr = d;
+    return DKV_OK;
+}
+
+dkv_status dkv_host_buffer_free(void *host_ptr) {
+    if (!host_ptr) return DKV_OK;
+    HIP_TRY(hipHostFree(host_ptr));
+    return DKV_OK;
+}
+
+dkv_status dkv_copy(void *dst, const void *src, uint64_t bytes, dkv_stream_t stream) {
+    if (!dst || !src) return fail(DKV_E_INVALID_ARG, "dkv_copy: null pointer");
+    if (!bytes) return DKV_OK;
+    HIP_TRY(hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyDefault, reinterpret_cast<hipStream_t>(stream)));
+    return DKV_OK;
+}
+
+dkv_status dkv_gemm_bf16_nt(const uint16_t *A, const uint16_t *B, float *C, int32_t M, int32_t N, int32_t K,
+                            int32_t tile_order, dkv_stream_t stream) {
+    if (!A || !B || !C || M <= 0 || N <= 0 || K <= 0 || M % 128 || N % 128 || K % 64 ||
+        (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15u) || (tile_order != 0 && tile_order != 1) ||
+        (tile_order == 1 && (N / 128) % 8 != 0))
+        return fail(DKV_E_INVALID_ARG,
+                    "dkv_gemm_bf16_nt: need M, N multiples of 128, K of 64, aligned pointers, tile_order 0/1 "
+                    "(1: N/128 a multiple of 8)");
+    hipError_t e = dkv::launch_gemm_nt(A, B, C, M, N, K, tile_order == 1, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "dkv_gemm_bf16_nt");
+    return DKV_OK;
+}
+
 dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid, int32_t unroll, int32_t reps,
                                  float *ms_median) {
     // unroll < 0 selects nontemporal loads with |unroll| in flight

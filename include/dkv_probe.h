@@ -60,6 +60,39 @@ dkv_status kv_layout_timing_enable(dkv_layout *layout, int32_t enable, int32_t m
 dkv_status kv_layout_timing_read(dkv_layout *layout, double *ms_projection, double *ms_split,
                                  double *ms_combine, int32_t *n_steps);
 
+/* ---------------------------------------------------------------------------
+ * GEMM with an operand in host memory: the experiment behind CPU-aware tiling
+ * ("KV Cache 内存层级" overview, opening section, Fig. 2(a): a 10240-square GEMM
+ * is 17x slower reading CPU memory directly than with a swap buffer; 2.1 去搬
+ * 运：DirectKV: CPU-aware tiling fetches each B tile over the link once and
+ * re-reads the HBM operand instead). Measurement only; not on the decode path.
+ * ------------------------------------------------------------------------- */
+
+/* Pinned host buffer of `bytes` bytes (hipHostMalloc, mapped, portable;
+ * flags as kv_alloc_host: DKV_HOST_COHERENT or DKV_HOST_NONCOHERENT).
+ * *host_ptr is the CPU address, *device_ptr the address kernels use. The
+ * caller frees it with dkv_host_buffer_free. Errors: DKV_E_INVALID_ARG,
+ * DKV_E_OUT_OF_MEMORY. */
+dkv_status dkv_host_buffer_alloc(uint64_t bytes, uint32_t flags, void **host_ptr, void **device_ptr);
+dkv_status dkv_host_buffer_free(void *host_ptr);
+
+/* Asynchronous copy of `bytes` bytes between any two addresses the HIP
+ * runtime knows (pinned host, HBM), on the copy engines, on `stream`: the
+ * swap-in of the staging design. Errors: DKV_E_INVALID_ARG, DKV_E_HIP. */
+dkv_status dkv_copy(void *dst, const void *src, uint64_t bytes, dkv_stream_t stream);
+
+/* C[M][N] (fp32, device) = A[M][K] (bf16, device) x B[N][K]^T (bf16; HBM or a
+ * mapped host buffer), fp32 accumulation on the matrix cores, enqueued on
+ * `stream`. tile_order 0 = row-major tile order (naive zero-copy: B column
+ * blocks are fetched again for every row block), 1 = CPU-aware order (each
+ * XCD owns every 8th column block and runs all row blocks of one column
+ * block back to back, so B crosses the link once). Same bits either way.
+ * Requires M, N multiples of 128, K a multiple of 64, 16-byte aligned
+ * pointers, and for tile_order 1 N / 128 a multiple of 8.
+ * Errors: DKV_E_INVALID_ARG (checked before anything is enqueued). */
+dkv_status dkv_gemm_bf16_nt(const uint16_t *A, const uint16_t *B, float *C, int32_t M, int32_t N,
+                            int32_t K, int32_t tile_order, dkv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

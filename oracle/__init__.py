@@ -68,6 +68,8 @@ class Oracle:
         L.oracle_decode_step.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, i64,
                                          p, p, p, p, ctypes.c_int]
         L.oracle_decode_step.restype = ctypes.c_int
+        L.oracle_gemm_nt_entries.argtypes = [p, p, i64, p, p, i64, p]
+        L.oracle_gemm_nt_entries.restype = None
 
     # -- scalars ---------------------------------------------------------------
     def bf16_to_f64(self, bits) -> np.ndarray:
@@ -169,6 +171,27 @@ class Oracle:
             raise ValueError("oracle_decode_step rejected its arguments")
         return {"attn_out": attn, "k_new": kn, "v_new": vn, "q": q}
 
+    # -- host-operand GEMM (C = A x B^T) ------------------------------------------
+    def gemm_nt_entries(self, A, B, rows, cols) -> np.ndarray:
+        """C[rows[e]][cols[e]] of C = A x B^T in fp64 (A [M][K], B [N][K] bf16 bits)."""
+        A = np.ascontiguousarray(A, dtype=np.uint16)
+        B = np.ascontiguousarray(B, dtype=np.uint16)
+        assert A.ndim == 2 and B.ndim == 2 and A.shape[1] == B.shape[1]
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        c = np.ascontiguousarray(cols, dtype=np.int64)
+        assert r.shape == c.shape
+        assert r.size == 0 or (0 <= r.min() and r.max() < A.shape[0]
+                               and 0 <= c.min() and c.max() < B.shape[0])
+        out = np.empty(r.shape, dtype=np.float64)
+        self.lib.oracle_gemm_nt_entries(_p(A), _p(B), A.shape[1], _p(r), _p(c), r.size, _p(out))
+        return out
+
+    def gemm_nt(self, A, B) -> np.ndarray:
+        """Full C = A x B^T in fp64 (small shapes)."""
+        M, N = np.asarray(A).shape[0], np.asarray(B).shape[0]
+        rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        return self.gemm_nt_entries(A, B, rows.reshape(-1), cols.reshape(-1)).reshape(M, N)
+
 
 _default: Oracle | None = None
 
@@ -178,3 +201,4 @@ def default() -> Oracle:
     if _default is None:
         _default = Oracle()
     return _default
+

@@ -254,3 +254,25 @@ int oracle_decode_step(int64_t B, int64_t hidden, int64_t n_q_heads,
     free(y);
     return 0;
 }
+
+/* ---- GEMM entries --------------------------------------------------------
+ * C = A x B^T for the host-operand GEMM experiment ("KV Cache 内存层级"
+ * overview, opening section, Fig. 2(a); 2.1 去搬运：DirectKV, CPU-aware
+ * tiling): out[e] = sum_k A[rows[e]][k] * B[cols[e]][k], A [M][K] and B [N][K]
+ * bf16 bit patterns, row-major; fp64 sums in k order. Only the requested
+ * entries are computed, so a 10240-square product can be sampled. */
+void oracle_gemm_nt_entries(const uint16_t *A, const uint16_t *B, int64_t K,
+                            const int64_t *rows, const int64_t *cols, int64_t n,
+                            double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n; ++e) {
+        const uint16_t *a = A + rows[e] * K;
+        const uint16_t *b = B + cols[e] * K;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += oracle_bf16_to_f64(a[k]) * oracle_bf16_to_f64(b[k]);
+        out[e] = acc;
+    }
+}
+

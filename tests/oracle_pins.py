@@ -326,4 +326,38 @@ def pin_gqa_grouping(o):
     assert o.kv_head_of(63, 64, 8) == 7 and o.kv_head_of(8, 64, 8) == 1
 
 
+def pin_gemm_brute_force(o):
+    """C = A x B^T, element by element in plain Python with math.fsum, on a
+    shape where rows, columns and k all differ (a transposed operand or a
+    swapped index changes the answer)."""
+    rng = np.random.default_rng(RNG_SEED + 40)
+    M, N, K = 3, 5, 7
+    A = _rand_bf16(rng, (M, K))
+    B = _rand_bf16(rng, (N, K))
+    a, b = _decode(A), _decode(B)
+    C = o.gemm_nt(A, B)
+    for i in range(M):
+        for j in range(N):
+            ref = math.fsum(float(a[i, k]) * float(b[j, k]) for k in range(K))
+            assert abs(C[i, j] - ref) <= 1e-12 * (1.0 + abs(ref)), (i, j)
+
+
+def pin_gemm_matches_numpy_and_is_exact_on_integers(o):
+    """Sampled entries equal numpy's fp64 matmul (library routine); with
+    small-integer operands every entry is an exact integer."""
+    rng = np.random.default_rng(RNG_SEED + 41)
+    M, N, K = 40, 24, 96
+    A = _rand_bf16(rng, (M, K))
+    B = _rand_bf16(rng, (N, K), 0.3)
+    ref = _decode(A) @ _decode(B).T
+    rows = rng.integers(0, M, 50)
+    cols = rng.integers(0, N, 50)
+    got = o.gemm_nt_entries(A, B, rows, cols)
+    assert np.allclose(got, ref[rows, cols], rtol=1e-12, atol=1e-12)
+    ai = rng.integers(-5, 6, (M, K))
+    bi = rng.integers(-5, 6, (N, K))
+    Ci = o.gemm_nt(_bf16_bits(ai), _bf16_bits(bi))
+    assert np.array_equal(Ci, (ai @ bi.T).astype(np.float64))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

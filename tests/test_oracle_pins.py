@@ -47,6 +47,9 @@ MUTANTS = [
      "double r = nearbyint(ldexp((double)(float)x, -qexp));"),
     ("bf16_decode_shift", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
     ("merge_unweighted_output", "acc += exp(m[s] - M) * o[s * d + i];", "acc += o[s * d + i];"),
+    ("gemm_operand_transposed", "const uint16_t *b = B + cols[e] * K;", "const uint16_t *b = B + cols[e];"),
+    ("gemm_k_range_short", "for (int64_t k = 0; k < K; ++k)\n            acc += oracle_bf16_to_f64(a[k])",
+     "for (int64_t k = 1; k < K; ++k)\n            acc += oracle_bf16_to_f64(a[k])"),
 ]
 
 
