@@ -268,6 +268,15 @@ def gemm_experiment(dkv, args):
         dkv.copy(B_hbm.data_ptr(), hb.device_ptr, b_bytes, stream)
         dkv.gemm_bf16_nt(A, B_hbm.data_ptr(), C, M, N, K, False, stream)
 
+    if args.gemm_profile:
+        for cpu_aware in (True, False):
+            gemm(hb.device_ptr, cpu_aware)()
+        dkv.copy(B_hbm.data_ptr(), hb.device_ptr, b_bytes, stream)
+        gemm(B_hbm.data_ptr(), False)()
+        torch.cuda.synchronize()
+        hb.free()
+        print(json.dumps({"gemm_profile_run": True, "S": S}), flush=True)
+        return 0
     results, outs = {}, {}
     reps = max(1, min(args.steps, 10))
     variants = [("gemm_B_in_hbm", None, reps), ("swap", swap, reps),
@@ -365,6 +374,8 @@ def main(argv=None):
     ap.add_argument("--gemm", type=int, default=0, metavar="S",
                     help="host-operand GEMM experiment instead of the bench line: C = A x B^T, "
                          "S x S x S, B in pinned host memory (the pages use S = 10240)")
+    ap.add_argument("--gemm-profile", action="store_true",
+                    help="with --gemm: run each zero-copy order once and exit (for rocprofv3)")
     ap.add_argument("--gemm-noncoherent", action="store_true",
                     help="with --gemm: allocate B non-coherent (cacheable in the GPU's L2)")
     ap.add_argument("--no-comparators", action="store_true",
