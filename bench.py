@@ -176,25 +176,32 @@ HOST_PROBES = [(64, 1), (256, 1), (512, 1), (1024, 2), (256, -1), (1024, -2)]
 HBM_PROBES = [(1024, -2), (2048, -2), (4096, -4), (8192, -8), (2048, 4)]
 
 
-SPLIT_KERNEL_SOURCES = ("attn_split.hip", "device_common.h", "dkv_internal.h")
+SPLIT_KERNEL_SOURCES = ("attn_split.hip", "device_common.h")
 
 
 def split_kernel_sha256() -> str:
-    """sha256 over the sources the split-attention kernel is compiled from."""
+    """sha256 over what the split-attention kernel is compiled from: its own
+    source, the device helpers, and the StepArgs struct it reads."""
     import hashlib
+    csrc = os.path.join(ROOT, "decode_attention_zero_amd", "csrc")
     h = hashlib.sha256()
     for name in SPLIT_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "decode_attention_zero_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(csrc, "dkv_internal.h")) as f:
+        text = f.read()
+    i = text.index("struct StepArgs {")
+    h.update(text[i:text.index("};", i)].encode())
     return h.hexdigest()
 
 
-def counter_traffic(workload: str):
+def counter_traffic(workload: str, all_hbm: bool = False):
     """HBM + host-link bytes per split-kernel launch from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a copy kernel of known
     size); None when the summary is missing or the kernel's sources have
     changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "attn_split_%s_traffic.json" % workload)
+    path = os.path.join(ROOT, "profiles", "attn_split_%s%s_traffic.json"
+                        % (workload, "_allhbm" if all_hbm else ""))
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -500,7 +507,14 @@ def main(argv=None):
         ms_h_graph = rh.graph_timed(n_hbm_steps)
         hbm_ceiling, hbm_rows, _ = probe_ceiling(dkv, rh.hbm_pool, HBM_PROBES)
         out_hbm = rh.out_bits(0)
+        hbm_split_gbps = kv_bytes / (kt_h["split"] * 1e-3) / 1e9
         hbm = {
+            "roofline": {"bound": "hbm", "kernel": "attn_split_kernel (one wavefront per item)"
+                         if rh.layout.split_waves == 0 else
+                         "attn_split_persistent_kernel (%d wavefronts)" % rh.layout.split_waves,
+                         "achieved": round(hbm_split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(hbm_split_gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": counter_traffic(wl.name, all_hbm=True)},
             "ms_per_step": round(ms_h, 4),
             "graph_ms_per_step": round(ms_h_graph, 4),
             "kv_GBps": round(kv_bytes / (ms_h * 1e-3) / 1e9, 1),
