@@ -76,6 +76,7 @@ uint16_t oracle_f64_to_bf16(double x)
 void oracle_qkv_projection(const uint16_t *x, const uint16_t *W,
                            int64_t hidden, int64_t n_out, double *y)
 {
+#pragma omp parallel for schedule(static) if (n_out * hidden > (1 << 20))
     for (int64_t n = 0; n < n_out; ++n) {
         const uint16_t *w = W + n * hidden;
         double acc = 0.0;
