@@ -17,8 +17,13 @@ per step / step time, steps enqueued eagerly), ms_per_step and
 graph_ms_per_step (the same step replayed from one captured HIP graph),
 roofline (dominant kernel = split attention, against the host link), the
 measured host-link streaming-read ceiling, the same step with every page in
-HBM (against 8 TB/s), the naive zero-copy and staging comparators, and the
-fp64 oracle timed on the host cores on the same workload.
+HBM (against 8 TB/s), the naive zero-copy, staging and host-CPU attention
+comparators, and the fp64 oracle timed on the host cores on the same workload.
+
+``--sweep`` steps the host-resident share of the KV from 0 to 100 %;
+``--sweep-ctx`` steps the context length (zero-copy, all-HBM, staging and
+host-CPU attention at each length); ``--gemm S`` runs the host-operand GEMM
+experiment.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -328,6 +333,115 @@ def gemm_experiment(dkv, args):
 
 
 SWEEP_HOST_FRACTIONS = (0.0, 0.01, 0.03, 0.1, 0.25, 0.5, 0.75, 1.0)
+SWEEP_CTX_LENGTHS = [1024, 4096, 16384, 32768, 65536, 131072]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_step_inputs(wl, B):
+    """Seeded queries (fp32) and fresh K/V (bf16) for the host-CPU attention comparator."""
+    import synth
+    d, Hq, Hkv = wl.head_dim, wl.n_q_heads, wl.n_kv_heads
+    q = np.stack([synth.normal_f64(wl.seed, 40, b, Hq * d) for b in range(B)]).astype(np.float32)
+    kn = np.stack([synth.normal_bf16(wl.seed, 41, b, Hkv * d, 1.0) for b in range(B)])
+    vn = np.stack([synth.normal_bf16(wl.seed, 42, b, Hkv * d, 1.0) for b in range(B)])
+    return q.reshape(B, Hq, d), kn.reshape(B, Hkv, d), vn.reshape(B, Hkv, d)
+
+
+def cpu_attention_timed(dkv, r, wl, ctx, threads, reps):
+    """Seconds per step (every layer) of the host-CPU attention over r's host
+    pages on `threads` threads: one warm-up layer, then the median of `reps`."""
+    q, kn, vn = cpu_step_inputs(wl, len(ctx))
+    dkv.cpu_attention(r.layout, 0, q, kn, vn, ctx, threads)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        for layer in range(wl.n_layers):
+            _, used = dkv.cpu_attention(r.layout, layer, q, kn, vn, ctx, threads)
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), used
+
+
+def cpu_dram_read_GBps(dkv, threads, nbytes=1 << 30):
+    """Host-DRAM streaming read by `threads` CPU threads over a fresh pinned buffer."""
+    buf = dkv.HostBuffer(nbytes)
+    try:
+        buf.array[::4096] = 1        # touch every page
+        dkv.cpu_stream_read(buf.host_ptr, nbytes, threads)
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            dkv.cpu_stream_read(buf.host_ptr, nbytes, threads)
+            times.append(time.perf_counter() - t0)
+        return nbytes / float(np.median(times)) / 1e9
+    finally:
+        buf.free()
+
+
+def sweep_ctx(dkv, wl, args):
+    """Step time against context length at the workload's batch: the method
+    (every cached page on the host, read in place), the same KV all in HBM,
+    staging (copy the host pool into HBM, then the HBM step) and attention on
+    the host CPU next to DRAM. Prints one JSON line with a row per length."""
+    import torch
+    rows = []
+    B = wl.batch
+    stream = torch.cuda.current_stream()
+    for L in SWEEP_CTX_LENGTHS:
+        if L > args.sweep_ctx_max:
+            break
+        w = wl.replace(ctx=L, ctx_range=None, hbm_tail_tokens=0, hbm_fraction=None)
+        ctx = w.ctx_lens()
+        kv_bytes = int(ctx.astype(np.int64).sum()) * w.kv_bytes_per_token * w.n_layers
+
+        def kv_source(layer, b, t0, t1):
+            return w.kv("k", layer, b, t0, t1), w.kv("v", layer, b, t0, t1)
+
+        steps = max(args.steps, 50) if L <= 8192 else args.steps
+        r = Resident(dkv, w, ctx, np.zeros(B, np.int32), kv_source)
+        ms_host = r.timed(steps, args.warmup)
+        out_host = r.out_bits(0)
+        cpu_s, used = cpu_attention_timed(dkv, r, w, ctx, args.cpu_threads, 3)
+        rh = Resident(dkv, w, ctx, np.full(B, 1 << 30, np.int32), kv_source)
+        ms_hbm = rh.timed(steps, args.warmup)
+        same = bool(np.array_equal(out_host, rh.out_bits(0)))
+        host_bytes = r.host_pool.info()[1]
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        copy_ms = step_ms = 0.0
+        n_cmp = 3
+        for i in range(n_cmp + 1):
+            e0.record(stream)
+            dkv.kv_pool_copy(rh.hbm_pool, r.host_pool, host_bytes, stream)
+            e1.record(stream)
+            rh.step()
+            e2.record(stream)
+            torch.cuda.synchronize()
+            if i:
+                copy_ms += e0.elapsed_time(e1) / n_cmp
+                step_ms += e1.elapsed_time(e2) / n_cmp
+        rh.free()
+        r.free()
+        row = {"ctx_tokens": L, "kv_bytes": kv_bytes,
+               "zero_copy_ms": round(ms_host, 4), "all_hbm_ms": round(ms_hbm, 4),
+               "staging_ms": round(copy_ms + step_ms, 4), "cpu_attention_ms": round(cpu_s * 1e3, 4),
+               "zero_copy_GBps": round(kv_bytes / (ms_host * 1e-3) / 1e9, 2),
+               "cpu_attention_GBps": round(kv_bytes / cpu_s / 1e9, 2),
+               "placements_bit_identical": same}
+        rows.append(row)
+        log("sweep ctx %d: zero-copy %.3f ms, all-HBM %.3f ms, staging %.3f ms, CPU %.3f ms"
+            % (L, ms_host, ms_hbm, copy_ms + step_ms, cpu_s * 1e3))
+    print(json.dumps({"sweep": "context_length", "workload": wl.name, "batch": B,
+                      "cpu_threads": args.cpu_threads, "cpu_model": cpu_model(), "rows": rows}), flush=True)
+    return 0
 
 
 def sweep(dkv, wl, ctx, kv_source, kv_bytes, args):
@@ -378,6 +492,13 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true",
                     help="crossover sweep instead of the bench line: the workload's KV with the "
                          "host-resident share stepped from 0 to 100 %% (rest in HBM)")
+    ap.add_argument("--sweep-ctx", action="store_true",
+                    help="context-length sweep instead of the bench line: zero-copy, all-HBM, "
+                         "staging and host-CPU attention at the workload's batch")
+    ap.add_argument("--sweep-ctx-max", type=int, default=65536,
+                    help="with --sweep-ctx: longest context swept (tokens per sequence)")
+    ap.add_argument("--cpu-threads", type=int, default=16,
+                    help="host threads of the CPU attention comparator and DRAM probe")
     ap.add_argument("--gemm", type=int, default=0, metavar="S",
                     help="host-operand GEMM experiment instead of the bench line: C = A x B^T, "
                          "S x S x S, B in pinned host memory (the pages use S = 10240)")
@@ -412,6 +533,8 @@ def main(argv=None):
     if args.gemm:
         return gemm_experiment(dkv, args)
     wl = configs.BY_NAME[args.workload]
+    if args.sweep_ctx:
+        return sweep_ctx(dkv, wl, args)
     ctx = wl.ctx_lens()
     B, Hkv, d = wl.batch, wl.n_kv_heads, wl.head_dim
     tail = wl.hbm_tail(ctx)
@@ -495,6 +618,22 @@ def main(argv=None):
             "bit_identical_to_method": bool(np.array_equal(out_own, out_naive)),
         }
         log("naive zero-copy: %.3f ms/step" % ms_n)
+
+    # ------------------------------------------------------------------ comparator: attention on the CPU
+    if r.host_pool is not None and r.hbm_pool is None and not args.no_comparators:
+        cpu_s, used = cpu_attention_timed(dkv, r, wl, ctx, args.cpu_threads, 3 if wl.n_layers == 1 else 1)
+        dram = cpu_dram_read_GBps(dkv, args.cpu_threads)
+        comparators["cpu_attention"] = {
+            "what": "attention computed by host threads reading the same host pages in place "
+                    "(next to DRAM, no link transfer), fp32; projection and write-back not included",
+            "threads": used,
+            "cpu_model": cpu_model(),
+            "ms_per_step": round(cpu_s * 1e3, 4),
+            "effective_kv_GBps": round(kv_bytes / cpu_s / 1e9, 3),
+            "host_dram_read_GBps": round(dram, 2),
+            "step_time_vs_method": round(cpu_s * 1e3 / ms, 3),
+        }
+        log("CPU attention (%d threads): %.3f ms/step; host DRAM read %.1f GB/s" % (used, cpu_s * 1e3, dram))
 
     # ------------------------------------------------------------------ every page in HBM
     hbm = None

@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
             "dkv_gemm_bf16_nt": ([P, P, P, I32, I32, I32, I32, P], I32),
             "kv_layout_timing_enable": ([P, I32, I32], I32),
             "kv_layout_timing_read": ([P, P, P, P, P], I32),
+            "dkv_cpu_attention": ([P, I32, P, P, P, P, P, I32, P], I32),
+            "dkv_cpu_stream_read": ([P, ctypes.c_uint64, I32, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -111,7 +113,8 @@ EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement",
             "kv_layout_create", "kv_layout_create_windowed", "kv_advance", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
             "kv_layout_split_kernel", "kv_layout_set_split_kernel", "kv_layout_split_waves", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
             "dkv_probe_stream_read", "kv_pool_copy", "dkv_host_buffer_alloc", "dkv_host_buffer_free",
-            "dkv_copy", "dkv_gemm_bf16_nt", "kv_layout_timing_enable", "kv_layout_timing_read"]
+            "dkv_copy", "dkv_gemm_bf16_nt", "kv_layout_timing_enable", "kv_layout_timing_read",
+            "dkv_cpu_attention", "dkv_cpu_stream_read"]
 
 
 def _check(status: int) -> None:
@@ -404,3 +407,32 @@ def gemm_bf16_nt(A, B_ptr: int, C, M: int, N: int, K: int, cpu_aware: bool, stre
                                   1 if cpu_aware else 0, _stream_ptr(stream)))
     return C
 
+
+
+# ----------------------------------------------------------------------------- attention on the host CPU
+def cpu_attention(layout: "Layout", layer: int, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+                  ctx_lens: np.ndarray, n_threads: int) -> tuple[np.ndarray, int]:
+    """Comparator: one step's attention computed by n_threads host threads over
+    the layout's host pages (q [B][Hq][d] fp32, k_new/v_new [B][Hkv][d] bf16
+    bits, ctx_lens [B] int32, all numpy). Returns (out [B][Hq][d] fp32, threads used)."""
+    s = layout.shape
+    B = layout.batch
+    q = np.ascontiguousarray(q, np.float32)
+    k_new = np.ascontiguousarray(k_new, np.uint16)
+    v_new = np.ascontiguousarray(v_new, np.uint16)
+    ctx = np.ascontiguousarray(ctx_lens, np.int32)
+    if q.shape != (B, s.n_q_heads, s.head_dim) or k_new.shape != (B, s.n_kv_heads, s.head_dim) \
+            or v_new.shape != k_new.shape or ctx.shape != (B,):
+        raise ValueError("cpu_attention: shapes must be q [B][Hq][d], k_new/v_new [B][Hkv][d], ctx_lens [B]")
+    out = np.empty_like(q)
+    used = ctypes.c_int32()
+    _check(lib().dkv_cpu_attention(layout.handle, layer, _np_ptr(q), _np_ptr(k_new), _np_ptr(v_new),
+                                   _np_ptr(ctx), _np_ptr(out), n_threads, ctypes.byref(used)))
+    return out, used.value
+
+
+def cpu_stream_read(host_ptr: int, nbytes: int, n_threads: int) -> int:
+    """Reads nbytes of host memory on n_threads threads; returns the 64-bit word sum."""
+    total = ctypes.c_uint64()
+    _check(lib().dkv_cpu_stream_read(host_ptr, nbytes, n_threads, ctypes.byref(total)))
+    return total.value

@@ -10,10 +10,15 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libdkv.so")
 SOURCES = ["proj.hip", "attn_split.hip", "attn_combine.hip", "window.hip", "gemm.hip", "probe.hip", "runtime.hip"]
-HEADERS = [os.path.join(CSRC, "dkv_internal.h"), os.path.join(CSRC, "device_common.h"), os.path.join(INCLUDE, "dkv.h"),
+# Host-only C++ (the CPU attention comparator), built with the system compiler.
+HOST_SOURCES = ["cpu_attention.cpp"]
+HEADERS = [os.path.join(CSRC, "cpu_attention.h"), os.path.join(CSRC, "dkv_internal.h"), os.path.join(CSRC, "device_common.h"), os.path.join(INCLUDE, "dkv.h"),
            os.path.join(INCLUDE, "dkv_probe.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fopenmp-simd", "-ffp-contract=fast", "-fno-math-errno",
+              "-Wall", "-I", INCLUDE, "-I", CSRC]
 ARCH = "gfx950"
 # Packed fp32 instructions are switched off for every HIP source.
 COMMON_FLAGS = ["-O3", "-std=c++17", "--offload-arch=" + ARCH, "-fPIC",
@@ -28,13 +33,26 @@ def sources() -> list[str]:
 def build_library(out: str = LIBRARY, verbose: bool = False) -> str:
     """Compiles every HIP source into one shared library (always recompiles)."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + COMMON_FLAGS + ["-shared", "-o", tmp] + sources()
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
-    if verbose:
-        print(res.stderr)
-    os.replace(tmp, out)
+    objects = []
+    try:
+        for src in HOST_SOURCES:
+            obj = "%s.%s.o" % (tmp, os.path.splitext(src)[0])
+            cmd = [CXX] + HOST_FLAGS + ["-c", "-o", obj, os.path.join(CSRC, src)]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError("host compiler failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+            objects.append(obj)
+        cmd = [HIPCC] + COMMON_FLAGS + ["-shared", "-o", tmp] + sources() + ["-x", "none"] + objects + ["-pthread"]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+        if verbose:
+            print(res.stderr)
+        os.replace(tmp, out)
+    finally:
+        for obj in objects:
+            if os.path.exists(obj):
+                os.remove(obj)
     return out
 
 

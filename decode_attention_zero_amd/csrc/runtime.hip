@@ -11,6 +11,7 @@
 #include <thread>
 #include <vector>
 
+#include "cpu_attention.h"
 #include "dkv_internal.h"
 #include "dkv_probe.h"
 
@@ -801,6 +802,64 @@ dkv_status kv_read(const dkv_layout *L, int32_t layer, int32_t seq, int32_t star
                 memcpy(v_out + dst, page + row_offset(s, t % DKV_PAGE_TOKENS, g, 1), row);
             }
     }
+    return DKV_OK;
+}
+
+dkv_status dkv_cpu_attention(const dkv_layout *L, int32_t layer, const float *q, const uint16_t *k_new,
+                             const uint16_t *v_new, const int32_t *ctx_lens, float *out, int32_t n_threads,
+                             int32_t *threads_used) {
+    if (!L) return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention: null layout");
+    if (layer < 0 || layer >= L->shape.n_layers)
+        return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention: layer %d out of range", layer);
+    if (!q || !k_new || !v_new || !ctx_lens || !out)
+        return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention: null pointer argument");
+    if (n_threads < 1 || n_threads > 1024)
+        return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention: n_threads %d outside [1, 1024]", n_threads);
+    const int B = L->batch;
+    for (int b = 0; b < B; ++b)
+        if (ctx_lens[b] < 0 || ctx_lens[b] > L->capacity[b] - 1)
+            return fail(DKV_E_CAPACITY, "dkv_cpu_attention: ctx_lens[%d] = %d outside [0, %d]", b, ctx_lens[b],
+                        L->capacity[b] - 1);
+    HIP_TRY(hipDeviceSynchronize());              // pages written by earlier steps are complete
+    std::vector<const char *> pages((size_t)B * L->max_pages, nullptr);
+    std::vector<uint64_t> addr;
+    for (int b = 0; b < B; ++b) {
+        const int n = (ctx_lens[b] + DKV_PAGE_TOKENS - 1) / DKV_PAGE_TOKENS;
+        if (n == 0) continue;
+        HIP_TRY(table_row(L, layer, b, 0, n - 1, addr));
+        for (int p = 0; p < n; ++p) {
+            const char *page = host_view(L, addr[(size_t)p]);
+            if (!page)
+                return fail(DKV_E_INVALID_ARG,
+                            "dkv_cpu_attention: page %d of sequence %d is in HBM; the CPU reads host pages only",
+                            p, b);
+            pages[(size_t)b * L->max_pages + p] = page;
+        }
+    }
+    dkv::CpuAttentionJob job{};
+    job.batch = B;
+    job.n_q_heads = L->shape.n_q_heads;
+    job.n_kv_heads = L->shape.n_kv_heads;
+    job.head_dim = L->shape.head_dim;
+    job.max_pages = L->max_pages;
+    job.pages = pages.data();
+    job.ctx_lens = ctx_lens;
+    job.q = q;
+    job.k_new = k_new;
+    job.v_new = v_new;
+    job.out = out;
+    job.n_threads = n_threads;
+    const int used = dkv::cpu_attention_run(job);
+    if (threads_used) *threads_used = used;
+    return DKV_OK;
+}
+
+dkv_status dkv_cpu_stream_read(const void *host_ptr, uint64_t bytes, int32_t n_threads, uint64_t *checksum) {
+    if (!host_ptr || bytes % 64 || n_threads < 1 || n_threads > 1024)
+        return fail(DKV_E_INVALID_ARG, "dkv_cpu_stream_read: null pointer, bytes not a multiple of 64, or "
+                                       "n_threads outside [1, 1024]");
+    const uint64_t sum = dkv::cpu_stream_read(host_ptr, bytes, n_threads);
+    if (checksum) *checksum = sum;
     return DKV_OK;
 }
 

@@ -93,6 +93,39 @@ dkv_status dkv_copy(void *dst, const void *src, uint64_t bytes, dkv_stream_t str
 dkv_status dkv_gemm_bf16_nt(const uint16_t *A, const uint16_t *B, float *C, int32_t M, int32_t N,
                             int32_t K, int32_t tile_order, dkv_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Attention on the host CPU: the comparator for moving decoding attention to
+ * where the KV lives instead of moving the KV to the GPU ("KV Cache 内存层级"
+ * overview, 2.2 挪计算：NEO: decoding attention is memory-bandwidth-bound on
+ * both processors and host DRAM bandwidth is within a small factor of the
+ * GPU's). Measurement only; decode_step never calls these.
+ * ------------------------------------------------------------------------- */
+
+/* Attention of one decode step of `layer`, computed by n_threads host
+ * threads that read the cached K/V in place from the layout's host pages
+ * (every page holding tokens [0, ctx_lens[b]) must be a host page), with the
+ * fresh token's K/V appended: for each sequence b and query head h (KV head
+ * h / G), softmax over ctx_lens[b] + 1 tokens of (q . k) / sqrt(d), applied
+ * to the values, fp32 arithmetic.
+ *   q            host [B][Hq][d] fp32 (unscaled)
+ *   k_new, v_new host [B][Hkv][d] bf16 bits
+ *   ctx_lens     host [B], each in [0, capacity - 1]
+ *   out          host [B][Hq][d] fp32, written
+ * Synchronises the device first (pages written by earlier steps are
+ * complete). *threads_used (may be NULL) gets the thread count.
+ * Errors: DKV_E_INVALID_ARG (null pointer, bad layer or thread count, an HBM
+ * page among the cached tokens), DKV_E_CAPACITY, DKV_E_HIP. */
+dkv_status dkv_cpu_attention(const dkv_layout *layout, int32_t layer, const float *q,
+                             const uint16_t *k_new, const uint16_t *v_new, const int32_t *ctx_lens,
+                             float *out, int32_t n_threads, int32_t *threads_used);
+
+/* Reads `bytes` bytes (a multiple of 64) of host memory at `host_ptr` on
+ * n_threads host threads as 64-bit words and returns their wrapping sum in
+ * *checksum (may be NULL): the host-DRAM streaming-read rate, timed by the
+ * caller. Errors: DKV_E_INVALID_ARG. */
+dkv_status dkv_cpu_stream_read(const void *host_ptr, uint64_t bytes, int32_t n_threads,
+                               uint64_t *checksum);
+
 #ifdef __cplusplus
 }
 #endif
