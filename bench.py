@@ -336,6 +336,15 @@ SWEEP_HOST_FRACTIONS = (0.0, 0.01, 0.03, 0.1, 0.25, 0.5, 0.75, 1.0)
 SWEEP_CTX_LENGTHS = [1024, 4096, 16384, 32768, 65536, 131072]
 
 
+def split_kernel_label(layout) -> str:
+    """Name of the split-attention kernel a layout launches, and its wavefronts."""
+    mfma = layout.split_kernel == "mfma"
+    if layout.split_waves > 0:
+        return "%s (%d wavefronts)" % ("attn_split_mfma_persistent_kernel" if mfma
+                                       else "attn_split_persistent_kernel", layout.split_waves)
+    return "%s (one wavefront per item)" % ("attn_split_mfma_kernel" if mfma else "attn_split_kernel")
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -589,8 +598,7 @@ def main(argv=None):
         return 0
     ms_graph = r.graph_timed(args.steps)
     out_own = r.out_bits(0)
-    split_kernel_name = ("attn_split_persistent_kernel (%d wavefronts)" % r.layout.split_waves
-                         if r.layout.split_waves > 0 else "attn_split_kernel")
+    split_kernel_name = split_kernel_label(r.layout)
     ceiling = ceiling_rows = None
     if r.host_pool is not None:
         ceiling, ceiling_rows, _ = probe_ceiling(dkv, r.host_pool, HOST_PROBES)
@@ -648,9 +656,7 @@ def main(argv=None):
         out_hbm = rh.out_bits(0)
         hbm_split_gbps = kv_bytes / (kt_h["split"] * 1e-3) / 1e9
         hbm = {
-            "roofline": {"bound": "hbm", "kernel": "attn_split_kernel (one wavefront per item)"
-                         if rh.layout.split_waves == 0 else
-                         "attn_split_persistent_kernel (%d wavefronts)" % rh.layout.split_waves,
+            "roofline": {"bound": "hbm", "kernel": split_kernel_label(rh.layout),
                          "achieved": round(hbm_split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(hbm_split_gbps / HBM_PEAK_GBPS, 4),
                          "traffic": counter_traffic(wl.name, all_hbm=True)},

@@ -48,6 +48,7 @@ struct SplitState {
 
     float q[G][8];
     float m[G], l[G], acc[G][8];
+    int sub;                       // page token of this lane in the wave's first load
 
     // `run` points at this lane's 16 bytes of the wave's first load of the run.
     __device__ __forceinline__ void load(const char *run, uint4 (&kr)[NLDW], uint4 (&vr)[NLDW]) const {
@@ -120,6 +121,11 @@ struct SplitState {
                 for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
             }
         }
+    }
+
+    template <bool PARTIAL>
+    __device__ __forceinline__ void page(const uint4 (&kr)[NLDW], const uint4 (&vr)[NLDW], int n_valid) {
+        page<PARTIAL>(kr, vr, sub, n_valid);
     }
 
     // Query rows of heads h0 .. h0 + G - 1 (this lane's 8 dims) and an empty
@@ -210,12 +216,46 @@ struct SplitState {
     }
 };
 
+// Streams the pages holding tokens [t0, t1) of one sequence through state
+// `st`: page runs at pt[p] + run_off are double-buffered in registers
+// (ping-pong, so no copies), the next page's loads in flight while the
+// current one is computed. Full pages take a mask-free path; only the last
+// page can be partial. (Reading the item's page addresses once, one per
+// lane, and broadcasting them with readlane avoids the page-table load
+// between page loads, but measured slower on MI355X: 1 GiB in HBM at group
+// 4, 0.176 vs 0.169 ms; on the host link it needs fewer looping wavefronts
+// to stay at the ceiling.)
+template <class S>
+__device__ __forceinline__ void stream_pages(S &st, const uint64_t *pt, size_t run_off, int t0, int t1) {
+    constexpr int NLD = S::NLDW;
+    const int p0 = t0 / kPageTokens;
+    const int p1 = (t1 + kPageTokens - 1) / kPageTokens;   // pages [p0, p1)
+    const int pf = t1 / kPageTokens;                        // pages [p0, pf) are full
+    auto run_of = [&](int p) { return reinterpret_cast<const char *>(pt[p]) + run_off; };
+    uint4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
+    int p = p0;
+    st.load(run_of(p), ka, va);
+    while (p + 1 < pf) {                 // pages p (in a) and p + 1 are full
+        st.load(run_of(p + 1), kb, vb);
+        st.template page<false>(ka, va, kPageTokens);
+        if (p + 2 < p1) st.load(run_of(p + 2), ka, va);
+        st.template page<false>(kb, vb, kPageTokens);
+        p += 2;
+    }
+    if (p < pf) {                        // one last full page (in a), maybe a partial one after
+        if (p + 1 < p1) st.load(run_of(p + 1), kb, vb);
+        st.template page<false>(ka, va, kPageTokens);
+        if (p + 1 < p1) st.template page<true>(kb, vb, t1 - (p + 1) * kPageTokens);
+    } else if (p < p1) {                 // the partial page (in a)
+        st.template page<true>(ka, va, t1 - p * kPageTokens);
+    }
+}
+
 // One work item: split s of sequence b, KV head g, query heads h0 .. h0 + G - 1,
 // on the WPI wavefronts of the workgroup.
 template <int D, int G, int WPI>
 __device__ __forceinline__ void split_item(const StepArgs &a, int s, int g, int h0, int b) {
     using S = SplitState<D, G, WPI>;
-    constexpr int NLD = S::NLDW;
     constexpr int LPT = S::LPT;
 
     const int L = a.ctx_lens[b];
@@ -226,37 +266,242 @@ __device__ __forceinline__ void split_item(const StepArgs &a, int s, int g, int 
 
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int sub = lane / LPT + w * S::NLDW * S::TPL;   // page token of the wave's first load
     const int dl = lane % LPT;
 
     S st;
     st.init(a, b, h0, dl);
-
-    const uint64_t *pt = a.page_table + (size_t)b * a.max_pages;
+    st.sub = lane / LPT + w * S::NLDW * S::TPL;
     const size_t run_off = (size_t)g * S::RUN + (size_t)w * S::NLDW * 1024 + (size_t)lane * 16;
-    auto run_of = [&](int p) { return reinterpret_cast<const char *>(pt[p]) + run_off; };
-
-    const int p0 = t0 / kPageTokens;
-    const int p1 = (t1 + kPageTokens - 1) / kPageTokens;   // pages [p0, p1)
-    const int pf = t1 / kPageTokens;                        // pages [p0, pf) are full
-    uint4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
-    int p = p0;
-    st.load(run_of(p), ka, va);
-    while (p + 1 < pf) {                 // pages p (in a) and p + 1 are full
-        st.load(run_of(p + 1), kb, vb);
-        st.template page<false>(ka, va, sub, kPageTokens);
-        if (p + 2 < p1) st.load(run_of(p + 2), ka, va);
-        st.template page<false>(kb, vb, sub, kPageTokens);
-        p += 2;
-    }
-    if (p < pf) {                        // one last full page (in a), maybe a partial one after
-        if (p + 1 < p1) st.load(run_of(p + 1), kb, vb);
-        st.template page<false>(ka, va, sub, kPageTokens);
-        if (p + 1 < p1) st.template page<true>(kb, vb, sub, t1 - (p + 1) * kPageTokens);
-    } else if (p < p1) {                 // the partial page (in a)
-        st.template page<true>(ka, va, sub, t1 - p * kPageTokens);
-    }
+    stream_pages(st, a.page_table + (size_t)b * a.max_pages, run_off, t0, t1);
     st.finish(a, b, h0, s, dl);
+}
+
+// ------------------------------------------------------------------------------
+// Matrix-core arithmetic for a group of query heads. Per page, the group's
+// scores are one dense product S = K Q^T ([16 tokens] x [d] x [G heads]) and
+// its output update one product O^T += V^T P^T, so they run on
+// v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x16_bf16; on VALU the same
+// work costs ~500 instructions per 8 KiB page run at G = 4 and ~830 at G = 8,
+// more than a CU issues in the time HBM delivers the run. The page loads are
+// the same contiguous 1 KiB wave loads as above; each run is then staged in
+// the wavefront's own LDS buffer to reach the MFMA operand layouts. Staged
+// token rows are padded by 16 bytes: that keeps the row-wise K reads, the
+// column-wise V reads and the staging writes free of bank conflicts, and
+// every lane's LDS addresses a single base plus constant offsets.
+//
+// Precision: the matrix cores take bf16 operands. K and V are bf16 already;
+// the fp32 queries and probabilities are each split into two bf16 terms, hi =
+// bf16(x) and lo = bf16(x - hi), which represent x to ~2^-17 relative, and
+// both terms go through the same product: the 16 MFMA columns hold the hi
+// terms of heads 0 .. G-1 in columns 0 .. G-1 and their lo terms mirrored in
+// columns 15 .. 16-G, and a row-mirror DPP add forms hi + lo. Products of
+// bf16 terms are exact in fp32 and accumulate in fp32.
+//
+// Lane l (column j = l % 16, row group q = l / 16) owns, for head min(j,
+// 15-j): the scores of page tokens 4q .. 4q+3, the output dims 16n + 4q ..
+// +3 of every 16-dim block n, and a running max and partial sum. The running
+// max is common to the four row groups (the PV product sums over all 16
+// tokens), so each page's max is reduced across them. Every column's
+// arithmetic depends only on its own head, so the per-query-head comparator
+// (one head per item) gives the same bits as the grouped kernel.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));   // round to nearest even
+}
+
+// s_waitcnt lgkmcnt(0) only (vmcnt and expcnt left unconstrained).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+template <int D, int G>
+struct MfmaState {
+    static constexpr int LPT = D / 8;               // 16-byte chunks per token row
+    static constexpr int TPL = 64 / LPT;            // tokens per wave load
+    static constexpr int NLDW = kPageTokens / TPL;  // wave loads per 16-token tile
+    static constexpr int TILE = kPageTokens * D * 2;
+    static constexpr int RUN = 2 * TILE;
+    static constexpr int ROW = D * 2 + 16;          // staged token row (padded)
+    static constexpr int STILE = kPageTokens * ROW; // staged K or V tile
+    static constexpr int STAGE = 2 * STILE;         // LDS bytes per wavefront
+    static constexpr int NKB = D / 32;              // 32-dim blocks of the score product
+    static constexpr int NDB = D / 16;              // 16-dim blocks of the output
+    static_assert(G >= 1 && G <= 8, "hi and lo terms of the group fill at most 16 columns");
+
+    char *lds;            // this wavefront's staging buffer
+    int lane, col, kq;
+    int x16, x32;         // ds_bpermute byte addresses of lanes lane ^ 16 and lane ^ 32
+    bf16x8 qop[NKB];      // B operand of the score product: this lane's column, dims 32c + 8kq ..
+    f32x4 o[NDB];         // O^T[16n + 4kq + r][col]
+    float m, l;
+
+
+    __device__ __forceinline__ void load(const char *run, uint4 (&kr)[NLDW], uint4 (&vr)[NLDW]) const {
+#pragma unroll
+        for (int j = 0; j < NLDW; ++j) kr[j] = load_stream(run + j * 1024);
+#pragma unroll
+        for (int j = 0; j < NLDW; ++j) vr[j] = load_stream(run + TILE + j * 1024);
+    }
+
+    __device__ __forceinline__ void init(const StepArgs &a, int b, int h0) {
+        lane = threadIdx.x & 63;
+        col = lane & 15;
+        kq = lane >> 4;
+        x16 = (lane ^ 16) << 2;
+        x32 = (lane ^ 32) << 2;
+        const int head = col < G ? col : (col >= 16 - G ? 15 - col : -1);
+#pragma unroll
+        for (int c = 0; c < NKB; ++c) {
+            uint32_t w[4] = {0u, 0u, 0u, 0u};
+            if (head >= 0) {
+                const float *qp = a.q + ((size_t)b * a.n_q_heads + (size_t)(h0 + head)) * D + 32 * c + 8 * kq;
+                const float4 f0 = *reinterpret_cast<const float4 *>(qp);
+                const float4 f1 = *reinterpret_cast<const float4 *>(qp + 4);
+                const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uint16_t t = bf16_bits(f[e]);
+                    if (col >= 8) t = bf16_bits(f[e] - __uint_as_float((uint32_t)t << 16));
+                    w[e >> 1] |= (uint32_t)t << (16 * (e & 1));
+                }
+            }
+            qop[c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+        m = kNegInf;
+        l = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NDB; ++n) o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    template <bool PARTIAL>
+    __device__ __forceinline__ void page(const uint4 (&kr)[NLDW], const uint4 (&vr)[NLDW], int n_valid) {
+        // Stage the run: lane l of wave load j holds token j*TPL + l/LPT, chunk l%LPT.
+        char *wr = lds + (lane / LPT) * ROW + (lane % LPT) * 16;
+#pragma unroll
+        for (int j = 0; j < NLDW; ++j) {
+            *reinterpret_cast<uint4 *>(wr + j * TPL * ROW) = kr[j];
+            *reinterpret_cast<uint4 *>(wr + STILE + j * TPL * ROW) = vr[j];
+        }
+        wait_lds();
+        asm volatile("" ::: "memory");
+
+        // S = K Q^T: A = K rows (token = col), B = the query terms.
+        f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+        const char *kt = lds + col * ROW + kq * 16;
+#pragma unroll
+        for (int c = 0; c < NKB; ++c) {
+            const uint4 kv = *reinterpret_cast<const uint4 *>(kt + c * 64);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qop[c], sc, 0, 0, 0);
+        }
+        float sv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sv[r] = sc[r] + dpp<0x140>(sc[r]);                   // hi + lo (row mirror)
+            if (PARTIAL && 4 * kq + r >= n_valid) sv[r] = kNegInf;
+        }
+        float pm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        pm = fmaxf(pm, __int_as_float(__builtin_amdgcn_ds_bpermute(x16, __float_as_int(pm))));
+        pm = fmaxf(pm, __int_as_float(__builtin_amdgcn_ds_bpermute(x32, __float_as_int(pm))));
+        const float mn = fmaxf(m, pm);
+        if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {
+            const float alpha = (mn == m) ? 1.0f : rescale(m, mn);
+            l *= alpha;
+#pragma unroll
+            for (int n = 0; n < NDB; ++n) o[n] *= alpha;
+            m = mn;
+        }
+        uint16_t pb[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(sv[r] - m);
+            l += p;
+            const uint16_t hi = bf16_bits(p);
+            pb[r] = col < 8 ? hi : bf16_bits(p - __uint_as_float((uint32_t)hi << 16));
+        }
+        const s16x4 pop = {(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
+
+        // O^T += V^T P^T: A = V^T (dim = col, tokens 4kq .. 4kq+3), B = P^T; in
+        // groups of four 16-dim blocks, so that only one group's V reads are
+        // held in registers at a time.
+        const char *vt = lds + STILE + 4 * kq * ROW + 2 * col;
+#pragma unroll
+        for (int n0 = 0; n0 < NDB; n0 += 4) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int n = n0; n < n0 + 4; ++n) {
+                s16x4 vop;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    vop[r] = *reinterpret_cast<const short *>(vt + r * ROW + n * 32);
+                    // Slots past the valid tokens may hold any bits (NaN times a zero
+                    // weight would still be NaN).
+                    if (PARTIAL && 4 * kq + r >= n_valid) vop[r] = 0;
+                }
+                o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, o[n], 0, 0, 0);
+            }
+        }
+        asm volatile("" ::: "memory");   // the next run's staging stays behind these reads
+    }
+
+    // Sums the partial sums over the row groups and the hi/lo output columns,
+    // and writes the partial (m, l, o) of heads h0 .. h0 + G - 1 for split s.
+    __device__ __forceinline__ void finish(const StepArgs &a, int b, int h0, int s) {
+        float lt = l + __shfl_xor(l, 16);
+        lt = lt + __shfl_xor(lt, 32);
+#pragma unroll
+        for (int n = 0; n < NDB; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[n][r] += dpp<0x140>(o[n][r]);
+        if (col < G) {
+            const size_t slot = ((size_t)b * a.n_q_heads + (size_t)(h0 + col)) * a.max_splits + s;
+            float *po = a.part_o + slot * D + 4 * kq;
+#pragma unroll
+            for (int n = 0; n < NDB; ++n)
+                *reinterpret_cast<float4 *>(po + 16 * n) = make_float4(o[n][0], o[n][1], o[n][2], o[n][3]);
+            if (kq == 0) a.part_ml[slot] = make_float2(m, lt);
+        }
+    }
+};
+
+template <int D, int G>
+__device__ __forceinline__ void split_item_mfma(const StepArgs &a, char *stage, int s, int g, int h0, int b) {
+    using S = MfmaState<D, G>;
+    const int L = a.ctx_lens[b];
+    if (L < 0 || L >= a.capacity[b]) return;
+    const int t0 = s * a.split_tokens;
+    if (t0 >= L) return;
+    const int t1 = min(t0 + a.split_tokens, L);
+    S st;
+    st.lds = stage;
+    st.init(a, b, h0);
+    const size_t run_off = (size_t)g * S::RUN + (size_t)(threadIdx.x & 63) * 16;
+    stream_pages(st, a.page_table + (size_t)b * a.max_pages, run_off, t0, t1);
+    st.finish(a, b, h0, s);
+}
+
+// Matrix-core split kernels: one wavefront per work item (s, g, b) =
+// blockIdx (x, y, z), or (PER_QUERY_HEAD, G = 1) the naive comparator with
+// one item per query head; and the looping form for host-dominated layouts.
+constexpr int kMfmaWavesPerSimd = 3;   // register budget: 168 per lane
+
+template <int D, int G, bool PER_QUERY_HEAD = false>
+__global__ __launch_bounds__(64, kMfmaWavesPerSimd) void attn_split_mfma_kernel(StepArgs a) {
+    __shared__ __attribute__((aligned(16))) char stage[MfmaState<D, G>::STAGE];
+    const int g = PER_QUERY_HEAD ? blockIdx.y / (a.n_q_heads / a.n_kv_heads) : blockIdx.y;
+    const int h0 = PER_QUERY_HEAD ? blockIdx.y : blockIdx.y * G;
+    split_item_mfma<D, G>(a, stage, blockIdx.x, g, h0, blockIdx.z);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(64, kMfmaWavesPerSimd) void attn_split_mfma_persistent_kernel(StepArgs a) {
+    __shared__ __attribute__((aligned(16))) char stage[MfmaState<D, G>::STAGE];
+    const int n_items = a.n_kv_heads * a.max_splits * a.batch;
+    for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
+        const int g = i % a.n_kv_heads;
+        const int rest = i / a.n_kv_heads;
+        split_item_mfma<D, G>(a, stage, rest % a.max_splits, g, g * G, rest / a.max_splits);
+    }
 }
 
 // One wavefront per work item (s, g, b) = blockIdx (x, y, z).
@@ -396,7 +641,13 @@ void launch(const StepArgs &a, hipStream_t st) {
     constexpr int WPI = G >= 8 ? 2 : 1;
     dim3 grid(a.max_splits, a.n_kv_heads, a.batch);
     if (a.split_variant == kSplitNaive) {
-        attn_split_kernel<D, 1, WPI, true><<<dim3(a.max_splits, a.n_q_heads, a.batch), 64 * WPI, 0, st>>>(a);
+        // Per query head, with the arithmetic of the layout's grouped kernel.
+        const dim3 heads(a.max_splits, a.n_q_heads, a.batch);
+        if (G >= kMfmaMinGroup) attn_split_mfma_kernel<D, 1, true><<<heads, 64, 0, st>>>(a);
+        else attn_split_kernel<D, 1, WPI, true><<<heads, 64 * WPI, 0, st>>>(a);
+    } else if (a.split_variant == kSplitMfma) {
+        if (a.split_waves > 0) attn_split_mfma_persistent_kernel<D, G><<<a.split_waves, 64, 0, st>>>(a);
+        else attn_split_mfma_kernel<D, G><<<grid, 64, 0, st>>>(a);
     } else if (a.split_variant == kSplitLds) {
         // Consumers own at most 4 query heads each; 4 ring slots (3 runs in flight).
         constexpr int NC = G > 4 ? G / 4 : 1;

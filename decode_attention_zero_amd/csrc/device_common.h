@@ -13,9 +13,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // KV pages are streamed once per step: nontemporal 16-byte loads keep them
 // from displacing reusable lines and measured ~13 % more HBM read bandwidth
 // on gfx950 than plain loads for the same page-run pattern.
+// The load goes through a global (address space 1) pointer: a generic
+// pointer would make it a flat load, which also counts on the LDS counter, so
+// any later wait for an LDS access would wait for every page load in flight.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef const u32x4 __attribute__((address_space(1))) global_u32x4;
 __device__ __forceinline__ uint4 load_stream(const void *p) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    const u32x4 v = __builtin_nontemporal_load((global_u32x4 *)p);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 

@@ -18,6 +18,10 @@ constexpr int kSplitRegisters = 0;
 constexpr int kSplitLds = 1;
 // Comparator: one wavefront per query head, each KV head fetched G times.
 constexpr int kSplitNaive = 2;
+// Register double buffer with the group's scores and output update on the
+// matrix cores (the default from groups of kMfmaMinGroup query heads).
+constexpr int kSplitMfma = 3;
+constexpr int kMfmaMinGroup = 4;
 
 // Everything one decode step's kernels read or write. Built on the host by
 // decode_step from the layout and the caller's pointers; passed by value.
@@ -33,7 +37,7 @@ struct StepArgs {
     int32_t split_tokens;   // tokens per attention work item (multiple of 16)
     int32_t max_splits;     // partial slots per (sequence, query head)
     float qscale;           // log2(e) / sqrt(head_dim): scores come out in log2 units
-    int32_t split_variant;  // kSplitRegisters, kSplitLds or kSplitNaive
+    int32_t split_variant;  // kSplitRegisters, kSplitLds, kSplitNaive or kSplitMfma
     int32_t split_waves;    // register kernel: > 0 = that many wavefronts loop over the items
     int32_t proj_mfma_min_batch;  // batches from this size on project on MFMA, below on VALU
     // this layer's page table [batch][max_pages] of device addresses

@@ -87,7 +87,7 @@ struct dkv_layout {
     int32_t max_pages;
     int32_t split_tokens;
     int32_t max_splits;
-    int32_t split_variant;             // dkv::kSplitRegisters, kSplitLds or kSplitNaive
+    int32_t split_variant;             // dkv::kSplitRegisters, kSplitLds, kSplitNaive or kSplitMfma
     int32_t split_waves;               // > 0: the register kernel runs on that many looping wavefronts
     int32_t proj_mfma_min_batch;       // batches from this size on project on the matrix cores
     dkv_pool *host_pool;
@@ -197,13 +197,14 @@ int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, int32_t max_cap) 
 // 189 us vs 258 us; group 8: 18.8 ms vs 27.6 ms for 64 GiB) and the same on
 // the host link. DKV_SPLIT_KERNEL=regs|lds overrides it; DKV_SPLIT_KERNEL=naive
 // selects the naive zero-copy comparator (one work item per query head).
-int32_t choose_split_variant(int32_t /*group*/) {
+int32_t choose_split_variant(int32_t group) {
     if (const char *env = getenv("DKV_SPLIT_KERNEL")) {
         if (!strcmp(env, "lds")) return dkv::kSplitLds;
         if (!strcmp(env, "regs")) return dkv::kSplitRegisters;
         if (!strcmp(env, "naive")) return dkv::kSplitNaive;
+        if (!strcmp(env, "mfma") && group >= dkv::kMfmaMinGroup) return dkv::kSplitMfma;
     }
-    return dkv::kSplitRegisters;
+    return group >= dkv::kMfmaMinGroup ? dkv::kSplitMfma : dkv::kSplitRegisters;
 }
 
 // Wavefronts of the split kernel. On the host link the number of reads in
@@ -700,7 +701,8 @@ int32_t kv_layout_split_kernel(const dkv_layout *L) { return L ? L->split_varian
 int32_t kv_layout_split_waves(const dkv_layout *L) { return L ? L->split_waves : -1; }
 
 dkv_status kv_layout_set_split_kernel(dkv_layout *L, int32_t kernel) {
-    if (!L || (kernel != dkv::kSplitRegisters && kernel != dkv::kSplitLds && kernel != dkv::kSplitNaive))
+    if (!L || (kernel != dkv::kSplitRegisters && kernel != dkv::kSplitLds && kernel != dkv::kSplitNaive &&
+               (kernel != dkv::kSplitMfma || L->shape.n_q_heads / L->shape.n_kv_heads < dkv::kMfmaMinGroup)))
         return fail(DKV_E_INVALID_ARG, "kv_layout_set_split_kernel: null layout or unknown kernel %d", kernel);
     L->split_variant = kernel;
     return DKV_OK;

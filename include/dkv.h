@@ -263,16 +263,23 @@ dkv_status kv_layout_check_status(dkv_layout *kv_layout);
  * of 16 fixed at creation, independent of placement. */
 int32_t kv_layout_split_tokens(const dkv_layout *kv_layout);
 
-/* Split-attention kernel the layout's decode steps use: 0 = one wavefront
- * per work item with a register double buffer (the default), 1 = a producer
- * wavefront that streams page runs with LDS DMA into a ring for consumer
- * wavefronts that own the group's query heads. Both compute every head in
- * the same order and give identical bits. 2 = the naive zero-copy
- * comparator (one wavefront per query head, so each KV head's pages are read
- * once per query head of its group), for measurement only; same bits too.
+/* Split-attention kernel the layout's decode steps use. All read each page
+ * run once per step for the whole group of query heads:
+ *   0 = one wavefront per work item with a register double buffer, VALU
+ *       arithmetic (the default below groups of 4 query heads);
+ *   1 = a producer wavefront that streams page runs with LDS DMA into a ring
+ *       for consumer wavefronts that own the group's query heads (same
+ *       arithmetic as 0; identical bits up to groups of 4);
+ *   3 = the register double buffer with the group's scores and output update
+ *       on the matrix cores (the default from groups of 4; queries and
+ *       probabilities enter as two bf16 terms each, see the kernel source);
+ *   2 = the naive zero-copy comparator (one wavefront per query head, so
+ *       each KV head's pages are read once per query head of its group), for
+ *       measurement only, with the arithmetic of the group's default kernel
+ *       and so the same bits as it.
  * Chosen at creation; the environment variable
- * DKV_SPLIT_KERNEL=regs|lds|naive, read by kv_layout_create, selects one.
- * -1 for a NULL layout. */
+ * DKV_SPLIT_KERNEL=regs|lds|naive|mfma, read by kv_layout_create, selects
+ * one (mfma only from groups of 4). -1 for a NULL layout. */
 int32_t kv_layout_split_kernel(const dkv_layout *kv_layout);
 
 /* Wavefronts the register split kernel runs on: 0 = one per work item
@@ -286,9 +293,9 @@ int32_t kv_layout_split_kernel(const dkv_layout *kv_layout);
  * either way. -1 for a NULL layout. */
 int32_t kv_layout_split_waves(const dkv_layout *kv_layout);
 
-/* Switches the layout's split-attention kernel (0, 1 or 2 as above) for the
+/* Switches the layout's split-attention kernel (0 to 3 as above) for the
  * decode steps enqueued after the call. Errors: DKV_E_INVALID_ARG for a NULL
- * layout or an unknown kernel. */
+ * layout, an unknown kernel, or 3 below groups of 4. */
 dkv_status kv_layout_set_split_kernel(dkv_layout *kv_layout, int32_t kernel);
 
 /* Thread-local message of the last failing call on this thread. */

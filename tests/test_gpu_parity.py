@@ -121,7 +121,27 @@ def test_llama70b_shape_group8(oracle):
         s.free()
 
 
-@pytest.mark.parametrize("split", [16, 64])
+@pytest.mark.parametrize("wl_name", ["tiny-h512-b1-ctx1024", "llama3-8b-b8-ctx32768-host",
+                                     "llama3-70b-b16-ctx131072-8layers-host"], ids=["g1", "g4", "g8"])
+def test_stale_slots_do_not_leak(oracle, wl_name):
+    """Slots past ctx_lens[b] in a sequence's last pages may hold any bits
+    (here NaN in K and V): the masked tokens must contribute nothing."""
+    ctx = [5, 16, 33, 700]
+    wl = configs.BY_NAME[wl_name].replace(batch=len(ctx), n_layers=1)
+    cap = [c + 40 for c in ctx]
+    s = H.Setup(wl, ctx_lens=ctx, capacity=cap, hbm_tail=[0, 1 << 20, 24, 0])
+    try:
+        for b, (L, C) in enumerate(zip(ctx, cap)):
+            nan = np.full((C - L, wl.n_kv_heads, wl.head_dim), 0x7FC0, np.uint16)
+            H.dkv.kv_append(s.layout, 0, b, L, nan, nan)
+        got = f32(s.run(f32=True))
+        assert np.all(np.isfinite(got))
+        check_tight(got, tight_reference(oracle, wl, 0, s.ctx), "%s stale NaN slots" % wl_name)
+    finally:
+        s.free()
+
+
+@pytest.mark.parametrize("split", [16, 64, 1024])
 def test_split_and_page_edges(oracle, monkeypatch, split):
     monkeypatch.setenv("DKV_SPLIT_TOKENS", str(split))
     T = split
@@ -309,13 +329,22 @@ def test_out_of_range_context_is_flagged():
 ], ids=["g1-d64", "g4-d128", "g8-d128"])
 def test_split_kernel_variants_bit_identical(oracle, monkeypatch, wl_name, ctx):
     """The register-double-buffer and the LDS producer/consumer split kernels
-    meet the oracle's gates with host and HBM pages mixed. Up to groups of 4
-    they compute every head in the same order (identical bits); at group 8
-    the register kernel splits each page's tokens over two wavefronts, which
-    changes the order of the fp32 sums."""
+    (VALU arithmetic) and, from groups of 4, the matrix-core kernel meet the
+    oracle's gates with host and HBM pages mixed. Up to groups of 4 the two
+    VALU kernels compute every head in the same order (identical bits); at
+    group 8 the register kernel splits each page's tokens over two
+    wavefronts, which changes the order of the fp32 sums. The layout's
+    default is the matrix-core kernel from groups of 4."""
     wl = configs.BY_NAME[wl_name].replace(batch=len(ctx), n_layers=1)
+    variants = ("regs", "lds", "mfma") if wl.group >= 4 else ("regs", "lds")
+    monkeypatch.delenv("DKV_SPLIT_KERNEL", raising=False)
+    s = H.Setup(wl, ctx_lens=ctx[:1], hbm_tail=0)
+    try:
+        assert s.layout.split_kernel == ("mfma" if wl.group >= 4 else "regs")
+    finally:
+        s.free()
     outs, outs32 = {}, {}
-    for variant in ("regs", "lds"):
+    for variant in variants:
         monkeypatch.setenv("DKV_SPLIT_KERNEL", variant)
         s = H.Setup(wl, ctx_lens=ctx, hbm_tail=[0, 40, 1 << 20, 16, 0][:len(ctx)])
         try:
@@ -329,7 +358,7 @@ def test_split_kernel_variants_bit_identical(oracle, monkeypatch, wl_name, ctx):
         assert np.array_equal(outs32["regs"].view(np.uint32), outs32["lds"].view(np.uint32))
     ref = H.oracle_full(oracle, wl, 0, np.asarray(ctx, np.int32))["attn_out"]
     tight = tight_reference(oracle, wl, 0, np.asarray(ctx, np.int32))
-    for variant in ("regs", "lds"):
+    for variant in variants:
         assert_gates(H.bf16_to_f64(outs[variant]), ref, "%s %s" % (wl_name, variant))
         check_tight(outs32[variant].astype(np.float64), tight, "%s %s" % (wl_name, variant))
 
@@ -349,22 +378,27 @@ def test_lds_split_kernel_split_edges(oracle, monkeypatch):
 
 
 # --------------------------------------------------------------------------- comparators
-def test_comparators_are_bit_identical(oracle):
+@pytest.mark.parametrize("wl_name", ["llama3-8b-b8-ctx32768-host", "llama3-70b-b16-ctx131072-8layers-host"],
+                         ids=["g4", "g8"])
+def test_comparators_are_bit_identical(oracle, wl_name):
     """The naive zero-copy comparator (one work item per query head) and the
     staging comparator (copy-engine copy of the host pool into an HBM pool,
     then the step on the HBM copy) compute the same bits as the method."""
-    wl = configs.LLAMA8B_HOST.replace(batch=3)
+    wl = configs.BY_NAME[wl_name].replace(batch=3, n_layers=1)
     ctx = [700, 1030, 64]
     host = H.Setup(wl, ctx_lens=ctx, hbm_tail=0)
     zeros = lambda layer, b, t0, t1: (np.zeros((t1 - t0, wl.n_kv_heads, wl.head_dim), np.uint16),) * 2
     staged = H.Setup(wl, ctx_lens=ctx, hbm_tail=1 << 20, kv_writer=zeros)
     try:
         want = bits(host.run())
-        assert host.layout.split_kernel == "regs"
+        want32 = host.run(f32=True).cpu().numpy().view(np.uint32)
+        default = host.layout.split_kernel
+        assert default == "mfma"
         host.layout.split_kernel = "naive"
         assert host.layout.split_kernel == "naive"
         assert np.array_equal(bits(host.run()), want)
-        host.layout.split_kernel = "regs"
+        assert np.array_equal(host.run(f32=True).cpu().numpy().view(np.uint32), want32)
+        host.layout.split_kernel = default
         assert staged.n_host_pages == 0 and staged.n_hbm_pages == host.n_host_pages
         assert not np.array_equal(bits(staged.run()), want)      # zeros before staging
         H.dkv.kv_pool_copy(staged.hbm_pool, host.host_pool, host.host_pool.info()[1])
