@@ -57,7 +57,7 @@ __device__ __forceinline__ float reduce_scatter(float (&v)[N], int lane) {
     return r;
 }
 
-// 1a. Batches below 32: a GEMV on VALU. A workgroup owns 4 W rows and BT
+// 1a. Small batches: a GEMV on VALU. A workgroup owns 4 W rows and BT
 // sequences; its KS wavefronts split the hidden dimension into equal ranges,
 // and each lane reads 16-byte (8 x bf16) chunks, so every W row is read as
 // contiguous 1 KiB wave loads, all of a wave's loads issued before its
@@ -218,6 +218,72 @@ __global__ __launch_bounds__(64 * KS) void qkv_proj_mfma_kernel(StepArgs a, int 
     }
 }
 
+// 1c. One tile of up to 16 sequences: the same 16x16x32 MFMA tiles, but each
+// wavefront streams its 16 W rows over a k range of hidden / KSPLIT in
+// 256-wide chunks, the next chunk's W and x loads in flight while the
+// current chunk's 8 MFMAs run (register double buffer), so a few thousand
+// wavefronts keep W streaming from HBM for the whole launch instead of
+// issuing one burst each. The KSPLIT wavefronts of a workgroup share the 16
+// rows and add their partial tiles through LDS in wave order.
+template <int KSPLIT>
+__global__ __launch_bounds__(64 * KSPLIT) void qkv_proj_stream_kernel(StepArgs a) {
+    constexpr int KC = 256;             // k per chunk
+    constexpr int NK = KC / 32;         // MFMA k steps per chunk
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int row0 = blockIdx.x * 16;
+    const int krange = a.hidden / KSPLIT;      // a multiple of 256 (checked at launch)
+    const int nch = krange / KC;
+
+    if (blockIdx.x == 0 && wave == 0 && lane < a.batch) check_context_range(a, lane);
+
+    // Lanes of sequences past the batch load nothing and feed zeros; their
+    // columns are never stored.
+    const bool live = i < a.batch;
+    const uint16_t *wrow = a.w + (size_t)(row0 + i) * a.hidden + wave * krange + kq;
+    const uint16_t *xrow = a.x + (size_t)min(i, a.batch - 1) * a.hidden + wave * krange + kq;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    uint4 wa[NK], xa[NK], wb[NK], xb[NK];
+    auto load_x = [&](uint4 (&v)[NK], int k0) {
+        if (live) load_slice(v, xrow, k0);
+        else {
+#pragma unroll
+            for (int u = 0; u < NK; ++u) v[u] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    load_slice(wa, wrow, 0);
+    load_x(xa, 0);
+    for (int c = 0; c < nch; c += 2) {
+        if (c + 1 < nch) {
+            load_slice(wb, wrow, (c + 1) * KC);
+            load_x(xb, (c + 1) * KC);
+        }
+        mfma_slice(acc, wa, xa);
+        if (c + 1 < nch) {
+            if (c + 2 < nch) {
+                load_slice(wa, wrow, (c + 2) * KC);
+                load_x(xa, (c + 2) * KC);
+            }
+            mfma_slice(acc, wb, xb);
+        }
+    }
+
+    if constexpr (KSPLIT > 1) {
+        __shared__ f32x4 partial[KSPLIT - 1][64];
+        if (wave > 0) partial[wave - 1][lane] = acc;
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int w = 1; w < KSPLIT; ++w) acc += partial[w - 1][lane];
+    }
+    if (i < a.batch) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) store_projection(a, row0 + 4 * (lane >> 4) + r, i, acc[r]);
+    }
+}
+
 template <int KS>
 void launch_mfma(const StepArgs &a, int ch, hipStream_t st) {
     const int nbt = (a.batch + 15) / 16;
@@ -250,7 +316,17 @@ hipError_t launch_gemv(const StepArgs &a, hipStream_t st) {
 
 hipError_t launch_projection(const StepArgs &a, hipStream_t st) {
     if (a.hidden % 512 != 0 || a.n_qkv % 16 != 0) return hipErrorInvalidValue;
-    if (a.batch >= a.proj_mfma_min_batch) {
+    if (a.batch >= a.proj_mfma_min_batch && a.batch <= 16) {
+        // One sequence tile: streamed over k by up to 4 wavefronts per row block.
+        int ksplit = 4;
+        while (ksplit > 1 && a.hidden % (256 * ksplit) != 0) ksplit >>= 1;
+        const dim3 grid(a.n_qkv / 16);
+        switch (ksplit) {
+            case 1: qkv_proj_stream_kernel<1><<<grid, 64, 0, st>>>(a); break;
+            case 2: qkv_proj_stream_kernel<2><<<grid, 128, 0, st>>>(a); break;
+            default: qkv_proj_stream_kernel<4><<<grid, 256, 0, st>>>(a); break;
+        }
+    } else if (a.batch >= a.proj_mfma_min_batch) {
         // Up to 8 wavefronts per workgroup over the 512-wide k slices.
         const int n_slices = a.hidden / 512;
         int ks = 8;

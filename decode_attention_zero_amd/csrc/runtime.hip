@@ -233,13 +233,13 @@ int32_t choose_split_waves(int64_t host_pages, int64_t hbm_pages) {
     return t_looping < t_per_item ? kHostSplitWaves : 0;
 }
 
-// Batch size from which the QKV projection runs on the matrix cores (one
-// full 16-sequence MFMA tile and up); smaller batches take the VALU GEMV.
-// Measured on MI355X (W read once per step, x from L2): batch 16 at hidden
-// 8192, 57 us on MFMA vs 132 us on VALU; batch 32 at 4096, 29 vs 57 us;
-// batch 64, 46 vs 109 us; batch 8, 22 vs 25 us with half of every MFMA tile
-// empty. DKV_PROJ_MFMA_MIN_BATCH=<n> overrides it.
-constexpr int32_t kProjMfmaMinBatch = 16;
+// Batch size from which the QKV projection runs on the matrix cores; smaller
+// batches take the VALU GEMV. Measured on MI355X (W read once per step, x
+// from L2; hidden 4096 / 8192): batch 1, 12.5 / 28.8 us on VALU vs 14.8 /
+// 34.1 us on MFMA; batch 4, 14.4 vs 16.3 us; batch 8, 21.2 / 53.1 vs 17.5 /
+// 40.1 us; batch 16, 31.8 / 124 vs 20.1 / 48.6 us; batch 32 at 4096, 57 vs
+// 29 us; batch 64, 109 vs 46 us. DKV_PROJ_MFMA_MIN_BATCH=<n> overrides it.
+constexpr int32_t kProjMfmaMinBatch = 8;
 
 int32_t choose_proj_mfma_min_batch() {
     if (const char *env = getenv("DKV_PROJ_MFMA_MIN_BATCH")) {

@@ -158,14 +158,21 @@ def test_split_and_page_edges(oracle, monkeypatch, split):
 
 
 # --------------------------------------------------------------------------- exactness
-@pytest.mark.parametrize("batch", [3, 16, 17, 32, 40, 64])
-def test_projection_integer_exact(oracle, batch):
+@pytest.mark.parametrize("batch,mfma_from", [(3, None), (3, 1), (1, 1), (8, None), (16, None), (17, None),
+                                             (32, None), (40, None), (64, None)])
+def test_projection_integer_exact(oracle, monkeypatch, batch, mfma_from):
     """Small-integer x and W make every product and fp32 sum exact, so the
     written-back K/V must equal the oracle's fp64 values rounded to bf16, bit
     for bit; with an empty history attn_out is exactly bf16(v_new). Batches
-    below 16 take the VALU projection, 16 and up the MFMA one in 16-sequence
-    tiles (17 and 40: a partly filled last tile)."""
+    below 8 take the VALU projection by default (and the streamed one-tile
+    MFMA kernel with DKV_PROJ_MFMA_MIN_BATCH=1), 8 to 16 the one-tile MFMA
+    kernel, larger batches the MFMA one in 16-sequence tiles (17 and 40: a
+    partly filled last tile)."""
     import synth
+    if mfma_from is None:
+        monkeypatch.delenv("DKV_PROJ_MFMA_MIN_BATCH", raising=False)
+    else:
+        monkeypatch.setenv("DKV_PROJ_MFMA_MIN_BATCH", str(mfma_from))
     wl = configs.LLAMA8B_HOST.replace(batch=batch)
     ctx = np.array([[0, 5, 16][b % 3] for b in range(batch)], np.int32)
     xi = synth.int_bf16(99, 20, 0, wl.batch * wl.hidden, -4, 4).reshape(wl.batch, wl.hidden)
@@ -284,6 +291,38 @@ def test_placement_bit_identity(oracle):
             assert np.array_equal(slots[0][b][1], slots[i][b][1])
     ref = H.oracle_full(oracle, wl, 0, ctx)["attn_out"]
     assert_gates(H.bf16_to_f64(outs[0]), ref, "placements")
+
+
+@pytest.mark.parametrize("head_dim,n_q_heads,n_kv_heads", [
+    (64, 8, 4), (64, 16, 4), (64, 32, 4), (128, 8, 4), (128, 2, 2)],
+    ids=["d64-g2", "d64-g4", "d64-g8", "d128-g2", "d128-g1"])
+def test_every_head_dim_and_group(oracle, head_dim, n_q_heads, n_kv_heads):
+    """Every supported (head_dim, group) pair that the workloads do not use:
+    the oracle's gates with host and HBM pages mixed, identical bits across
+    placements, and the naive per-query-head comparator identical to the
+    grouped kernel."""
+    wl = configs.TINY.replace(batch=4, hidden=1024, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
+                              head_dim=head_dim)
+    ctx = np.array([0, 17, 300, 1100], np.int32)
+    outs32 = []
+    for tail in ([0, 40, 1 << 20, 200], 0, 1 << 20):
+        s = H.Setup(wl, ctx_lens=ctx, hbm_tail=tail)
+        try:
+            outs32.append(s.run(f32=True).cpu().numpy())
+            if len(outs32) == 1:
+                check_tight(outs32[0].astype(np.float64), tight_reference(oracle, wl, 0, ctx),
+                            "d%d g%d" % (head_dim, wl.group))
+                assert_gates(H.bf16_to_f64(bits(s.run())), H.oracle_full(oracle, wl, 0, ctx)["attn_out"],
+                             "d%d g%d" % (head_dim, wl.group))
+                default = s.layout.split_kernel
+                assert default == ("mfma" if wl.group >= 4 else "regs")
+                s.layout.split_kernel = "naive"
+                assert np.array_equal(s.run(f32=True).cpu().numpy().view(np.uint32), outs32[0].view(np.uint32))
+                s.layout.split_kernel = default
+        finally:
+            s.free()
+    for o in outs32[1:]:
+        assert np.array_equal(o.view(np.uint32), outs32[0].view(np.uint32))
 
 
 def test_repeat_runs_are_bitwise_identical():
