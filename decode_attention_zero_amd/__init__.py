@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
             "kv_layout_timing_read": ([P, P, P, P, P], I32),
             "dkv_cpu_attention": ([P, I32, P, P, P, P, P, I32, P], I32),
             "dkv_cpu_stream_read": ([P, ctypes.c_uint64, I32, P], I32),
+            "dkv_cpu_attention_pages": ([P, I32, SP, I32, P, P, P, P, P, I32, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -114,7 +115,7 @@ EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement",
             "kv_layout_split_kernel", "kv_layout_set_split_kernel", "kv_layout_split_waves", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
             "dkv_probe_stream_read", "kv_pool_copy", "dkv_host_buffer_alloc", "dkv_host_buffer_free",
             "dkv_copy", "dkv_gemm_bf16_nt", "kv_layout_timing_enable", "kv_layout_timing_read",
-            "dkv_cpu_attention", "dkv_cpu_stream_read"]
+            "dkv_cpu_attention", "dkv_cpu_stream_read", "dkv_cpu_attention_pages"]
 
 
 def _check(status: int) -> None:
@@ -428,6 +429,34 @@ def cpu_attention(layout: "Layout", layer: int, q: np.ndarray, k_new: np.ndarray
     used = ctypes.c_int32()
     _check(lib().dkv_cpu_attention(layout.handle, layer, _np_ptr(q), _np_ptr(k_new), _np_ptr(v_new),
                                    _np_ptr(ctx), _np_ptr(out), n_threads, ctypes.byref(used)))
+    return out, used.value
+
+
+def cpu_attention_pages(shape: Shape, pages: list, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+                        ctx_lens: np.ndarray, n_threads: int) -> tuple[np.ndarray, int]:
+    """The host-CPU attention on plain host pages, no GPU: pages[b] is a list
+    of C-contiguous uint16 numpy arrays of kv_page_bytes(shape) bytes each
+    (sequence b's pages in order). Returns (out [B][Hq][d] fp32, threads used)."""
+    B = len(pages)
+    max_pages = max(1, max(len(p) for p in pages))
+    table = (ctypes.c_void_p * (B * max_pages))()
+    for b, row in enumerate(pages):
+        for i, page in enumerate(row):
+            if page.nbytes != kv_page_bytes(shape):
+                raise ValueError("page of the wrong size")
+            table[b * max_pages + i] = _np_ptr(page)
+    q = np.ascontiguousarray(q, np.float32)
+    k_new = np.ascontiguousarray(k_new, np.uint16)
+    v_new = np.ascontiguousarray(v_new, np.uint16)
+    ctx = np.ascontiguousarray(ctx_lens, np.int32)
+    if q.shape != (B, shape.n_q_heads, shape.head_dim) or k_new.shape != (B, shape.n_kv_heads, shape.head_dim) \
+            or v_new.shape != k_new.shape or ctx.shape != (B,):
+        raise ValueError("cpu_attention_pages: shapes must be q [B][Hq][d], k_new/v_new [B][Hkv][d], ctx_lens [B]")
+    out = np.empty_like(q)
+    used = ctypes.c_int32()
+    _check(lib().dkv_cpu_attention_pages(table, max_pages, ctypes.byref(shape), B, _np_ptr(q), _np_ptr(k_new),
+                                         _np_ptr(v_new), _np_ptr(ctx), _np_ptr(out), n_threads,
+                                         ctypes.byref(used)))
     return out, used.value
 
 

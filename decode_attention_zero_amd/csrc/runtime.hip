@@ -838,13 +838,35 @@ dkv_status dkv_cpu_attention(const dkv_layout *L, int32_t layer, const float *q,
             pages[(size_t)b * L->max_pages + p] = page;
         }
     }
+    return dkv_cpu_attention_pages(reinterpret_cast<const void *const *>(pages.data()), L->max_pages, &L->shape, B,
+                                   q, k_new, v_new, ctx_lens, out, n_threads, threads_used);
+}
+
+dkv_status dkv_cpu_attention_pages(const void *const *pages, int32_t max_pages, const dkv_shape *shape,
+                                   int32_t batch, const float *q, const uint16_t *k_new, const uint16_t *v_new,
+                                   const int32_t *ctx_lens, float *out, int32_t n_threads, int32_t *threads_used) {
+    if (!shape_ok(shape) || !shape_supported(shape))
+        return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention_pages: invalid or unsupported shape");
+    if (!pages || !q || !k_new || !v_new || !ctx_lens || !out || batch < 1 || max_pages < 1)
+        return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention_pages: null pointer, batch or max_pages");
+    if (n_threads < 1 || n_threads > 1024)
+        return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention_pages: n_threads %d outside [1, 1024]", n_threads);
+    for (int b = 0; b < batch; ++b) {
+        const int n = (ctx_lens[b] + DKV_PAGE_TOKENS - 1) / DKV_PAGE_TOKENS;
+        if (ctx_lens[b] < 0 || n > max_pages)
+            return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention_pages: ctx_lens[%d] = %d does not fit %d pages", b,
+                        ctx_lens[b], max_pages);
+        for (int p = 0; p < n; ++p)
+            if (!pages[(size_t)b * max_pages + p])
+                return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention_pages: page %d of sequence %d is missing", p, b);
+    }
     dkv::CpuAttentionJob job{};
-    job.batch = B;
-    job.n_q_heads = L->shape.n_q_heads;
-    job.n_kv_heads = L->shape.n_kv_heads;
-    job.head_dim = L->shape.head_dim;
-    job.max_pages = L->max_pages;
-    job.pages = pages.data();
+    job.batch = batch;
+    job.n_q_heads = shape->n_q_heads;
+    job.n_kv_heads = shape->n_kv_heads;
+    job.head_dim = shape->head_dim;
+    job.max_pages = max_pages;
+    job.pages = reinterpret_cast<const char *const *>(pages);
     job.ctx_lens = ctx_lens;
     job.q = q;
     job.k_new = k_new;

@@ -119,6 +119,17 @@ dkv_status dkv_cpu_attention(const dkv_layout *layout, int32_t layer, const floa
                              const uint16_t *k_new, const uint16_t *v_new, const int32_t *ctx_lens,
                              float *out, int32_t n_threads, int32_t *threads_used);
 
+/* The same computation on plain host page pointers, no GPU needed:
+ * pages[b * max_pages + p] is the CPU address of page p of sequence b in the
+ * page layout above (NULL allowed past the cached tokens), every other
+ * argument as in dkv_cpu_attention; `batch` sequences of `shape` (its
+ * n_layers is ignored). Errors: DKV_E_INVALID_ARG (null pointer, bad shape,
+ * thread count, or a missing page among the cached tokens). */
+dkv_status dkv_cpu_attention_pages(const void *const *pages, int32_t max_pages, const dkv_shape *shape,
+                                   int32_t batch, const float *q, const uint16_t *k_new,
+                                   const uint16_t *v_new, const int32_t *ctx_lens, float *out,
+                                   int32_t n_threads, int32_t *threads_used);
+
 /* Reads `bytes` bytes (a multiple of 64) of host memory at `host_ptr` on
  * n_threads host threads as 64-bit words and returns their wrapping sum in
  * *checksum (may be NULL): the host-DRAM streaming-read rate, timed by the
