@@ -7,8 +7,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <thread>
+#include <unordered_set>
 #include <vector>
 
 #include "cpu_attention.h"
@@ -18,6 +20,28 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Handles (pools and layouts) that are alive. The free calls and the calls
+// that use a handle check it here, so a double free or a call on a freed
+// handle fails with DKV_E_INVALID_ARG instead of touching freed memory
+// (unless a newer handle has taken the same address).
+std::mutex g_handles_mu;
+std::unordered_set<const void *> g_handles;
+
+void track(const void *h) {
+    std::lock_guard<std::mutex> lock(g_handles_mu);
+    g_handles.insert(h);
+}
+
+bool untrack(const void *h) {
+    std::lock_guard<std::mutex> lock(g_handles_mu);
+    return g_handles.erase(h) == 1;
+}
+
+bool live(const void *h) {
+    std::lock_guard<std::mutex> lock(g_handles_mu);
+    return g_handles.count(h) == 1;
+}
 
 dkv_status fail(dkv_status st, const char *fmt, ...) {
     char buf[512];
@@ -347,6 +371,7 @@ dkv_status kv_alloc_host(const dkv_shape *shape, int64_t n_pages, uint32_t flags
     p->n_free = n_pages;
     p->scan = 0;
     p->n_layouts = 0;
+    track(p);
     *out = p;
     return DKV_OK;
 }
@@ -374,18 +399,19 @@ dkv_status kv_alloc_hbm(const dkv_shape *shape, int64_t n_pages, dkv_pool **out)
     p->n_free = n_pages;
     p->scan = 0;
     p->n_layouts = 0;
+    track(p);
     *out = p;
     return DKV_OK;
 }
 
 dkv_status kv_pool_free_pages(const dkv_pool *pool, int64_t *n_free) {
-    if (!pool || !n_free) return fail(DKV_E_INVALID_ARG, "kv_pool_free_pages: null argument");
+    if (!pool || !n_free || !live(pool)) return fail(DKV_E_INVALID_ARG, "kv_pool_free_pages: null or freed pool");
     *n_free = pool->n_free;
     return DKV_OK;
 }
 
 dkv_status kv_pool_info(const dkv_pool *pool, void **device_base, int64_t *bytes, int32_t *tier) {
-    if (!pool) return fail(DKV_E_INVALID_ARG, "kv_pool_info: null pool");
+    if (!pool || !live(pool)) return fail(DKV_E_INVALID_ARG, "kv_pool_info: null or freed pool");
     if (device_base) *device_base = pool->dev_base;
     if (bytes) *bytes = pool->n_pages * pool->page_bytes;
     if (tier) *tier = pool->tier;
@@ -394,9 +420,11 @@ dkv_status kv_pool_info(const dkv_pool *pool, void **device_base, int64_t *bytes
 
 dkv_status kv_pool_free(dkv_pool *pool) {
     if (!pool) return DKV_OK;
+    if (!live(pool)) return fail(DKV_E_INVALID_ARG, "kv_pool_free: not a live pool (freed twice?)");
     if (pool->n_layouts > 0)
         return fail(DKV_E_INVALID_ARG, "kv_pool_free: %lld layout(s) still use this pool",
                     (long long)pool->n_layouts);
+    untrack(pool);
     hipError_t e = pool->tier == 0 ? hipHostFree(pool->host_base) : hipFree(pool->dev_base);
     delete pool;
     if (e != hipSuccess) return hip_fail(e, "kv_pool_free");
@@ -411,6 +439,7 @@ static dkv_status check_pools(const dkv_shape *shape, int32_t batch, const int32
         return fail(DKV_E_UNSUPPORTED, "%s: head_dim must be 64/128, group 1/2/4/8, hidden a multiple of 512", who);
     if (batch > 65535) return fail(DKV_E_INVALID_ARG, "%s: batch > 65535", who);
     for (dkv_pool *p : {host_pool, hbm_pool}) {
+        if (p && !live(p)) return fail(DKV_E_INVALID_ARG, "%s: a pool argument is not a live pool", who);
         if (p && (p->shape.n_kv_heads != shape->n_kv_heads || p->shape.head_dim != shape->head_dim))
             return fail(DKV_E_INVALID_ARG, "%s: pool page shape differs from the layout's", who);
     }
@@ -498,6 +527,7 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
         hip_fail(e, "kv_layout_create: initialising device tables");
         return cleanup(DKV_E_HIP);
     }
+    track(L);
     *out = L;
     return DKV_OK;
 }
@@ -674,6 +704,7 @@ dkv_status kv_layout_timing_read(dkv_layout *L, double *ms_proj, double *ms_spli
 
 dkv_status kv_layout_free(dkv_layout *L) {
     if (!L) return DKV_OK;
+    if (!untrack(L)) return fail(DKV_E_INVALID_ARG, "kv_layout_free: not a live layout (freed twice?)");
     (void)hipDeviceSynchronize();
     for (hipEvent_t e : L->timing_events) (void)hipEventDestroy(e);
     free_device(L);
@@ -710,7 +741,7 @@ dkv_status kv_layout_set_split_kernel(dkv_layout *L, int32_t kernel) {
 
 static dkv_status check_range(const dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n,
                               const char *who) {
-    if (!L) return fail(DKV_E_INVALID_ARG, "%s: null layout", who);
+    if (!L || !live(L)) return fail(DKV_E_INVALID_ARG, "%s: null or freed layout", who);
     if (layer < 0 || layer >= L->shape.n_layers || seq < 0 || seq >= L->batch || start < 0 || n < 0)
         return fail(DKV_E_INVALID_ARG, "%s: layer/seq/start/n out of range", who);
     if ((int64_t)start + n > L->capacity[seq])
@@ -810,7 +841,7 @@ dkv_status kv_read(const dkv_layout *L, int32_t layer, int32_t seq, int32_t star
 dkv_status dkv_cpu_attention(const dkv_layout *L, int32_t layer, const float *q, const uint16_t *k_new,
                              const uint16_t *v_new, const int32_t *ctx_lens, float *out, int32_t n_threads,
                              int32_t *threads_used) {
-    if (!L) return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention: null layout");
+    if (!L || !live(L)) return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention: null or freed layout");
     if (layer < 0 || layer >= L->shape.n_layers)
         return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention: layer %d out of range", layer);
     if (!q || !k_new || !v_new || !ctx_lens || !out)
@@ -890,7 +921,7 @@ dkv_status dkv_cpu_stream_read(const void *host_ptr, uint64_t bytes, int32_t n_t
 static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, const uint16_t *W,
                             const int32_t *ctx_lens, void *out, int out_f32, dkv_stream_t stream,
                             const char *who) {
-    if (!L) return fail(DKV_E_INVALID_ARG, "%s: null layout", who);
+    if (!L || !live(L)) return fail(DKV_E_INVALID_ARG, "%s: null or freed layout", who);
     if (layer < 0 || layer >= L->shape.n_layers) return fail(DKV_E_INVALID_ARG, "%s: layer %d out of range", who, layer);
     if (!q_in || !W || !ctx_lens || !out) return fail(DKV_E_INVALID_ARG, "%s: null pointer argument", who);
     if (((uintptr_t)q_in | (uintptr_t)W) & 15u)
@@ -943,7 +974,7 @@ dkv_status decode_step_f32(dkv_layout *L, int32_t layer, const uint16_t *q_in, c
 }
 
 dkv_status kv_advance(dkv_layout *L, int32_t *ctx_lens, dkv_stream_t stream) {
-    if (!L || !ctx_lens) return fail(DKV_E_INVALID_ARG, "kv_advance: null argument");
+    if (!L || !ctx_lens || !live(L)) return fail(DKV_E_INVALID_ARG, "kv_advance: null argument or freed layout");
     if ((uintptr_t)ctx_lens & 3u) return fail(DKV_E_INVALID_ARG, "kv_advance: misaligned ctx_lens");
     dkv::AdvanceArgs a{};
     a.batch = L->batch;
@@ -965,7 +996,7 @@ dkv_status kv_advance(dkv_layout *L, int32_t *ctx_lens, dkv_stream_t stream) {
 }
 
 dkv_status kv_layout_check_status(dkv_layout *L) {
-    if (!L) return fail(DKV_E_INVALID_ARG, "kv_layout_check_status: null layout");
+    if (!L || !live(L)) return fail(DKV_E_INVALID_ARG, "kv_layout_check_status: null or freed layout");
     HIP_TRY(hipDeviceSynchronize());
     uint32_t flag = 0;
     HIP_TRY(hipMemcpy(&flag, L->d_status, sizeof flag, hipMemcpyDeviceToHost));
@@ -976,7 +1007,7 @@ dkv_status kv_layout_check_status(dkv_layout *L) {
 }
 
 dkv_status kv_pool_copy(dkv_pool *dst, const dkv_pool *src, int64_t bytes, dkv_stream_t stream) {
-    if (!dst || !src || bytes < 0 || dst->page_bytes != src->page_bytes ||
+    if (!dst || !src || !live(dst) || !live(src) || bytes < 0 || dst->page_bytes != src->page_bytes ||
         bytes > dst->n_pages * dst->page_bytes || bytes > src->n_pages * src->page_bytes)
         return fail(DKV_E_INVALID_ARG, "kv_pool_copy: null pool, page sizes differ or bytes out of range");
     if (bytes == 0) return DKV_OK;

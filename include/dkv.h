@@ -124,7 +124,8 @@ dkv_status kv_pool_free_pages(const dkv_pool *pool, int64_t *n_free);
 
 /* Frees the pool's memory. The caller must first free every layout that
  * borrows pages from it (DKV_E_INVALID_ARG otherwise, and nothing is freed).
- * NULL is accepted and ignored. */
+ * NULL is accepted and ignored; a pool freed already (or never returned by
+ * kv_alloc_*) gives DKV_E_INVALID_ARG, as does any call that is handed one. */
 dkv_status kv_pool_free(dkv_pool *pool);
 
 /* ---------------------------------------------------------------------------
@@ -170,7 +171,9 @@ dkv_status kv_layout_create_windowed(const dkv_shape *shape, int32_t batch,
                                      dkv_layout **out);
 
 /* Returns the layout's pages to their pools and frees its device memory.
- * Synchronises the device first. NULL is accepted and ignored. */
+ * Synchronises the device first. NULL is accepted and ignored; a layout freed
+ * already (or never returned by kv_layout_create*) gives DKV_E_INVALID_ARG,
+ * as does any call that is handed one. */
 dkv_status kv_layout_free(dkv_layout *layout);
 
 /* Tier of page `page` of sequence `seq` (same in every layer) as the page

@@ -1,0 +1,117 @@
+"""Error paths of the C ABI that need a device: every one returns a status
+and a message before anything is enqueued, and leaves the library usable.
+
+Covered: double free of pools and layouts, calls on a freed layout or pool,
+a pool freed while a layout still holds its pages, null and misaligned
+pointers handed to decode_step, an HBM pool larger than HBM, unsupported
+shapes and bad capacities at layout creation. (A host pool larger than host
+memory is not exercised: pinning is not guaranteed to fail before it has
+touched memory.)"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import decode_attention_zero_amd as dkv
+from tests.conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
+
+E_INVALID_ARG, E_OUT_OF_MEMORY, E_UNSUPPORTED = -1, -2, -5
+
+
+def small_layout():
+    shape = dkv.Shape.of(512, 8, 4, 64, 1)
+    host = dkv.kv_alloc_host(shape, 4)
+    layout = dkv.kv_layout_create(shape, np.array([20, 30], np.int32), None, host, None)
+    return shape, host, layout
+
+
+def test_double_free_and_use_after_free_are_refused():
+    L = dkv.lib()
+    shape, host, layout = small_layout()
+    h_layout, h_pool = layout.handle, host.handle
+    assert L.kv_pool_free(h_pool) == E_INVALID_ARG          # a layout still holds its pages
+    assert "still use" in L.dkv_last_error().decode()
+    layout.free()
+    assert L.kv_layout_free(h_layout) == E_INVALID_ARG      # freed twice
+    assert L.kv_layout_check_status(h_layout) == E_INVALID_ARG
+    ctx = np.zeros(2, np.int32)
+    assert L.kv_advance(h_layout, ctx.ctypes.data, None) == E_INVALID_ARG
+    k = np.zeros((1, 4, 64), np.uint16)
+    assert L.kv_append(h_layout, 0, 0, 0, 1, k.ctypes.data, k.ctypes.data, None) == E_INVALID_ARG
+    host.free()
+    assert L.kv_pool_free(h_pool) == E_INVALID_ARG          # freed twice
+    n = ctypes.c_int64()
+    assert L.kv_pool_free_pages(h_pool, ctypes.byref(n)) == E_INVALID_ARG
+    out = ctypes.c_void_p()
+    assert L.kv_layout_create(ctypes.byref(shape), 1, np.array([4], np.int32).ctypes.data, None, h_pool, None,
+                              ctypes.byref(out)) == E_INVALID_ARG
+    assert L.kv_pool_free(None) == 0 and L.kv_layout_free(None) == 0
+    # the library still works
+    shape, host, layout = small_layout()
+    layout.free()
+    host.free()
+
+
+def test_decode_step_rejects_null_and_misaligned_pointers():
+    import torch
+    L = dkv.lib()
+    shape, host, layout = small_layout()
+    try:
+        dev = torch.device("cuda", 0)
+        x = torch.zeros((2, 512 + 8), dtype=torch.bfloat16, device=dev)
+        W = torch.zeros((8 * 64 + 2 * 4 * 64, 512), dtype=torch.bfloat16, device=dev)
+        ctx = torch.tensor([3, 5], dtype=torch.int32, device=dev)
+        raw = torch.zeros(64, dtype=torch.uint8, device=dev)
+        out = torch.empty((2, 8 * 64), dtype=torch.bfloat16, device=dev)
+        step = L.decode_step
+        ok = (layout.handle, 0, x.data_ptr(), W.data_ptr(), ctx.data_ptr(), out.data_ptr(), None)
+        for i in (2, 3, 4, 5):
+            args = list(ok)
+            args[i] = None
+            assert step(*args) == E_INVALID_ARG, i
+        bad = [list(ok) for _ in range(3)]
+        bad[0][2] = x.data_ptr() + 2                       # q_in off 16-byte alignment
+        bad[1][4] = raw.data_ptr() + 1                     # ctx_lens off 4-byte alignment
+        bad[2][5] = out.data_ptr() + 1                     # attn_out off 2-byte alignment
+        for args in bad:
+            assert step(*args) == E_INVALID_ARG
+            assert "align" in L.dkv_last_error().decode()
+        assert step(*ok) == 0                              # the valid call still runs
+        torch.cuda.synchronize()
+        layout.check_status()
+    finally:
+        layout.free()
+        host.free()
+
+
+def test_hbm_pool_larger_than_hbm_is_out_of_memory():
+    L = dkv.lib()
+    shape = dkv.Shape.of(4096, 32, 8, 128, 1)            # 64 KiB pages
+    out = ctypes.c_void_p()
+    assert L.kv_alloc_hbm(ctypes.byref(shape), 1 << 24, ctypes.byref(out)) == E_OUT_OF_MEMORY   # 1 TiB
+    assert out.value is None
+    pool = dkv.kv_alloc_hbm(shape, 2)                     # and a normal allocation still works
+    pool.free()
+
+
+def test_layout_creation_errors():
+    L = dkv.lib()
+    shape = dkv.Shape.of(512, 8, 4, 64, 1)
+    host = dkv.kv_alloc_host(shape, 2)
+    try:
+        out = ctypes.c_void_p()
+        cap = np.array([40], np.int32)                    # 3 pages, the pool has 2
+        assert L.kv_layout_create(ctypes.byref(shape), 1, cap.ctypes.data, None, host.handle, None,
+                                  ctypes.byref(out)) != 0
+        assert out.value is None and host.free_pages() == 2
+        cap0 = np.array([0], np.int32)
+        assert L.kv_layout_create(ctypes.byref(shape), 1, cap0.ctypes.data, None, host.handle, None,
+                                  ctypes.byref(out)) == E_INVALID_ARG
+        odd = dkv.Shape.of(512, 12, 4, 64, 1)             # group of 3
+        assert L.kv_layout_create(ctypes.byref(odd), 1, np.array([4], np.int32).ctypes.data, None, None,
+                                  None, ctypes.byref(out)) == E_UNSUPPORTED
+    finally:
+        host.free()
