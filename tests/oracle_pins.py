@@ -7,6 +7,8 @@ must fail at least one). The facts:
 
 * library routines: numpy's fp64 matmul for the projection, torch's fp64
   ``scaled_dot_product_attention`` (grouped heads, one query) for attention;
+* a second implementation: attention in plain Python loops with math.exp
+  and math.fsum on tiny shapes;
 * closed forms: a one-token context returns its V exactly; equal scores return
   the mean of V; adding a constant to every score changes nothing; the output
   is affine in V; a dominant planted key returns its V; hand-derived softmax
@@ -129,6 +131,29 @@ def pin_attention_matches_torch_sdpa(o):
         ref = _sdpa_ref(q[None], _decode(K)[:, None, :], _decode(V)[:, None, :], kn[None],
                         vn[None], 1, 1)[0]
         assert _rel(got, ref) < 1e-12, (L, d, _rel(got, ref))
+
+
+def pin_attention_brute_force_fsum(o):
+    """A second, independent fp64 implementation on tiny shapes: plain Python
+    loops, math.exp and math.fsum (exactly rounded sums), softmax written out
+    with its max subtracted."""
+    rng = np.random.default_rng(RNG_SEED + 13)
+    for L, d in [(1, 3), (4, 5), (9, 8)]:
+        q = [float(v) for v in rng.standard_normal(d)]
+        K = _rand_bf16(rng, (L, d))
+        V = _rand_bf16(rng, (L, d))
+        kn = [float(v) for v in rng.standard_normal(d)]
+        vn = [float(v) for v in rng.standard_normal(d)]
+        keys = [[float(x) for x in row] for row in _decode(K)] + [kn]
+        vals = [[float(x) for x in row] for row in _decode(V)] + [vn]
+        scale = 1.0 / math.sqrt(d)
+        scores = [math.fsum(q[i] * k[i] for i in range(d)) * scale for k in keys]
+        top = max(scores)
+        w = [math.exp(sc - top) for sc in scores]
+        total = math.fsum(w)
+        ref = [math.fsum(w[j] * vals[j][i] for j in range(L + 1)) / total for i in range(d)]
+        got = o.attention_head(np.array(q), K, V, np.array(kn), np.array(vn))
+        assert _rel(got, ref) < 1e-13, (L, d, _rel(got, ref))
 
 
 def pin_one_token_context_returns_v(o):
