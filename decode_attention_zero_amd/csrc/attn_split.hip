@@ -4,7 +4,9 @@
 // HBM, chosen only by the page's address -- and keeps an online-softmax state
 // for the G query heads that share the KV head, so each remote byte is read
 // once for all of them. Writes an unnormalised partial (m, l, o) per query
-// head and split.
+// head and split. Two arithmetic forms share the page streaming: VALU with
+// DPP row sums (SplitState; groups of 1 and 2, and on request) and the
+// matrix cores (MfmaState; the default from groups of 4).
 //
 // Method (pages): "长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）" (DirectKV
 // digest), 核心方法: the attention kernel reads CPU-resident KV directly, with a
@@ -17,7 +19,7 @@
 namespace dkv {
 namespace {
 
-// Split attention. Work item (s, g, b) = blockIdx (x, y, z); one wavefront.
+// VALU split attention. Work item (s, g, b) = blockIdx (x, y, z).
 //
 // Lane mapping inside a page run (K tile then V tile, each [16 tok][D] bf16):
 // wave load j reads bytes [j*1024, (j+1)*1024) of a tile, lane l the 16 bytes
@@ -35,7 +37,8 @@ namespace {
 // = 2: wave 0 takes tokens 0-7 of every page, wave 1 tokens 8-15), so every
 // byte is still read once; their softmax states are merged through LDS at
 // the end of the item, in a fixed order. Used for groups of 8 query heads,
-// whose single-wave state would need 367 registers (one wave per SIMD).
+// whose single-wave state would need 367 registers (one wave per SIMD); even
+// so that form spills, which is why groups of 8 run on the matrix cores.
 template <int D, int G, int WPI = 1>
 struct SplitState {
     static constexpr int LPT = D / 8;               // lanes per token

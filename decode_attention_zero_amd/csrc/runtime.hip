@@ -215,12 +215,15 @@ int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, int32_t max_cap) 
     return t;
 }
 
-// Split-attention kernel variant. The register double buffer is the default
-// for every group size: on MI355X it measured faster than the LDS
+// Split-attention kernel variant. Every default streams pages through a
+// register double buffer, which measured faster on MI355X than the LDS
 // producer/consumer ring in the all-HBM placement (1 GiB of KV at group 4:
 // 189 us vs 258 us; group 8: 18.8 ms vs 27.6 ms for 64 GiB) and the same on
-// the host link. DKV_SPLIT_KERNEL=regs|lds overrides it; DKV_SPLIT_KERNEL=naive
-// selects the naive zero-copy comparator (one work item per query head).
+// the host link. From groups of 4 the group's products run on the matrix
+// cores (all-HBM, 1 GiB at group 4: 161 us vs 174 us on VALU; 8 GiB layers
+// at group 8: 1.41 ms vs 2.0 ms); smaller groups keep the VALU form.
+// DKV_SPLIT_KERNEL=regs|lds|mfma overrides it; DKV_SPLIT_KERNEL=naive selects
+// the naive zero-copy comparator (one work item per query head).
 int32_t choose_split_variant(int32_t group) {
     if (const char *env = getenv("DKV_SPLIT_KERNEL")) {
         if (!strcmp(env, "lds")) return dkv::kSplitLds;
