@@ -184,19 +184,30 @@ HBM_PROBES = [(1024, -2), (2048, -2), (4096, -4), (8192, -8), (2048, 4)]
 SPLIT_KERNEL_SOURCES = ("attn_split.hip", "device_common.h")
 
 
+def code_tokens(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed (the sources
+    hashed here hold no string literal with a comment marker)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def split_kernel_sha256() -> str:
-    """sha256 over what the split-attention kernel is compiled from: its own
-    source, the device helpers, and the StepArgs struct it reads."""
+    """sha256 over the code the split-attention kernel is compiled from: its
+    own source, the device helpers, and the StepArgs struct it reads, with
+    comments and whitespace left out (so editing a comment keeps the counter
+    records valid; any code change invalidates them)."""
     import hashlib
     csrc = os.path.join(ROOT, "decode_attention_zero_amd", "csrc")
     h = hashlib.sha256()
     for name in SPLIT_KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
-    with open(os.path.join(csrc, "dkv_internal.h")) as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(code_tokens(f.read()).encode())
+    with open(os.path.join(csrc, "dkv_internal.h"), encoding="utf-8") as f:
         text = f.read()
     i = text.index("struct StepArgs {")
-    h.update(text[i:text.index("};", i)].encode())
+    h.update(code_tokens(text[i:text.index("};", i)]).encode())
     return h.hexdigest()
 
 
