@@ -213,14 +213,19 @@ dkv_status kv_read(const dkv_layout *layout, int32_t layer, int32_t seq,
  *             slot ctx_lens[b] of the sequence's pages (host or HBM)
  *   attn_out[b][h*d : (h+1)*d] = softmax((q_h . K_j) / sqrt(d)) . V_j over
  *             the ctx_lens[b] cached tokens and the fresh one, with
- *             KV head g = h / (Hq/Hkv); rounded to bf16 (nearest even).
+ *             KV head g = h / (Hq/Hkv); fp32 softmax state and sums, rounded
+ *             to bf16 (nearest even). From groups of 4 query heads the
+ *             group's score and output products run on the matrix cores,
+ *             which take q and the probabilities as two bf16 terms each
+ *             (x ~ bf16(x) + bf16(x - bf16(x)), ~2^-17 relative).
  * Arguments (all device pointers, caller-owned, never retained):
- *   q_in     [batch][hidden] bf16 hidden states of this layer
+ *   q_in     [batch][hidden] bf16 hidden states of this layer (16-byte aligned)
  *   W_qkv    [(Hq + 2 Hkv) * d][hidden] bf16, row-major, rows ordered
  *            [Q heads | K heads | V heads], each head's d rows contiguous
+ *            (16-byte aligned)
  *   ctx_lens [batch] int32: cached tokens per sequence before this step
- *            (0 allowed). Not modified; the caller advances it.
- *   attn_out [batch][Hq * d] bf16
+ *            (0 allowed; 4-byte aligned). Not modified; the caller advances it.
+ *   attn_out [batch][Hq * d] bf16 (2-byte aligned)
  * The call enqueues kernels on `stream` and returns; it allocates nothing,
  * copies nothing and does not synchronise, so it can be captured in a HIP
  * graph (the stable-address property the KV-hierarchy overview, 2.1, says
