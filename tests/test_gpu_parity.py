@@ -336,6 +336,35 @@ def test_repeat_runs_are_bitwise_identical():
         s.free()
 
 
+def test_layouts_on_concurrent_streams():
+    """Two layouts (group 4 with host pages, group 8 all in HBM) stepped on two
+    streams at once, several steps interleaved: each keeps its own page
+    tables and scratch, so every output equals the same layout's output on
+    one stream, bit for bit."""
+    import torch
+    s4 = H.Setup(configs.LLAMA8B_HOST.replace(batch=3), ctx_lens=[700, 1030, 64], hbm_tail=0)
+    s8 = H.Setup(configs.LLAMA70B_LONG.replace(batch=2, n_layers=1), ctx_lens=[2000, 333], hbm_tail=1 << 20)
+    try:
+        want4 = s4.run(f32=True).cpu().numpy().view(np.uint32)
+        want8 = s8.run(f32=True).cpu().numpy().view(np.uint32)
+        a, b = torch.cuda.Stream(), torch.cuda.Stream()
+        outs4 = [torch.empty_like(torch.from_numpy(want4.view(np.float32))).cuda() for _ in range(3)]
+        outs8 = [torch.empty_like(torch.from_numpy(want8.view(np.float32))).cuda() for _ in range(3)]
+        torch.cuda.synchronize()
+        for i in range(3):
+            H.dkv.decode_step_f32(s4.layout, 0, s4.x[0], s4.W[0], s4.ctx_dev, outs4[i], a)
+            H.dkv.decode_step_f32(s8.layout, 0, s8.x[0], s8.W[0], s8.ctx_dev, outs8[i], b)
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert np.array_equal(outs4[i].cpu().numpy().view(np.uint32), want4), i
+            assert np.array_equal(outs8[i].cpu().numpy().view(np.uint32), want8), i
+        s4.layout.check_status()
+        s8.layout.check_status()
+    finally:
+        s4.free()
+        s8.free()
+
+
 def test_out_of_range_context_is_flagged():
     import torch
     wl = configs.LLAMA8B_HOST.replace(batch=2)
