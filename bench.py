@@ -97,19 +97,23 @@ class Resident:
                                  self.out[layer], self.stream)
 
     def timed(self, steps, warmup):
-        """Milliseconds per step over `steps` steps (HIP events on the step's stream)."""
+        """Milliseconds per step over `steps` steps (HIP events on the step's
+        stream around the whole run); per-step median / min / max from an
+        event between consecutive steps are kept in self.step_stats."""
         import torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(self.stream)
-        for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(self.stream)
+        for i in range(steps):
             self.step()
-        e1.record(self.stream)
+            ev[i + 1].record(self.stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        self.step_stats = {"median": round(float(np.median(per)), 4), "min": round(per[0], 4),
+                           "max": round(per[-1], 4)}
+        return ev[0].elapsed_time(ev[steps]) / steps
 
     def graph_timed(self, steps):
         """Milliseconds per step with one step (every layer) captured in a HIP
@@ -345,6 +349,31 @@ def gemm_experiment(dkv, args):
 
 SWEEP_HOST_FRACTIONS = (0.0, 0.01, 0.03, 0.1, 0.25, 0.5, 0.75, 1.0)
 SWEEP_CTX_LENGTHS = [1024, 4096, 16384, 32768, 65536, 131072]
+
+
+def host_facts() -> dict:
+    """Host logistics of the run: CPU, memory, the GPU's NUMA node, IOMMU."""
+    facts = {"cpu_model": cpu_model(), "nproc": os.cpu_count()}
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    facts["mem_total_GiB"] = round(int(line.split()[1]) / 2**20, 1)
+    except OSError:
+        pass
+    try:
+        import torch
+        p = torch.cuda.get_device_properties(0)
+        bus = "%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+        with open("/sys/bus/pci/devices/%s/numa_node" % bus) as f:
+            facts["gpu_numa_node"] = int(f.read().strip())
+    except Exception:          # not every container exposes sysfs
+        facts["gpu_numa_node"] = None
+    try:
+        facts["iommu_groups"] = len(os.listdir("/sys/kernel/iommu_groups"))
+    except OSError:
+        facts["iommu_groups"] = None
+    return facts
 
 
 def split_kernel_label(layout) -> str:
@@ -598,6 +627,7 @@ def main(argv=None):
     host_kv = host_kv_layer * wl.n_layers
     hbm_kv = kv_bytes - host_kv
     ms = r.timed(args.steps, args.warmup)
+    step_stats = r.step_stats
     kt = r.kernel_times(args.steps)
     if args.profile_run:
         if args.calibrate:
@@ -756,6 +786,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": step_stats,
         "graph_ms_per_step": round(ms_graph, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -785,6 +816,7 @@ def main(argv=None):
         "comparators": comparators,
         "parity": parity,
         "cpu_baseline": cpu,
+        "host": host_facts(),
     }
     print(json.dumps(result), flush=True)
     return 0
