@@ -115,3 +115,20 @@ def test_swap_buffer_fact_is_two_byte_elements(golden):
     elements (bf16/fp16), the element size of this library's KV pages."""
     f = golden["swap_buffer_bytes"]
     assert f["matrix_dim"] ** 2 * f["bytes_per_element"] == 200 * 2 ** 20
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library every entry point raises; nothing falls
+    back to another implementation."""
+    import torch
+    monkeypatch.setattr(dkv, "LIBRARY", str(tmp_path / "libdkv.so"))
+    monkeypatch.setattr(dkv, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        dkv.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        dkv.kv_page_bytes(dkv.Shape.of(4096, 32, 8, 128, 1))
+    x = torch.zeros((1, 512), dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="not built"):
+        dkv.decode_step(dkv.Layout(1, dkv.Shape.of(512, 8, 8, 64, 1), 1, np.array([2], np.int32)), 0, x,
+                        torch.zeros((1536, 512), dtype=torch.bfloat16), torch.zeros(1, dtype=torch.int32),
+                        torch.zeros((1, 512), dtype=torch.bfloat16))
