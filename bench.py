@@ -493,6 +493,90 @@ def sweep_ctx(dkv, wl, args):
     return 0
 
 
+def multistep(dkv, wl, kv_source, args):
+    """Multi-step decode: one HIP graph holding decode_step (every layer) and
+    kv_advance, replayed step after step while the contexts grow, on three
+    layouts of the same KV: all host pages, a sliding HBM window of the most
+    recent --window-tokens tokens per sequence over host pages (kv_advance
+    demotes the window's oldest page every 16 tokens), and all HBM pages.
+    Prints one JSON line with ms per step and effective KV GB/s of each, and
+    whether the host and windowed layouts end with identical bits."""
+    import torch
+    ctx0 = wl.ctx_lens()
+    B = len(ctx0)
+    K, W = args.steps, args.warmup
+    cap = (ctx0 + K + W + 2).astype(np.int32)
+    shape = dkv.Shape.of(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_layers)
+    dev = torch.device("cuda", 0)
+    xs = [torch.from_numpy(wl.x(layer).view(np.int16)).to(dev).view(torch.bfloat16) for layer in range(wl.n_layers)]
+    Ws = [torch.from_numpy(wl.W(layer).view(np.int16)).to(dev).view(torch.bfloat16) for layer in range(wl.n_layers)]
+    pages = [int(dkv.kv_placement(int(c), 0)[0]) for c in cap]
+    win_pages = -(-args.window_tokens // dkv.PAGE_TOKENS)
+    rows, finals = [], {}
+    for kind in ("host", "window", "hbm"):
+        host = hbm = None
+        if kind == "host":
+            host = dkv.kv_alloc_host(shape, sum(pages) * wl.n_layers)
+            layout = dkv.kv_layout_create(shape, cap, None, host, None)
+        elif kind == "window":
+            host = dkv.kv_alloc_host(shape, sum(pages) * wl.n_layers)
+            hbm = dkv.kv_alloc_hbm(shape, sum(min(p, win_pages) for p in pages) * wl.n_layers)
+            layout = dkv.kv_layout_create_windowed(shape, cap, args.window_tokens, ctx0, host, hbm)
+        else:
+            hbm = dkv.kv_alloc_hbm(shape, sum(pages) * wl.n_layers)
+            layout = dkv.kv_layout_create(shape, cap, np.full(B, 1 << 30, np.int32), None, hbm)
+        for layer in range(wl.n_layers):
+            for b in range(B):
+                for t0 in range(0, int(ctx0[b]), CHUNK):
+                    t1 = min(int(ctx0[b]), t0 + CHUNK)
+                    k, v = kv_source(layer, b, t0, t1)
+                    dkv.kv_append(layout, layer, b, t0, k, v)
+        ctx = torch.from_numpy(ctx0.copy()).to(dev)
+        outs = [torch.empty((B, wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16, device=dev)
+                for _ in range(wl.n_layers)]
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            for layer in range(wl.n_layers):
+                dkv.decode_step(layout, layer, xs[layer], Ws[layer], ctx, outs[layer])
+            dkv.kv_advance(layout, ctx)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        for _ in range(W):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        del graph
+        layout.check_status()
+        assert np.array_equal(ctx.cpu().numpy(), ctx0 + W + K)
+        final = dkv.decode_step_f32(layout, 0, xs[0], Ws[0], ctx)
+        finals[kind] = final.cpu().numpy().view(np.uint32)
+        mean_ctx = ctx0.astype(np.float64) + W + (K - 1) / 2.0
+        kv_bytes = float(mean_ctx.sum()) * wl.kv_bytes_per_token * wl.n_layers
+        hbm_tokens = 0.0 if kind == "host" else (float(mean_ctx.sum()) if kind == "hbm" else
+                                                  float(np.minimum(mean_ctx, args.window_tokens).sum()))
+        rows.append({"layout": kind, "ms_per_step": round(ms, 4), "effective_kv_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+                     "hbm_share_of_kv": round(hbm_tokens / float(mean_ctx.sum()), 4)})
+        log("multistep %s: %.4f ms/step" % (kind, ms))
+        torch.cuda.synchronize()
+        layout.free()
+        for p in (host, hbm):
+            if p:
+                p.free()
+    print(json.dumps({"multistep": wl.name, "steps": K, "warmup": W, "window_tokens": args.window_tokens,
+                      "graph": "decode_step per layer + kv_advance, replayed once per step", "rows": rows,
+                      "window_and_host_bit_identical": bool(np.array_equal(finals["host"], finals["window"])),
+                      "hbm_and_host_bit_identical": bool(np.array_equal(finals["host"], finals["hbm"]))}), flush=True)
+    return 0
+
+
 def sweep(dkv, wl, ctx, kv_source, kv_bytes, args):
     """Step time as the host-resident share of the same KV goes from 0 to 1:
     the first round(f * L_b) cached tokens of each sequence on the host, the
@@ -541,6 +625,11 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true",
                     help="crossover sweep instead of the bench line: the workload's KV with the "
                          "host-resident share stepped from 0 to 100 %% (rest in HBM)")
+    ap.add_argument("--multistep", action="store_true",
+                    help="multi-step decode from one replayed HIP graph (decode_step + kv_advance) on "
+                         "all-host, sliding-window and all-HBM layouts of the workload")
+    ap.add_argument("--window-tokens", type=int, default=4096,
+                    help="with --multistep: HBM window per sequence (tokens)")
     ap.add_argument("--sweep-ctx", action="store_true",
                     help="context-length sweep instead of the bench line: zero-copy, all-HBM, "
                          "staging and host-CPU attention at the workload's batch")
@@ -613,6 +702,8 @@ def main(argv=None):
 
     if args.sweep:
         return sweep(dkv, wl, ctx, kv_source, kv_bytes, args)
+    if args.multistep:
+        return multistep(dkv, wl, kv_source, args)
 
     # ------------------------------------------------------------------ the workload's placement
     if args.profile_run and args.all_hbm:
