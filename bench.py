@@ -373,6 +373,12 @@ def host_facts() -> dict:
         facts["iommu_groups"] = len(os.listdir("/sys/kernel/iommu_groups"))
     except OSError:
         facts["iommu_groups"] = None
+    facts["host_page_bytes"] = os.sysconf("SC_PAGE_SIZE")
+    try:
+        with open("/sys/kernel/mm/transparent_hugepage/enabled") as f:
+            facts["transparent_hugepages"] = f.read().strip()
+    except OSError:
+        facts["transparent_hugepages"] = None
     return facts
 
 

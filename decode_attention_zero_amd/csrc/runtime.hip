@@ -456,6 +456,27 @@ static dkv_status check_pools(const dkv_shape *shape, int32_t batch, const int32
 // Allocates the layout's device tables and scratch, uploads the page table
 // (and the window tables), and hands the layout out; frees everything on
 // failure.
+// DKV_LOG=1: one line per layout on stderr with the launch plan its decode
+// steps will use (measurement and debugging aid; nothing else changes).
+static void log_plan(const dkv_layout *L, int64_t n_host, int64_t n_hbm) {
+    const char *env = getenv("DKV_LOG");
+    if (!env || strcmp(env, "1") != 0) return;
+    static const char *const kSplitNames[] = {"regs", "lds", "naive", "mfma"};
+    const dkv_shape *s = &L->shape;
+    const int B = L->batch;
+    const char *proj = B >= L->proj_mfma_min_batch ? (B <= 16 ? "mfma one-tile streamed" : "mfma tiled") : "gemv";
+    fprintf(stderr,
+            "[dkv] layout: batch %d, hidden %d, heads %d/%d, head_dim %d, layers %d; pages per layer: "
+            "%lld host, %lld HBM%s; split %d tokens (%d per sequence at most), split kernel %s on %s; "
+            "projection %s\n",
+            B, s->hidden, s->n_q_heads, s->n_kv_heads, s->head_dim, s->n_layers, (long long)n_host,
+            (long long)n_hbm, L->windowed ? " (sliding window)" : "", L->split_tokens, L->max_splits,
+            kSplitNames[L->split_variant],
+            L->split_waves > 0 ? (std::to_string(L->split_waves) + " looping wavefronts").c_str()
+                               : "one wavefront per item",
+            proj);
+}
+
 static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &table,
                                 const std::vector<uint64_t> *host_pages, const std::vector<uint64_t> *ring,
                                 dkv_layout **out) {
@@ -474,6 +495,7 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
     }
     L->split_waves = choose_split_waves(n_host, n_hbm);
     L->proj_mfma_min_batch = choose_proj_mfma_min_batch();
+    log_plan(L, n_host, n_hbm);
     if (L->host_pool) ++L->host_pool->n_layouts;
     if (L->hbm_pool) ++L->hbm_pool->n_layouts;
 

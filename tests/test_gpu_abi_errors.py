@@ -115,3 +115,17 @@ def test_layout_creation_errors():
                                   None, ctypes.byref(out)) == E_UNSUPPORTED
     finally:
         host.free()
+
+
+def test_plan_log(monkeypatch, capfd):
+    """DKV_LOG=1 prints the layout's launch plan on stderr; nothing else changes."""
+    monkeypatch.setenv("DKV_LOG", "1")
+    shape = dkv.Shape.of(4096, 32, 8, 128, 1)
+    host = dkv.kv_alloc_host(shape, 8)
+    try:
+        layout = dkv.kv_layout_create(shape, np.array([40, 50], np.int32), None, host, None)
+        layout.free()
+    finally:
+        host.free()
+    err = capfd.readouterr().err
+    assert "[dkv] layout: batch 2" in err and "split kernel mfma" in err, err
