@@ -613,7 +613,18 @@ __global__ __launch_bounds__(64 * (NC + 1)) void attn_split_lds_kernel(StepArgs 
             if (i + NS - 2 < np) wait_vmcnt<LPP * (NS - 2)>();   // runs i + 1 .. i + NS - 2 may still fly
             else wait_vmcnt<0>();
             ring_barrier();
-            if (i + NS - 1 < np) issue(i + NS - 1);              // refills the slot of run i - 1
+            if (i + NS - 1 < np) {                                // refills the slot of run i - 1
+                if (a.lds_poison) {
+                    // Debug: NaN over the freed slot, landed before its refill is issued.
+                    char *dst = ring[(i + NS - 1) % NS] + lane * 16;
+#pragma unroll
+                    for (int j = 0; j < LPP; ++j)
+                        *reinterpret_cast<uint4 *>(dst + j * 1024) = make_uint4(0x7FC07FC0u, 0x7FC07FC0u,
+                                                                               0x7FC07FC0u, 0x7FC07FC0u);
+                    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+                }
+                issue(i + NS - 1);
+            }
         }
         return;
     }
@@ -652,9 +663,12 @@ void launch(const StepArgs &a, hipStream_t st) {
         if (a.split_waves > 0) attn_split_mfma_persistent_kernel<D, G><<<a.split_waves, 64, 0, st>>>(a);
         else attn_split_mfma_kernel<D, G><<<grid, 64, 0, st>>>(a);
     } else if (a.split_variant == kSplitLds) {
-        // Consumers own at most 4 query heads each; 4 ring slots (3 runs in flight).
+        // Consumers own at most 4 query heads each; 4 ring slots (3 runs in
+        // flight) unless a debug knob asks for 2 or 3.
         constexpr int NC = G > 4 ? G / 4 : 1;
-        attn_split_lds_kernel<D, G, NC, 4><<<grid, 64 * (NC + 1), 0, st>>>(a);
+        if (a.lds_ring == 2) attn_split_lds_kernel<D, G, NC, 2><<<grid, 64 * (NC + 1), 0, st>>>(a);
+        else if (a.lds_ring == 3) attn_split_lds_kernel<D, G, NC, 3><<<grid, 64 * (NC + 1), 0, st>>>(a);
+        else attn_split_lds_kernel<D, G, NC, 4><<<grid, 64 * (NC + 1), 0, st>>>(a);
     } else if (a.split_waves > 0) {
         attn_split_persistent_kernel<D, G, WPI><<<a.split_waves, 64 * WPI, 0, st>>>(a);
     } else {

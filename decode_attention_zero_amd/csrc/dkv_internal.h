@@ -40,6 +40,8 @@ struct StepArgs {
     int32_t split_variant;  // kSplitRegisters, kSplitLds, kSplitNaive or kSplitMfma
     int32_t split_waves;    // register kernel: > 0 = that many wavefronts loop over the items
     int32_t proj_mfma_min_batch;  // batches from this size on project on MFMA, below on VALU
+    int32_t lds_ring;       // LDS producer/consumer kernel: ring slots (2, 3 or 4)
+    int32_t lds_poison;     // LDS producer/consumer kernel: 1 = fill each freed slot with NaN first
     // this layer's page table [batch][max_pages] of device addresses
     const uint64_t *page_table;
     const int32_t *capacity;  // [batch] slots per sequence (device)

@@ -114,6 +114,8 @@ struct dkv_layout {
     int32_t split_variant;             // dkv::kSplitRegisters, kSplitLds, kSplitNaive or kSplitMfma
     int32_t split_waves;               // > 0: the register kernel runs on that many looping wavefronts
     int32_t proj_mfma_min_batch;       // batches from this size on project on the matrix cores
+    int32_t lds_ring;                  // LDS producer/consumer kernel: ring slots
+    int32_t lds_poison;                // LDS producer/consumer kernel: NaN-fill freed slots
     dkv_pool *host_pool;
     dkv_pool *hbm_pool;
     std::vector<std::pair<dkv_pool *, int64_t>> owned;   // every page the layout holds
@@ -456,6 +458,21 @@ static dkv_status check_pools(const dkv_shape *shape, int32_t batch, const int32
 // Allocates the layout's device tables and scratch, uploads the page table
 // (and the window tables), and hands the layout out; frees everything on
 // failure.
+// Debug knobs of the LDS producer/consumer split kernel, the race detector
+// of its handoff: DKV_LDS_RING=2|3|4 ring slots (default 4: three runs in
+// flight), DKV_POISON=1 fills every slot with NaN before it is refilled, so a
+// consumer that read a slot before its loads landed would produce NaN
+// instead of a silently stale result. Neither changes the arithmetic.
+static void choose_lds_ring(dkv_layout *L) {
+    L->lds_ring = 4;
+    if (const char *env = getenv("DKV_LDS_RING")) {
+        const int v = atoi(env);
+        if (v >= 2 && v <= 4) L->lds_ring = v;
+    }
+    const char *poison = getenv("DKV_POISON");
+    L->lds_poison = poison && strcmp(poison, "1") == 0;
+}
+
 // DKV_LOG=1: one line per layout on stderr with the launch plan its decode
 // steps will use (measurement and debugging aid; nothing else changes).
 static void log_plan(const dkv_layout *L, int64_t n_host, int64_t n_hbm) {
@@ -495,6 +512,7 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
     }
     L->split_waves = choose_split_waves(n_host, n_hbm);
     L->proj_mfma_min_batch = choose_proj_mfma_min_batch();
+    choose_lds_ring(L);
     log_plan(L, n_host, n_hbm);
     if (L->host_pool) ++L->host_pool->n_layouts;
     if (L->hbm_pool) ++L->hbm_pool->n_layouts;
@@ -965,6 +983,8 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     a.split_tokens = L->split_tokens;
     a.split_variant = L->split_variant;
     a.split_waves = L->split_waves;
+    a.lds_ring = L->lds_ring;
+    a.lds_poison = L->lds_poison;
     a.proj_mfma_min_batch = L->proj_mfma_min_batch;
     a.max_splits = L->max_splits;
     a.qscale = (float)(1.4426950408889634074 / std::sqrt((double)s->head_dim));

@@ -445,6 +445,40 @@ def test_lds_split_kernel_split_edges(oracle, monkeypatch):
         s.free()
 
 
+@pytest.mark.parametrize("wl_name", ["llama3-8b-b8-ctx32768-host", "llama3-70b-b16-ctx131072-8layers-host"],
+                         ids=["g4", "g8"])
+def test_lds_ring_depths_and_poison(oracle, monkeypatch, wl_name):
+    """Race detector of the LDS producer/consumer handoff: ring depths 2, 3
+    and 4, each with every freed slot filled with NaN before its refill
+    (DKV_POISON=1), give the same bits as the unpoisoned 4-slot ring (and, at
+    group 4, as the register kernel); a consumer reading a slot before its
+    loads landed would show up as NaN."""
+    wl = configs.BY_NAME[wl_name].replace(batch=4, n_layers=1)
+    ctx = [1, 300, 1030, 2100]
+    tail = [0, 40, 1 << 20, 300]
+
+    def run(env):
+        for k in ("DKV_SPLIT_KERNEL", "DKV_LDS_RING", "DKV_POISON"):
+            monkeypatch.delenv(k, raising=False)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        s = H.Setup(wl, ctx_lens=ctx, hbm_tail=tail)
+        try:
+            return s.run(f32=True).cpu().numpy().view(np.uint32)
+        finally:
+            s.free()
+
+    base = run({"DKV_SPLIT_KERNEL": "lds"})
+    assert np.all(np.isfinite(base.view(np.float32)))
+    for ring in ("2", "3", "4"):
+        got = run({"DKV_SPLIT_KERNEL": "lds", "DKV_LDS_RING": ring, "DKV_POISON": "1"})
+        assert np.array_equal(got, base), ring
+    if wl.group <= 4:
+        assert np.array_equal(run({"DKV_SPLIT_KERNEL": "regs"}), base)
+    check_tight(base.view(np.float32).astype(np.float64), tight_reference(oracle, wl, 0, np.asarray(ctx, np.int32)),
+                "lds ring %s" % wl_name)
+
+
 # --------------------------------------------------------------------------- comparators
 @pytest.mark.parametrize("wl_name", ["llama3-8b-b8-ctx32768-host", "llama3-70b-b16-ctx131072-8layers-host"],
                          ids=["g4", "g8"])
