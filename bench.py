@@ -382,6 +382,24 @@ def host_facts() -> dict:
     return facts
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+
+
+def projection_facts(wl, ms):
+    """The QKV projection of one step (summed over layers): which kernel, its W
+    read rate and its matrix-core use against the dense bf16 peak."""
+    B = wl.batch
+    kernel = ("qkv_proj_gemv_kernel" if B < 8 else
+              "qkv_proj_stream_kernel" if B <= 16 else "qkv_proj_mfma_kernel")
+    w_bytes = wl.n_qkv * wl.hidden * 2 * wl.n_layers
+    flop = 2.0 * B * wl.hidden * wl.n_qkv * wl.n_layers
+    return {"kernel": kernel, "ms": round(ms, 4), "W_bytes": w_bytes,
+            "W_GBps": round(w_bytes / (ms * 1e-3) / 1e9, 1),
+            "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
+            "mfma_utilisation": (round(flop / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)
+                                 if kernel != "qkv_proj_gemv_kernel" else None)}
+
+
 def split_kernel_label(layout) -> str:
     """Name of the split-attention kernel a layout launches, and its wavefronts."""
     mfma = layout.split_kernel == "mfma"
@@ -908,6 +926,7 @@ def main(argv=None):
         "combined_roofline": {"t_star_ms": round(t_star * 1e3, 4),
                               "frac": round(t_star * 1e3 / ms, 4) if t_star else None},
         "kernel_ms": {k: round(v, 4) for k, v in kt.items()},
+        "projection": projection_facts(wl, kt["projection"]),
         "host_link_probe": ceiling_rows,
         "hbm_placement": hbm,
         "comparators": comparators,
