@@ -496,8 +496,10 @@ __global__ __launch_bounds__(64, kMfmaWavesPerSimd) void attn_split_mfma_kernel(
     split_item_mfma<D, G>(a, stage, blockIdx.x, g, h0, blockIdx.z);
 }
 
+// The looping form runs a few hundred wavefronts in all (one or two per CU),
+// so it may use the registers of a whole SIMD.
 template <int D, int G>
-__global__ __launch_bounds__(64, kMfmaWavesPerSimd) void attn_split_mfma_persistent_kernel(StepArgs a) {
+__global__ __launch_bounds__(64, 1) void attn_split_mfma_persistent_kernel(StepArgs a) {
     __shared__ __attribute__((aligned(16))) char stage[MfmaState<D, G>::STAGE];
     const int n_items = a.n_kv_heads * a.max_splits * a.batch;
     for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
