@@ -7,7 +7,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <mutex>
+#include <new>
+#include <stdexcept>
 #include <string>
 #include <thread>
 #include <unordered_set>
@@ -43,19 +46,44 @@ bool live(const void *h) {
     return g_handles.count(h) == 1;
 }
 
-dkv_status fail(dkv_status st, const char *fmt, ...) {
+// Records the message of a failing call; never throws (a message that
+// cannot be stored is dropped), so it is safe on every error path.
+dkv_status fail(dkv_status st, const char *fmt, ...) noexcept {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
-    g_last_error = buf;
+    try {
+        g_last_error = buf;
+    } catch (...) {
+        g_last_error.clear();
+    }
     return st;
 }
 
 dkv_status hip_fail(hipError_t e, const char *what) {
     return fail(DKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+// Entry points that allocate host memory or start threads run their body
+// through this: a std::bad_alloc (or any other exception of the C++ runtime,
+// such as thread creation failing) becomes DKV_E_OUT_OF_MEMORY with a
+// message, so nothing unwinds across the C ABI.
+template <class F>
+dkv_status guarded(const char *who, F &&body) {
+    try {
+        return body();
+    } catch (const std::bad_alloc &) {
+        return fail(DKV_E_OUT_OF_MEMORY, "%s: host memory exhausted", who);
+    } catch (const std::exception &ex) {
+        return fail(DKV_E_OUT_OF_MEMORY, "%s: host resources exhausted (%s)", who, ex.what());
+    }
+}
+
+// Largest pool, in bytes, a request may ask for (1 PiB): keeps page counts
+// times page bytes far from overflow.
+constexpr uint64_t kMaxPoolBytes = 1ull << 50;
 
 #define HIP_TRY(call)                                        \
     do {                                                     \
@@ -296,6 +324,27 @@ void parallel_for(int64_t n, F f) {
     for (auto &t : ts) t.join();
 }
 
+// Pool bookkeeping (the struct, its page map and its registry entry) comes
+// first, so that nothing is left to undo if one of them throws.
+std::unique_ptr<dkv_pool> new_pool(const dkv_shape *shape, int64_t n_pages, int32_t tier) {
+    std::unique_ptr<dkv_pool> p(new dkv_pool());
+    p->shape = *shape;
+    p->tier = tier;
+    p->n_pages = n_pages;
+    p->page_bytes = page_bytes_of(shape);
+    p->host_base = nullptr;
+    p->dev_base = nullptr;
+    p->used.assign((size_t)n_pages, 0);
+    p->n_free = n_pages;
+    p->scan = 0;
+    p->n_layouts = 0;
+    return p;
+}
+
+bool pool_too_large(const dkv_shape *shape, int64_t n_pages) {
+    return (uint64_t)n_pages > kMaxPoolBytes / (uint64_t)page_bytes_of(shape);
+}
+
 }  // namespace
 
 namespace dkv {
@@ -348,65 +397,57 @@ dkv_status kv_placement(int32_t capacity_tokens, int32_t hbm_tail_tokens, int32_
 dkv_status kv_alloc_host(const dkv_shape *shape, int64_t n_pages, uint32_t flags, dkv_pool **out) {
     if (!out || !shape_ok(shape) || n_pages <= 0 || flags > DKV_HOST_NONCOHERENT)
         return fail(DKV_E_INVALID_ARG, "kv_alloc_host: bad shape, n_pages, flags or null output");
-    const int64_t pb = page_bytes_of(shape);
-    const size_t bytes = (size_t)pb * (size_t)n_pages;
-    void *h = nullptr;
-    unsigned hflags = hipHostMallocMapped | hipHostMallocPortable |
-                      (flags == DKV_HOST_NONCOHERENT ? hipHostMallocNonCoherent : hipHostMallocCoherent);
-    hipError_t e = hipHostMalloc(&h, bytes, hflags);
-    if (e != hipSuccess || !h) {
-        (void)hipGetLastError();
-        return fail(DKV_E_OUT_OF_MEMORY, "kv_alloc_host: hipHostMalloc of %zu bytes failed: %s", bytes,
-                    hipGetErrorString(e));
-    }
-    void *d = nullptr;
-    e = hipHostGetDevicePointer(&d, h, 0);
-    if (e != hipSuccess || !d) {
-        (void)hipHostFree(h);
-        return hip_fail(e, "kv_alloc_host: hipHostGetDevicePointer");
-    }
-    dkv_pool *p = new dkv_pool();
-    p->shape = *shape;
-    p->tier = 0;
-    p->n_pages = n_pages;
-    p->page_bytes = pb;
-    p->host_base = static_cast<char *>(h);
-    p->dev_base = static_cast<char *>(d);
-    p->used.assign((size_t)n_pages, 0);
-    p->n_free = n_pages;
-    p->scan = 0;
-    p->n_layouts = 0;
-    track(p);
-    *out = p;
-    return DKV_OK;
+    if (pool_too_large(shape, n_pages))
+        return fail(DKV_E_OUT_OF_MEMORY, "kv_alloc_host: %lld pages exceed the 1 PiB pool limit", (long long)n_pages);
+    return guarded("kv_alloc_host", [&]() -> dkv_status {
+        std::unique_ptr<dkv_pool> p = new_pool(shape, n_pages, 0);
+        const size_t bytes = (size_t)p->page_bytes * (size_t)n_pages;
+        track(p.get());
+        void *h = nullptr;
+        const unsigned hflags = hipHostMallocMapped | hipHostMallocPortable |
+                                (flags == DKV_HOST_NONCOHERENT ? hipHostMallocNonCoherent : hipHostMallocCoherent);
+        hipError_t e = hipHostMalloc(&h, bytes, hflags);
+        if (e != hipSuccess || !h) {
+            (void)hipGetLastError();
+            untrack(p.get());
+            return fail(DKV_E_OUT_OF_MEMORY, "kv_alloc_host: hipHostMalloc of %zu bytes failed: %s", bytes,
+                        hipGetErrorString(e));
+        }
+        void *d = nullptr;
+        e = hipHostGetDevicePointer(&d, h, 0);
+        if (e != hipSuccess || !d) {
+            (void)hipHostFree(h);
+            untrack(p.get());
+            return hip_fail(e, "kv_alloc_host: hipHostGetDevicePointer");
+        }
+        p->host_base = static_cast<char *>(h);
+        p->dev_base = static_cast<char *>(d);
+        *out = p.release();
+        return DKV_OK;
+    });
 }
 
 dkv_status kv_alloc_hbm(const dkv_shape *shape, int64_t n_pages, dkv_pool **out) {
     if (!out || !shape_ok(shape) || n_pages <= 0)
         return fail(DKV_E_INVALID_ARG, "kv_alloc_hbm: bad shape, n_pages or null output");
-    const int64_t pb = page_bytes_of(shape);
-    const size_t bytes = (size_t)pb * (size_t)n_pages;
-    void *d = nullptr;
-    hipError_t e = hipMalloc(&d, bytes);
-    if (e != hipSuccess || !d) {
-        (void)hipGetLastError();
-        return fail(DKV_E_OUT_OF_MEMORY, "kv_alloc_hbm: hipMalloc of %zu bytes failed: %s", bytes,
-                    hipGetErrorString(e));
-    }
-    dkv_pool *p = new dkv_pool();
-    p->shape = *shape;
-    p->tier = 1;
-    p->n_pages = n_pages;
-    p->page_bytes = pb;
-    p->host_base = nullptr;
-    p->dev_base = static_cast<char *>(d);
-    p->used.assign((size_t)n_pages, 0);
-    p->n_free = n_pages;
-    p->scan = 0;
-    p->n_layouts = 0;
-    track(p);
-    *out = p;
-    return DKV_OK;
+    if (pool_too_large(shape, n_pages))
+        return fail(DKV_E_OUT_OF_MEMORY, "kv_alloc_hbm: %lld pages exceed the 1 PiB pool limit", (long long)n_pages);
+    return guarded("kv_alloc_hbm", [&]() -> dkv_status {
+        std::unique_ptr<dkv_pool> p = new_pool(shape, n_pages, 1);
+        const size_t bytes = (size_t)p->page_bytes * (size_t)n_pages;
+        track(p.get());
+        void *d = nullptr;
+        hipError_t e = hipMalloc(&d, bytes);
+        if (e != hipSuccess || !d) {
+            (void)hipGetLastError();
+            untrack(p.get());
+            return fail(DKV_E_OUT_OF_MEMORY, "kv_alloc_hbm: hipMalloc of %zu bytes failed: %s", bytes,
+                        hipGetErrorString(e));
+        }
+        p->dev_base = static_cast<char *>(d);
+        *out = p.release();
+        return DKV_OK;
+    });
 }
 
 dkv_status kv_pool_free_pages(const dkv_pool *pool, int64_t *n_free) {
@@ -451,7 +492,8 @@ static dkv_status check_pools(const dkv_shape *shape, int32_t batch, const int32
     if (host_pool && host_pool->tier != 0) return fail(DKV_E_INVALID_ARG, "%s: host_pool is HBM", who);
     if (hbm_pool && hbm_pool->tier != 1) return fail(DKV_E_INVALID_ARG, "%s: hbm_pool is host", who);
     for (int b = 0; b < batch; ++b)
-        if (capacity_tokens[b] <= 0) return fail(DKV_E_INVALID_ARG, "%s: capacity of sequence %d is not positive", who, b);
+        if (capacity_tokens[b] <= 0)
+            return fail(DKV_E_INVALID_ARG, "%s: capacity of sequence %d is not positive", who, b);
     return DKV_OK;
 }
 
@@ -514,10 +556,12 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
     L->proj_mfma_min_batch = choose_proj_mfma_min_batch();
     choose_lds_ring(L);
     log_plan(L, n_host, n_hbm);
+    track(L);                          // the last step that can throw
     if (L->host_pool) ++L->host_pool->n_layouts;
     if (L->hbm_pool) ++L->hbm_pool->n_layouts;
 
     auto cleanup = [&](dkv_status st) {
+        untrack(L);
         free_device(L);
         release_pages(L);
         if (L->host_pool) --L->host_pool->n_layouts;
@@ -570,17 +614,22 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
         hip_fail(e, "kv_layout_create: initialising device tables");
         return cleanup(DKV_E_HIP);
     }
-    track(L);
     *out = L;
     return DKV_OK;
 }
 
-dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t *capacity_tokens,
-                            const int32_t *hbm_tail_tokens, dkv_pool *host_pool, dkv_pool *hbm_pool,
-                            dkv_layout **out) {
-    dkv_status st = check_pools(shape, batch, capacity_tokens, host_pool, hbm_pool, out, "kv_layout_create");
-    if (st != DKV_OK) return st;
-    dkv_layout *L = new dkv_layout();
+// A layout under construction that an exception interrupted: its pages go
+// back to their pools (it was neither tracked nor counted by them yet).
+static void abandon_layout(dkv_layout *L) {
+    if (!L) return;
+    release_pages(L);
+    delete L;
+}
+
+static dkv_status layout_create_static(const dkv_shape *shape, int32_t batch, const int32_t *capacity_tokens,
+                                       const int32_t *hbm_tail_tokens, dkv_pool *host_pool, dkv_pool *hbm_pool,
+                                       dkv_layout **out, dkv_layout *&L) {
+    L = new dkv_layout();
     L->shape = *shape;
     L->batch = batch;
     L->capacity.assign(capacity_tokens, capacity_tokens + batch);
@@ -605,7 +654,8 @@ dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t
     need_hbm *= shape->n_layers;
     if ((need_host > 0 && !host_pool) || (need_hbm > 0 && !hbm_pool)) {
         delete L;
-        return fail(DKV_E_INVALID_ARG, "kv_layout_create: placement needs %lld host and %lld HBM pages but a pool is missing",
+        return fail(DKV_E_INVALID_ARG,
+                    "kv_layout_create: placement needs %lld host and %lld HBM pages but a pool is missing",
                     (long long)need_host, (long long)need_hbm);
     }
     if ((host_pool && host_pool->n_free < need_host) || (hbm_pool && hbm_pool->n_free < need_hbm)) {
@@ -615,6 +665,7 @@ dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t
                     (long long)(hbm_pool ? hbm_pool->n_free : 0));
     }
     L->max_pages = max_pages;
+    L->owned.reserve((size_t)(need_host + need_hbm));   // so that recording a taken page cannot throw
 
     // Pages are taken in (layer, sequence, page) order, so each sequence's
     // pages of a tier are consecutive in their pool when it is fresh.
@@ -639,15 +690,25 @@ dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t
     return finish_layout(L, table, nullptr, nullptr, out);
 }
 
-dkv_status kv_layout_create_windowed(const dkv_shape *shape, int32_t batch, const int32_t *capacity_tokens,
-                                     const int32_t *window_tokens, const int32_t *ctx_lens, dkv_pool *host_pool,
-                                     dkv_pool *hbm_pool, dkv_layout **out) {
-    const char *who = "kv_layout_create_windowed";
-    dkv_status st = check_pools(shape, batch, capacity_tokens, host_pool, hbm_pool, out, who);
+dkv_status kv_layout_create(const dkv_shape *shape, int32_t batch, const int32_t *capacity_tokens,
+                            const int32_t *hbm_tail_tokens, dkv_pool *host_pool, dkv_pool *hbm_pool,
+                            dkv_layout **out) {
+    dkv_status st = check_pools(shape, batch, capacity_tokens, host_pool, hbm_pool, out, "kv_layout_create");
     if (st != DKV_OK) return st;
-    if (!window_tokens || !ctx_lens || !host_pool || !hbm_pool)
-        return fail(DKV_E_INVALID_ARG, "%s: window_tokens, ctx_lens and both pools are required", who);
-    dkv_layout *L = new dkv_layout();
+    dkv_layout *L = nullptr;
+    try {
+        return layout_create_static(shape, batch, capacity_tokens, hbm_tail_tokens, host_pool, hbm_pool, out, L);
+    } catch (const std::exception &ex) {
+        abandon_layout(L);
+        return fail(DKV_E_OUT_OF_MEMORY, "kv_layout_create: host memory exhausted (%s)", ex.what());
+    }
+}
+
+static dkv_status layout_create_windowed(const dkv_shape *shape, int32_t batch, const int32_t *capacity_tokens,
+                                         const int32_t *window_tokens, const int32_t *ctx_lens, dkv_pool *host_pool,
+                                         dkv_pool *hbm_pool, dkv_layout **out, dkv_layout *&L) {
+    const char *who = "kv_layout_create_windowed";
+    L = new dkv_layout();
     L->shape = *shape;
     L->batch = batch;
     L->windowed = 1;
@@ -666,7 +727,8 @@ dkv_status kv_layout_create_windowed(const dkv_shape *shape, int32_t batch, cons
                         who, b, window_tokens[b], ctx_lens[b], capacity_tokens[b]);
         }
         L->n_pages[b] = (int32_t)(((int64_t)capacity_tokens[b] + DKV_PAGE_TOKENS - 1) / DKV_PAGE_TOKENS);
-        L->window[b] = std::min<int32_t>(L->n_pages[b], (window_tokens[b] + DKV_PAGE_TOKENS - 1) / DKV_PAGE_TOKENS);
+        L->window[b] = (int32_t)std::min<int64_t>(L->n_pages[b],
+                                                  ((int64_t)window_tokens[b] + DKV_PAGE_TOKENS - 1) / DKV_PAGE_TOKENS);
         L->first_hbm[b] = L->n_pages[b];
         need_host += L->n_pages[b];
         need_hbm += L->window[b];
@@ -683,6 +745,7 @@ dkv_status kv_layout_create_windowed(const dkv_shape *shape, int32_t batch, cons
     }
     L->max_pages = max_pages;
     L->max_window = max_window;
+    L->owned.reserve((size_t)(need_host + need_hbm));   // so that recording a taken page cannot throw
 
     // Every page has a host page; page p of the window uses HBM ring slot
     // p % W. The pages [P - W + 1, P] up to the one holding slot ctx_lens[b]
@@ -712,8 +775,27 @@ dkv_status kv_layout_create_windowed(const dkv_shape *shape, int32_t batch, cons
     return finish_layout(L, table, &host_pages, &ring, out);
 }
 
-dkv_status kv_layout_timing_enable(dkv_layout *L, int32_t enable, int32_t max_steps) {
-    if (!L || (enable && max_steps <= 0)) return fail(DKV_E_INVALID_ARG, "kv_layout_timing_enable: bad argument");
+dkv_status kv_layout_create_windowed(const dkv_shape *shape, int32_t batch, const int32_t *capacity_tokens,
+                                     const int32_t *window_tokens, const int32_t *ctx_lens, dkv_pool *host_pool,
+                                     dkv_pool *hbm_pool, dkv_layout **out) {
+    const char *who = "kv_layout_create_windowed";
+    dkv_status st = check_pools(shape, batch, capacity_tokens, host_pool, hbm_pool, out, who);
+    if (st != DKV_OK) return st;
+    if (!window_tokens || !ctx_lens || !host_pool || !hbm_pool)
+        return fail(DKV_E_INVALID_ARG, "%s: window_tokens, ctx_lens and both pools are required", who);
+    dkv_layout *L = nullptr;
+    try {
+        return layout_create_windowed(shape, batch, capacity_tokens, window_tokens, ctx_lens, host_pool, hbm_pool,
+                                      out, L);
+    } catch (const std::exception &ex) {
+        abandon_layout(L);
+        return fail(DKV_E_OUT_OF_MEMORY, "%s: host memory exhausted (%s)", who, ex.what());
+    }
+}
+
+static dkv_status kv_layout_timing_enable_body(dkv_layout *L, int32_t enable, int32_t max_steps) {
+    if (!L || !live(L) || (enable && max_steps <= 0))
+        return fail(DKV_E_INVALID_ARG, "kv_layout_timing_enable: null or freed layout, or max_steps <= 0");
     HIP_TRY(hipDeviceSynchronize());
     for (hipEvent_t e : L->timing_events) (void)hipEventDestroy(e);
     L->timing_events.clear();
@@ -724,9 +806,14 @@ dkv_status kv_layout_timing_enable(dkv_layout *L, int32_t enable, int32_t max_st
     return DKV_OK;
 }
 
+dkv_status kv_layout_timing_enable(dkv_layout *L, int32_t enable, int32_t max_steps) {
+    return guarded("kv_layout_timing_enable",
+                   [&] { return kv_layout_timing_enable_body(L, enable, max_steps); });
+}
+
 dkv_status kv_layout_timing_read(dkv_layout *L, double *ms_proj, double *ms_split, double *ms_combine,
                                  int32_t *n_steps) {
-    if (!L) return fail(DKV_E_INVALID_ARG, "kv_layout_timing_read: null layout");
+    if (!L || !live(L)) return fail(DKV_E_INVALID_ARG, "kv_layout_timing_read: null or freed layout");
     HIP_TRY(hipDeviceSynchronize());
     double sum[3] = {0.0, 0.0, 0.0};
     for (int32_t i = 0; i < L->timing_recorded; ++i) {
@@ -758,8 +845,9 @@ dkv_status kv_layout_free(dkv_layout *L) {
     return DKV_OK;
 }
 
-dkv_status kv_layout_page_tier(const dkv_layout *L, int32_t seq, int32_t page, int32_t *tier) {
-    if (!L || !tier || seq < 0 || seq >= L->batch || page < 0 || page >= L->n_pages[seq])
+static dkv_status kv_layout_page_tier_body(const dkv_layout *L, int32_t seq, int32_t page, int32_t *tier) {
+    if (!L || !tier || !live(L)) return fail(DKV_E_INVALID_ARG, "kv_layout_page_tier: null or freed layout");
+    if (seq < 0 || seq >= L->batch || page < 0 || page >= L->n_pages[seq])
         return fail(DKV_E_INVALID_ARG, "kv_layout_page_tier: index out of range");
     std::vector<uint64_t> row;
     HIP_TRY(hipDeviceSynchronize());
@@ -768,16 +856,21 @@ dkv_status kv_layout_page_tier(const dkv_layout *L, int32_t seq, int32_t page, i
     return DKV_OK;
 }
 
-int32_t kv_layout_split_tokens(const dkv_layout *L) { return L ? L->split_tokens : 0; }
+dkv_status kv_layout_page_tier(const dkv_layout *L, int32_t seq, int32_t page, int32_t *tier) {
+    return guarded("kv_layout_page_tier", [&] { return kv_layout_page_tier_body(L, seq, page, tier); });
+}
 
-int32_t kv_layout_split_kernel(const dkv_layout *L) { return L ? L->split_variant : -1; }
+int32_t kv_layout_split_tokens(const dkv_layout *L) { return L && live(L) ? L->split_tokens : 0; }
 
-int32_t kv_layout_split_waves(const dkv_layout *L) { return L ? L->split_waves : -1; }
+int32_t kv_layout_split_kernel(const dkv_layout *L) { return L && live(L) ? L->split_variant : -1; }
+
+int32_t kv_layout_split_waves(const dkv_layout *L) { return L && live(L) ? L->split_waves : -1; }
 
 dkv_status kv_layout_set_split_kernel(dkv_layout *L, int32_t kernel) {
-    if (!L || (kernel != dkv::kSplitRegisters && kernel != dkv::kSplitLds && kernel != dkv::kSplitNaive &&
+    if (!L || !live(L) || (kernel != dkv::kSplitRegisters && kernel != dkv::kSplitLds && kernel != dkv::kSplitNaive &&
                (kernel != dkv::kSplitMfma || L->shape.n_q_heads / L->shape.n_kv_heads < dkv::kMfmaMinGroup)))
-        return fail(DKV_E_INVALID_ARG, "kv_layout_set_split_kernel: null layout or unknown kernel %d", kernel);
+        return fail(DKV_E_INVALID_ARG, "kv_layout_set_split_kernel: null or freed layout, or unknown kernel %d",
+                    kernel);
     L->split_variant = kernel;
     return DKV_OK;
 }
@@ -793,8 +886,8 @@ static dkv_status check_range(const dkv_layout *L, int32_t layer, int32_t seq, i
     return DKV_OK;
 }
 
-dkv_status kv_append(dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n, const uint16_t *k,
-                     const uint16_t *v, dkv_stream_t stream) {
+static dkv_status kv_append_body(dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n,
+                                 const uint16_t *k, const uint16_t *v, dkv_stream_t stream) {
     dkv_status st = check_range(L, layer, seq, start, n, "kv_append");
     if (st != DKV_OK) return st;
     if (n == 0) return DKV_OK;
@@ -847,8 +940,13 @@ dkv_status kv_append(dkv_layout *L, int32_t layer, int32_t seq, int32_t start, i
     return DKV_OK;
 }
 
-dkv_status kv_read(const dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n, uint16_t *k_out,
-                   uint16_t *v_out) {
+dkv_status kv_append(dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n, const uint16_t *k,
+                     const uint16_t *v, dkv_stream_t stream) {
+    return guarded("kv_append", [&] { return kv_append_body(L, layer, seq, start, n, k, v, stream); });
+}
+
+static dkv_status kv_read_body(const dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n,
+                               uint16_t *k_out, uint16_t *v_out) {
     dkv_status st = check_range(L, layer, seq, start, n, "kv_read");
     if (st != DKV_OK) return st;
     if (n == 0) return DKV_OK;
@@ -881,9 +979,14 @@ dkv_status kv_read(const dkv_layout *L, int32_t layer, int32_t seq, int32_t star
     return DKV_OK;
 }
 
-dkv_status dkv_cpu_attention(const dkv_layout *L, int32_t layer, const float *q, const uint16_t *k_new,
-                             const uint16_t *v_new, const int32_t *ctx_lens, float *out, int32_t n_threads,
-                             int32_t *threads_used) {
+dkv_status kv_read(const dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n, uint16_t *k_out,
+                   uint16_t *v_out) {
+    return guarded("kv_read", [&] { return kv_read_body(L, layer, seq, start, n, k_out, v_out); });
+}
+
+static dkv_status dkv_cpu_attention_body(const dkv_layout *L, int32_t layer, const float *q, const uint16_t *k_new,
+                                         const uint16_t *v_new, const int32_t *ctx_lens, float *out,
+                                         int32_t n_threads, int32_t *threads_used) {
     if (!L || !live(L)) return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention: null or freed layout");
     if (layer < 0 || layer >= L->shape.n_layers)
         return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention: layer %d out of range", layer);
@@ -916,9 +1019,18 @@ dkv_status dkv_cpu_attention(const dkv_layout *L, int32_t layer, const float *q,
                                    q, k_new, v_new, ctx_lens, out, n_threads, threads_used);
 }
 
-dkv_status dkv_cpu_attention_pages(const void *const *pages, int32_t max_pages, const dkv_shape *shape,
-                                   int32_t batch, const float *q, const uint16_t *k_new, const uint16_t *v_new,
-                                   const int32_t *ctx_lens, float *out, int32_t n_threads, int32_t *threads_used) {
+dkv_status dkv_cpu_attention(const dkv_layout *L, int32_t layer, const float *q, const uint16_t *k_new,
+                             const uint16_t *v_new, const int32_t *ctx_lens, float *out, int32_t n_threads,
+                             int32_t *threads_used) {
+    return guarded("dkv_cpu_attention", [&] {
+        return dkv_cpu_attention_body(L, layer, q, k_new, v_new, ctx_lens, out, n_threads, threads_used);
+    });
+}
+
+static dkv_status dkv_cpu_attention_pages_body(const void *const *pages, int32_t max_pages, const dkv_shape *shape,
+                                               int32_t batch, const float *q, const uint16_t *k_new,
+                                               const uint16_t *v_new, const int32_t *ctx_lens, float *out,
+                                               int32_t n_threads, int32_t *threads_used) {
     if (!shape_ok(shape) || !shape_supported(shape))
         return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention_pages: invalid or unsupported shape");
     if (!pages || !q || !k_new || !v_new || !ctx_lens || !out || batch < 1 || max_pages < 1)
@@ -926,7 +1038,7 @@ dkv_status dkv_cpu_attention_pages(const void *const *pages, int32_t max_pages, 
     if (n_threads < 1 || n_threads > 1024)
         return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention_pages: n_threads %d outside [1, 1024]", n_threads);
     for (int b = 0; b < batch; ++b) {
-        const int n = (ctx_lens[b] + DKV_PAGE_TOKENS - 1) / DKV_PAGE_TOKENS;
+        const int64_t n = ((int64_t)ctx_lens[b] + DKV_PAGE_TOKENS - 1) / DKV_PAGE_TOKENS;
         if (ctx_lens[b] < 0 || n > max_pages)
             return fail(DKV_E_INVALID_ARG, "dkv_cpu_attention_pages: ctx_lens[%d] = %d does not fit %d pages", b,
                         ctx_lens[b], max_pages);
@@ -952,7 +1064,17 @@ dkv_status dkv_cpu_attention_pages(const void *const *pages, int32_t max_pages, 
     return DKV_OK;
 }
 
-dkv_status dkv_cpu_stream_read(const void *host_ptr, uint64_t bytes, int32_t n_threads, uint64_t *checksum) {
+dkv_status dkv_cpu_attention_pages(const void *const *pages, int32_t max_pages, const dkv_shape *shape,
+                                   int32_t batch, const float *q, const uint16_t *k_new, const uint16_t *v_new,
+                                   const int32_t *ctx_lens, float *out, int32_t n_threads, int32_t *threads_used) {
+    return guarded("dkv_cpu_attention_pages", [&] {
+        return dkv_cpu_attention_pages_body(pages, max_pages, shape, batch, q, k_new, v_new, ctx_lens, out,
+                                            n_threads, threads_used);
+    });
+}
+
+static dkv_status dkv_cpu_stream_read_body(const void *host_ptr, uint64_t bytes, int32_t n_threads,
+                                           uint64_t *checksum) {
     if (!host_ptr || bytes % 64 || n_threads < 1 || n_threads > 1024)
         return fail(DKV_E_INVALID_ARG, "dkv_cpu_stream_read: null pointer, bytes not a multiple of 64, or "
                                        "n_threads outside [1, 1024]");
@@ -961,11 +1083,17 @@ dkv_status dkv_cpu_stream_read(const void *host_ptr, uint64_t bytes, int32_t n_t
     return DKV_OK;
 }
 
+dkv_status dkv_cpu_stream_read(const void *host_ptr, uint64_t bytes, int32_t n_threads, uint64_t *checksum) {
+    return guarded("dkv_cpu_stream_read",
+                   [&] { return dkv_cpu_stream_read_body(host_ptr, bytes, n_threads, checksum); });
+}
+
 static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, const uint16_t *W,
                             const int32_t *ctx_lens, void *out, int out_f32, dkv_stream_t stream,
                             const char *who) {
     if (!L || !live(L)) return fail(DKV_E_INVALID_ARG, "%s: null or freed layout", who);
-    if (layer < 0 || layer >= L->shape.n_layers) return fail(DKV_E_INVALID_ARG, "%s: layer %d out of range", who, layer);
+    if (layer < 0 || layer >= L->shape.n_layers)
+        return fail(DKV_E_INVALID_ARG, "%s: layer %d out of range", who, layer);
     if (!q_in || !W || !ctx_lens || !out) return fail(DKV_E_INVALID_ARG, "%s: null pointer argument", who);
     if (((uintptr_t)q_in | (uintptr_t)W) & 15u)
         return fail(DKV_E_INVALID_ARG, "%s: q_in and W_qkv must be 16-byte aligned", who);
@@ -1110,8 +1238,8 @@ dkv_status dkv_gemm_bf16_nt(const uint16_t *A, const uint16_t *B, float *C, int3
     return DKV_OK;
 }
 
-dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid, int32_t unroll, int32_t reps,
-                                 float *ms_median) {
+static dkv_status dkv_probe_stream_read_body(const void *ptr, uint64_t bytes, int32_t grid, int32_t unroll,
+                                             int32_t reps, float *ms_median) {
     // unroll < 0 selects nontemporal loads with |unroll| in flight
     const bool nt = unroll < 0;
     if (nt) unroll = -unroll;
@@ -1121,7 +1249,7 @@ dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid, 
     hipStream_t st;
     HIP_TRY(hipStreamCreate(&st));
     uint32_t *sink = nullptr;
-    hipEvent_t e0, e1;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
     std::vector<float> ts;
     hipError_t e = hipMalloc(&sink, 64);
     if (e == hipSuccess) e = hipEventCreate(&e0);
@@ -1137,14 +1265,20 @@ dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid, 
         if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
         ts.push_back(ms);
     }
-    (void)hipEventDestroy(e0);
-    (void)hipEventDestroy(e1);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
     (void)hipFree(sink);
     (void)hipStreamDestroy(st);
     if (e != hipSuccess) return hip_fail(e, "dkv_probe_stream_read");
     std::sort(ts.begin(), ts.end());
     *ms_median = ts[ts.size() / 2];
     return DKV_OK;
+}
+
+dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid, int32_t unroll, int32_t reps,
+                                 float *ms_median) {
+    return guarded("dkv_probe_stream_read",
+                   [&] { return dkv_probe_stream_read_body(ptr, bytes, grid, unroll, reps, ms_median); });
 }
 
 }  // extern "C"

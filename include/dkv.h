@@ -32,6 +32,9 @@
  *  - dkv_stream_t is a hipStream_t passed as an opaque pointer (NULL = the
  *    null stream). Work is enqueued on it; nothing synchronises unless said.
  *  - Handles are not thread-safe: one thread at a time per handle.
+ *  - No C++ exception leaves the library: host memory or threads running
+ *    out inside a call is reported as DKV_E_OUT_OF_MEMORY, with nothing
+ *    left allocated or taken by the failed call.
  */
 #ifndef DKV_H
 #define DKV_H
@@ -112,7 +115,8 @@ typedef struct dkv_pool dkv_pool;
  * with hipHostMalloc (mapped, portable) on the current device's host NUMA
  * node; the GPU reads it in place. The pool owns the memory until
  * kv_pool_free. Errors: DKV_E_INVALID_ARG (null/shape/n_pages <= 0),
- * DKV_E_OUT_OF_MEMORY (pinning failed). */
+ * DKV_E_OUT_OF_MEMORY (pinning failed, or n_pages pages would exceed
+ * 2^50 bytes). */
 dkv_status kv_alloc_host(const dkv_shape *shape, int64_t n_pages, uint32_t flags,
                          dkv_pool **out);
 

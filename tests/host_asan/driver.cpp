@@ -58,7 +58,21 @@ int main() {
     EXPECT(kv_alloc_host(nullptr, 4, 0, &pool) == DKV_E_INVALID_ARG && pool == nullptr);
     EXPECT(kv_alloc_host(&s, 0, 0, &pool) == DKV_E_INVALID_ARG);
     EXPECT(kv_alloc_hbm(&bad, 4, &pool) == DKV_E_INVALID_ARG);
+    EXPECT(kv_alloc_host(&s, (int64_t)1 << 40, 0, &pool) == DKV_E_OUT_OF_MEMORY && pool == nullptr);
+    EXPECT(kv_alloc_hbm(&s, INT64_MAX, &pool) == DKV_E_OUT_OF_MEMORY && pool == nullptr);
     EXPECT(kv_pool_free(nullptr) == DKV_OK && kv_layout_free(nullptr) == DKV_OK);
+    // A pointer that no kv_layout_create returned is refused without being read.
+    int64_t not_a_layout[4] = {0, 0, 0, 0};
+    dkv_layout *stranger = reinterpret_cast<dkv_layout *>(not_a_layout);
+    int32_t tier = -7;
+    EXPECT(kv_layout_split_tokens(stranger) == 0 && kv_layout_split_kernel(stranger) == -1 &&
+           kv_layout_split_waves(stranger) == -1);
+    EXPECT(kv_layout_set_split_kernel(stranger, 0) == DKV_E_INVALID_ARG);
+    EXPECT(kv_layout_page_tier(stranger, 0, 0, &tier) == DKV_E_INVALID_ARG && tier == -7);
+    EXPECT(kv_layout_timing_enable(stranger, 1, 4) == DKV_E_INVALID_ARG);
+    EXPECT(kv_layout_timing_read(stranger, nullptr, nullptr, nullptr, nullptr) == DKV_E_INVALID_ARG);
+    EXPECT(kv_layout_check_status(stranger) == DKV_E_INVALID_ARG);
+    EXPECT(kv_layout_free(stranger) == DKV_E_INVALID_ARG);
     EXPECT(std::strlen(dkv_last_error()) > 0);
     dkv_layout *layout = nullptr;
     const int32_t cap1[1] = {4};
@@ -91,6 +105,9 @@ int main() {
     const void *holes[3] = {nullptr, nullptr, nullptr};
     const int32_t one[1] = {1};
     EXPECT(dkv_cpu_attention_pages(holes, 3, &s2, 1, q.data(), kn.data(), vn.data(), one, out.data(), 1,
+                                   nullptr) == DKV_E_INVALID_ARG);
+    const int32_t huge[1] = {INT32_MAX};                         // rounds up to pages without overflow
+    EXPECT(dkv_cpu_attention_pages(holes, 3, &s2, 1, q.data(), kn.data(), vn.data(), huge, out.data(), 1,
                                    nullptr) == DKV_E_INVALID_ARG);
     // Host-DRAM probe.
     std::vector<uint64_t> words(1 << 16);

@@ -1,12 +1,12 @@
 """Error paths of the C ABI that need a device: every one returns a status
 and a message before anything is enqueued, and leaves the library usable.
 
-Covered: double free of pools and layouts, calls on a freed layout or pool,
-a pool freed while a layout still holds its pages, null and misaligned
-pointers handed to decode_step, an HBM pool larger than HBM, unsupported
-shapes and bad capacities at layout creation. (A host pool larger than host
-memory is not exercised: pinning is not guaranteed to fail before it has
-touched memory.)"""
+Covered: double free of pools and layouts, calls (the accessors included) on
+a freed layout or pool, a pool freed while a layout still holds its pages,
+null and misaligned pointers handed to decode_step, an HBM pool larger than
+HBM, unsupported shapes and bad capacities at layout creation. (A host pool
+larger than host memory is not exercised: pinning is not guaranteed to fail
+before it has touched memory.)"""
 import ctypes
 
 import numpy as np
@@ -37,6 +37,13 @@ def test_double_free_and_use_after_free_are_refused():
     layout.free()
     assert L.kv_layout_free(h_layout) == E_INVALID_ARG      # freed twice
     assert L.kv_layout_check_status(h_layout) == E_INVALID_ARG
+    assert L.kv_layout_split_tokens(h_layout) == 0 and L.kv_layout_split_kernel(h_layout) == -1
+    assert L.kv_layout_split_waves(h_layout) == -1
+    assert L.kv_layout_set_split_kernel(h_layout, 0) == E_INVALID_ARG
+    tier = ctypes.c_int32(-7)
+    assert L.kv_layout_page_tier(h_layout, 0, 0, ctypes.byref(tier)) == E_INVALID_ARG and tier.value == -7
+    assert L.kv_layout_timing_enable(h_layout, 1, 4) == E_INVALID_ARG
+    assert L.kv_layout_timing_read(h_layout, None, None, None, None) == E_INVALID_ARG
     ctx = np.zeros(2, np.int32)
     assert L.kv_advance(h_layout, ctx.ctypes.data, None) == E_INVALID_ARG
     k = np.zeros((1, 4, 64), np.uint16)
