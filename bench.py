@@ -389,8 +389,8 @@ def projection_facts(wl, ms):
     """The QKV projection of one step (summed over layers): which kernel, its W
     read rate and its matrix-core use against the dense bf16 peak."""
     B = wl.batch
-    kernel = ("qkv_proj_gemv_kernel" if B < 8 else
-              "qkv_proj_stream_kernel" if B <= 16 else "qkv_proj_mfma_kernel")
+    kernel = ("qkv_proj_gemv_kernel" if B < 8 else "qkv_proj_stream_kernel" if B < 16 else
+              "qkv_proj_splitk_kernel + qkv_proj_finish_kernel")
     w_bytes = wl.n_qkv * wl.hidden * 2 * wl.n_layers
     flop = 2.0 * B * wl.hidden * wl.n_qkv * wl.n_layers
     return {"kernel": kernel, "ms": round(ms, 4), "W_bytes": w_bytes,

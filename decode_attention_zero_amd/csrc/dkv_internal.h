@@ -78,14 +78,22 @@ struct AdvanceArgs {
 
 hipError_t launch_advance(const AdvanceArgs &a, hipStream_t stream);
 
+// From this batch size the matrix-core projection splits the hidden dimension
+// into at most kProjMaxSplits ranges and adds their fp32 partials in a second
+// kernel; the partials take kProjMaxSplits * batch * n_qkv floats of
+// layout-owned scratch (`proj_part` below).
+constexpr int kProjSplitkMinBatch = 16;
+constexpr int kProjMaxSplits = 8;
+
 // Enqueues the decode step's kernels on `stream`. With `events` non-null,
 // records events[0] before the projection, events[1] after it, events[2]
-// after the split attention and events[3] after the combine.
-hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream, hipEvent_t *events);
+// after the split attention and events[3] after the combine. `proj_part` is
+// the projection's partial-sum scratch (null for batches that do not use it).
+hipError_t launch_decode_step(const StepArgs &a, float *proj_part, hipStream_t stream, hipEvent_t *events);
 
 // The three kernels of a step (each returns hipErrorInvalidValue for a shape
 // outside its compiled variants, before launching anything).
-hipError_t launch_projection(const StepArgs &a, hipStream_t stream);
+hipError_t launch_projection(const StepArgs &a, float *proj_part, hipStream_t stream);
 hipError_t launch_split(const StepArgs &a, hipStream_t stream);
 hipError_t launch_combine(const StepArgs &a, hipStream_t stream);
 

@@ -121,23 +121,10 @@ __global__ __launch_bounds__(64 * KS) void qkv_proj_gemv_kernel(StepArgs a) {
     }
 }
 
-// 1b. Larger batches: the projection is a dense [N_qkv x hidden] x [hidden x B]
-// contraction, done on the matrix cores with v_mfma_f32_16x16x32_bf16 (bf16
-// in, fp32 accumulate). Operand layout of the 16x16x32 MFMA: lane l supplies
+// Matrix-core operands below use the 16x16x32 MFMA layout: lane l supplies
 // A[i = l%16][k = 8*(l/16) .. +7] and B[k = 8*(l/16) .. +7][j = l%16], and
 // receives D[i = 4*(l/16) + r][j = l%16], r < 4. A is a W tile (W rows are
-// contiguous in k), B is x^T (x rows are contiguous in k), so both operands
-// are plain 16-byte loads from row-major memory.
-//
-// One wavefront owns 16 W rows x a 512-wide slice of k x up to 64 sequences
-// (NBT tiles of 16): it loads its W slice once (16 KiB, issued together with
-// the first sequence tile's x slice, all before the first MFMA) and keeps it
-// in registers while it walks the sequence tiles, the next tile's x slice
-// in flight during the current tile's 16 MFMAs. x is small and shared by
-// every workgroup, so it comes from L2; W crosses HBM once. The KS
-// wavefronts of a workgroup cover the hidden dimension (CH slices each) and
-// add their partial tiles through LDS in wave order, so the result does not
-// depend on timing. Batches above 64 take more workgroup columns.
+// contiguous in k, so a lane's operand is one 16-byte load), B is x^T.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -155,70 +142,7 @@ __device__ __forceinline__ void mfma_slice(f32x4 &acc, const uint4 (&w)[NK], con
                                                       __builtin_bit_cast(bf16x8, x[u]), acc, 0, 0, 0);
 }
 
-template <int KS, int NBT>
-__global__ __launch_bounds__(64 * KS) void qkv_proj_mfma_kernel(StepArgs a, int ch) {
-    constexpr int KSL = 512;            // k per slice
-    constexpr int NK = KSL / 32;        // MFMA k steps per slice
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int i = lane & 15;
-    const int kq = (lane >> 4) * 8;
-    const int row0 = blockIdx.x * 16;
-    const int b0 = blockIdx.y * 16 * NBT;
-
-    if (blockIdx.x == 0 && wave == 0)
-        for (int b = b0 + lane; b < min(a.batch, b0 + 16 * NBT); b += 64) check_context_range(a, b);
-
-    // Sequences past the batch read a valid row (the last one) and are never stored.
-    const uint16_t *wrow = a.w + (size_t)(row0 + i) * a.hidden + kq;
-    const uint16_t *xrow[NBT];
-#pragma unroll
-    for (int t = 0; t < NBT; ++t) xrow[t] = a.x + (size_t)min(b0 + 16 * t + i, a.batch - 1) * a.hidden + kq;
-
-    f32x4 acc[NBT];
-#pragma unroll
-    for (int t = 0; t < NBT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c = 0; c < ch; ++c) {
-        const int k0 = (wave * ch + c) * KSL;
-        uint4 wv[NK], xa[NK], xb[NK];
-        load_slice(wv, wrow, k0);
-        load_slice(xa, xrow[0], k0);
-        __builtin_amdgcn_sched_barrier(0);     // the slice's loads go out before the first MFMA
-#pragma unroll
-        for (int t = 0; t < NBT; t += 2) {
-            if (t + 1 < NBT) load_slice(xb, xrow[t + 1], k0);
-            mfma_slice(acc[t], wv, xa);
-            if (t + 1 < NBT) {
-                if (t + 2 < NBT) load_slice(xa, xrow[t + 2], k0);
-                mfma_slice(acc[t + 1], wv, xb);
-            }
-        }
-    }
-
-    if constexpr (KS > 1) {
-        __shared__ f32x4 partial[KS - 1][NBT][64];
-        if (wave > 0) {
-#pragma unroll
-            for (int t = 0; t < NBT; ++t) partial[wave - 1][t][lane] = acc[t];
-        }
-        __syncthreads();
-        if (wave != 0) return;
-#pragma unroll
-        for (int w = 1; w < KS; ++w)
-#pragma unroll
-            for (int t = 0; t < NBT; ++t) acc[t] += partial[w - 1][t][lane];
-    }
-#pragma unroll
-    for (int t = 0; t < NBT; ++t) {
-        const int b = b0 + 16 * t + i;
-        if (b < a.batch) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) store_projection(a, row0 + 4 * (lane >> 4) + r, b, acc[t][r]);
-        }
-    }
-}
-
-// 1c. One tile of up to 16 sequences: the same 16x16x32 MFMA tiles, but each
+// 1b. Batches of 8 to 15 sequences (one tile of 16): the same 16x16x32 MFMA tiles, but each
 // wavefront streams its 16 W rows over a k range of hidden / KSPLIT in
 // 256-wide chunks, the next chunk's W and x loads in flight while the
 // current chunk's 8 MFMAs run (register double buffer), so a few thousand
@@ -284,16 +208,152 @@ __global__ __launch_bounds__(64 * KSPLIT) void qkv_proj_stream_kernel(StepArgs a
     }
 }
 
-template <int KS>
-void launch_mfma(const StepArgs &a, int ch, hipStream_t st) {
-    const int nbt = (a.batch + 15) / 16;
-    if (nbt == 1) {
-        qkv_proj_mfma_kernel<KS, 1><<<dim3(a.n_qkv / 16, 1), 64 * KS, 0, st>>>(a, ch);
-    } else if (nbt == 2) {
-        qkv_proj_mfma_kernel<KS, 2><<<dim3(a.n_qkv / 16, 1), 64 * KS, 0, st>>>(a, ch);
-    } else {
-        qkv_proj_mfma_kernel<KS, 4><<<dim3(a.n_qkv / 16, (nbt + 3) / 4), 64 * KS, 0, st>>>(a, ch);
+// 1c. From 16 sequences: W crosses HBM once; what limits a plain tiling is
+// x. Every 16-row W tile needs the whole batch's x slice, so reading x per
+// wavefront from L2 costs B/16 times the W bytes (measured on MI355X at hidden
+// 4096: 19 -> 41 us from batch 16 to 64, linear in that x traffic, against
+// ~10 us for reading W alone). Here a workgroup of four wavefronts owns 64 W
+// rows (16 per wave) and one of KS equal ranges of the hidden dimension, and
+// walks its range in KC-wide chunks: each chunk of x (up to 64 sequences) is
+// staged once in LDS and read by all four waves, which cuts x's L2 traffic to
+// B/64 of W. The next x chunk is prefetched into registers and the next W
+// chunk is in flight (ping-pong register buffers) while the current chunk's
+// MFMAs run. Each workgroup writes its fp32 partial tile to layout-owned
+// scratch, and qkv_proj_finish_kernel adds the KS partials in range order and
+// stores q, k_new and v_new. Other ways of adding the partials measured
+// slower: the last workgroup of each row block to finish doing it (2-10x: its
+// device-scope fences write back the L2), one workgroup per row block holding
+// every range (~2x: 96 workgroups fill too few CUs), and the consumers adding
+// them when they read q (every split item re-reads KS partials: +4 % on the
+// all-HBM split kernel).
+constexpr int kProjRowBlocks = 4;        // 16-row W blocks per workgroup, one per wavefront
+
+// NBT tiles of 16 sequences (batch tile b0 = blockIdx.z * 16 * NBT), KC-wide chunks.
+template <int NBT, int KC>
+__global__ __launch_bounds__(64 * kProjRowBlocks) void qkv_proj_splitk_kernel(StepArgs a, float *part, int krange) {
+    constexpr int NT = 64 * kProjRowBlocks;
+    constexpr int NK = KC / 32;                 // MFMA k steps per chunk
+    constexpr int XROW = KC * 2 + 16;           // staged x row, bytes (padded by 16)
+    constexpr int XV = 16 * NBT * KC / 8;       // 16-byte pieces of one x chunk
+    constexpr int XPT = (XV + NT - 1) / NT;     // of those, per thread
+    __shared__ __attribute__((aligned(16))) char xs[16 * NBT][XROW];
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const int row0 = (blockIdx.x * kProjRowBlocks + wave) * 16;
+    const int ks = blockIdx.y;
+    const int b0 = blockIdx.z * 16 * NBT;
+    const int kb = ks * krange;
+    const int nch = krange / KC;
+    const uint16_t *wrow = a.w + (size_t)(row0 + i) * a.hidden + kb + kq;
+
+    // x chunk c: piece v is sequence b0 + v / (KC/8), k offset 8 * (v % (KC/8));
+    // sequences past the batch stage zeros (their columns are never stored).
+    uint4 xr[XPT];
+    auto load_x = [&](int c) {
+#pragma unroll
+        for (int j = 0; j < XPT; ++j) {
+            const int v = threadIdx.x + j * NT;
+            const int r = v / (KC / 8), cc = v % (KC / 8);
+            xr[j] = (v < XV && b0 + r < a.batch)
+                        ? *reinterpret_cast<const uint4 *>(a.x + (size_t)(b0 + r) * a.hidden + kb + c * KC + cc * 8)
+                        : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store_x = [&]() {
+#pragma unroll
+        for (int j = 0; j < XPT; ++j) {
+            const int v = threadIdx.x + j * NT;
+            if (v < XV) *reinterpret_cast<uint4 *>(&xs[v / (KC / 8)][(v % (KC / 8)) * 16]) = xr[j];
+        }
+    };
+
+    f32x4 acc[NBT];
+#pragma unroll
+    for (int t = 0; t < NBT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](const uint4 (&wv)[NK]) {
+#pragma unroll
+        for (int u = 0; u < NK; ++u)
+#pragma unroll
+            for (int t = 0; t < NBT; ++t) {
+                const uint4 xv = *reinterpret_cast<const uint4 *>(&xs[16 * t + i][(32 * u + kq) * 2]);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[u]),
+                                                                 __builtin_bit_cast(bf16x8, xv), acc[t], 0, 0, 0);
+            }
+    };
+
+    uint4 wa[NK], wb[NK];
+    load_slice(wa, wrow, 0);
+    load_x(0);
+    store_x();
+    __syncthreads();
+    if (nch > 1) {
+        load_slice(wb, wrow, KC);
+        load_x(1);
     }
+    // Chunk c from `cur` and the staged x; then x chunk c + 1 replaces it in
+    // LDS, and chunk c + 2's loads go out into `cur` and the x registers.
+    auto step = [&](uint4 (&cur)[NK], int c) {
+        compute(cur);
+        if (c + 1 < nch) {
+            __syncthreads();
+            store_x();
+            __syncthreads();
+        }
+        if (c + 2 < nch) {
+            load_slice(cur, wrow, (c + 2) * KC);
+            load_x(c + 2);
+        }
+    };
+    for (int c = 0; c < nch; c += 2) {
+        step(wa, c);
+        if (c + 1 < nch) step(wb, c + 1);
+    }
+
+#pragma unroll
+    for (int t = 0; t < NBT; ++t) {
+        const int b = b0 + 16 * t + i;
+        if (b < a.batch) {
+            float *pp = part + ((size_t)ks * a.batch + b) * a.n_qkv + row0 + 4 * (lane >> 4);
+            *reinterpret_cast<float4 *>(pp) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+        }
+    }
+}
+
+// Adds the KS partials of every output in range order and stores it (q scaled
+// in fp32, k_new / v_new rounded once to bf16). One thread per (sequence, row).
+__global__ __launch_bounds__(256) void qkv_proj_finish_kernel(StepArgs a, const float *part, int ksplit) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= a.batch * a.n_qkv) return;
+    const int b = idx / a.n_qkv, n = idx - b * a.n_qkv;
+    if (n == 0) check_context_range(a, b);
+    const size_t stride = (size_t)a.batch * a.n_qkv;
+    float y = part[idx];
+    for (int k = 1; k < ksplit; ++k) y += part[(size_t)k * stride + idx];
+    store_projection(a, n, b, y);
+}
+
+// Number of ranges of the hidden dimension: the largest of 8, 4, 2, 1 that
+// leaves whole KC-wide chunks and ranges of at least `min_range`.
+int splitk_ranges(int hidden, int kc, int min_range) {
+    for (int ks = kProjMaxSplits; ks > 1; ks >>= 1)
+        if (hidden % (ks * kc) == 0 && hidden / ks >= min_range) return ks;
+    return 1;
+}
+
+// Chunk width and minimum range per tile height, measured best on MI355X at
+// hidden 4096 and 8192: 128-wide chunks in ranges of 1024 for one 16-sequence
+// tile (4 ranges at hidden 4096), 256-wide chunks in ranges of 512 for two
+// and four (8 ranges).
+template <int NBT>
+void launch_splitk(const StepArgs &a, float *part, hipStream_t st) {
+    constexpr int KC = NBT == 1 ? 128 : 256;
+    const int ks = splitk_ranges(a.hidden, KC, NBT == 1 ? 1024 : 512);
+    const dim3 grid(a.n_qkv / (16 * kProjRowBlocks), ks, (a.batch + 16 * NBT - 1) / (16 * NBT));
+    qkv_proj_splitk_kernel<NBT, KC><<<grid, 64 * kProjRowBlocks, 0, st>>>(a, part, a.hidden / ks);
+    const int n = a.batch * a.n_qkv;
+    qkv_proj_finish_kernel<<<(n + 255) / 256, 256, 0, st>>>(a, part, ks);
 }
 
 template <int BT>
@@ -314,9 +374,9 @@ hipError_t launch_gemv(const StepArgs &a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_projection(const StepArgs &a, hipStream_t st) {
-    if (a.hidden % 512 != 0 || a.n_qkv % 16 != 0) return hipErrorInvalidValue;
-    if (a.batch >= a.proj_mfma_min_batch && a.batch <= 16) {
+hipError_t launch_projection(const StepArgs &a, float *part, hipStream_t st) {
+    if (a.hidden % 512 != 0 || a.n_qkv % (16 * kProjRowBlocks) != 0) return hipErrorInvalidValue;
+    if (a.batch >= a.proj_mfma_min_batch && a.batch < kProjSplitkMinBatch) {
         // One sequence tile: streamed over k by up to 4 wavefronts per row block.
         int ksplit = 4;
         while (ksplit > 1 && a.hidden % (256 * ksplit) != 0) ksplit >>= 1;
@@ -327,17 +387,10 @@ hipError_t launch_projection(const StepArgs &a, hipStream_t st) {
             default: qkv_proj_stream_kernel<4><<<grid, 256, 0, st>>>(a); break;
         }
     } else if (a.batch >= a.proj_mfma_min_batch) {
-        // Up to 8 wavefronts per workgroup over the 512-wide k slices.
-        const int n_slices = a.hidden / 512;
-        int ks = 8;
-        while (ks > 1 && n_slices % ks != 0) ks >>= 1;
-        const int ch = n_slices / ks;
-        switch (ks) {
-            case 1: launch_mfma<1>(a, ch, st); break;
-            case 2: launch_mfma<2>(a, ch, st); break;
-            case 4: launch_mfma<4>(a, ch, st); break;
-            default: launch_mfma<8>(a, ch, st); break;
-        }
+        if (!part) return hipErrorInvalidValue;
+        if (a.batch <= 16) launch_splitk<1>(a, part, st);
+        else if (a.batch <= 32) launch_splitk<2>(a, part, st);
+        else launch_splitk<4>(a, part, st);
     } else if (a.batch <= 4) {
         (void)launch_gemv<4>(a, st);
     } else if (a.batch <= 8) {

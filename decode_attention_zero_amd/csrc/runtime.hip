@@ -153,6 +153,7 @@ struct dkv_layout {
     uint16_t *d_kv_new;
     float *d_part_o;
     float2 *d_part_ml;
+    float *d_proj_part = nullptr;      // [kProjMaxSplits][batch][n_qkv] split-k projection partials
     uint32_t *d_status;
     // sliding hot window (kv_layout_create_windowed); windowed == 0 otherwise
     int32_t windowed = 0;
@@ -201,7 +202,7 @@ uint64_t page_addr(const dkv_pool *pool, int64_t idx) {
 
 void free_device(dkv_layout *L) {
     for (void *p : {(void *)L->d_page_table, (void *)L->d_capacity, (void *)L->d_q, (void *)L->d_kv_new,
-                    (void *)L->d_part_o, (void *)L->d_part_ml, (void *)L->d_status, (void *)L->d_host_pages,
+                    (void *)L->d_part_o, (void *)L->d_part_ml, (void *)L->d_proj_part, (void *)L->d_status, (void *)L->d_host_pages,
                     (void *)L->d_ring, (void *)L->d_window})
         if (p) (void)hipFree(p);
 }
@@ -349,13 +350,13 @@ bool pool_too_large(const dkv_shape *shape, int64_t n_pages) {
 
 namespace dkv {
 
-hipError_t launch_decode_step(const StepArgs &a, hipStream_t st, hipEvent_t *ev) {
+hipError_t launch_decode_step(const StepArgs &a, float *proj_part, hipStream_t st, hipEvent_t *ev) {
     const int G = a.n_q_heads / a.n_kv_heads;
     if (!((a.head_dim == 128 || a.head_dim == 64) && (G == 1 || G == 2 || G == 4 || G == 8)))
         return hipErrorInvalidValue;
     hipError_t e;
     if (ev) (void)hipEventRecord(ev[0], st);
-    if ((e = launch_projection(a, st)) != hipSuccess) return e;
+    if ((e = launch_projection(a, proj_part, st)) != hipSuccess) return e;
     if (ev) (void)hipEventRecord(ev[1], st);
     if ((e = launch_split(a, st)) != hipSuccess) return e;
     if (ev) (void)hipEventRecord(ev[2], st);
@@ -523,7 +524,9 @@ static void log_plan(const dkv_layout *L, int64_t n_host, int64_t n_hbm) {
     static const char *const kSplitNames[] = {"regs", "lds", "naive", "mfma"};
     const dkv_shape *s = &L->shape;
     const int B = L->batch;
-    const char *proj = B >= L->proj_mfma_min_batch ? (B <= 16 ? "mfma one-tile streamed" : "mfma tiled") : "gemv";
+    const char *proj = B < L->proj_mfma_min_batch ? "gemv"
+                       : B < dkv::kProjSplitkMinBatch ? "mfma one-tile streamed"
+                                                      : "mfma split-k (x staged in LDS) + partial sums";
     fprintf(stderr,
             "[dkv] layout: batch %d, hidden %d, heads %d/%d, head_dim %d, layers %d; pages per layer: "
             "%lld host, %lld HBM%s; split %d tokens (%d per sequence at most), split kernel %s on %s; "
@@ -575,6 +578,9 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
     const size_t bytes_kv = (size_t)batch * Hkv * 2 * D * sizeof(uint16_t);
     const size_t bytes_po = (size_t)batch * Hq * L->max_splits * D * sizeof(float);
     const size_t bytes_ml = (size_t)batch * Hq * L->max_splits * sizeof(float2);
+    const size_t bytes_pp = batch >= L->proj_mfma_min_batch && batch >= dkv::kProjSplitkMinBatch
+                                ? (size_t)dkv::kProjMaxSplits * batch * (Hq + 2 * Hkv) * D * sizeof(float)
+                                : 0;
     struct {
         void **ptr;
         size_t bytes;
@@ -584,6 +590,7 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
                   {(void **)&L->d_kv_new, bytes_kv},
                   {(void **)&L->d_part_o, bytes_po},
                   {(void **)&L->d_part_ml, bytes_ml},
+                  {(void **)&L->d_proj_part, bytes_pp},
                   {(void **)&L->d_status, 256},
                   {(void **)&L->d_host_pages, host_pages ? host_pages->size() * sizeof(uint64_t) : 0},
                   {(void **)&L->d_ring, ring ? ring->size() * sizeof(uint64_t) : 0},
@@ -1131,7 +1138,7 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     hipEvent_t *ev = nullptr;
     if (!L->timing_events.empty() && (size_t)(L->timing_recorded + 1) * 4 <= L->timing_events.size())
         ev = &L->timing_events[(size_t)L->timing_recorded++ * 4];
-    hipError_t e = dkv::launch_decode_step(a, reinterpret_cast<hipStream_t>(stream), ev);
+    hipError_t e = dkv::launch_decode_step(a, L->d_proj_part, reinterpret_cast<hipStream_t>(stream), ev);
     if (e != hipSuccess) return hip_fail(e, who);
     return DKV_OK;
 }

@@ -159,15 +159,16 @@ def test_split_and_page_edges(oracle, monkeypatch, split):
 
 # --------------------------------------------------------------------------- exactness
 @pytest.mark.parametrize("batch,mfma_from", [(3, None), (3, 1), (1, 1), (8, None), (16, None), (17, None),
-                                             (32, None), (40, None), (64, None)])
+                                             (32, None), (40, None), (64, None), (70, None)])
 def test_projection_integer_exact(oracle, monkeypatch, batch, mfma_from):
     """Small-integer x and W make every product and fp32 sum exact, so the
     written-back K/V must equal the oracle's fp64 values rounded to bf16, bit
     for bit; with an empty history attn_out is exactly bf16(v_new). Batches
     below 8 take the VALU projection by default (and the streamed one-tile
-    MFMA kernel with DKV_PROJ_MFMA_MIN_BATCH=1), 8 to 16 the one-tile MFMA
-    kernel, larger batches the MFMA one in 16-sequence tiles (17 and 40: a
-    partly filled last tile)."""
+    MFMA kernel with DKV_PROJ_MFMA_MIN_BATCH=1), 8 to 15 the one-tile MFMA
+    kernel; from 16 the split-k MFMA kernel stages x in tiles of 16, 32 or 64
+    sequences and a second kernel adds the partial sums (17, 40: a partly
+    filled tile; 70: a second 64-sequence tile)."""
     import synth
     if mfma_from is None:
         monkeypatch.delenv("DKV_PROJ_MFMA_MIN_BATCH", raising=False)
