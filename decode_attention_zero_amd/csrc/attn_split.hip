@@ -19,7 +19,8 @@
 namespace dkv {
 namespace {
 
-// VALU split attention. Work item (s, g, b) = blockIdx (x, y, z).
+// VALU split attention. Work item (KV head g, split s, sequence b) = blockIdx
+// (x, y, z) in the one-wavefront-per-item launches (XCD-aware order, see launch).
 //
 // Lane mapping inside a page run (K tile then V tile, each [16 tok][D] bf16):
 // wave load j reads bytes [j*1024, (j+1)*1024) of a tile, lane l the 16 bytes
@@ -483,7 +484,7 @@ __device__ __forceinline__ void split_item_mfma(const StepArgs &a, char *stage, 
     st.finish(a, b, h0, s);
 }
 
-// Matrix-core split kernels: one wavefront per work item (s, g, b) =
+// Matrix-core split kernels: one wavefront per work item (g, s, b) =
 // blockIdx (x, y, z), or (PER_QUERY_HEAD, G = 1) the naive comparator with
 // one item per query head; and the looping form for host-dominated layouts.
 constexpr int kMfmaWavesPerSimd = 3;   // register budget: 168 per lane
@@ -491,47 +492,58 @@ constexpr int kMfmaWavesPerSimd = 3;   // register budget: 168 per lane
 template <int D, int G, bool PER_QUERY_HEAD = false>
 __global__ __launch_bounds__(64, kMfmaWavesPerSimd) void attn_split_mfma_kernel(StepArgs a) {
     __shared__ __attribute__((aligned(16))) char stage[MfmaState<D, G>::STAGE];
-    const int g = PER_QUERY_HEAD ? blockIdx.y / (a.n_q_heads / a.n_kv_heads) : blockIdx.y;
-    const int h0 = PER_QUERY_HEAD ? blockIdx.y : blockIdx.y * G;
-    split_item_mfma<D, G>(a, stage, blockIdx.x, g, h0, blockIdx.z);
+    const int g = PER_QUERY_HEAD ? blockIdx.x / (a.n_q_heads / a.n_kv_heads) : blockIdx.x;
+    const int h0 = PER_QUERY_HEAD ? blockIdx.x : blockIdx.x * G;
+    split_item_mfma<D, G>(a, stage, blockIdx.y, g, h0, blockIdx.z);
 }
 
 // The looping form runs a few hundred wavefronts in all (one or two per CU),
-// so it may use the registers of a whole SIMD.
+// so it may use the registers of a whole SIMD; it takes its items from the
+// same queue as attn_split_persistent_kernel below.
 template <int D, int G>
 __global__ __launch_bounds__(64, 1) void attn_split_mfma_persistent_kernel(StepArgs a) {
     __shared__ __attribute__((aligned(16))) char stage[MfmaState<D, G>::STAGE];
+    __shared__ int item;
     const int n_items = a.n_kv_heads * a.max_splits * a.batch;
-    for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
+    for (;;) {
+        const int i = take_item(a, &item);
+        if (i >= n_items) break;
         const int g = i % a.n_kv_heads;
         const int rest = i / a.n_kv_heads;
         split_item_mfma<D, G>(a, stage, rest % a.max_splits, g, g * G, rest / a.max_splits);
     }
 }
 
-// One wavefront per work item (s, g, b) = blockIdx (x, y, z).
+// One wavefront per work item (g, s, b) = blockIdx (x, y, z).
 // PER_QUERY_HEAD (with G = 1) is the naive zero-copy comparator, not the
-// method: one work item per query head (blockIdx.y), so each KV head's pages
+// method: one work item per query head (blockIdx.x), so each KV head's pages
 // cross the link once per query head of its group (G times per step) instead
 // of once. Each head's arithmetic is the same as in the grouped kernel.
 template <int D, int G, int WPI, bool PER_QUERY_HEAD = false>
 __global__ __launch_bounds__(64 * WPI, WPI) void attn_split_kernel(StepArgs a) {
-    const int g = PER_QUERY_HEAD ? blockIdx.y / (a.n_q_heads / a.n_kv_heads) : blockIdx.y;
-    const int h0 = PER_QUERY_HEAD ? blockIdx.y : blockIdx.y * G;
-    split_item<D, G, WPI>(a, blockIdx.x, g, h0, blockIdx.z);
+    const int g = PER_QUERY_HEAD ? blockIdx.x / (a.n_q_heads / a.n_kv_heads) : blockIdx.x;
+    const int h0 = PER_QUERY_HEAD ? blockIdx.x : blockIdx.x * G;
+    split_item<D, G, WPI>(a, blockIdx.y, g, h0, blockIdx.z);
 }
 
-// The same work items on a fixed number of wavefronts (gridDim.x), each
-// taking items i, i + gridDim.x, ... in the order (KV head fastest, then
-// split, then sequence), so the waves in flight read the runs of the same
-// pages together. Bounding the waves in flight bounds the requests queued on
-// the host link, where too many outstanding reads lower its bandwidth (the
-// streaming-read probe drops from 57.5 to 56.0 GB/s when it keeps 8 MiB in
-// flight instead of 1 MiB). Each item is computed exactly as above.
+// The same work items on a fixed number of workgroups (gridDim.x), each
+// taking the next item from a shared queue (take_item) in the order (KV head
+// fastest, then split, then sequence), so the waves in flight read the runs
+// of the same pages together. Bounding the waves in flight bounds the
+// requests queued on the host link, where too many outstanding reads lower
+// its bandwidth (the streaming-read probe drops from 57.5 to 56.0 GB/s when
+// it keeps 8 MiB in flight instead of 1 MiB). Taking items as waves free up,
+// rather than every gridDim.x-th item, keeps ragged contexts balanced: with
+// 8192-token items of sequences of 8192 to 131072 tokens the fixed stride
+// left the link 1.3 % idle at the end of a step. Each item is computed
+// exactly as above, whichever wave takes it.
 template <int D, int G, int WPI>
 __global__ __launch_bounds__(64 * WPI, WPI) void attn_split_persistent_kernel(StepArgs a) {
+    __shared__ int item;
     const int n_items = a.n_kv_heads * a.max_splits * a.batch;
-    for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
+    for (;;) {
+        const int i = take_item(a, &item);
+        if (i >= n_items) break;
         const int g = i % a.n_kv_heads;
         const int rest = i / a.n_kv_heads;
         const int s = rest % a.max_splits;
@@ -579,7 +591,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void attn_split_lds_kernel(StepArgs 
     constexpr int LPP = 2 * NLD;               // DMA loads per page run
     __shared__ __attribute__((aligned(16))) char ring[NS][S::RUN];
 
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
     const int L = a.ctx_lens[b];
     if (L < 0 || L >= a.capacity[b]) return;
     const int t0 = s * a.split_tokens;
@@ -651,14 +663,24 @@ __global__ __launch_bounds__(64 * (NC + 1)) void attn_split_lds_kernel(StepArgs 
     st.finish(a, b, h0, s, dl);
 }
 
+// XCD-aware item order of the one-wavefront-per-item launches: the KV head is
+// the fastest grid dimension. Workgroups go to the GPU's 8 XCDs round-robin
+// in linear order, so with 8 KV heads each XCD (its own L2 and a fixed share
+// of the fabric bandwidth) serves one KV head, and every KV head carries the
+// same bytes whatever the sequences' lengths. With the split index fastest,
+// XCD k got splits s = k (mod 8): with ragged contexts every sequence has a
+// split 0 but only the long ones a split 7 or 15, so one XCD streamed 2.3x
+// the bytes of another (MI355X, batch 32, contexts U[8192, 131072], all in
+// HBM, 8192-token splits: 1.87 ms, the busiest XCD's bytes at 1/8 of the
+// chip's bandwidth).
 template <int D, int G>
 void launch(const StepArgs &a, hipStream_t st) {
     // Groups of 8 query heads share each work item between two wavefronts.
     constexpr int WPI = G >= 8 ? 2 : 1;
-    dim3 grid(a.max_splits, a.n_kv_heads, a.batch);
+    dim3 grid(a.n_kv_heads, a.max_splits, a.batch);
     if (a.split_variant == kSplitNaive) {
         // Per query head, with the arithmetic of the layout's grouped kernel.
-        const dim3 heads(a.max_splits, a.n_q_heads, a.batch);
+        const dim3 heads(a.n_q_heads, a.max_splits, a.batch);
         if (G >= kMfmaMinGroup) attn_split_mfma_kernel<D, 1, true><<<heads, 64, 0, st>>>(a);
         else attn_split_kernel<D, 1, WPI, true><<<heads, 64 * WPI, 0, st>>>(a);
     } else if (a.split_variant == kSplitMfma) {

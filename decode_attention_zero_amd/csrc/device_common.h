@@ -82,6 +82,25 @@ __device__ __forceinline__ float rescale(float x, float M) {
     return x == kNegInf ? 0.0f : fast_exp2(x - M);
 }
 
+// Work queue of the looping split kernels: the workgroup takes the next item
+// index (one atomic per item); every workgroup ends on an index past the last
+// item. The step's projection kernel zeroes the counter first (reset_items),
+// so the queue needs no memset and a captured step replays as it ran. Both
+// use system scope, which makes them go through to memory, so the workgroups
+// on all eight XCDs (each with its own L2) share one counter.
+__device__ __forceinline__ int take_item(const StepArgs &a, int *slot) {
+    __syncthreads();                   // the previous index has been read by every wave
+    if (threadIdx.x == 0)
+        *slot = (int)__hip_atomic_fetch_add(a.item_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __syncthreads();
+    return *slot;
+}
+
+__device__ __forceinline__ void reset_items(const StepArgs &a) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+        __hip_atomic_store(a.item_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Sequences whose ctx_lens entry is out of range raise the layout's flag.
 __device__ __forceinline__ void check_context_range(const StepArgs &a, int b) {
     const int L = a.ctx_lens[b];

@@ -57,6 +57,8 @@ struct StepArgs {
     float *part_o;            // [batch][Hq][max_splits][d] unnormalised outputs
     float2 *part_ml;          // [batch][Hq][max_splits] (running max, sum of weights)
     uint32_t *status;         // range flag (bit 0: a ctx_lens entry out of range)
+    uint32_t *item_counter;   // looping split kernels: next work item to take (zeroed by the
+                              // step's projection kernel before the split kernel runs)
 };
 
 // What kv_advance's kernel reads and writes (see kv_advance in dkv.h).

@@ -76,6 +76,7 @@ __global__ __launch_bounds__(64 * KS) void qkv_proj_gemv_kernel(StepArgs a) {
     const int kbeg = wave * krange;
 
     if (blockIdx.x == 0 && threadIdx.x < nb) check_context_range(a, b0 + threadIdx.x);
+    reset_items(a);
 
     float acc[NV];
 #pragma unroll
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void qkv_proj_stream_kernel(StepArgs a
     const int nch = krange / KC;
 
     if (blockIdx.x == 0 && wave == 0 && lane < a.batch) check_context_range(a, lane);
+    reset_items(a);
 
     // Lanes of sequences past the batch load nothing and feed zeros; their
     // columns are never stored.
@@ -328,6 +330,7 @@ __global__ __launch_bounds__(256) void qkv_proj_finish_kernel(StepArgs a, const 
     if (idx >= a.batch * a.n_qkv) return;
     const int b = idx / a.n_qkv, n = idx - b * a.n_qkv;
     if (n == 0) check_context_range(a, b);
+    reset_items(a);
     const size_t stride = (size_t)a.batch * a.n_qkv;
     float y = part[idx];
     for (int k = 1; k < ksplit; ++k) y += part[(size_t)k * stride + idx];

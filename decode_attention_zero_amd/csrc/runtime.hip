@@ -155,6 +155,7 @@ struct dkv_layout {
     float2 *d_part_ml;
     float *d_proj_part = nullptr;      // [kProjMaxSplits][batch][n_qkv] split-k projection partials
     uint32_t *d_status;
+    uint32_t *d_item_counter = nullptr;   // work queue of the looping split kernels
     // sliding hot window (kv_layout_create_windowed); windowed == 0 otherwise
     int32_t windowed = 0;
     std::vector<int32_t> window;       // HBM window pages per sequence
@@ -202,7 +203,7 @@ uint64_t page_addr(const dkv_pool *pool, int64_t idx) {
 
 void free_device(dkv_layout *L) {
     for (void *p : {(void *)L->d_page_table, (void *)L->d_capacity, (void *)L->d_q, (void *)L->d_kv_new,
-                    (void *)L->d_part_o, (void *)L->d_part_ml, (void *)L->d_proj_part, (void *)L->d_status, (void *)L->d_host_pages,
+                    (void *)L->d_part_o, (void *)L->d_part_ml, (void *)L->d_proj_part, (void *)L->d_status, (void *)L->d_item_counter, (void *)L->d_host_pages,
                     (void *)L->d_ring, (void *)L->d_window})
         if (p) (void)hipFree(p);
 }
@@ -234,12 +235,18 @@ int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, int32_t max_cap) 
         const int v = atoi(env);
         if (v >= DKV_PAGE_TOKENS && v % DKV_PAGE_TOKENS == 0) return v;
     }
-    // Enough work items to spread over 256 CUs, each at most 1024 tokens.
-    // Longer splits mean fewer partials to write and combine; with every page
-    // in HBM, 1024 measured faster than 512 and 256 (1 GiB at batch 8:
-    // 0.178 / 0.181 / 0.189 ms; 4 GiB at batch 64: 0.686 / 0.712 / 0.728 ms).
+    // The longest split (at most 8192 tokens) that still leaves at least 2048
+    // work items to spread over 256 CUs. A longer split is a longer
+    // contiguous page stream per wavefront, fewer partials to write and
+    // combine, and fewer waves starting up; with every page in HBM on MI355X
+    // (one wave per item): 1 GiB at batch 8 (2048 items at 1024 tokens),
+    // 1024 / 2048 / 4096 tokens: 0.169 / 0.198 / 0.297 ms (too few items);
+    // an 8 GiB layer at batch 16, 131072 tokens, group 8: 1024 / 2048 / 8192
+    // tokens: 1.415 / 1.348 / 1.252 ms (6.07 -> 6.86 TB/s), group 4: 1.40 /
+    // 1.35 / 1.25-1.31 ms. The choice depends on the shape and capacities
+    // only, never on placement.
     const int64_t max_cached = std::max(1, max_cap - 1);
-    int32_t t = 1024;
+    int32_t t = 8192;
     while (t > DKV_PAGE_TOKENS &&
            (int64_t)batch * n_kv_heads * ((max_cached + t - 1) / t) < 2048)
         t /= 2;
@@ -572,6 +579,13 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
         delete L;
         return st;
     };
+    // The one-wavefront-per-item launches put the splits of a sequence in
+    // grid dimension y (at most 65535).
+    if (L->max_splits > 65535) {
+        fail(DKV_E_UNSUPPORTED, "kv_layout_create: %d splits per sequence (capacity / split size) exceed 65535",
+             L->max_splits);
+        return cleanup(DKV_E_UNSUPPORTED);
+    }
     const int D = shape->head_dim, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads;
     const size_t n_entries = table.size();
     const size_t bytes_q = (size_t)batch * Hq * D * sizeof(float);
@@ -592,6 +606,7 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
                   {(void **)&L->d_part_ml, bytes_ml},
                   {(void **)&L->d_proj_part, bytes_pp},
                   {(void **)&L->d_status, 256},
+                  {(void **)&L->d_item_counter, 256},
                   {(void **)&L->d_host_pages, host_pages ? host_pages->size() * sizeof(uint64_t) : 0},
                   {(void **)&L->d_ring, ring ? ring->size() * sizeof(uint64_t) : 0},
                   {(void **)&L->d_window, L->windowed ? (size_t)batch * sizeof(int32_t) : 0}};
@@ -616,6 +631,7 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
         e = hipMemcpy(L->d_window, L->window.data(), (size_t)batch * sizeof(int32_t), hipMemcpyHostToDevice);
     }
     if (e == hipSuccess) e = hipMemset(L->d_status, 0, 256);
+    if (e == hipSuccess) e = hipMemset(L->d_item_counter, 0, 256);
     if (e == hipSuccess) e = hipMemset(L->d_kv_new, 0, bytes_kv);
     if (e != hipSuccess) {
         hip_fail(e, "kv_layout_create: initialising device tables");
@@ -1135,6 +1151,7 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     a.part_o = L->d_part_o;
     a.part_ml = L->d_part_ml;
     a.status = L->d_status;
+    a.item_counter = L->d_item_counter;
     hipEvent_t *ev = nullptr;
     if (!L->timing_events.empty() && (size_t)(L->timing_recorded + 1) * 4 <= L->timing_events.size())
         ev = &L->timing_events[(size_t)L->timing_recorded++ * 4];
