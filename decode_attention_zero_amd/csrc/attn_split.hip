@@ -486,15 +486,18 @@ __device__ __forceinline__ void split_item_mfma(const StepArgs &a, char *stage, 
 
 // Matrix-core split kernels: one wavefront per work item (g, s, b) =
 // blockIdx (x, y, z), or (PER_QUERY_HEAD, G = 1) the naive comparator with
-// one item per query head; and the looping form for host-dominated layouts.
+// one item per query head, (s, h, b) = blockIdx (x, y, z); and the looping form for host-dominated layouts.
 constexpr int kMfmaWavesPerSimd = 3;   // register budget: 168 per lane
 
 template <int D, int G, bool PER_QUERY_HEAD = false>
 __global__ __launch_bounds__(64, kMfmaWavesPerSimd) void attn_split_mfma_kernel(StepArgs a) {
     __shared__ __attribute__((aligned(16))) char stage[MfmaState<D, G>::STAGE];
-    const int g = PER_QUERY_HEAD ? blockIdx.x / (a.n_q_heads / a.n_kv_heads) : blockIdx.x;
-    const int h0 = PER_QUERY_HEAD ? blockIdx.x : blockIdx.x * G;
-    split_item_mfma<D, G>(a, stage, blockIdx.y, g, h0, blockIdx.z);
+    // The naive comparator keeps a plain (split, query head, sequence) order.
+    const int head = PER_QUERY_HEAD ? blockIdx.y : blockIdx.x;
+    const int s = PER_QUERY_HEAD ? blockIdx.x : blockIdx.y;
+    const int g = PER_QUERY_HEAD ? head / (a.n_q_heads / a.n_kv_heads) : head;
+    const int h0 = PER_QUERY_HEAD ? head : head * G;
+    split_item_mfma<D, G>(a, stage, s, g, h0, blockIdx.z);
 }
 
 // The looping form runs a few hundred wavefronts in all (one or two per CU),
@@ -516,14 +519,16 @@ __global__ __launch_bounds__(64, 1) void attn_split_mfma_persistent_kernel(StepA
 
 // One wavefront per work item (g, s, b) = blockIdx (x, y, z).
 // PER_QUERY_HEAD (with G = 1) is the naive zero-copy comparator, not the
-// method: one work item per query head (blockIdx.x), so each KV head's pages
+// method: one work item per query head (s, h, b) = blockIdx (x, y, z), so each KV head's pages
 // cross the link once per query head of its group (G times per step) instead
 // of once. Each head's arithmetic is the same as in the grouped kernel.
 template <int D, int G, int WPI, bool PER_QUERY_HEAD = false>
 __global__ __launch_bounds__(64 * WPI, WPI) void attn_split_kernel(StepArgs a) {
-    const int g = PER_QUERY_HEAD ? blockIdx.x / (a.n_q_heads / a.n_kv_heads) : blockIdx.x;
-    const int h0 = PER_QUERY_HEAD ? blockIdx.x : blockIdx.x * G;
-    split_item<D, G, WPI>(a, blockIdx.y, g, h0, blockIdx.z);
+    const int head = PER_QUERY_HEAD ? blockIdx.y : blockIdx.x;
+    const int s = PER_QUERY_HEAD ? blockIdx.x : blockIdx.y;
+    const int g = PER_QUERY_HEAD ? head / (a.n_q_heads / a.n_kv_heads) : head;
+    const int h0 = PER_QUERY_HEAD ? head : head * G;
+    split_item<D, G, WPI>(a, s, g, h0, blockIdx.z);
 }
 
 // The same work items on a fixed number of workgroups (gridDim.x), each
@@ -680,7 +685,7 @@ void launch(const StepArgs &a, hipStream_t st) {
     dim3 grid(a.n_kv_heads, a.max_splits, a.batch);
     if (a.split_variant == kSplitNaive) {
         // Per query head, with the arithmetic of the layout's grouped kernel.
-        const dim3 heads(a.n_q_heads, a.max_splits, a.batch);
+        const dim3 heads(a.max_splits, a.n_q_heads, a.batch);
         if (G >= kMfmaMinGroup) attn_split_mfma_kernel<D, 1, true><<<heads, 64, 0, st>>>(a);
         else attn_split_kernel<D, 1, WPI, true><<<heads, 64 * WPI, 0, st>>>(a);
     } else if (a.split_variant == kSplitMfma) {
