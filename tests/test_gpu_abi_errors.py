@@ -4,7 +4,8 @@ and a message before anything is enqueued, and leaves the library usable.
 Covered: double free of pools and layouts, calls (the accessors included) on
 a freed layout or pool, a pool freed while a layout still holds its pages,
 null and misaligned pointers handed to decode_step, an HBM pool larger than
-HBM, unsupported shapes and bad capacities at layout creation. (A host pool
+HBM, unsupported shapes and bad capacities at layout creation, more splits
+per sequence than a launch grid holds. (A host pool
 larger than host memory is not exercised: pinning is not guaranteed to fail
 before it has touched memory.)"""
 import ctypes
@@ -122,6 +123,31 @@ def test_layout_creation_errors():
                                   None, ctypes.byref(out)) == E_UNSUPPORTED
     finally:
         host.free()
+
+
+def test_too_many_splits_per_sequence_is_unsupported(monkeypatch):
+    """Splits of a sequence are a launch-grid dimension (at most 65535): a
+    layout whose capacity needs more (here 16-token splits of 1,048,592
+    tokens, 65,537 splits) is refused at creation, its pages given back; one
+    split fewer is accepted."""
+    L = dkv.lib()
+    monkeypatch.setenv("DKV_SPLIT_TOKENS", "16")
+    shape = dkv.Shape.of(512, 8, 8, 64, 1)                # 32 KiB pages
+    n_pages = 65537 + 1                                   # cached tokens / 16, plus the fresh slot's page
+    pool = dkv.kv_alloc_hbm(shape, n_pages)
+    try:
+        out = ctypes.c_void_p()
+        cap = np.array([65537 * 16 + 1], np.int32)
+        assert L.kv_layout_create(ctypes.byref(shape), 1, cap.ctypes.data, cap.ctypes.data, None, pool.handle,
+                                  ctypes.byref(out)) == E_UNSUPPORTED
+        assert "65535" in L.dkv_last_error().decode()
+        assert out.value is None and pool.free_pages() == n_pages
+        ok = dkv.kv_layout_create(shape, np.array([65535 * 16 + 1], np.int32), np.array([1 << 30], np.int32),
+                                  None, pool)
+        assert ok.split_tokens == 16
+        ok.free()
+    finally:
+        pool.free()
 
 
 def test_plan_log(monkeypatch, capfd):
