@@ -238,7 +238,10 @@ dkv_status kv_read(const dkv_layout *layout, int32_t layer, int32_t seq,
  * on the device, so its range is checked by the kernels: a sequence with
  * ctx_lens[b] < 0 or ctx_lens[b] >= its capacity writes nothing to the
  * cache, gets attn_out rows of NaN, and raises the flag that
- * kv_layout_check_status reports. */
+ * kv_layout_check_status reports. A layout's steps share its scratch (the
+ * projection's output, the split partials and the work queue of the
+ * looping split kernel), so steps of one layout must be ordered (one stream,
+ * or events between streams); steps of different layouts may overlap. */
 dkv_status decode_step(dkv_layout *kv_layout, int32_t layer,
                        const uint16_t *q_in, const uint16_t *W_qkv,
                        const int32_t *ctx_lens, uint16_t *attn_out,
