@@ -158,9 +158,11 @@ def test_split_and_page_edges(oracle, monkeypatch, split):
 
 
 # --------------------------------------------------------------------------- exactness
-@pytest.mark.parametrize("batch,mfma_from", [(3, None), (3, 1), (1, 1), (8, None), (16, None), (17, None),
-                                             (32, None), (40, None), (64, None), (70, None)])
-def test_projection_integer_exact(oracle, monkeypatch, batch, mfma_from):
+@pytest.mark.parametrize("shape_name,batch,mfma_from", [
+    ("llama8b", 3, None), ("llama8b", 3, 1), ("llama8b", 1, 1), ("llama8b", 8, None), ("llama8b", 16, None),
+    ("llama8b", 17, None), ("llama8b", 32, None), ("llama8b", 40, None), ("llama8b", 64, None),
+    ("llama8b", 70, None), ("llama70b", 16, None), ("llama70b", 33, None)])
+def test_projection_integer_exact(oracle, monkeypatch, shape_name, batch, mfma_from):
     """Small-integer x and W make every product and fp32 sum exact, so the
     written-back K/V must equal the oracle's fp64 values rounded to bf16, bit
     for bit; with an empty history attn_out is exactly bf16(v_new). Batches
@@ -168,13 +170,15 @@ def test_projection_integer_exact(oracle, monkeypatch, batch, mfma_from):
     MFMA kernel with DKV_PROJ_MFMA_MIN_BATCH=1), 8 to 15 the one-tile MFMA
     kernel; from 16 the split-k MFMA kernel stages x in tiles of 16, 32 or 64
     sequences and a second kernel adds the partial sums (17, 40: a partly
-    filled tile; 70: a second 64-sequence tile)."""
+    filled tile; 70: a second 64-sequence tile). The Llama-3-70B shape
+    (hidden 8192) splits the hidden dimension into 8 ranges."""
     import synth
     if mfma_from is None:
         monkeypatch.delenv("DKV_PROJ_MFMA_MIN_BATCH", raising=False)
     else:
         monkeypatch.setenv("DKV_PROJ_MFMA_MIN_BATCH", str(mfma_from))
-    wl = configs.LLAMA8B_HOST.replace(batch=batch)
+    base = configs.LLAMA8B_HOST if shape_name == "llama8b" else configs.LLAMA70B_LONG
+    wl = base.replace(batch=batch, n_layers=1)
     ctx = np.array([[0, 5, 16][b % 3] for b in range(batch)], np.int32)
     xi = synth.int_bf16(99, 20, 0, wl.batch * wl.hidden, -4, 4).reshape(wl.batch, wl.hidden)
     Wi = synth.int_bf16(99, 21, 0, wl.n_qkv * wl.hidden, -4, 4).reshape(wl.n_qkv, wl.hidden)
