@@ -135,65 +135,92 @@ __device__ __forceinline__ void load_slice(uint4 (&v)[NK], const uint16_t *row, 
     for (int u = 0; u < NK; ++u) v[u] = *reinterpret_cast<const uint4 *>(row + k0 + 32 * u);
 }
 
-template <int NK>
-__device__ __forceinline__ void mfma_slice(f32x4 &acc, const uint4 (&w)[NK], const uint4 (&x)[NK]) {
-#pragma unroll
-    for (int u = 0; u < NK; ++u)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[u]),
-                                                      __builtin_bit_cast(bf16x8, x[u]), acc, 0, 0, 0);
-}
-
-// 1b. Batches of 8 to 15 sequences (one tile of 16): the same 16x16x32 MFMA tiles, but each
-// wavefront streams its 16 W rows over a k range of hidden / KSPLIT in
-// 256-wide chunks, the next chunk's W and x loads in flight while the
-// current chunk's 8 MFMAs run (register double buffer), so a few thousand
-// wavefronts keep W streaming from HBM for the whole launch instead of
-// issuing one burst each. The KSPLIT wavefronts of a workgroup share the 16
-// rows and add their partial tiles through LDS in wave order.
+// 1b. Batches of 8 to 15 sequences (one tile of 16): each workgroup owns 16 W
+// rows; its KSPLIT wavefronts split the hidden dimension into equal ranges,
+// and each walks its range in 128-wide chunks. A wave stages its x chunk (the
+// 16 sequences' 128 k values, loaded as contiguous 256-byte row pieces; rows
+// past the batch as zeros) in its own LDS slot and reads the MFMA B operands
+// from there; the next x chunk is prefetched into registers and the next W
+// chunk is in flight (ping-pong registers) while the current chunk's MFMAs
+// run. The KSPLIT partial tiles are added through LDS in wave order. (Loading
+// the x operand straight from L2 in the MFMA layout, 16 rows x 64 B per load,
+// measured 17.7 us for the projection of a decode step at batch 8 and hidden
+// 4096, HIP events, against 14.5 us this way; at hidden 8192 the two are
+// within 5 %. The MFMA k order, and so every bit, is the same.)
 template <int KSPLIT>
 __global__ __launch_bounds__(64 * KSPLIT) void qkv_proj_stream_kernel(StepArgs a) {
-    constexpr int KC = 256;             // k per chunk
+    constexpr int KC = 128;             // k per chunk
     constexpr int NK = KC / 32;         // MFMA k steps per chunk
+    constexpr int XROW = KC * 2 + 16;   // staged x row, bytes (padded by 16)
+    constexpr int XPT = 16 * KC / 8 / 64;   // 16-byte x pieces per lane per chunk
+    __shared__ __attribute__((aligned(16))) char xs[KSPLIT][16][XROW];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int i = lane & 15;
     const int kq = (lane >> 4) * 8;
     const int row0 = blockIdx.x * 16;
-    const int krange = a.hidden / KSPLIT;      // a multiple of 256 (checked at launch)
+    const int krange = a.hidden / KSPLIT;      // a multiple of 128 (checked at launch)
+    const int kb = wave * krange;
     const int nch = krange / KC;
 
     if (blockIdx.x == 0 && wave == 0 && lane < a.batch) check_context_range(a, lane);
     reset_items(a);
 
-    // Lanes of sequences past the batch load nothing and feed zeros; their
-    // columns are never stored.
-    const bool live = i < a.batch;
-    const uint16_t *wrow = a.w + (size_t)(row0 + i) * a.hidden + wave * krange + kq;
-    const uint16_t *xrow = a.x + (size_t)min(i, a.batch - 1) * a.hidden + wave * krange + kq;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    uint4 wa[NK], xa[NK], wb[NK], xb[NK];
-    auto load_x = [&](uint4 (&v)[NK], int k0) {
-        if (live) load_slice(v, xrow, k0);
-        else {
+    const uint16_t *wrow = a.w + (size_t)(row0 + i) * a.hidden + kb + kq;
+    char *xw = xs[wave][0];
+    uint4 xr[XPT];
+    auto load_x = [&](int c) {
 #pragma unroll
-            for (int u = 0; u < NK; ++u) v[u] = make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < XPT; ++j) {
+            const int v = lane + 64 * j;
+            const int r = v / (KC / 8), cc = v % (KC / 8);
+            xr[j] = r < a.batch ? *reinterpret_cast<const uint4 *>(a.x + (size_t)r * a.hidden + kb + c * KC + cc * 8)
+                                : make_uint4(0u, 0u, 0u, 0u);
         }
     };
+    auto store_x = [&]() {
+#pragma unroll
+        for (int j = 0; j < XPT; ++j) {
+            const int v = lane + 64 * j;
+            *reinterpret_cast<uint4 *>(xw + (v / (KC / 8)) * XROW + (v % (KC / 8)) * 16) = xr[j];
+        }
+    };
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](const uint4 (&wv)[NK]) {
+#pragma unroll
+        for (int u = 0; u < NK; ++u) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(xw + i * XROW + (32 * u + kq) * 2);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[u]),
+                                                          __builtin_bit_cast(bf16x8, xv), acc, 0, 0, 0);
+        }
+    };
+
+    uint4 wa[NK], wb[NK];
     load_slice(wa, wrow, 0);
-    load_x(xa, 0);
+    load_x(0);
+    store_x();
+    __syncthreads();
+    if (nch > 1) {
+        load_slice(wb, wrow, KC);
+        load_x(1);
+    }
+    // Chunk c from `cur` and the staged x; then x chunk c + 1 replaces it in
+    // LDS, and chunk c + 2's loads go out into `cur` and the x registers.
+    auto step = [&](uint4 (&cur)[NK], int c) {
+        compute(cur);
+        if (c + 1 < nch) {
+            __syncthreads();
+            store_x();
+            __syncthreads();
+        }
+        if (c + 2 < nch) {
+            load_slice(cur, wrow, (c + 2) * KC);
+            load_x(c + 2);
+        }
+    };
     for (int c = 0; c < nch; c += 2) {
-        if (c + 1 < nch) {
-            load_slice(wb, wrow, (c + 1) * KC);
-            load_x(xb, (c + 1) * KC);
-        }
-        mfma_slice(acc, wa, xa);
-        if (c + 1 < nch) {
-            if (c + 2 < nch) {
-                load_slice(wa, wrow, (c + 2) * KC);
-                load_x(xa, (c + 2) * KC);
-            }
-            mfma_slice(acc, wb, xb);
-        }
+        step(wa, c);
+        if (c + 1 < nch) step(wb, c + 1);
     }
 
     if constexpr (KSPLIT > 1) {
@@ -213,8 +240,8 @@ __global__ __launch_bounds__(64 * KSPLIT) void qkv_proj_stream_kernel(StepArgs a
 // 1c. From 16 sequences: W crosses HBM once; what limits a plain tiling is
 // x. Every 16-row W tile needs the whole batch's x slice, so reading x per
 // wavefront from L2 costs B/16 times the W bytes (measured on MI355X at hidden
-// 4096: 19 -> 41 us from batch 16 to 64, linear in that x traffic, against
-// ~10 us for reading W alone). Here a workgroup of four wavefronts owns 64 W
+// 4096: 19 -> 41 us from batch 16 to 64, linear in that x traffic; W alone is
+// 6.3 us at 8 TB/s). Here a workgroup of four wavefronts owns 64 W
 // rows (16 per wave) and one of KS equal ranges of the hidden dimension, and
 // walks its range in KC-wide chunks: each chunk of x (up to 64 sequences) is
 // staged once in LDS and read by all four waves, which cuts x's L2 traffic to
@@ -382,7 +409,7 @@ hipError_t launch_projection(const StepArgs &a, float *part, hipStream_t st) {
     if (a.batch >= a.proj_mfma_min_batch && a.batch < kProjSplitkMinBatch) {
         // One sequence tile: streamed over k by up to 4 wavefronts per row block.
         int ksplit = 4;
-        while (ksplit > 1 && a.hidden % (256 * ksplit) != 0) ksplit >>= 1;
+        while (ksplit > 1 && a.hidden % (128 * ksplit) != 0) ksplit >>= 1;
         const dim3 grid(a.n_qkv / 16);
         switch (ksplit) {
             case 1: qkv_proj_stream_kernel<1><<<grid, 64, 0, st>>>(a); break;
