@@ -400,6 +400,33 @@ def projection_facts(wl, ms):
                                  if kernel != "qkv_proj_gemv_kernel" else None)}
 
 
+def window_only_leg(dkv, wl, ctx, tail, kv_source, args):
+    """The HBM-resident window of a hybrid placement timed alone: a layout
+    holding, for each sequence, as many cached tokens as its window has, every
+    page in HBM, stepped like the workload. Returns the split kernel's time
+    and rate on those bytes (a timing run: the tokens are the sequence's
+    first ones, so the outputs are not the workload's)."""
+    win = np.zeros(len(ctx), np.int32)
+    for b in range(len(ctx)):
+        n, first = dkv.kv_placement(int(ctx[b]) + 1, int(tail[b]))
+        win[b] = int(ctx[b]) - min(int(ctx[b]), first * dkv.PAGE_TOKENS)
+    if int(win.min()) <= 0:
+        return None
+    log("HBM window alone: %d-%d tokens per sequence" % (int(win.min()), int(win.max())))
+    rw = Resident(dkv, wl, win, np.full(len(ctx), 1 << 30, np.int32), kv_source)
+    steps = max(args.steps, 50) if wl.n_layers == 1 else args.steps
+    ms_w = rw.timed(steps, args.warmup)
+    kt_w = rw.kernel_times(steps)
+    split_tokens = rw.layout.split_tokens
+    rw.free()
+    w_bytes = int(win.astype(np.int64).sum()) * wl.kv_bytes_per_token * wl.n_layers
+    gbps = w_bytes / (kt_w["split"] * 1e-3) / 1e9
+    return {"tokens_per_sequence": [int(win.min()), int(win.max())], "kv_bytes_per_step": w_bytes,
+            "split_tokens": split_tokens, "ms_per_step": round(ms_w, 4),
+            "split_kernel_ms": round(kt_w["split"], 4), "split_kernel_GBps": round(gbps, 1),
+            "split_kernel_frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def split_kernel_label(layout) -> str:
     """Name of the split-attention kernel a layout launches, and its wavefronts."""
     mfma = layout.split_kernel == "mfma"
@@ -829,6 +856,10 @@ def main(argv=None):
             "bit_identical_to_own_placement": bool(np.array_equal(out_own, out_hbm)),
         }
         log("HBM leg: %.4f ms/step, split kernel %.1f GB/s" % (ms_h, hbm["split_kernel_GBps"]))
+
+        # -------------------------------------------------------------- the HBM window alone
+        if host_kv > 0 and hbm_kv > 0 and not args.no_comparators:
+            hbm["window_only"] = window_only_leg(dkv, wl, ctx, tail, kv_source, args)
 
         # -------------------------------------------------------------- comparator: staging
         if r.hbm_pool is None and r.host_pool is not None and not args.no_comparators:
