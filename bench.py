@@ -928,6 +928,8 @@ def main(argv=None):
                   "gates": {"max_abs": 2e-2, "rel_l2": 5e-3}}
 
     t_star = max(host_kv / (ceiling * 1e9) if ceiling else 0.0, hbm_kv / (HBM_PEAK_GBPS * 1e9))
+    # The same two streams one after the other (the serial reading of the combined roofline).
+    t_serial = (host_kv / (ceiling * 1e9) if ceiling else 0.0) + hbm_kv / (HBM_PEAK_GBPS * 1e9)
     placement = ("100% host-pinned, read in place" if hbm_kv == 0 else
                  "%.1f%% host-pinned (read in place) / %.1f%% HBM" %
                  (100.0 * host_kv / kv_bytes, 100.0 * hbm_kv / kv_bytes))
@@ -962,7 +964,9 @@ def main(argv=None):
                      if ceiling else None,
                      "split_kernel_ms": round(kt["split"], 4)},
         "combined_roofline": {"t_star_ms": round(t_star * 1e3, 4),
-                              "frac": round(t_star * 1e3 / ms, 4) if t_star else None},
+                              "frac": round(t_star * 1e3 / ms, 4) if t_star else None,
+                              "serial_ms": round(t_serial * 1e3, 4),
+                              "frac_of_serial": round(t_serial * 1e3 / ms, 4) if t_serial else None},
         "kernel_ms": {k: round(v, 4) for k, v in kt.items()},
         "projection": projection_facts(wl, kt["projection"]),
         "host_link_probe": ceiling_rows,
