@@ -427,20 +427,26 @@ struct MfmaState {
 
         // O^T += V^T P^T: A = V^T (dim = col, tokens 4kq .. 4kq+3), B = P^T; in
         // groups of four 16-dim blocks, so that only one group's V reads are
-        // held in registers at a time.
-        const char *vt = lds + STILE + 4 * kq * ROW + 2 * col;
+        // held in registers at a time. The A operand comes from one transposing
+        // LDS read (ds_read_b64_tr_b16) per block: within each 16-lane group,
+        // lane i receives element i % 4 of the 8-byte pieces addressed by lanes
+        // i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 (measured on gfx950), so
+        // lane j of row group kq addresses dims 16n + 4 (j % 4) .. +3 of token
+        // 4kq + j / 4, and lane col gets dim 16n + col of tokens 4kq .. 4kq+3.
+        const char *vtr = lds + STILE + (4 * kq + (col >> 2)) * ROW + (col & 3) * 8;
 #pragma unroll
         for (int n0 = 0; n0 < NDB; n0 += 4) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int n = n0; n < n0 + 4; ++n) {
-                s16x4 vop;
+                s16x4 vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(vtr + n * 32));
+                if (PARTIAL) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    vop[r] = *reinterpret_cast<const short *>(vt + r * ROW + n * 32);
-                    // Slots past the valid tokens may hold any bits (NaN times a zero
-                    // weight would still be NaN).
-                    if (PARTIAL && 4 * kq + r >= n_valid) vop[r] = 0;
+                    for (int r = 0; r < 4; ++r)
+                        // Slots past the valid tokens may hold any bits (NaN times a
+                        // zero weight would still be NaN).
+                        if (4 * kq + r >= n_valid) vop[r] = 0;
                 }
                 o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, o[n], 0, 0, 0);
             }
