@@ -5,13 +5,13 @@
 // rounded once to bf16. The projection that produces the new token's K/V is
 // part of the decode step, as in the core-method section of the DirectKV
 // digest ("长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）"); the step is bound
-// by reading W from HBM at every batch size here, so both variants are built
-// to stream W once at full bandwidth.
+// by reading W from HBM at every batch size here, so each of the three forms
+// (1a VALU GEMV below batch 8, 1b one 16-sequence MFMA tile up to batch 15,
+// 1c split-k MFMA from batch 16) is built to stream W once at full bandwidth.
 #include "device_common.h"
 
 namespace dkv {
 namespace {
-
 
 __device__ __forceinline__ void store_projection(const StepArgs &a, int n, int b, float y) {
     const int D = a.head_dim;
