@@ -471,6 +471,85 @@ def cpu_attention_timed(dkv, r, wl, ctx, threads, reps):
     return float(np.median(times)), used
 
 
+def cpu_gpu_split(dkv, wl, ctx, kv_source, K_all, V_all, ms_gpu_all, cpu_s_all, threads, steps):
+    """The batch split between the two readers of host memory: the first k
+    sequences' attention on `threads` host threads over their pages in host
+    DRAM, the other B - k sequences' decode step on the GPU reading their
+    pages over the host link, at the same time. k balances the two from their
+    separate full-batch times. Pages for the CPU side are built in the
+    library's page layout from the same logical K/V, in pinned host memory;
+    queries and fresh K/V are seeded inputs, as in the CPU comparator (a
+    timing run)."""
+    import threading
+    import torch
+    B, Hkv, d = len(ctx), wl.n_kv_heads, wl.head_dim
+    k = int(round(B * ms_gpu_all / (ms_gpu_all + cpu_s_all * 1e3)))
+    k = min(max(k, 1), B - 1)
+    shape = dkv.Shape.of(wl.hidden, wl.n_q_heads, Hkv, d, 1)
+    page_elems = dkv.kv_page_bytes(shape) // 2
+    n_pages = [(int(ctx[b]) + dkv.PAGE_TOKENS - 1) // dkv.PAGE_TOKENS for b in range(k)]
+    # The CPU side's pages live in pinned host memory (hipHostMalloc), like the pool's.
+    buf = dkv.HostBuffer(sum(n_pages) * page_elems * 2)
+    mem = buf.view(np.uint16, (sum(n_pages), Hkv, 2, dkv.PAGE_TOKENS, d))
+    pages, first = [], 0
+    for b in range(k):
+        L, P = int(ctx[b]), n_pages[b]
+        kv = np.zeros((2, P * dkv.PAGE_TOKENS, Hkv, d), np.uint16)
+        kv[0, :L], kv[1, :L] = K_all[b, :L], V_all[b, :L]
+        # [K|V][page][token][head][dim] -> [page][head][K|V][token][dim]
+        mem[first:first + P] = kv.reshape(2, P, dkv.PAGE_TOKENS, Hkv, d).transpose(1, 3, 0, 2, 4)
+        pages.append([mem[first + p] for p in range(P)])
+        first += P
+    q, kn, vn = cpu_step_inputs(wl, k)
+    q = np.ascontiguousarray(q, np.float32)
+    kn, vn = np.ascontiguousarray(kn, np.uint16), np.ascontiguousarray(vn, np.uint16)
+    ctx_c = np.ascontiguousarray(ctx[:k], np.int32)
+    out = np.empty_like(q)
+    # The page table is built once, outside the timed calls (building it in
+    # Python costs milliseconds per step).
+    import ctypes
+    max_pages = max(n_pages)
+    table = (ctypes.c_void_p * (k * max_pages))()
+    for b in range(k):
+        for i, page in enumerate(pages[b]):
+            table[b * max_pages + i] = page.ctypes.data
+    used = ctypes.c_int32()
+    L = dkv.lib()
+
+    def cpu_once():
+        st = L.dkv_cpu_attention_pages(table, max_pages, ctypes.byref(shape), k, q.ctypes.data, kn.ctypes.data,
+                                       vn.ctypes.data, ctx_c.ctypes.data, out.ctypes.data, threads,
+                                       ctypes.byref(used))
+        if st != 0:
+            raise RuntimeError("dkv_cpu_attention_pages: status %d" % st)
+
+    cpu_once()
+    t_cpu = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        cpu_once()
+        t_cpu.append(time.perf_counter() - t0)
+    rg = Resident(dkv, wl.replace(batch=B - k), np.ascontiguousarray(ctx[k:]), np.zeros(B - k, np.int32),
+                  lambda layer, b, t0, t1: kv_source(layer, b + k, t0, t1))
+    ms_g = rg.timed(steps, 2)
+    together = []
+    for _ in range(max(5, steps // 2)):
+        th = threading.Thread(target=cpu_once)
+        t0 = time.perf_counter()
+        th.start()
+        rg.step()
+        torch.cuda.synchronize()
+        th.join()
+        together.append(time.perf_counter() - t0)
+    rg.free()
+    pages = mem = None
+    buf.free()
+    ms_t = float(np.median(together)) * 1e3
+    return {"cpu_sequences": k, "gpu_sequences": B - k, "cpu_threads": threads,
+            "cpu_alone_ms": round(float(np.median(t_cpu)) * 1e3, 4), "gpu_alone_ms": round(ms_g, 4),
+            "together_ms": round(ms_t, 4)}
+
+
 def cpu_dram_read_GBps(dkv, threads, nbytes=1 << 30):
     """Host-DRAM streaming read by `threads` CPU threads over a fresh pinned buffer."""
     buf = dkv.HostBuffer(nbytes)
@@ -825,6 +904,18 @@ def main(argv=None):
             "step_time_vs_method": round(cpu_s * 1e3 / ms, 3),
         }
         log("CPU attention (%d threads): %.3f ms/step; host DRAM read %.1f GB/s" % (used, cpu_s * 1e3, dram))
+        if K_all is not None and wl.n_layers == 1 and B > 1:
+            split = cpu_gpu_split(dkv, wl, ctx, kv_source, K_all, V_all, ms, cpu_s, args.cpu_threads, args.steps)
+            split.update({
+                "what": "the batch split between host threads reading their sequences' pages in host DRAM "
+                        "and the GPU's zero-copy step reading the other sequences' pages over the host link, "
+                        "run at the same time (wall time per step, both done)",
+                "effective_kv_GBps": round(kv_bytes / (split["together_ms"] * 1e-3) / 1e9, 3),
+                "step_time_vs_method": round(split["together_ms"] / ms, 3)})
+            comparators["cpu_gpu_split"] = split
+            log("CPU/GPU split (%d/%d sequences): %.3f ms/step (CPU alone %.3f, GPU alone %.3f)"
+                % (split["cpu_sequences"], split["gpu_sequences"], split["together_ms"], split["cpu_alone_ms"],
+                   split["gpu_alone_ms"]))
 
     # ------------------------------------------------------------------ every page in HBM
     hbm = None
