@@ -471,6 +471,17 @@ def cpu_attention_timed(dkv, r, wl, ctx, threads, reps):
     return float(np.median(times)), used
 
 
+def kv_pages(K, V, page_tokens):
+    """One sequence's cached K and V ([L][Hkv][d] bf16 bits each) in the
+    library's page layout: [page][KV head][K|V][token in page][dim], the last
+    page zero-padded."""
+    L, Hkv, d = K.shape
+    P = (L + page_tokens - 1) // page_tokens
+    kv = np.zeros((2, P * page_tokens, Hkv, d), np.uint16)
+    kv[0, :L], kv[1, :L] = K, V
+    return np.ascontiguousarray(kv.reshape(2, P, page_tokens, Hkv, d).transpose(1, 3, 0, 2, 4))
+
+
 def cpu_gpu_split(dkv, wl, ctx, kv_source, K_all, V_all, ms_gpu_all, cpu_s_all, threads, steps):
     """The batch split between the two readers of host memory: the first k
     sequences' attention on `threads` host threads over their pages in host
@@ -493,11 +504,8 @@ def cpu_gpu_split(dkv, wl, ctx, kv_source, K_all, V_all, ms_gpu_all, cpu_s_all, 
     mem = buf.view(np.uint16, (sum(n_pages), Hkv, 2, dkv.PAGE_TOKENS, d))
     pages, first = [], 0
     for b in range(k):
-        L, P = int(ctx[b]), n_pages[b]
-        kv = np.zeros((2, P * dkv.PAGE_TOKENS, Hkv, d), np.uint16)
-        kv[0, :L], kv[1, :L] = K_all[b, :L], V_all[b, :L]
-        # [K|V][page][token][head][dim] -> [page][head][K|V][token][dim]
-        mem[first:first + P] = kv.reshape(2, P, dkv.PAGE_TOKENS, Hkv, d).transpose(1, 3, 0, 2, 4)
+        P = n_pages[b]
+        mem[first:first + P] = kv_pages(K_all[b, :int(ctx[b])], V_all[b, :int(ctx[b])], dkv.PAGE_TOKENS)
         pages.append([mem[first + p] for p in range(P)])
         first += P
     q, kn, vn = cpu_step_inputs(wl, k)
