@@ -137,7 +137,8 @@ __device__ __forceinline__ void load_slice(uint4 (&v)[NK], const uint16_t *row, 
 
 // 1b. Batches of 8 to 15 sequences (one tile of 16): each workgroup owns 16 W
 // rows; its KSPLIT wavefronts split the hidden dimension into equal ranges,
-// and each walks its range in 128-wide chunks. A wave stages its x chunk (the
+// and each walks its range in KC-wide chunks (128, or 256 for ranges of 2048
+// and more). A wave stages its x chunk (the
 // 16 sequences' 128 k values, loaded as contiguous 256-byte row pieces; rows
 // past the batch as zeros) in its own LDS slot and reads the MFMA B operands
 // from there; the next x chunk is prefetched into registers and the next W
@@ -147,9 +148,8 @@ __device__ __forceinline__ void load_slice(uint4 (&v)[NK], const uint16_t *row, 
 // measured 17.7 us for the projection of a decode step at batch 8 and hidden
 // 4096, HIP events, against 14.5 us this way; at hidden 8192 the two are
 // within 5 %. The MFMA k order, and so every bit, is the same.)
-template <int KSPLIT>
+template <int KSPLIT, int KC = 128>
 __global__ __launch_bounds__(64 * KSPLIT) void qkv_proj_stream_kernel(StepArgs a) {
-    constexpr int KC = 128;             // k per chunk
     constexpr int NK = KC / 32;         // MFMA k steps per chunk
     constexpr int XROW = KC * 2 + 16;   // staged x row, bytes (padded by 16)
     constexpr int XPT = 16 * KC / 8 / 64;   // 16-byte x pieces per lane per chunk
@@ -372,16 +372,16 @@ int splitk_ranges(int hidden, int kc, int min_range) {
     return 1;
 }
 
-// Chunk width and minimum range per tile height, measured best on MI355X at
-// hidden 4096 and 8192: 128-wide chunks in ranges of 1024 for one 16-sequence
-// tile (4 ranges at hidden 4096), 256-wide chunks in ranges of 512 for two
-// and four (8 ranges).
+// 256-wide chunks; ranges of at least 1024 for one 16-sequence tile (4 ranges
+// at hidden 4096, 8 at 8192), 512 for two and four (8 ranges): measured best
+// on MI355X at hidden 4096 and 8192 (128-wide chunks in the one-tile case:
+// 18.3 vs 17.9 us at hidden 4096, 41.5 vs 39.7 us at 8192, batch 16, with
+// the partial sums).
 template <int NBT>
 void launch_splitk(const StepArgs &a, float *part, hipStream_t st) {
-    constexpr int KC = NBT == 1 ? 128 : 256;
-    const int ks = splitk_ranges(a.hidden, KC, NBT == 1 ? 1024 : 512);
+    const int ks = splitk_ranges(a.hidden, 256, NBT == 1 ? 1024 : 512);
     const dim3 grid(a.n_qkv / (16 * kProjRowBlocks), ks, (a.batch + 16 * NBT - 1) / (16 * NBT));
-    qkv_proj_splitk_kernel<NBT, KC><<<grid, 64 * kProjRowBlocks, 0, st>>>(a, part, a.hidden / ks);
+    qkv_proj_splitk_kernel<NBT, 256><<<grid, 64 * kProjRowBlocks, 0, st>>>(a, part, a.hidden / ks);
     const int n = a.batch * a.n_qkv;
     qkv_proj_finish_kernel<<<(n + 255) / 256, 256, 0, st>>>(a, part, ks);
 }
@@ -411,7 +411,13 @@ hipError_t launch_projection(const StepArgs &a, float *part, hipStream_t st) {
         int ksplit = 4;
         while (ksplit > 1 && a.hidden % (128 * ksplit) != 0) ksplit >>= 1;
         const dim3 grid(a.n_qkv / 16);
-        switch (ksplit) {
+        // 256-wide chunks once each wave's range reaches 2048 (hidden 8192 at
+        // batch 8: 45.7 -> 42.1 us; at hidden 4096, ranges of 1024, 128-wide
+        // chunks stay ahead: 16.7 vs 18.9 us; decode-step HIP events, W
+        // evicted from the caches).
+        if (ksplit == 4 && a.hidden % 1024 == 0 && a.hidden / 4 >= 2048)
+            qkv_proj_stream_kernel<4, 256><<<grid, 256, 0, st>>>(a);
+        else switch (ksplit) {
             case 1: qkv_proj_stream_kernel<1><<<grid, 64, 0, st>>>(a); break;
             case 2: qkv_proj_stream_kernel<2><<<grid, 128, 0, st>>>(a); break;
             default: qkv_proj_stream_kernel<4><<<grid, 256, 0, st>>>(a); break;
