@@ -190,18 +190,32 @@ def test_multistep_window_other_shapes(oracle, case):
     check_against_oracle(oracle, case, True)
 
 
-def test_multistep_graph_replay_matches_eager(oracle):
+@pytest.mark.parametrize("case,waves", [(TINY, 0), (TINY, 256), (MFMA16, 0), (MFMA16, 256)],
+                         ids=["tiny-per-item", "tiny-looping", "batch16-per-item", "batch16-looping"])
+def test_multistep_graph_replay_matches_eager(oracle, monkeypatch, case, waves):
     """One captured graph (decode_step + kv_advance) replayed for every step,
     with the next step's x copied in and a synchronisation between replays;
-    every replay equals the eager run bit for bit."""
+    every replay equals the eager run bit for bit. The split kernel runs as
+    one wavefront per item or as looping wavefronts that take items from the
+    layout's shared counter; the step's projection kernel (at batch 16 its
+    partial-sum kernel) zeroes that counter, so each replay starts the queue
+    afresh. The eager outputs are the same bits under either form."""
     import torch
-    c = TINY
+    c = case
     wl = c.wl
     xs, W = step_inputs(c)
-    eager, dkv, layout, host, hbm = run_eager(c, True, xs, W)
+    monkeypatch.setenv("DKV_SPLIT_WAVES", "0")
+    plain, dkv, layout, host, hbm = run_eager(c, True, xs, W)
     free_all(layout, host, hbm)
+    monkeypatch.setenv("DKV_SPLIT_WAVES", str(waves))
+    eager, dkv, layout, host, hbm = run_eager(c, True, xs, W)
+    assert layout.split_waves == waves
+    free_all(layout, host, hbm)
+    for t in range(c.steps):
+        assert np.array_equal(eager[t].view(np.uint32), plain[t].view(np.uint32)), t
     dkv, layout, host, hbm, ctx = make_layout(c, True)
     try:
+        assert layout.split_waves == waves
         Wd = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
         x_buf = torch.empty((wl.batch, wl.hidden), dtype=torch.bfloat16, device="cuda")
         out = torch.empty((wl.batch, wl.n_q_heads * wl.head_dim), dtype=torch.float32, device="cuda")
