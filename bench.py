@@ -233,6 +233,77 @@ def counter_traffic(workload: str, all_hbm: bool = False):
     return int(rec["traffic_bytes_per_launch"])
 
 
+def pmc_per_dispatch(path: str, counter: str):
+    """{dispatch id: (kernel name, summed counter value)} from one rocprofv3
+    `pmc_counter_collection.csv` (the counter's per-instance rows added up)."""
+    import csv
+    vals, names = {}, {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            i = int(row["Dispatch_Id"])
+            vals[i] = vals.get(i, 0.0) + float(row["Counter_Value"])
+            names[i] = row["Kernel_Name"]
+    return {i: (names[i], vals[i]) for i in vals}
+
+
+def write_traffic_record(wl, args) -> int:
+    """Reduces the two counter runs of a workload (rocprofv3 --pmc FETCH_SIZE,
+    then WRITE_SIZE, each over `bench.py --profile-run --calibrate` with the
+    same --workload, --all-hbm, --steps and --warmup as this call; their -d
+    directories are `<prefix>_FETCH_SIZE` and `<prefix>_WRITE_SIZE`) to the
+    split kernel's traffic record under profiles/, which counter_traffic reads.
+    FETCH_SIZE and WRITE_SIZE are scaled by what they read for the run's
+    256 MiB HBM-to-HBM copy. Runs on the host alone; no GPU."""
+    prefix = args.traffic_record
+    fetch = pmc_per_dispatch(os.path.join(prefix + "_FETCH_SIZE", "pmc_counter_collection.csv"), "FETCH_SIZE")
+    write = pmc_per_dispatch(os.path.join(prefix + "_WRITE_SIZE", "pmc_counter_collection.csv"), "WRITE_SIZE")
+
+    def of(rows, key):
+        return [v for name, v in rows.values() if key in name]
+
+    split_f, split_w = of(fetch, "attn_split"), of(write, "attn_split")
+    if not split_f or not split_w:
+        print("no split-kernel dispatches under %s_{FETCH,WRITE}_SIZE" % prefix, file=sys.stderr)
+        return 1
+    kernel = [name for name, _ in fetch.values() if "attn_split" in name][0]
+    kernel = kernel.replace("void dkv::(anonymous namespace)::", "").split("(dkv::StepArgs)")[0]
+    copy_f, copy_w = max(of(fetch, "copyBuffer")), max(of(write, "copyBuffer"))
+    fetch_scale, write_scale = 262144.0 / copy_f, 262144.0 / copy_w       # 256 MiB in KiB
+    mf, mw = sum(split_f) / len(split_f), sum(split_w) / len(split_w)
+    traffic = (mf * fetch_scale + mw * write_scale) * 1024
+    alg = int(wl.ctx_lens().astype(np.int64).sum()) * wl.kv_bytes_per_token   # one layer = one launch
+    sfx = "_allhbm" if args.all_hbm else ""
+    run = "python3 $REPO/bench.py --workload %s --profile-run%s --calibrate --steps %d --warmup %d" % (
+        wl.name, " --all-hbm" if args.all_hbm else "", args.steps, args.warmup)
+    rec = {"kernel": kernel,
+           "workload": wl.name + (", every page in HBM" if args.all_hbm else ""),
+           "split_kernel_sources_sha256": split_kernel_sha256(),
+           "fetch_size_kib_per_dispatch": round(mf, 3), "write_size_kib_per_dispatch": round(mw, 3),
+           "dispatches": len(split_f),
+           "calibration": {"copy_kernel": "__amd_rocclr_copyBuffer, 256 MiB HBM -> HBM",
+                           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+                           "fetch_scale": fetch_scale, "write_scale": write_scale,
+                           "stream_read_fetch_kib": sorted(of(fetch, "stream_read"))},
+           "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": alg,
+           "traffic_over_algorithmic": traffic / alg,
+           "commands": ["cd /tmp && export TMPDIR=/tmp"] + [
+               "rocprofv3 --pmc %s --output-format csv -d $REPO/gpurun_out/pmc_%s%s_%s -o pmc -- %s"
+               % (c, wl.name, sfx, c, run) for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
+               "python3 $REPO/bench.py --workload %s%s --steps %d --warmup %d --traffic-record "
+               "$REPO/gpurun_out/pmc_%s%s" % (wl.name, " --all-hbm" if args.all_hbm else "", args.steps,
+                                               args.warmup, wl.name, sfx)],
+           "hashed_sources": "attn_split.hip, device_common.h, struct StepArgs of dkv_internal.h; "
+                             "comments and whitespace removed"}
+    out = os.path.join(ROOT, "profiles", "attn_split_%s%s_traffic.json" % (wl.name, sfx))
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({"record": os.path.relpath(out, ROOT), "kernel": kernel, "dispatches": len(split_f),
+                      "traffic_over_algorithmic": round(traffic / alg, 4)}))
+    return 0
+
+
 def calibrate(dkv, r):
     """Kernels whose HBM / host traffic is known exactly, for counter scaling."""
     import torch
@@ -793,7 +864,14 @@ def main(argv=None):
                     help="with --profile-run: also run kernels of known traffic (a 256 MiB "
                          "HBM-to-HBM copy, 1 GiB streaming reads of the host pool and of HBM) "
                          "to scale counter readings")
+    ap.add_argument("--traffic-record", metavar="PREFIX",
+                    help="write the split kernel's traffic record under profiles/ from the "
+                         "FETCH_SIZE and WRITE_SIZE counter runs in PREFIX_FETCH_SIZE/ and "
+                         "PREFIX_WRITE_SIZE/ (host only, no GPU)")
     args = ap.parse_args(argv)
+    if args.traffic_record:
+        from synth import configs
+        return write_traffic_record(configs.BY_NAME[args.workload], args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the decode path runs on one MI355X and this build "
               "launches nothing on a second GPU (--gpus %d is not supported)." % args.gpus,
