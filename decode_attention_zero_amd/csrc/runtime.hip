@@ -235,8 +235,15 @@ int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, int32_t max_cap) 
         const int v = atoi(env);
         if (v >= DKV_PAGE_TOKENS && v % DKV_PAGE_TOKENS == 0) return v;
     }
-    // The longest split (at most 8192 tokens) that still leaves at least 2048
-    // work items to spread over 256 CUs. A longer split is a longer
+    // The longest split (at most 8192 tokens) that still leaves at least 1536
+    // full work items (splits of T tokens at the longest capacity; a short
+    // tail split is not counted) to spread over 256 CUs. Halving the split
+    // at most doubles
+    // the items, so a uniform batch lands in [1536, 3072) items: never more
+    // than the 3072 wavefronts the matrix-core split kernel keeps resident
+    // (3 per SIMD), which a second round of items would leave idling at the
+    // end (32 sequences of 57344 tokens, all in HBM: 1792 items of 8192
+    // tokens 1.09 ms, 6.9 TB/s; 3584 of 4096 tokens 1.28 ms). A longer split is a longer
     // contiguous page stream per wavefront, fewer partials to write and
     // combine, and fewer waves starting up; with every page in HBM on MI355X
     // (one wave per item): 1 GiB at batch 8 (2048 items at 1024 tokens),
@@ -248,7 +255,7 @@ int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, int32_t max_cap) 
     const int64_t max_cached = std::max(1, max_cap - 1);
     int32_t t = 8192;
     while (t > DKV_PAGE_TOKENS &&
-           (int64_t)batch * n_kv_heads * ((max_cached + t - 1) / t) < 2048)
+           (int64_t)batch * n_kv_heads * (max_cached / t) < 1536)
         t /= 2;
     return t;
 }
