@@ -151,7 +151,7 @@ class Resident:
         t = self.layout.timing_read()
         self.layout.timing_enable(False)
         n = max(1, t["steps"]) / self.n_layers
-        return {k: t[k] / n for k in ("projection", "split", "combine")}
+        return {k: t[k] / n for k in ("projection", "fresh", "split", "combine")}
 
     def out_bits(self, layer=0):
         import torch

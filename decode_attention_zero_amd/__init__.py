@@ -96,7 +96,7 @@ def lib() -> ctypes.CDLL:
             "dkv_copy": ([P, P, ctypes.c_uint64, P], I32),
             "dkv_gemm_bf16_nt": ([P, P, P, I32, I32, I32, I32, P], I32),
             "kv_layout_timing_enable": ([P, I32, I32], I32),
-            "kv_layout_timing_read": ([P, P, P, P, P], I32),
+            "kv_layout_timing_read": ([P, P, P, P, P, P], I32),
             "dkv_cpu_attention": ([P, I32, P, P, P, P, P, I32, P], I32),
             "dkv_cpu_stream_read": ([P, ctypes.c_uint64, I32, P], I32),
             "dkv_cpu_attention_pages": ([P, I32, SP, I32, P, P, P, P, P, I32, P], I32),
@@ -236,11 +236,12 @@ class Layout:
 
     def timing_read(self) -> dict:
         """Summed per-kernel milliseconds and the step count since the last read."""
-        p, s, c = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        p, f, s, c = ctypes.c_double(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
         n = ctypes.c_int32()
-        _check(lib().kv_layout_timing_read(self.handle, ctypes.byref(p), ctypes.byref(s),
+        _check(lib().kv_layout_timing_read(self.handle, ctypes.byref(p), ctypes.byref(f), ctypes.byref(s),
                                            ctypes.byref(c), ctypes.byref(n)))
-        return {"projection": p.value, "split": s.value, "combine": c.value, "steps": n.value}
+        return {"projection": p.value, "fresh": f.value, "split": s.value, "combine": c.value,
+                "steps": n.value}
 
     def free(self) -> None:
         if self.handle:

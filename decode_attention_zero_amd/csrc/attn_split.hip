@@ -210,7 +210,7 @@ struct SplitState {
         if (row0) {
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const size_t slot = ((size_t)b * a.n_q_heads + (size_t)h0 + h) * a.max_splits + s;
+                const size_t slot = ((size_t)b * a.n_q_heads + (size_t)h0 + h) * a.part_slots + s;
                 float *po = a.part_o + slot * D + dl * 8;
                 *reinterpret_cast<float4 *>(po) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
                 *reinterpret_cast<float4 *>(po + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
@@ -464,7 +464,7 @@ struct MfmaState {
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[n][r] += dpp<0x140>(o[n][r]);
         if (col < G) {
-            const size_t slot = ((size_t)b * a.n_q_heads + (size_t)(h0 + col)) * a.max_splits + s;
+            const size_t slot = ((size_t)b * a.n_q_heads + (size_t)(h0 + col)) * a.part_slots + s;
             float *po = a.part_o + slot * D + 4 * kq;
 #pragma unroll
             for (int n = 0; n < NDB; ++n)

@@ -35,7 +35,9 @@ struct StepArgs {
     int32_t n_qkv;          // (Hq + 2 Hkv) * d
     int32_t max_pages;      // page-table row length
     int32_t split_tokens;   // tokens per attention work item (multiple of 16)
-    int32_t max_splits;     // partial slots per (sequence, query head)
+    int32_t max_splits;     // splits of the cached tokens per sequence, at most
+    int32_t part_slots;     // partial slots per (sequence, query head): max_splits + 1; sequence b's
+                            // fresh token takes slot ceil(ctx_lens[b] / split_tokens), after its splits
     float qscale;           // log2(e) / sqrt(head_dim): scores come out in log2 units
     int32_t split_variant;  // kSplitRegisters, kSplitLds, kSplitNaive or kSplitMfma
     int32_t split_waves;    // register kernel: > 0 = that many wavefronts loop over the items
@@ -51,14 +53,15 @@ struct StepArgs {
     const int32_t *ctx_lens;  // [batch]
     void *out;                // [batch][Hq * d] bf16 or fp32
     int32_t out_f32;
-    // layout-owned scratch
+    // scratch (the layout's, or the static array of decode_step_noalloc)
+    float *proj_part;         // [ranges][batch][n_qkv] fp32 projection sums, one slab per range of
+                              // the hidden dimension (one range below kProjSplitkMinBatch)
     float *q;                 // [batch][Hq][d] fp32, scaled by log2(e) / sqrt(d)
-    uint16_t *kv_new;         // [batch][Hkv][2][d] bf16 (fresh K then V)
-    float *part_o;            // [batch][Hq][max_splits][d] unnormalised outputs
-    float2 *part_ml;          // [batch][Hq][max_splits] (running max, sum of weights)
+    float *part_o;            // [batch][Hq][part_slots][d] unnormalised outputs
+    float2 *part_ml;          // [batch][Hq][part_slots] (running max, sum of weights)
     uint32_t *status;         // range flag (bit 0: a ctx_lens entry out of range)
     uint32_t *item_counter;   // looping split kernels: next work item to take (zeroed by the
-                              // step's projection kernel before the split kernel runs)
+                              // step's fresh-token kernel before the split kernel runs)
 };
 
 // What kv_advance's kernel reads and writes (see kv_advance in dkv.h).
@@ -81,21 +84,36 @@ struct AdvanceArgs {
 hipError_t launch_advance(const AdvanceArgs &a, hipStream_t stream);
 
 // From this batch size the matrix-core projection splits the hidden dimension
-// into at most kProjMaxSplits ranges and adds their fp32 partials in a second
-// kernel; the partials take kProjMaxSplits * batch * n_qkv floats of
-// layout-owned scratch (`proj_part` below).
+// into at most kProjMaxSplits ranges, each writing its own fp32 slab of
+// StepArgs::proj_part; below it the projection writes one slab. The
+// fresh-token kernel adds the slabs of its group's rows in range order.
 constexpr int kProjSplitkMinBatch = 16;
 constexpr int kProjMaxSplits = 8;
 
+// Projection slabs a batch uses.
+inline int proj_ranges_max(int batch) { return batch >= kProjSplitkMinBatch ? kProjMaxSplits : 1; }
+
+// Scratch bytes of one decode step (each buffer 256-byte aligned in the order
+// proj_part, q, part_o, part_ml, item counter), so that one carve serves the
+// layout-owned scratch and the static array of decode_step_noalloc alike.
+struct ScratchPlan {
+    size_t proj_part, q, part_o, part_ml, item_counter, total;
+};
+ScratchPlan scratch_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int part_slots);
+// Points a's scratch fields into `base` (an allocation of plan.total bytes).
+void carve_scratch(StepArgs &a, char *base, const ScratchPlan &plan);
+
 // Enqueues the decode step's kernels on `stream`. With `events` non-null,
 // records events[0] before the projection, events[1] after it, events[2]
-// after the split attention and events[3] after the combine. `proj_part` is
-// the projection's partial-sum scratch (null for batches that do not use it).
-hipError_t launch_decode_step(const StepArgs &a, float *proj_part, hipStream_t stream, hipEvent_t *events);
+// after the fresh-token kernel, events[3] after the split attention and
+// events[4] after the combine.
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream, hipEvent_t *events);
 
-// The three kernels of a step (each returns hipErrorInvalidValue for a shape
-// outside its compiled variants, before launching anything).
-hipError_t launch_projection(const StepArgs &a, float *proj_part, hipStream_t stream);
+// The four kernels of a step (each returns hipErrorInvalidValue for a shape
+// outside its compiled variants, before launching anything). The projection
+// reports how many slabs of proj_part it wrote.
+hipError_t launch_projection(const StepArgs &a, int *ranges, hipStream_t stream);
+hipError_t launch_fresh(const StepArgs &a, int ranges, hipStream_t stream);
 hipError_t launch_split(const StepArgs &a, hipStream_t stream);
 hipError_t launch_combine(const StepArgs &a, hipStream_t stream);
 

@@ -1,0 +1,141 @@
+// The new token of one decode step on gfx950: its query, key and value are
+// formed from the projection's fp32 sums, the key and value are consumed on
+// chip and written back once.
+//
+// One workgroup of four wavefronts per (sequence b, KV head g):
+//  * adds the projection slabs of the group's rows (G query heads, then the
+//    K and V head) in range order; the queries are scaled by log2(e)/sqrt(d)
+//    (scores in log2 units) and stored in fp32 for the split kernel; k_new
+//    and v_new are rounded once to bf16 (nearest even) and kept in LDS;
+//  * scores the fresh token against each of the G query heads from LDS and
+//    writes its one-token softmax state (s_new, 1, v_new) into the partial
+//    slot after the sequence's splits, where the combine merges it like any
+//    split;
+//  * writes the bf16 K and V rows once into slot ctx_lens[b] of the
+//    sequence's pages, host or HBM (the "storer" role).
+// The new K/V thus exist only in this kernel's registers and LDS before the
+// single write-back: the fusion of the projection that generates them with
+// the attention that consumes them, in the core-method section of the
+// DirectKV digest ("长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）") and in
+// "KV Cache 内存层级" overview, 2.1 去搬运：DirectKV (fresh K/V consumed from
+// shared memory instead of written out and read back). The projection itself
+// stays a separate launch spread over hundreds of workgroups, which is what
+// reading W at HBM speed takes; what crosses between the two launches is fp32
+// partial sums, not K/V.
+//
+// The step's other bookkeeping happens here too: the range check of
+// ctx_lens and the reset of the split kernel's work queue.
+#include "device_common.h"
+
+namespace dkv {
+namespace {
+
+constexpr int kFreshWaves = 4;
+constexpr int kFreshThreads = 64 * kFreshWaves;
+
+template <int D, int G>
+__global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a, int ranges) {
+    constexpr int DPL = D / 64;        // dims per lane
+    constexpr int NR = (G + 2) * D;    // the group's rows: G query heads, K, V
+    const int b = blockIdx.x / a.n_kv_heads;
+    const int g = blockIdx.x - b * a.n_kv_heads;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    __shared__ float s_q[G][D];
+    __shared__ float s_kv[2][D];               // rounded K and V, as fp32 (exact)
+    __shared__ __attribute__((aligned(16))) uint16_t s_kvb[2][D];   // their bf16 bits
+
+    reset_items(a);
+    const int L = a.ctx_lens[b];
+    const bool in_range = L >= 0 && L < a.capacity[b];
+    if (g == 0 && tid == 0) check_context_range(a, b);
+
+    const size_t slab = (size_t)a.batch * a.n_qkv;
+    const float *yb = a.proj_part + (size_t)b * a.n_qkv;
+    const int krow = a.n_q_heads * D + g * D;
+    const int vrow = krow + a.n_kv_heads * D;
+    float *qout = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
+    for (int r = tid; r < NR; r += kFreshThreads) {
+        const int n = r < G * D ? g * G * D + r : r < (G + 1) * D ? krow + (r - G * D) : vrow + (r - (G + 1) * D);
+        float y = yb[n];
+        for (int k = 1; k < ranges; ++k) y += yb[(size_t)k * slab + n];
+        if (r < G * D) {
+            const float qv = y * a.qscale;
+            s_q[r / D][r % D] = qv;
+            qout[r] = qv;
+        } else {
+            const int c = (r - G * D) / D, i = (r - G * D) % D;
+            const uint16_t h = f32_to_bf16(y);
+            s_kvb[c][i] = h;
+            s_kv[c][i] = __uint_as_float((uint32_t)h << 16);
+        }
+    }
+    __syncthreads();
+    if (!in_range) return;
+
+    // One-token state of each query head: m = s_new, l = 1, o = v_new.
+    const int slot_s = (L + a.split_tokens - 1) / a.split_tokens;
+    for (int h = wave; h < G; h += kFreshWaves) {
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) part = fmaf(s_q[h][lane * DPL + e], s_kv[0][lane * DPL + e], part);
+        const float s_new = wave_sum(part);
+        const size_t slot = ((size_t)b * a.n_q_heads + (size_t)g * G + h) * a.part_slots + slot_s;
+        float *po = a.part_o + slot * D + lane * DPL;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) po[e] = s_kv[1][lane * DPL + e];
+        if (lane == 0) a.part_ml[slot] = make_float2(s_new, 1.0f);
+    }
+
+    // The single write-back: lanes 0-31 of the last wave store the K row,
+    // lanes 32-63 the V row.
+    if (wave == kFreshWaves - 1) {
+        const int c = lane >> 5;
+        const int li = lane & 31;
+        char *page = reinterpret_cast<char *>(a.page_table[(size_t)b * a.max_pages + L / kPageTokens]);
+        char *dst = page + ((size_t)((g * 2 + c) * kPageTokens + (L % kPageTokens)) * D) * 2;
+        const char *src = reinterpret_cast<const char *>(s_kvb[c]);
+        constexpr int BPL = D * 2 / 32;    // bytes per lane
+        if constexpr (BPL == 8) {
+            *reinterpret_cast<uint2 *>(dst + li * 8) = *reinterpret_cast<const uint2 *>(src + li * 8);
+        } else {
+            *reinterpret_cast<uint32_t *>(dst + li * 4) = *reinterpret_cast<const uint32_t *>(src + li * 4);
+        }
+    }
+}
+
+template <int D, int G>
+void launch(const StepArgs &a, int ranges, hipStream_t st) {
+    fresh_token_kernel<D, G><<<a.batch * a.n_kv_heads, kFreshThreads, 0, st>>>(a, ranges);
+}
+
+}  // namespace
+
+hipError_t launch_fresh(const StepArgs &a, int ranges, hipStream_t st) {
+    const int G = a.n_q_heads / a.n_kv_heads;
+    if (ranges < 1 || ranges > kProjMaxSplits) return hipErrorInvalidValue;
+    if (a.head_dim == 128) {
+        switch (G) {
+            case 1: launch<128, 1>(a, ranges, st); break;
+            case 2: launch<128, 2>(a, ranges, st); break;
+            case 4: launch<128, 4>(a, ranges, st); break;
+            case 8: launch<128, 8>(a, ranges, st); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else if (a.head_dim == 64) {
+        switch (G) {
+            case 1: launch<64, 1>(a, ranges, st); break;
+            case 2: launch<64, 2>(a, ranges, st); break;
+            case 4: launch<64, 4>(a, ranges, st); break;
+            case 8: launch<64, 8>(a, ranges, st); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dkv

@@ -1,11 +1,11 @@
-// Fused QKV projection of one decode step on gfx950: y_b = W_qkv x_b for
-// every sequence b, fp32 accumulation of exact bf16 products. Rows below
-// Hq*d are the query (kept in fp32, pre-scaled by log2(e)/sqrt(d) so that
-// scores come out in log2 units); the rest are the fresh K then V heads,
-// rounded once to bf16. The projection that produces the new token's K/V is
-// part of the decode step, as in the core-method section of the DirectKV
-// digest ("长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）"); the step is bound
-// by reading W from HBM at every batch size here, so each of the three forms
+// QKV projection of one decode step on gfx950: y_b = W_qkv x_b for every
+// sequence b, fp32 accumulation of exact bf16 products, written as fp32 sums
+// (one slab per range of the hidden dimension) for the fresh-token kernel,
+// which adds them, keeps the query in fp32 and rounds the new token's K and
+// V once. The projection that produces the new token's K/V is part of the
+// decode step, as in the core-method section of the DirectKV digest
+// ("长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）"); the step is bound by
+// reading W from HBM at every batch size here, so each of the three forms
 // (1a VALU GEMV below batch 8, 1b one 16-sequence MFMA tile up to batch 15,
 // 1c split-k MFMA from batch 16) is built to stream W once at full bandwidth.
 #include "device_common.h"
@@ -13,18 +13,9 @@
 namespace dkv {
 namespace {
 
+// Below batch 16 every form writes one slab: y of output row n of sequence b.
 __device__ __forceinline__ void store_projection(const StepArgs &a, int n, int b, float y) {
-    const int D = a.head_dim;
-    const int nq = a.n_q_heads * D;
-    if (n < nq) {
-        a.q[(size_t)b * nq + n] = y * a.qscale;
-    } else {
-        const int n2 = n - nq;
-        const int c = n2 / (a.n_kv_heads * D);
-        const int rem = n2 - c * (a.n_kv_heads * D);
-        const int g = rem / D, i = rem - g * D;
-        a.kv_new[(((size_t)b * a.n_kv_heads + g) * 2 + c) * D + i] = f32_to_bf16(y);
-    }
+    a.proj_part[(size_t)b * a.n_qkv + n] = y;
 }
 
 // Sums each of the N values (N a power of two <= 64) over the 64 lanes of
@@ -74,9 +65,6 @@ __global__ __launch_bounds__(64 * KS) void qkv_proj_gemv_kernel(StepArgs a) {
     const int nb = min(BT, a.batch - b0);
     const int krange = a.hidden / KS;     // a multiple of 512 (checked at launch)
     const int kbeg = wave * krange;
-
-    if (blockIdx.x == 0 && threadIdx.x < nb) check_context_range(a, b0 + threadIdx.x);
-    reset_items(a);
 
     float acc[NV];
 #pragma unroll
@@ -163,9 +151,6 @@ __global__ __launch_bounds__(64 * KSPLIT) void qkv_proj_stream_kernel(StepArgs a
     const int kb = wave * krange;
     const int nch = krange / KC;
 
-    if (blockIdx.x == 0 && wave == 0 && lane < a.batch) check_context_range(a, lane);
-    reset_items(a);
-
     const uint16_t *wrow = a.w + (size_t)(row0 + i) * a.hidden + kb + kq;
     char *xw = xs[wave][0];
     uint4 xr[XPT];
@@ -247,19 +232,19 @@ __global__ __launch_bounds__(64 * KSPLIT) void qkv_proj_stream_kernel(StepArgs a
 // staged once in LDS and read by all four waves, which cuts x's L2 traffic to
 // B/64 of W. The next x chunk is prefetched into registers and the next W
 // chunk is in flight (ping-pong register buffers) while the current chunk's
-// MFMAs run. Each workgroup writes its fp32 partial tile to layout-owned
-// scratch, and qkv_proj_finish_kernel adds the KS partials in range order and
-// stores q, k_new and v_new. Other ways of adding the partials measured
+// MFMAs run. Each workgroup writes its fp32 partial tile to its range's slab
+// of the step's scratch, and the fresh-token kernel adds the KS slabs of its
+// group's rows in range order. Other ways of adding the partials measured
 // slower: the last workgroup of each row block to finish doing it (2-10x: its
 // device-scope fences write back the L2), one workgroup per row block holding
-// every range (~2x: 96 workgroups fill too few CUs), and the consumers adding
-// them when they read q (every split item re-reads KS partials: +4 % on the
-// all-HBM split kernel).
+// every range (~2x: 96 workgroups fill too few CUs), and the split kernel's
+// consumers adding them when they read q (every split item re-reads KS
+// partials: +4 % on the all-HBM split kernel).
 constexpr int kProjRowBlocks = 4;        // 16-row W blocks per workgroup, one per wavefront
 
 // NBT tiles of 16 sequences (batch tile b0 = blockIdx.z * 16 * NBT), KC-wide chunks.
 template <int NBT, int KC>
-__global__ __launch_bounds__(64 * kProjRowBlocks) void qkv_proj_splitk_kernel(StepArgs a, float *part, int krange) {
+__global__ __launch_bounds__(64 * kProjRowBlocks) void qkv_proj_splitk_kernel(StepArgs a, int krange) {
     constexpr int NT = 64 * kProjRowBlocks;
     constexpr int NK = KC / 32;                 // MFMA k steps per chunk
     constexpr int XROW = KC * 2 + 16;           // staged x row, bytes (padded by 16)
@@ -344,24 +329,10 @@ __global__ __launch_bounds__(64 * kProjRowBlocks) void qkv_proj_splitk_kernel(St
     for (int t = 0; t < NBT; ++t) {
         const int b = b0 + 16 * t + i;
         if (b < a.batch) {
-            float *pp = part + ((size_t)ks * a.batch + b) * a.n_qkv + row0 + 4 * (lane >> 4);
+            float *pp = a.proj_part + ((size_t)ks * a.batch + b) * a.n_qkv + row0 + 4 * (lane >> 4);
             *reinterpret_cast<float4 *>(pp) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
         }
     }
-}
-
-// Adds the KS partials of every output in range order and stores it (q scaled
-// in fp32, k_new / v_new rounded once to bf16). One thread per (sequence, row).
-__global__ __launch_bounds__(256) void qkv_proj_finish_kernel(StepArgs a, const float *part, int ksplit) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= a.batch * a.n_qkv) return;
-    const int b = idx / a.n_qkv, n = idx - b * a.n_qkv;
-    if (n == 0) check_context_range(a, b);
-    reset_items(a);
-    const size_t stride = (size_t)a.batch * a.n_qkv;
-    float y = part[idx];
-    for (int k = 1; k < ksplit; ++k) y += part[(size_t)k * stride + idx];
-    store_projection(a, n, b, y);
 }
 
 // Number of ranges of the hidden dimension: the largest of 8, 4, 2, 1 that
@@ -378,12 +349,11 @@ int splitk_ranges(int hidden, int kc, int min_range) {
 // 18.3 vs 17.9 us at hidden 4096, 41.5 vs 39.7 us at 8192, batch 16, with
 // the partial sums).
 template <int NBT>
-void launch_splitk(const StepArgs &a, float *part, hipStream_t st) {
+int launch_splitk(const StepArgs &a, hipStream_t st) {
     const int ks = splitk_ranges(a.hidden, 256, NBT == 1 ? 1024 : 512);
     const dim3 grid(a.n_qkv / (16 * kProjRowBlocks), ks, (a.batch + 16 * NBT - 1) / (16 * NBT));
-    qkv_proj_splitk_kernel<NBT, 256><<<grid, 64 * kProjRowBlocks, 0, st>>>(a, part, a.hidden / ks);
-    const int n = a.batch * a.n_qkv;
-    qkv_proj_finish_kernel<<<(n + 255) / 256, 256, 0, st>>>(a, part, ks);
+    qkv_proj_splitk_kernel<NBT, 256><<<grid, 64 * kProjRowBlocks, 0, st>>>(a, a.hidden / ks);
+    return ks;
 }
 
 template <int BT>
@@ -404,8 +374,9 @@ hipError_t launch_gemv(const StepArgs &a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_projection(const StepArgs &a, float *part, hipStream_t st) {
-    if (a.hidden % 512 != 0 || a.n_qkv % (16 * kProjRowBlocks) != 0) return hipErrorInvalidValue;
+hipError_t launch_projection(const StepArgs &a, int *ranges, hipStream_t st) {
+    if (a.hidden % 512 != 0 || a.n_qkv % (16 * kProjRowBlocks) != 0 || !a.proj_part) return hipErrorInvalidValue;
+    *ranges = 1;
     if (a.batch >= a.proj_mfma_min_batch && a.batch < kProjSplitkMinBatch) {
         // One sequence tile: streamed over k by up to 4 wavefronts per row block.
         int ksplit = 4;
@@ -423,10 +394,9 @@ hipError_t launch_projection(const StepArgs &a, float *part, hipStream_t st) {
             default: qkv_proj_stream_kernel<4><<<grid, 256, 0, st>>>(a); break;
         }
     } else if (a.batch >= a.proj_mfma_min_batch) {
-        if (!part) return hipErrorInvalidValue;
-        if (a.batch <= 16) launch_splitk<1>(a, part, st);
-        else if (a.batch <= 32) launch_splitk<2>(a, part, st);
-        else launch_splitk<4>(a, part, st);
+        if (a.batch <= 16) *ranges = launch_splitk<1>(a, st);
+        else if (a.batch <= 32) *ranges = launch_splitk<2>(a, st);
+        else *ranges = launch_splitk<4>(a, st);
     } else if (a.batch <= 4) {
         (void)launch_gemv<4>(a, st);
     } else if (a.batch <= 8) {

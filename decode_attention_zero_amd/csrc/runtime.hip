@@ -81,6 +81,10 @@ dkv_status guarded(const char *who, F &&body) {
     }
 }
 
+// HIP events a timed decode step records: before the projection, after it,
+// after the fresh-token kernel, after the split attention, after the combine.
+constexpr int kTimingEvents = 5;
+
 // Largest pool, in bytes, a request may ask for (1 PiB): keeps page counts
 // times page bytes far from overflow.
 constexpr uint64_t kMaxPoolBytes = 1ull << 50;
@@ -149,13 +153,10 @@ struct dkv_layout {
     std::vector<std::pair<dkv_pool *, int64_t>> owned;   // every page the layout holds
     uint64_t *d_page_table;            // [n_layers][batch][max_pages] current device address of each page
     int32_t *d_capacity;
-    float *d_q;
-    uint16_t *d_kv_new;
-    float *d_part_o;
-    float2 *d_part_ml;
-    float *d_proj_part = nullptr;      // [kProjMaxSplits][batch][n_qkv] split-k projection partials
+    char *d_scratch = nullptr;         // one allocation carved by dkv::carve_scratch (projection slabs,
+                                       // queries, split partials, work-queue counter)
+    dkv::ScratchPlan scratch{};
     uint32_t *d_status;
-    uint32_t *d_item_counter = nullptr;   // work queue of the looping split kernels
     // sliding hot window (kv_layout_create_windowed); windowed == 0 otherwise
     int32_t windowed = 0;
     std::vector<int32_t> window;       // HBM window pages per sequence
@@ -164,7 +165,7 @@ struct dkv_layout {
     uint64_t *d_ring = nullptr;        // [n_layers][batch][max_window] HBM pages of the window
     int32_t *d_window = nullptr;       // [batch] window pages per sequence
     // per-kernel timing (measurement mode only)
-    std::vector<hipEvent_t> timing_events;   // 4 per recorded step
+    std::vector<hipEvent_t> timing_events;   // kTimingEvents per recorded step
     int32_t timing_recorded = 0;
 };
 
@@ -202,9 +203,8 @@ uint64_t page_addr(const dkv_pool *pool, int64_t idx) {
 }
 
 void free_device(dkv_layout *L) {
-    for (void *p : {(void *)L->d_page_table, (void *)L->d_capacity, (void *)L->d_q, (void *)L->d_kv_new,
-                    (void *)L->d_part_o, (void *)L->d_part_ml, (void *)L->d_proj_part, (void *)L->d_status, (void *)L->d_item_counter, (void *)L->d_host_pages,
-                    (void *)L->d_ring, (void *)L->d_window})
+    for (void *p : {(void *)L->d_page_table, (void *)L->d_capacity, (void *)L->d_scratch, (void *)L->d_status,
+                    (void *)L->d_host_pages, (void *)L->d_ring, (void *)L->d_window})
         if (p) (void)hipFree(p);
 }
 
@@ -364,18 +364,51 @@ bool pool_too_large(const dkv_shape *shape, int64_t n_pages) {
 
 namespace dkv {
 
-hipError_t launch_decode_step(const StepArgs &a, float *proj_part, hipStream_t st, hipEvent_t *ev) {
+namespace {
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+}  // namespace
+
+ScratchPlan scratch_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int part_slots) {
+    ScratchPlan p{};
+    const size_t B = (size_t)batch, Hq = (size_t)n_q_heads, D = (size_t)head_dim;
+    const size_t n_qkv = (Hq + 2 * (size_t)n_kv_heads) * D;
+    p.proj_part = align256((size_t)proj_ranges_max(batch) * B * n_qkv * sizeof(float));
+    p.q = align256(B * Hq * D * sizeof(float));
+    p.part_o = align256(B * Hq * (size_t)part_slots * D * sizeof(float));
+    p.part_ml = align256(B * Hq * (size_t)part_slots * sizeof(float2));
+    p.item_counter = 256;
+    p.total = p.proj_part + p.q + p.part_o + p.part_ml + p.item_counter;
+    return p;
+}
+
+void carve_scratch(StepArgs &a, char *base, const ScratchPlan &p) {
+    char *c = base;
+    a.proj_part = reinterpret_cast<float *>(c);
+    c += p.proj_part;
+    a.q = reinterpret_cast<float *>(c);
+    c += p.q;
+    a.part_o = reinterpret_cast<float *>(c);
+    c += p.part_o;
+    a.part_ml = reinterpret_cast<float2 *>(c);
+    c += p.part_ml;
+    a.item_counter = reinterpret_cast<uint32_t *>(c);
+}
+
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t st, hipEvent_t *ev) {
     const int G = a.n_q_heads / a.n_kv_heads;
     if (!((a.head_dim == 128 || a.head_dim == 64) && (G == 1 || G == 2 || G == 4 || G == 8)))
         return hipErrorInvalidValue;
     hipError_t e;
+    int ranges = 1;
     if (ev) (void)hipEventRecord(ev[0], st);
-    if ((e = launch_projection(a, proj_part, st)) != hipSuccess) return e;
+    if ((e = launch_projection(a, &ranges, st)) != hipSuccess) return e;
     if (ev) (void)hipEventRecord(ev[1], st);
-    if ((e = launch_split(a, st)) != hipSuccess) return e;
+    if ((e = launch_fresh(a, ranges, st)) != hipSuccess) return e;
     if (ev) (void)hipEventRecord(ev[2], st);
-    if ((e = launch_combine(a, st)) != hipSuccess) return e;
+    if ((e = launch_split(a, st)) != hipSuccess) return e;
     if (ev) (void)hipEventRecord(ev[3], st);
+    if ((e = launch_combine(a, st)) != hipSuccess) return e;
+    if (ev) (void)hipEventRecord(ev[4], st);
     return hipSuccess;
 }
 
@@ -540,7 +573,7 @@ static void log_plan(const dkv_layout *L, int64_t n_host, int64_t n_hbm) {
     const int B = L->batch;
     const char *proj = B < L->proj_mfma_min_batch ? "gemv"
                        : B < dkv::kProjSplitkMinBatch ? "mfma one-tile streamed"
-                                                      : "mfma split-k (x staged in LDS) + partial sums";
+                                                      : "mfma split-k (x staged in LDS)";
     fprintf(stderr,
             "[dkv] layout: batch %d, hidden %d, heads %d/%d, head_dim %d, layers %d; pages per layer: "
             "%lld host, %lld HBM%s; split %d tokens (%d per sequence at most), split kernel %s on %s; "
@@ -562,6 +595,7 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
     for (int b = 0; b < batch; ++b) max_cap = std::max(max_cap, L->capacity[b]);
     L->split_tokens = choose_split_tokens(batch, shape->n_kv_heads, max_cap);
     L->max_splits = std::max(1, (std::max(1, max_cap - 1) + L->split_tokens - 1) / L->split_tokens);
+    L->scratch = dkv::scratch_plan(batch, shape->n_q_heads, shape->n_kv_heads, shape->head_dim, L->max_splits + 1);
     L->split_variant = choose_split_variant(shape->n_q_heads / shape->n_kv_heads);
     int64_t n_host = 0, n_hbm = 0;
     for (int b = 0; b < batch; ++b) {
@@ -593,27 +627,14 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
              L->max_splits);
         return cleanup(DKV_E_UNSUPPORTED);
     }
-    const int D = shape->head_dim, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads;
     const size_t n_entries = table.size();
-    const size_t bytes_q = (size_t)batch * Hq * D * sizeof(float);
-    const size_t bytes_kv = (size_t)batch * Hkv * 2 * D * sizeof(uint16_t);
-    const size_t bytes_po = (size_t)batch * Hq * L->max_splits * D * sizeof(float);
-    const size_t bytes_ml = (size_t)batch * Hq * L->max_splits * sizeof(float2);
-    const size_t bytes_pp = batch >= L->proj_mfma_min_batch && batch >= dkv::kProjSplitkMinBatch
-                                ? (size_t)dkv::kProjMaxSplits * batch * (Hq + 2 * Hkv) * D * sizeof(float)
-                                : 0;
     struct {
         void **ptr;
         size_t bytes;
     } allocs[] = {{(void **)&L->d_page_table, n_entries * sizeof(uint64_t)},
                   {(void **)&L->d_capacity, (size_t)batch * sizeof(int32_t)},
-                  {(void **)&L->d_q, bytes_q},
-                  {(void **)&L->d_kv_new, bytes_kv},
-                  {(void **)&L->d_part_o, bytes_po},
-                  {(void **)&L->d_part_ml, bytes_ml},
-                  {(void **)&L->d_proj_part, bytes_pp},
+                  {(void **)&L->d_scratch, L->scratch.total},
                   {(void **)&L->d_status, 256},
-                  {(void **)&L->d_item_counter, 256},
                   {(void **)&L->d_host_pages, host_pages ? host_pages->size() * sizeof(uint64_t) : 0},
                   {(void **)&L->d_ring, ring ? ring->size() * sizeof(uint64_t) : 0},
                   {(void **)&L->d_window, L->windowed ? (size_t)batch * sizeof(int32_t) : 0}};
@@ -638,8 +659,7 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
         e = hipMemcpy(L->d_window, L->window.data(), (size_t)batch * sizeof(int32_t), hipMemcpyHostToDevice);
     }
     if (e == hipSuccess) e = hipMemset(L->d_status, 0, 256);
-    if (e == hipSuccess) e = hipMemset(L->d_item_counter, 0, 256);
-    if (e == hipSuccess) e = hipMemset(L->d_kv_new, 0, bytes_kv);
+    if (e == hipSuccess) e = hipMemset(L->d_scratch, 0, L->scratch.total);
     if (e != hipSuccess) {
         hip_fail(e, "kv_layout_create: initialising device tables");
         return cleanup(DKV_E_HIP);
@@ -831,7 +851,7 @@ static dkv_status kv_layout_timing_enable_body(dkv_layout *L, int32_t enable, in
     L->timing_events.clear();
     L->timing_recorded = 0;
     if (!enable) return DKV_OK;
-    L->timing_events.resize((size_t)max_steps * 4);
+    L->timing_events.resize((size_t)max_steps * kTimingEvents);
     for (auto &e : L->timing_events) HIP_TRY(hipEventCreate(&e));
     return DKV_OK;
 }
@@ -841,22 +861,23 @@ dkv_status kv_layout_timing_enable(dkv_layout *L, int32_t enable, int32_t max_st
                    [&] { return kv_layout_timing_enable_body(L, enable, max_steps); });
 }
 
-dkv_status kv_layout_timing_read(dkv_layout *L, double *ms_proj, double *ms_split, double *ms_combine,
-                                 int32_t *n_steps) {
+dkv_status kv_layout_timing_read(dkv_layout *L, double *ms_proj, double *ms_fresh, double *ms_split,
+                                 double *ms_combine, int32_t *n_steps) {
     if (!L || !live(L)) return fail(DKV_E_INVALID_ARG, "kv_layout_timing_read: null or freed layout");
     HIP_TRY(hipDeviceSynchronize());
-    double sum[3] = {0.0, 0.0, 0.0};
+    double sum[kTimingEvents - 1] = {};
     for (int32_t i = 0; i < L->timing_recorded; ++i) {
-        hipEvent_t *ev = &L->timing_events[(size_t)i * 4];
-        for (int k = 0; k < 3; ++k) {
+        hipEvent_t *ev = &L->timing_events[(size_t)i * kTimingEvents];
+        for (int k = 0; k + 1 < kTimingEvents; ++k) {
             float ms = 0.0f;
             HIP_TRY(hipEventElapsedTime(&ms, ev[k], ev[k + 1]));
             sum[k] += ms;
         }
     }
     if (ms_proj) *ms_proj = sum[0];
-    if (ms_split) *ms_split = sum[1];
-    if (ms_combine) *ms_combine = sum[2];
+    if (ms_fresh) *ms_fresh = sum[1];
+    if (ms_split) *ms_split = sum[2];
+    if (ms_combine) *ms_combine = sum[3];
     if (n_steps) *n_steps = L->timing_recorded;
     L->timing_recorded = 0;
     return DKV_OK;
@@ -1145,6 +1166,7 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     a.lds_poison = L->lds_poison;
     a.proj_mfma_min_batch = L->proj_mfma_min_batch;
     a.max_splits = L->max_splits;
+    a.part_slots = L->max_splits + 1;
     a.qscale = (float)(1.4426950408889634074 / std::sqrt((double)s->head_dim));
     a.page_table = L->d_page_table + (size_t)layer * L->batch * L->max_pages;
     a.capacity = L->d_capacity;
@@ -1153,16 +1175,12 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     a.ctx_lens = ctx_lens;
     a.out = out;
     a.out_f32 = out_f32;
-    a.q = L->d_q;
-    a.kv_new = L->d_kv_new;
-    a.part_o = L->d_part_o;
-    a.part_ml = L->d_part_ml;
+    dkv::carve_scratch(a, L->d_scratch, L->scratch);
     a.status = L->d_status;
-    a.item_counter = L->d_item_counter;
     hipEvent_t *ev = nullptr;
-    if (!L->timing_events.empty() && (size_t)(L->timing_recorded + 1) * 4 <= L->timing_events.size())
-        ev = &L->timing_events[(size_t)L->timing_recorded++ * 4];
-    hipError_t e = dkv::launch_decode_step(a, L->d_proj_part, reinterpret_cast<hipStream_t>(stream), ev);
+    if (!L->timing_events.empty() && (size_t)(L->timing_recorded + 1) * kTimingEvents <= L->timing_events.size())
+        ev = &L->timing_events[(size_t)L->timing_recorded++ * kTimingEvents];
+    hipError_t e = dkv::launch_decode_step(a, reinterpret_cast<hipStream_t>(stream), ev);
     if (e != hipSuccess) return hip_fail(e, who);
     return DKV_OK;
 }

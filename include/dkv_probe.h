@@ -49,16 +49,16 @@ dkv_status kv_pool_copy(dkv_pool *dst, const dkv_pool *src, int64_t bytes, dkv_s
 
 /* Per-kernel timing of a layout's decode steps. While enabled, decode_step
  * records HIP events on its stream before and after each of its kernels
- * (projection, split attention, combine) for up to max_steps steps; enabling
- * creates those events, so do it outside graph capture. Disabling (enable =
- * 0) destroys them. */
+ * (projection, fresh token, split attention, combine) for up to max_steps
+ * steps; enabling creates those events, so do it outside graph capture.
+ * Disabling (enable = 0) destroys them. */
 dkv_status kv_layout_timing_enable(dkv_layout *layout, int32_t enable, int32_t max_steps);
 
 /* Synchronises, then returns the milliseconds each kernel took summed over
  * the steps recorded since the last read (*n_steps of them), and restarts
  * the count. Any output pointer may be NULL. */
-dkv_status kv_layout_timing_read(dkv_layout *layout, double *ms_projection, double *ms_split,
-                                 double *ms_combine, int32_t *n_steps);
+dkv_status kv_layout_timing_read(dkv_layout *layout, double *ms_projection, double *ms_fresh,
+                                 double *ms_split, double *ms_combine, int32_t *n_steps);
 
 /* ---------------------------------------------------------------------------
  * GEMM with an operand in host memory: the experiment behind CPU-aware tiling

@@ -70,7 +70,7 @@ int main() {
     EXPECT(kv_layout_set_split_kernel(stranger, 0) == DKV_E_INVALID_ARG);
     EXPECT(kv_layout_page_tier(stranger, 0, 0, &tier) == DKV_E_INVALID_ARG && tier == -7);
     EXPECT(kv_layout_timing_enable(stranger, 1, 4) == DKV_E_INVALID_ARG);
-    EXPECT(kv_layout_timing_read(stranger, nullptr, nullptr, nullptr, nullptr) == DKV_E_INVALID_ARG);
+    EXPECT(kv_layout_timing_read(stranger, nullptr, nullptr, nullptr, nullptr, nullptr) == DKV_E_INVALID_ARG);
     EXPECT(kv_layout_check_status(stranger) == DKV_E_INVALID_ARG);
     EXPECT(kv_layout_free(stranger) == DKV_E_INVALID_ARG);
     EXPECT(std::strlen(dkv_last_error()) > 0);

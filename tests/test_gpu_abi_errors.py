@@ -44,7 +44,7 @@ def test_double_free_and_use_after_free_are_refused():
     tier = ctypes.c_int32(-7)
     assert L.kv_layout_page_tier(h_layout, 0, 0, ctypes.byref(tier)) == E_INVALID_ARG and tier.value == -7
     assert L.kv_layout_timing_enable(h_layout, 1, 4) == E_INVALID_ARG
-    assert L.kv_layout_timing_read(h_layout, None, None, None, None) == E_INVALID_ARG
+    assert L.kv_layout_timing_read(h_layout, None, None, None, None, None) == E_INVALID_ARG
     ctx = np.zeros(2, np.int32)
     assert L.kv_advance(h_layout, ctx.ctypes.data, None) == E_INVALID_ARG
     k = np.zeros((1, 4, 64), np.uint16)
