@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
             "kv_read": ([P, I32, I32, I32, I32, P, P], I32),
             "decode_step": ([P, I32, P, P, P, P, P], I32),
             "decode_step_f32": ([P, I32, P, P, P, P, P], I32),
+            "decode_step_noalloc": ([P, I32, P, P, P, P, P], I32),
+            "decode_step_noalloc_scratch_bytes": ([], ctypes.c_size_t),
             "dkv_probe_stream_read": ([P, ctypes.c_uint64, I32, I32, I32, P], I32),
             "kv_pool_copy": ([P, P, I64, P], I32),
             "dkv_host_buffer_alloc": ([ctypes.c_uint64, U32, P, P], I32),
@@ -113,7 +115,7 @@ EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement",
             "kv_alloc_hbm", "kv_pool_free_pages", "kv_pool_info", "kv_pool_free",
             "kv_layout_create", "kv_layout_create_windowed", "kv_advance", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
             "kv_layout_split_kernel", "kv_layout_set_split_kernel", "kv_layout_split_waves", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
-            "dkv_probe_stream_read", "kv_pool_copy", "dkv_host_buffer_alloc", "dkv_host_buffer_free",
+            "decode_step_noalloc", "decode_step_noalloc_scratch_bytes", "dkv_probe_stream_read", "kv_pool_copy", "dkv_host_buffer_alloc", "dkv_host_buffer_free",
             "dkv_copy", "dkv_gemm_bf16_nt", "kv_layout_timing_enable", "kv_layout_timing_read",
             "dkv_cpu_attention", "dkv_cpu_stream_read", "dkv_cpu_attention_pages"]
 
@@ -361,6 +363,19 @@ def decode_step_f32(layout: Layout, layer: int, q_in, W_qkv, ctx_lens, attn_out=
     if attn_out.dtype != torch.float32:
         raise ValueError("attn_out must be float32")
     return _step(lib().decode_step_f32, layout, layer, q_in, W_qkv, ctx_lens, attn_out, stream)
+
+
+def decode_step_noalloc(layout: Layout, layer: int, q_in, W_qkv, ctx_lens, attn_out, stream=None):
+    """decode_step on the library's static device scratch (no allocation in the
+    call); attn_out [batch][Hq*d] bf16 must be given."""
+    import torch
+    if attn_out is None or attn_out.dtype != torch.bfloat16:
+        raise ValueError("attn_out must be a bfloat16 device tensor")
+    return _step(lib().decode_step_noalloc, layout, layer, q_in, W_qkv, ctx_lens, attn_out, stream)
+
+
+def decode_step_noalloc_scratch_bytes() -> int:
+    return int(lib().decode_step_noalloc_scratch_bytes())
 
 
 def probe_stream_read(device_ptr: int, nbytes: int, grid: int = 256, unroll: int = 2,

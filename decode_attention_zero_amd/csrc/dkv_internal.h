@@ -103,6 +103,16 @@ ScratchPlan scratch_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim,
 // Points a's scratch fields into `base` (an allocation of plan.total bytes).
 void carve_scratch(StepArgs &a, char *base, const ScratchPlan &plan);
 
+// Records a failed HIP call as the thread's last error; returns DKV_E_HIP.
+dkv_status report_hip_error(hipError_t e, const char *what);
+
+// Runs decode_step on `scratch` (capacity bytes of device memory) instead of
+// the layout's own scratch: DKV_E_CAPACITY, with nothing enqueued, when the
+// layout's step needs more. `who` names the entry point in error messages.
+dkv_status decode_step_on_scratch(dkv_layout *layout, int32_t layer, const uint16_t *q_in, const uint16_t *W,
+                                  const int32_t *ctx_lens, uint16_t *attn_out, dkv_stream_t stream, char *scratch,
+                                  size_t capacity, const char *who);
+
 // Enqueues the decode step's kernels on `stream`. With `events` non-null,
 // records events[0] before the projection, events[1] after it, events[2]
 // after the fresh-token kernel, events[3] after the split attention and

@@ -1141,7 +1141,7 @@ dkv_status dkv_cpu_stream_read(const void *host_ptr, uint64_t bytes, int32_t n_t
 
 static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, const uint16_t *W,
                             const int32_t *ctx_lens, void *out, int out_f32, dkv_stream_t stream,
-                            const char *who) {
+                            const char *who, char *scratch = nullptr, size_t scratch_capacity = 0) {
     if (!L || !live(L)) return fail(DKV_E_INVALID_ARG, "%s: null or freed layout", who);
     if (layer < 0 || layer >= L->shape.n_layers)
         return fail(DKV_E_INVALID_ARG, "%s: layer %d out of range", who, layer);
@@ -1175,7 +1175,10 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     a.ctx_lens = ctx_lens;
     a.out = out;
     a.out_f32 = out_f32;
-    dkv::carve_scratch(a, L->d_scratch, L->scratch);
+    if (scratch && L->scratch.total > scratch_capacity)
+        return fail(DKV_E_CAPACITY, "%s: this layout's step needs %zu bytes of scratch, more than the %zu available",
+                    who, L->scratch.total, scratch_capacity);
+    dkv::carve_scratch(a, scratch ? scratch : L->d_scratch, L->scratch);
     a.status = L->d_status;
     hipEvent_t *ev = nullptr;
     if (!L->timing_events.empty() && (size_t)(L->timing_recorded + 1) * kTimingEvents <= L->timing_events.size())
@@ -1189,6 +1192,19 @@ dkv_status decode_step(dkv_layout *L, int32_t layer, const uint16_t *q_in, const
                        const int32_t *ctx_lens, uint16_t *attn_out, dkv_stream_t stream) {
     return step_impl(L, layer, q_in, W_qkv, ctx_lens, attn_out, 0, stream, "decode_step");
 }
+
+}  // extern "C"
+
+dkv_status dkv::report_hip_error(hipError_t e, const char *what) { return hip_fail(e, what); }
+
+dkv_status dkv::decode_step_on_scratch(dkv_layout *L, int32_t layer, const uint16_t *q_in, const uint16_t *W,
+                                       const int32_t *ctx_lens, uint16_t *attn_out, dkv_stream_t stream,
+                                       char *scratch, size_t capacity, const char *who) {
+    if (!scratch) return fail(DKV_E_INVALID_ARG, "%s: no scratch", who);
+    return step_impl(L, layer, q_in, W, ctx_lens, attn_out, 0, stream, who, scratch, capacity);
+}
+
+extern "C" {
 
 dkv_status decode_step_f32(dkv_layout *L, int32_t layer, const uint16_t *q_in, const uint16_t *W_qkv,
                            const int32_t *ctx_lens, float *attn_out, dkv_stream_t stream) {

@@ -254,6 +254,27 @@ dkv_status decode_step_f32(dkv_layout *kv_layout, int32_t layer,
                            const int32_t *ctx_lens, float *attn_out,
                            dkv_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as decode_step, with the same arguments, errors and results (identical
+ * bits), whose scratch (projection sums, queries, split partials, work-queue
+ * counter) is a file-scope device array of decode_step_noalloc_scratch_bytes()
+ * bytes (32 MiB) instead of the layout's. The call allocates nothing; its
+ * first call on a device looks the array's address up once. A layout whose
+ * step needs more scratch than the array holds gets DKV_E_CAPACITY and
+ * nothing is enqueued. Every buffer of the array that a step reads is written
+ * earlier in the same step (the work-queue counter is zeroed by the step's
+ * own kernel), so no clearing is needed between calls. All calls on one GPU
+ * share its one array: calls that overlap on a GPU (different streams without
+ * ordering, other threads) race and give undefined results; order them. */
+dkv_status decode_step_noalloc(dkv_layout *kv_layout, int32_t layer,
+                               const uint16_t *q_in, const uint16_t *W_qkv,
+                               const int32_t *ctx_lens, uint16_t *attn_out,
+                               dkv_stream_t stream);
+
+/* Size in bytes of decode_step_noalloc's static scratch array. */
+size_t decode_step_noalloc_scratch_bytes(void);
+
 /* Advances every sequence by one decoded token, on the device: for each b
  * with ctx_lens[b] + 1 < capacity, ctx_lens[b] += 1 (in place; ctx_lens is
  * the device array decode_step reads). In a windowed layout, when the new
