@@ -1,11 +1,12 @@
 """Decode-step benchmark: effective KV bandwidth of one zero-copy decode step.
 
-Workload (default): Llama-3-8B-shaped layer (hidden 4096, 32 query / 8 KV
-heads, head_dim 128), batch 8, 32768 cached tokens per sequence, KV 100 % in
-host-pinned memory read in place over the host link; synthetic bf16 inputs
-from the seeded generator (W ~ N(0, 0.02^2), x and K/V ~ N(0, 1)).
-``--workload`` selects any of the five workloads (see synth/configs.py); for
-a multi-layer workload a step runs every layer in order.
+Workload (default): eight Llama-3-70B-shaped layers (hidden 8192, 64 query /
+8 KV heads, head_dim 128), batch 16, 131072 cached tokens per sequence, KV
+100 % in host-pinned memory (8 GiB per layer, 64 GiB per step) read in place
+over the host link; synthetic bf16 inputs from the seeded generator (W ~
+N(0, 0.015^2), x and K/V ~ N(0, 1)). ``--workload`` selects any of the five
+workloads (see synth/configs.py); for a multi-layer workload a step runs
+every layer in order.
 
 A step is one decode_step call per layer: QKV projection, attention over
 every cached token plus the fresh one, fresh K/V write-back, split combine.
@@ -18,7 +19,9 @@ graph_ms_per_step (the same step replayed from one captured HIP graph),
 roofline (dominant kernel = split attention, against the host link), the
 measured host-link streaming-read ceiling, the same step with every page in
 HBM (against 8 TB/s), the naive zero-copy, staging and host-CPU attention
-comparators, and the fp64 oracle timed on the host cores on the same workload.
+comparators, and the fp64 oracle timed on the host cores on the same workload
+(whole steps of a one-layer workload; one whole layer of a multi-layer one),
+with the parity of the bench's own output against it.
 
 ``--sweep`` steps the host-resident share of the KV from 0 to 100 %;
 ``--sweep-ctx`` steps the context length (zero-copy, all-HBM, staging and
@@ -53,7 +56,11 @@ class Resident:
     """One workload's KV in its pools (placed by `tail`), plus x, W, ctx_lens
     in HBM, for every layer."""
 
-    def __init__(self, dkv, wl, ctx, tail, kv_source):
+    def __init__(self, dkv, wl, ctx, tail, kv_source, copy_from=None):
+        """copy_from: a Resident of the same workload whose pool holds every
+        page on the host; this one's (every page in HBM) is then filled by a
+        copy-engine copy of that pool instead of drawing the KV again (pages
+        are handed out in the same order, so every page keeps its offset)."""
         import torch
         self.dkv = dkv
         self.wl = wl
@@ -76,23 +83,28 @@ class Resident:
         self.layout = dkv.kv_layout_create(self.shape, cap, tail, self.host_pool, self.hbm_pool)
         dev = torch.device("cuda", 0)
         self.x, self.W = [], []
+        if copy_from is not None:
+            src = copy_from.host_pool
+            assert n_host == 0 and copy_from.hbm_pool is None and src.info()[1] == n_hbm * self.page_bytes
+            dkv.kv_pool_copy(self.hbm_pool, src, src.info()[1])
+            torch.cuda.synchronize()
         for layer in range(wl.n_layers):
-            for b in range(len(ctx)):
+            for b in range(len(ctx) if copy_from is None else 0):
                 for t0 in range(0, int(ctx[b]), CHUNK):
                     t1 = min(int(ctx[b]), t0 + CHUNK)
                     k, v = kv_source(layer, b, t0, t1)
                     dkv.kv_append(self.layout, layer, b, t0, k, v)
             self.x.append(torch.from_numpy(wl.x(layer).view(np.int16)).to(dev).view(torch.bfloat16))
             self.W.append(torch.from_numpy(wl.W(layer).view(np.int16)).to(dev).view(torch.bfloat16))
-            if wl.n_layers > 1:
+            if wl.n_layers > 1 and copy_from is None:
                 log("layer %d resident" % layer)
         self.ctx = torch.from_numpy(ctx.copy()).to(dev)
         self.out = [torch.empty((len(ctx), wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16,
                                 device=dev) for _ in range(wl.n_layers)]
         self.stream = torch.cuda.current_stream()
 
-    def step(self):
-        for layer in range(self.n_layers):
+    def step(self, layers=None):
+        for layer in (range(self.n_layers) if layers is None else layers):
             self.dkv.decode_step(self.layout, layer, self.x[layer], self.W[layer], self.ctx,
                                  self.out[layer], self.stream)
 
@@ -166,10 +178,27 @@ class Resident:
                 p.free()
 
 
-def probe_ceiling(dkv, pool, configs_, max_bytes=4 << 30):
+HOST_PROBE_BYTES = 4 << 30
+
+
+def probe_ceiling(dkv, pool, configs_, max_bytes=HOST_PROBE_BYTES):
     base, nbytes, _ = pool.info()
     nbytes = min(nbytes, max_bytes)
     nbytes -= nbytes % (1 << 20)
+    return probe_region(dkv, base, nbytes, configs_)
+
+
+def probe_host_link(dkv, configs_, nbytes=HOST_PROBE_BYTES, flags=0):
+    """The host-link streaming-read ceiling on a fresh pinned buffer of
+    `nbytes` (4 GiB), allocated like a host pool (mapped, coherent)."""
+    buf = dkv.HostBuffer(nbytes, flags)
+    try:
+        return probe_region(dkv, buf.device_ptr, nbytes, configs_)
+    finally:
+        buf.free()
+
+
+def probe_region(dkv, base, nbytes, configs_):
     best = 0.0
     rows = []
     for grid, unroll in configs_:
@@ -215,22 +244,32 @@ def split_kernel_sha256() -> str:
     return h.hexdigest()
 
 
-def counter_traffic(workload: str, all_hbm: bool = False):
+def traffic_record_path(workload: str, all_hbm: bool = False, kernel: str | None = None) -> str:
+    return os.path.join(ROOT, "profiles", "attn_split_%s%s%s_traffic.json"
+                        % (workload, "_allhbm" if all_hbm else "", "_" + kernel if kernel else ""))
+
+
+def counter_traffic(workload: str, all_hbm: bool = False, kernel: str | None = None):
     """HBM + host-link bytes per split-kernel launch from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a copy kernel of known
     size); None when the summary is missing or the kernel's sources have
-    changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "attn_split_%s%s_traffic.json"
-                        % (workload, "_allhbm" if all_hbm else ""))
+    changed since the counters were taken. kernel: None for the layout's
+    default split kernel, or a --split-kernel name (naive: the comparator)."""
+    rec = counter_record(workload, all_hbm, kernel)
+    return None if rec is None else int(rec["traffic_bytes_per_launch"])
+
+
+def counter_record(workload: str, all_hbm: bool = False, kernel: str | None = None):
+    """The committed counter record of a split kernel (see counter_traffic),
+    or None when it is missing or stale."""
+    path = traffic_record_path(workload, all_hbm, kernel)
     try:
         with open(path) as f:
             rec = json.load(f)
         sha = split_kernel_sha256()
     except OSError:
         return None
-    if rec.get("split_kernel_sources_sha256") != sha:
-        return None
-    return int(rec["traffic_bytes_per_launch"])
+    return rec if rec.get("split_kernel_sources_sha256") == sha else None
 
 
 def pmc_per_dispatch(path: str, counter: str):
@@ -246,6 +285,9 @@ def pmc_per_dispatch(path: str, counter: str):
             vals[i] = vals.get(i, 0.0) + float(row["Counter_Value"])
             names[i] = row["Kernel_Name"]
     return {i: (names[i], vals[i]) for i in vals}
+
+
+TCC_ROUTE_COUNTERS = ("TCC_EA0_RDREQ_IO_32B_sum", "TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_HIT_sum", "TCC_MISS_sum")
 
 
 def write_traffic_record(wl, args) -> int:
@@ -274,11 +316,13 @@ def write_traffic_record(wl, args) -> int:
     mf, mw = sum(split_f) / len(split_f), sum(split_w) / len(split_w)
     traffic = (mf * fetch_scale + mw * write_scale) * 1024
     alg = int(wl.ctx_lens().astype(np.int64).sum()) * wl.kv_bytes_per_token   # one layer = one launch
-    sfx = "_allhbm" if args.all_hbm else ""
+    sfx = ("_allhbm" if args.all_hbm else "") + ("_" + args.split_kernel if args.split_kernel else "")
+    opts = (" --all-hbm" if args.all_hbm else "") + (" --split-kernel " + args.split_kernel if args.split_kernel else "")
     run = "python3 $REPO/bench.py --workload %s --profile-run%s --calibrate --steps %d --warmup %d" % (
-        wl.name, " --all-hbm" if args.all_hbm else "", args.steps, args.warmup)
+        wl.name, opts, args.steps, args.warmup)
     rec = {"kernel": kernel,
-           "workload": wl.name + (", every page in HBM" if args.all_hbm else ""),
+           "workload": wl.name + (", every page in HBM" if args.all_hbm else "")
+           + (", split kernel " + args.split_kernel if args.split_kernel else ""),
            "split_kernel_sources_sha256": split_kernel_sha256(),
            "fetch_size_kib_per_dispatch": round(mf, 3), "write_size_kib_per_dispatch": round(mw, 3),
            "dispatches": len(split_f),
@@ -292,15 +336,36 @@ def write_traffic_record(wl, args) -> int:
                "rocprofv3 --pmc %s --output-format csv -d $REPO/gpurun_out/pmc_%s%s_%s -o pmc -- %s"
                % (c, wl.name, sfx, c, run) for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
                "python3 $REPO/bench.py --workload %s%s --steps %d --warmup %d --traffic-record "
-               "$REPO/gpurun_out/pmc_%s%s" % (wl.name, " --all-hbm" if args.all_hbm else "", args.steps,
-                                               args.warmup, wl.name, sfx)],
+               "$REPO/gpurun_out/pmc_%s%s" % (wl.name, opts, args.steps, args.warmup, wl.name, sfx)],
            "hashed_sources": "attn_split.hip, device_common.h, struct StepArgs of dkv_internal.h; "
                              "comments and whitespace removed"}
-    out = os.path.join(ROOT, "profiles", "attn_split_%s%s_traffic.json" % (wl.name, sfx))
+    # Optional third pass: where the L2's read requests went (host link = IO,
+    # HBM = DRAM, in 32-byte units) and its hit rate.
+    tcc_dir = os.path.join(prefix + "_TCC", "pmc_counter_collection.csv")
+    if os.path.exists(tcc_dir):
+        cnt = {c: pmc_per_dispatch(tcc_dir, c) for c in TCC_ROUTE_COUNTERS}
+
+        def mean_of(c, key="attn_split"):
+            v = of(cnt[c], key)
+            return sum(v) / len(v) if v else None
+
+        io, dram = mean_of("TCC_EA0_RDREQ_IO_32B_sum"), mean_of("TCC_EA0_RDREQ_DRAM_32B_sum")
+        hit, miss = mean_of("TCC_HIT_sum"), mean_of("TCC_MISS_sum")
+        rec["l2_read_routes"] = {
+            "host_link_read_bytes_per_dispatch": io * 32, "hbm_read_bytes_per_dispatch": dram * 32,
+            "l2_hit_rate": hit / (hit + miss) if hit is not None and hit + miss > 0 else None,
+            "host_link_reads_over_algorithmic": io * 32 / alg,
+            "calibration_host_stream_read_bytes_per_dispatch": sorted(
+                v * 32 for v in of(cnt["TCC_EA0_RDREQ_IO_32B_sum"], "stream_read")),
+            "counters": list(TCC_ROUTE_COUNTERS)}
+        rec["commands"].insert(3, "rocprofv3 --pmc %s --output-format csv -d $REPO/gpurun_out/pmc_%s%s_TCC -o pmc "
+                                  "-- %s" % (" ".join(TCC_ROUTE_COUNTERS), wl.name, sfx, run))
+    out = traffic_record_path(wl.name, args.all_hbm, args.split_kernel)
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps({"record": os.path.relpath(out, ROOT), "kernel": kernel, "dispatches": len(split_f),
-                      "traffic_over_algorithmic": round(traffic / alg, 4)}))
+                      "traffic_over_algorithmic": round(traffic / alg, 4),
+                      "l2_read_routes": rec.get("l2_read_routes")}))
     return 0
 
 
@@ -461,7 +526,7 @@ def projection_facts(wl, ms):
     read rate and its matrix-core use against the dense bf16 peak."""
     B = wl.batch
     kernel = ("qkv_proj_gemv_kernel" if B < 8 else "qkv_proj_stream_kernel" if B < 16 else
-              "qkv_proj_splitk_kernel + qkv_proj_finish_kernel")
+              "qkv_proj_splitk_kernel")
     w_bytes = wl.n_qkv * wl.hidden * 2 * wl.n_layers
     flop = 2.0 * B * wl.hidden * wl.n_qkv * wl.n_layers
     return {"kernel": kernel, "ms": round(ms, 4), "W_bytes": w_bytes,
@@ -540,93 +605,6 @@ def cpu_attention_timed(dkv, r, wl, ctx, threads, reps):
             _, used = dkv.cpu_attention(r.layout, layer, q, kn, vn, ctx, threads)
         times.append(time.perf_counter() - t0)
     return float(np.median(times)), used
-
-
-def kv_pages(K, V, page_tokens):
-    """One sequence's cached K and V ([L][Hkv][d] bf16 bits each) in the
-    library's page layout: [page][KV head][K|V][token in page][dim], the last
-    page zero-padded."""
-    L, Hkv, d = K.shape
-    P = (L + page_tokens - 1) // page_tokens
-    kv = np.zeros((2, P * page_tokens, Hkv, d), np.uint16)
-    kv[0, :L], kv[1, :L] = K, V
-    return np.ascontiguousarray(kv.reshape(2, P, page_tokens, Hkv, d).transpose(1, 3, 0, 2, 4))
-
-
-def cpu_gpu_split(dkv, wl, ctx, kv_source, K_all, V_all, ms_gpu_all, cpu_s_all, threads, steps):
-    """The batch split between the two readers of host memory: the first k
-    sequences' attention on `threads` host threads over their pages in host
-    DRAM, the other B - k sequences' decode step on the GPU reading their
-    pages over the host link, at the same time. k balances the two from their
-    separate full-batch times. Pages for the CPU side are built in the
-    library's page layout from the same logical K/V, in pinned host memory;
-    queries and fresh K/V are seeded inputs, as in the CPU comparator (a
-    timing run)."""
-    import threading
-    import torch
-    B, Hkv, d = len(ctx), wl.n_kv_heads, wl.head_dim
-    k = int(round(B * ms_gpu_all / (ms_gpu_all + cpu_s_all * 1e3)))
-    k = min(max(k, 1), B - 1)
-    shape = dkv.Shape.of(wl.hidden, wl.n_q_heads, Hkv, d, 1)
-    page_elems = dkv.kv_page_bytes(shape) // 2
-    n_pages = [(int(ctx[b]) + dkv.PAGE_TOKENS - 1) // dkv.PAGE_TOKENS for b in range(k)]
-    # The CPU side's pages live in pinned host memory (hipHostMalloc), like the pool's.
-    buf = dkv.HostBuffer(sum(n_pages) * page_elems * 2)
-    mem = buf.view(np.uint16, (sum(n_pages), Hkv, 2, dkv.PAGE_TOKENS, d))
-    pages, first = [], 0
-    for b in range(k):
-        P = n_pages[b]
-        mem[first:first + P] = kv_pages(K_all[b, :int(ctx[b])], V_all[b, :int(ctx[b])], dkv.PAGE_TOKENS)
-        pages.append([mem[first + p] for p in range(P)])
-        first += P
-    q, kn, vn = cpu_step_inputs(wl, k)
-    q = np.ascontiguousarray(q, np.float32)
-    kn, vn = np.ascontiguousarray(kn, np.uint16), np.ascontiguousarray(vn, np.uint16)
-    ctx_c = np.ascontiguousarray(ctx[:k], np.int32)
-    out = np.empty_like(q)
-    # The page table is built once, outside the timed calls (building it in
-    # Python costs milliseconds per step).
-    import ctypes
-    max_pages = max(n_pages)
-    table = (ctypes.c_void_p * (k * max_pages))()
-    for b in range(k):
-        for i, page in enumerate(pages[b]):
-            table[b * max_pages + i] = page.ctypes.data
-    used = ctypes.c_int32()
-    L = dkv.lib()
-
-    def cpu_once():
-        st = L.dkv_cpu_attention_pages(table, max_pages, ctypes.byref(shape), k, q.ctypes.data, kn.ctypes.data,
-                                       vn.ctypes.data, ctx_c.ctypes.data, out.ctypes.data, threads,
-                                       ctypes.byref(used))
-        if st != 0:
-            raise RuntimeError("dkv_cpu_attention_pages: status %d" % st)
-
-    cpu_once()
-    t_cpu = []
-    for _ in range(3):
-        t0 = time.perf_counter()
-        cpu_once()
-        t_cpu.append(time.perf_counter() - t0)
-    rg = Resident(dkv, wl.replace(batch=B - k), np.ascontiguousarray(ctx[k:]), np.zeros(B - k, np.int32),
-                  lambda layer, b, t0, t1: kv_source(layer, b + k, t0, t1))
-    ms_g = rg.timed(steps, 2)
-    together = []
-    for _ in range(max(5, steps // 2)):
-        th = threading.Thread(target=cpu_once)
-        t0 = time.perf_counter()
-        th.start()
-        rg.step()
-        torch.cuda.synchronize()
-        th.join()
-        together.append(time.perf_counter() - t0)
-    rg.free()
-    pages = mem = None
-    buf.free()
-    ms_t = float(np.median(together)) * 1e3
-    return {"cpu_sequences": k, "gpu_sequences": B - k, "cpu_threads": threads,
-            "cpu_alone_ms": round(float(np.median(t_cpu)) * 1e3, 4), "gpu_alone_ms": round(ms_g, 4),
-            "together_ms": round(ms_t, 4)}
 
 
 def cpu_dram_read_GBps(dkv, threads, nbytes=1 << 30):
@@ -828,7 +806,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama3-8b-b8-ctx32768-host")
+    ap.add_argument("--workload", default="llama3-70b-b16-ctx131072-8layers-host")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-leg", action="store_true")
     ap.add_argument("--sweep", action="store_true",
@@ -860,6 +838,9 @@ def main(argv=None):
     ap.add_argument("--all-hbm", action="store_true",
                     help="with --profile-run: place every page in HBM instead of the "
                          "workload's own placement")
+    ap.add_argument("--split-kernel", choices=("regs", "lds", "mfma", "naive"),
+                    help="with --profile-run (and --traffic-record): the split kernel to run instead of "
+                         "the layout's default (naive: the per-query-head comparator)")
     ap.add_argument("--calibrate", action="store_true",
                     help="with --profile-run: also run kernels of known traffic (a 256 MiB "
                          "HBM-to-HBM copy, 1 GiB streaming reads of the host pool and of HBM) "
@@ -892,22 +873,24 @@ def main(argv=None):
     ctx = wl.ctx_lens()
     B, Hkv, d = wl.batch, wl.n_kv_heads, wl.head_dim
     tail = wl.hbm_tail(ctx)
-    # The oracle baseline needs the logical-order KV; keep it for single-layer
-    # workloads (the default one is 1 GiB), otherwise draw chunks on demand.
-    keep = wl.n_layers == 1 and not args.no_cpu_baseline and not args.profile_run
-    K_all = V_all = None
+    multi = wl.n_layers > 1
+    # Layer 0's KV in logical order, for the oracle (the CPU baseline and the
+    # parity of this run's own output): drawn once, and layer 0's pages are
+    # appended from it; the other layers are drawn chunk by chunk.
+    keep = not args.no_cpu_baseline and not args.profile_run and not args.sweep and not args.multistep
+    K0 = V0 = None
     if keep:
-        log("generating inputs for %s" % wl.name)
+        log("drawing layer 0's KV of %s" % wl.name)
         Lmax = int(ctx.max())
-        K_all = np.zeros((B, Lmax, Hkv, d), np.uint16)
-        V_all = np.zeros_like(K_all)
+        K0 = np.zeros((B, Lmax, Hkv, d), np.uint16)
+        V0 = np.zeros_like(K0)
         for b in range(B):
-            wl.kv("k", 0, b, 0, int(ctx[b]), out=K_all[b, :ctx[b]])
-            wl.kv("v", 0, b, 0, int(ctx[b]), out=V_all[b, :ctx[b]])
+            wl.kv("k", 0, b, 0, int(ctx[b]), out=K0[b, :ctx[b]])
+            wl.kv("v", 0, b, 0, int(ctx[b]), out=V0[b, :ctx[b]])
 
     def kv_source(layer, b, t0, t1):
-        if K_all is not None:
-            return K_all[b, t0:t1], V_all[b, t0:t1]
+        if layer == 0 and K0 is not None:
+            return K0[b, t0:t1], V0[b, t0:t1]
         return wl.kv("k", layer, b, t0, t1), wl.kv("v", layer, b, t0, t1)
 
     kv_layer_bytes = int(ctx.astype(np.int64).sum()) * wl.kv_bytes_per_token
@@ -926,6 +909,8 @@ def main(argv=None):
         tail = np.full(B, 1 << 30, np.int32)
     log("%s: %s placement leg" % (wl.name, "all-HBM" if args.profile_run and args.all_hbm else "own"))
     r = Resident(dkv, wl, ctx, tail, kv_source)
+    if args.split_kernel:
+        r.layout.split_kernel = args.split_kernel
     host_kv_layer = 0
     for b in range(B):
         n, first = dkv.kv_placement(int(ctx[b]) + 1, int(tail[b]))
@@ -935,49 +920,83 @@ def main(argv=None):
     hbm_kv = kv_bytes - host_kv
     ms = r.timed(args.steps, args.warmup)
     step_stats = r.step_stats
-    kt = r.kernel_times(args.steps)
+    # Per-kernel events and the graph replay: every step of a one-layer
+    # workload again; a few steps of a multi-layer one (each is 8 layers).
+    n_aux = args.steps if not multi else max(1, min(args.steps, 3))
+    kt = r.kernel_times(n_aux)
     if args.profile_run:
         if args.calibrate:
             calibrate(dkv, r)
+        label = split_kernel_label(r.layout)
         r.free()
         print(json.dumps({"profile_run": True, "workload": wl.name, "all_hbm": bool(args.all_hbm),
-                          "ms_per_step": ms,
-                          "kernel_ms": kt}), flush=True)
+                          "split_kernel": label, "ms_per_step": ms, "kernel_ms": kt}), flush=True)
         return 0
-    ms_graph = r.graph_timed(args.steps)
+    ms_graph = r.graph_timed(n_aux)
     out_own = r.out_bits(0)
     split_kernel_name = split_kernel_label(r.layout)
-    ceiling = ceiling_rows = None
+    ceiling = ceiling_rows = probe_bytes = None
     if r.host_pool is not None:
-        ceiling, ceiling_rows, _ = probe_ceiling(dkv, r.host_pool, HOST_PROBES)
-    log("own placement: %.3f ms/step, split kernel %.3f ms" % (ms, kt["split"]))
+        # On at least 4 GiB of pinned memory: the pool itself when it is that
+        # large (a second pinned buffer beside a 64 GiB pool is refused on these
+        # hosts), else a fresh 4 GiB buffer allocated like the pool.
+        if r.host_pool.info()[1] >= HOST_PROBE_BYTES:
+            ceiling, ceiling_rows, probe_bytes = probe_ceiling(dkv, r.host_pool, HOST_PROBES)
+        else:
+            ceiling, ceiling_rows, probe_bytes = probe_host_link(dkv, HOST_PROBES)
+    log("own placement: %.3f ms/step, split kernel %.3f ms; host-link ceiling %.2f GB/s"
+        % (ms, kt["split"], ceiling or 0.0))
 
     value = kv_bytes / (ms * 1e-3) / 1e9
     split_gbps = kv_bytes / (kt["split"] * 1e-3) / 1e9
+    method_traffic = counter_traffic(wl.name)
 
     # ------------------------------------------------------------------ comparator: naive zero-copy
     comparators = {}
     if r.host_pool is not None and not args.no_comparators:
         default_kernel = r.layout.split_kernel
         r.layout.split_kernel = "naive"
-        n_cmp = max(1, min(args.steps, 5))
-        ms_n = r.timed(n_cmp, 1)
+        if multi:
+            r.step(layers=[0])             # warm-up: one layer
+            ms_n = r.timed(1, 0)
+        else:
+            ms_n = r.timed(max(1, min(args.steps, 5)), 1)
         out_naive = r.out_bits(0)
         r.layout.split_kernel = default_kernel
-        comparators["naive_zero_copy"] = {
-            "what": "one work item per query head: each KV head's pages read once per query "
-                    "head of its group (%dx the link bytes of the grouped kernel)" % wl.group,
+        naive_traffic = counter_traffic(wl.name, kernel="naive")
+        per_step = lambda t: None if t is None else int(t * wl.n_layers)
+
+        def link_reads(rec):
+            routes = (rec or {}).get("l2_read_routes")
+            return None if not routes else routes["host_link_read_bytes_per_dispatch"] * wl.n_layers
+
+        naive_rec, method_rec = counter_record(wl.name, kernel="naive"), counter_record(wl.name)
+        naive = {
+            "what": "one work item per query head: each KV head's pages requested once per query "
+                    "head of its group (%dx the bytes the grouped kernel requests)" % wl.group,
             "ms_per_step": round(ms_n, 4),
             "effective_kv_GBps": round(kv_bytes / (ms_n * 1e-3) / 1e9, 3),
-            "host_link_bytes_per_step": host_kv * wl.group,
+            "requested_bytes_per_step": host_kv * wl.group + hbm_kv * wl.group,
+            "link_bytes_bound_per_step": int(ceiling * 1e9 * ms_n * 1e-3) if ceiling else None,
+            "counter_bytes_per_step": per_step(naive_traffic),
+            "method_counter_bytes_per_step": per_step(method_traffic),
+            "host_link_read_bytes_per_step": link_reads(naive_rec),
+            "method_host_link_read_bytes_per_step": link_reads(method_rec),
+            "l2_hit_rate": ((naive_rec or {}).get("l2_read_routes") or {}).get("l2_hit_rate"),
             "step_time_vs_method": round(ms_n / ms, 3),
             "bit_identical_to_method": bool(np.array_equal(out_own, out_naive)),
         }
+        if naive_traffic and method_traffic:
+            naive["method_transfer_vs_naive"] = round(method_traffic / naive_traffic, 4)
+            naive["pages_claim"] = "up to 50% less CPU-GPU transfer than naive zero-copy (GH200)"
+        if link_reads(naive_rec) and link_reads(method_rec):
+            naive["method_host_link_reads_vs_naive"] = round(link_reads(method_rec) / link_reads(naive_rec), 4)
+        comparators["naive_zero_copy"] = naive
         log("naive zero-copy: %.3f ms/step" % ms_n)
 
     # ------------------------------------------------------------------ comparator: attention on the CPU
     if r.host_pool is not None and r.hbm_pool is None and not args.no_comparators:
-        cpu_s, used = cpu_attention_timed(dkv, r, wl, ctx, args.cpu_threads, 3 if wl.n_layers == 1 else 1)
+        cpu_s, used = cpu_attention_timed(dkv, r, wl, ctx, args.cpu_threads, 3 if not multi else 1)
         dram = cpu_dram_read_GBps(dkv, args.cpu_threads)
         comparators["cpu_attention"] = {
             "what": "attention computed by host threads reading the same host pages in place "
@@ -990,25 +1009,14 @@ def main(argv=None):
             "step_time_vs_method": round(cpu_s * 1e3 / ms, 3),
         }
         log("CPU attention (%d threads): %.3f ms/step; host DRAM read %.1f GB/s" % (used, cpu_s * 1e3, dram))
-        if K_all is not None and wl.n_layers == 1 and B > 1:
-            split = cpu_gpu_split(dkv, wl, ctx, kv_source, K_all, V_all, ms, cpu_s, args.cpu_threads, args.steps)
-            split.update({
-                "what": "the batch split between host threads reading their sequences' pages in host DRAM "
-                        "and the GPU's zero-copy step reading the other sequences' pages over the host link, "
-                        "run at the same time (wall time per step, both done)",
-                "effective_kv_GBps": round(kv_bytes / (split["together_ms"] * 1e-3) / 1e9, 3),
-                "step_time_vs_method": round(split["together_ms"] / ms, 3)})
-            comparators["cpu_gpu_split"] = split
-            log("CPU/GPU split (%d/%d sequences): %.3f ms/step (CPU alone %.3f, GPU alone %.3f)"
-                % (split["cpu_sequences"], split["gpu_sequences"], split["together_ms"], split["cpu_alone_ms"],
-                   split["gpu_alone_ms"]))
 
     # ------------------------------------------------------------------ every page in HBM
     hbm = None
     if not args.no_hbm_leg:
         log("HBM-placement leg")
-        rh = Resident(dkv, wl, ctx, np.full(B, 1 << 30, np.int32), kv_source)
-        n_hbm_steps = max(args.steps, 50) if wl.n_layers == 1 else args.steps
+        all_host = r.hbm_pool is None
+        rh = Resident(dkv, wl, ctx, np.full(B, 1 << 30, np.int32), kv_source, copy_from=r if all_host else None)
+        n_hbm_steps = max(args.steps, 50) if not multi else args.steps
         ms_h = rh.timed(n_hbm_steps, args.warmup)
         kt_h = rh.kernel_times(n_hbm_steps)
         ms_h_graph = rh.graph_timed(n_hbm_steps)
@@ -1020,6 +1028,7 @@ def main(argv=None):
                          "achieved": round(hbm_split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(hbm_split_gbps / HBM_PEAK_GBPS, 4),
                          "traffic": counter_traffic(wl.name, all_hbm=True)},
+            "kv_filled_by": "copy-engine copy of the host pool" if all_host else "the generator",
             "ms_per_step": round(ms_h, 4),
             "graph_ms_per_step": round(ms_h_graph, 4),
             "kv_GBps": round(kv_bytes / (ms_h * 1e-3) / 1e9, 1),
@@ -1028,6 +1037,7 @@ def main(argv=None):
             "split_kernel_frac_of_8TBps": round(kv_bytes / (kt_h["split"] * 1e-3) / 1e9
                                                 / HBM_PEAK_GBPS, 4),
             "kernel_ms": {k: round(v, 4) for k, v in kt_h.items()},
+            "projection": projection_facts(wl, kt_h["projection"]),
             "measured_hbm_read_GBps": round(hbm_ceiling, 1),
             "hbm_probe": hbm_rows,
             "bit_identical_to_own_placement": bool(np.array_equal(out_own, out_hbm)),
@@ -1040,10 +1050,9 @@ def main(argv=None):
 
         # -------------------------------------------------------------- comparator: staging
         if r.hbm_pool is None and r.host_pool is not None and not args.no_comparators:
-            import torch
             stream = torch.cuda.current_stream()
             host_bytes = r.host_pool.info()[1]
-            n_cmp = max(1, min(args.steps, 5))
+            n_cmp = max(1, min(args.steps, 5)) if not multi else 1
             e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             copy_ms = step_ms = 0.0
             for i in range(n_cmp + 1):
@@ -1076,33 +1085,42 @@ def main(argv=None):
     # ------------------------------------------------------------------ CPU oracle
     cpu = None
     parity = None
-    if K_all is not None:
+    if K0 is not None:
         import oracle
         orc = oracle.default()
         threads = oracle.DEFAULT_THREADS
-        x = wl.x(0)
-        W = wl.W(0)
-        # Whole steps of the workload, repeated until about 10 s of CPU time
-        # (at least one step, at most 200).
+        x0, W0 = wl.x(0), wl.W(0)
+        # A one-layer workload: whole steps, repeated until about 10 s (at
+        # least one, at most 200). A multi-layer one: one whole layer (layer 0,
+        # every sequence and query head), the same work as each other layer.
         reps, t_cpu, ref = 0, 0.0, None
-        while reps == 0 or (t_cpu < 10.0 and reps < 200):
+        while reps == 0 or (not multi and t_cpu < 10.0 and reps < 200):
             t0 = time.perf_counter()
-            out = orc.decode_step(x, W, ctx, K_all, V_all, wl.n_q_heads, Hkv, d, threads=threads)
+            out = orc.decode_step(x0, W0, ctx, K0, V0, wl.n_q_heads, Hkv, d, threads=threads)
             t_cpu += time.perf_counter() - t0
             ref = ref or out
             reps += 1
-        log("oracle on %d threads: %d full steps in %.2f s" % (threads, reps, t_cpu))
-        cpu = {"value": round(kv_bytes * reps / t_cpu / 1e9, 3), "unit": "GB/s", "cores": threads,
-               "kind": "oracle", "seconds": round(t_cpu, 2), "steps": reps,
-               "ms_per_step": round(t_cpu / reps * 1e3, 2),
-               "sample": "%d full step(s) of the bench workload (all %d sequences x %d query heads, "
-                         "%d KV bytes each), fp64, plain C + OpenMP" % (reps, B, wl.n_q_heads, kv_bytes)}
+        log("oracle on %d threads: %d x layer 0 in %.2f s" % (threads, reps, t_cpu))
+        layer_s = t_cpu / reps
+        cpu = {"value": round(kv_layer_bytes * reps / t_cpu / 1e9, 3), "unit": "GB/s", "cores": threads,
+               "kind": "oracle", "seconds": round(t_cpu, 2),
+               "ms_per_step": round(layer_s * wl.n_layers * 1e3, 2),
+               "sample": ("%d full step(s) of the bench workload (all %d sequences x %d query heads, "
+                          "%d KV bytes each), fp64, plain C + OpenMP" % (reps, B, wl.n_q_heads, kv_bytes))
+               if not multi else
+               ("layer 0 of the %d, whole (all %d sequences x %d query heads over %d KV bytes), fp64, plain "
+                "C + OpenMP; every layer is the same work, so ms_per_step is %d x that layer"
+                % (wl.n_layers, B, wl.n_q_heads, kv_layer_bytes, wl.n_layers))}
         got = (out_own.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         err = np.abs(got - ref["attn_out"])
-        parity = {"max_abs": float(err.max()),
-                  "rel_l2": float(np.linalg.norm(got - ref["attn_out"]) /
-                                  np.linalg.norm(ref["attn_out"])),
+        worst = np.unravel_index(int(np.argmax(err)), err.shape)
+        parity = {"scope": ("whole attn_out" if not multi else
+                            "whole attn_out of layer 0 (%d x %d)" % (B, wl.n_q_heads * d)),
+                  "max_abs": float(err.max()),
+                  "rel_l2": float(np.linalg.norm(got - ref["attn_out"]) / np.linalg.norm(ref["attn_out"])),
+                  "worst": {"seq": int(worst[0]), "q_head": int(worst[1]) // d},
                   "gates": {"max_abs": 2e-2, "rel_l2": 5e-3}}
+        parity["within_gates"] = parity["max_abs"] <= 2e-2 and parity["rel_l2"] <= 5e-3
 
     t_star = max(host_kv / (ceiling * 1e9) if ceiling else 0.0, hbm_kv / (HBM_PEAK_GBPS * 1e9))
     # The same two streams one after the other (the serial reading of the combined roofline).
@@ -1134,8 +1152,10 @@ def main(argv=None):
         "roofline": {"bound": "host_link", "kernel": split_kernel_name,
                      "achieved": round(split_gbps, 3), "peak": PCIE_GEN5_X16_GBPS,
                      "unit": "GB/s", "frac": round(split_gbps / PCIE_GEN5_X16_GBPS, 4),
-                     "traffic": counter_traffic(wl.name),
+                     "traffic": method_traffic,
+                     "bytes_per_launch": kv_layer_bytes,
                      "measured_ceiling_GBps": round(ceiling, 3) if ceiling else None,
+                     "ceiling_probe_bytes": probe_bytes,
                      "frac_of_measured_ceiling": round(split_gbps / ceiling, 4) if ceiling else None,
                      "host_GBps_vs_ceiling": round(host_kv / (kt["split"] * 1e-3) / 1e9 / ceiling, 4)
                      if ceiling else None,

@@ -289,12 +289,24 @@ def kv_advance(layout: Layout, ctx_lens, stream=None) -> None:
     _check(lib().kv_advance(layout.handle, _dev_ptr(ctx_lens, "ctx_lens"), _stream_ptr(stream)))
 
 
-def kv_append(layout: Layout, layer: int, seq: int, start_token: int, k: np.ndarray,
-              v: np.ndarray, stream=0) -> None:
-    """k, v: host uint16 arrays [n][Hkv][d] (bf16 bits) in logical order."""
+def kv_append(layout: Layout, layer: int, seq: int, start_token: int, k, v, stream=0) -> None:
+    """k, v: [n][Hkv][d] bf16 in logical order -- host uint16 numpy arrays (bf16
+    bits), or contiguous bf16/int16 device tensors (scattered into the pages by
+    a kernel on `stream`, default: the null stream)."""
+    s = layout.shape
+    if hasattr(k, "is_cuda") or hasattr(v, "is_cuda"):
+        import torch
+        for t, name in ((k, "k"), (v, "v")):
+            if not (hasattr(t, "is_cuda") and t.is_cuda) or t.dtype not in (torch.bfloat16, torch.int16):
+                raise ValueError("%s must be a bf16 (or int16) device tensor like the other" % name)
+        n = k.shape[0]
+        if tuple(k.shape) != (n, s.n_kv_heads, s.head_dim) or tuple(v.shape) != tuple(k.shape):
+            raise ValueError("k and v must be [n][n_kv_heads][head_dim]")
+        _check(lib().kv_append(layout.handle, layer, seq, start_token, n, _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                               _stream_ptr(stream) if stream else None))
+        return
     k = np.ascontiguousarray(k, dtype=np.uint16)
     v = np.ascontiguousarray(v, dtype=np.uint16)
-    s = layout.shape
     n = k.shape[0] if k.ndim > 0 else 0
     if k.shape != (n, s.n_kv_heads, s.head_dim) or v.shape != k.shape:
         raise ValueError("k and v must be [n][n_kv_heads][head_dim]")

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libdkv.so")
 SOURCES = ["proj.hip", "fresh.hip", "attn_split.hip", "attn_combine.hip", "window.hip", "gemm.hip", "probe.hip",
-           "runtime.hip", "noalloc.hip"]
+           "runtime.hip", "noalloc.hip", "append.hip"]
 # Host-only C++ (the CPU attention comparator), built with the system compiler.
 HOST_SOURCES = ["cpu_attention.cpp"]
 HEADERS = [os.path.join(CSRC, "cpu_attention.h"), os.path.join(CSRC, "dkv_internal.h"), os.path.join(CSRC, "device_common.h"), os.path.join(INCLUDE, "dkv.h"),

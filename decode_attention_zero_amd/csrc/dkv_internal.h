@@ -83,6 +83,20 @@ struct AdvanceArgs {
 
 hipError_t launch_advance(const AdvanceArgs &a, hipStream_t stream);
 
+// What kv_append's device path reads and writes: tokens [start, start + n)
+// of one sequence and layer, from device buffers k, v [n][Hkv][d] bf16
+// (16-byte aligned) into the pages of `page_table` (that sequence's row).
+struct AppendArgs {
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t start;
+    const uint64_t *page_table;
+    const uint16_t *k;
+    const uint16_t *v;
+};
+
+hipError_t launch_append(const AppendArgs &a, int n_tokens, hipStream_t stream);
+
 // From this batch size the matrix-core projection splits the hidden dimension
 // into at most kProjMaxSplits ranges, each writing its own fp32 slab of
 // StepArgs::proj_part; below it the projection writes one slab. The

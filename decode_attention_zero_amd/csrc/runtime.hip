@@ -937,12 +937,45 @@ static dkv_status check_range(const dkv_layout *L, int32_t layer, int32_t seq, i
     return DKV_OK;
 }
 
+// Memory a kernel can read in place: HBM (hipMalloc) or managed memory.
+// Pinned host memory and ordinary CPU memory (which the runtime does not
+// know, an error it reports and that is cleared here) are host memory.
+static bool device_resident(const void *p) {
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+}
+
 static dkv_status kv_append_body(dkv_layout *L, int32_t layer, int32_t seq, int32_t start, int32_t n,
                                  const uint16_t *k, const uint16_t *v, dkv_stream_t stream) {
     dkv_status st = check_range(L, layer, seq, start, n, "kv_append");
     if (st != DKV_OK) return st;
     if (n == 0) return DKV_OK;
     if (!k || !v) return fail(DKV_E_INVALID_ARG, "kv_append: null k or v");
+    const bool on_device = device_resident(k);
+    if (on_device != device_resident(v))
+        return fail(DKV_E_INVALID_ARG, "kv_append: k and v must both be device or both be host buffers");
+    if (on_device) {
+        // Device buffers: one kernel scatters the rows into the pages on
+        // `stream` (after any earlier work there that moves pages), then waits.
+        if (((uintptr_t)k | (uintptr_t)v) & 15u)
+            return fail(DKV_E_INVALID_ARG, "kv_append: device k and v must be 16-byte aligned");
+        dkv::AppendArgs a{};
+        a.n_kv_heads = L->shape.n_kv_heads;
+        a.head_dim = L->shape.head_dim;
+        a.start = start;
+        a.page_table = L->d_page_table + pt_index(L, layer, seq, 0);
+        a.k = k;
+        a.v = v;
+        hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+        hipError_t e = dkv::launch_append(a, n, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        if (e != hipSuccess) return hip_fail(e, "kv_append");
+        return DKV_OK;
+    }
     const dkv_shape *s = &L->shape;
     const int D = s->head_dim, Hkv = s->n_kv_heads;
     const size_t row = (size_t)D * 2;

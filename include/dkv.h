@@ -113,14 +113,17 @@ typedef struct dkv_pool dkv_pool;
 
 /* Host-pinned page pool of n_pages pages of kv_page_bytes(shape), allocated
  * with hipHostMalloc (mapped, portable) on the current device's host NUMA
- * node; the GPU reads it in place. The pool owns the memory until
- * kv_pool_free. Errors: DKV_E_INVALID_ARG (null/shape/n_pages <= 0),
- * DKV_E_OUT_OF_MEMORY (pinning failed, or n_pages pages would exceed
- * 2^50 bytes). */
+ * node; the GPU reads it in place (DirectKV digest, 核心方法: the attention
+ * kernel reads KV in CPU pinned/unified memory directly, with no staging
+ * buffer in HBM). The pool owns the memory until kv_pool_free. Errors:
+ * DKV_E_INVALID_ARG (null/shape/n_pages <= 0), DKV_E_OUT_OF_MEMORY (pinning
+ * failed, or n_pages pages would exceed 2^50 bytes). */
 dkv_status kv_alloc_host(const dkv_shape *shape, int64_t n_pages, uint32_t flags,
                          dkv_pool **out);
 
-/* HBM page pool (hipMalloc) of n_pages pages. Same ownership and errors. */
+/* HBM page pool (hipMalloc) of n_pages pages, for the hot part of the KV
+ * (DirectKV digest, 局限与后续工作: hot KV stays in HBM, cold KV is read
+ * directly from CPU memory). Same ownership and errors as kv_alloc_host. */
 dkv_status kv_alloc_hbm(const dkv_shape *shape, int64_t n_pages, dkv_pool **out);
 
 /* Pages of the pool not yet handed to a layout. */
@@ -138,7 +141,11 @@ dkv_status kv_pool_free(dkv_pool *pool);
 typedef struct dkv_layout dkv_layout;
 
 /* Creates the KV layout of a batch of `batch` sequences for all
- * shape->n_layers layers. Sequence b gets room for capacity_tokens[b] slots
+ * shape->n_layers layers: fixed page tables and scratch, set up once, so that
+ * every decode step runs on stable addresses ("KV Cache 内存层级" overview,
+ * 2.1 去搬运：DirectKV: staging's per-step copy addresses break graph
+ * replay; DirectKV digest, 核心方法: a KV layout arranged for the remote
+ * reads). Sequence b gets room for capacity_tokens[b] slots
  * (cached tokens plus the token the next decode_step writes) in every layer;
  * its pages are placed by kv_placement(capacity_tokens[b],
  * hbm_tail_tokens[b]) and taken from host_pool / hbm_pool (hbm_pool may be
@@ -187,12 +194,22 @@ dkv_status kv_layout_page_tier(const dkv_layout *layout, int32_t seq, int32_t pa
                                int32_t *tier);
 
 /* Stores n_tokens tokens of one sequence and layer at slots
- * [start_token, start_token + n_tokens). k and v are HOST pointers to
- * [n_tokens][n_kv_heads][head_dim] bf16 in logical order; they are
- * rearranged into the page layout. Host pages are written by the CPU
- * directly; HBM pages through a synchronous copy on `stream`. This is the
- * set-up path (prefill / tests), not part of a decode step.
- * Errors: DKV_E_INVALID_ARG, DKV_E_CAPACITY (slots beyond capacity). */
+ * [start_token, start_token + n_tokens), rearranged from logical order into
+ * the page layout: the write of history KV into its tier (KV Offload wiki,
+ * 为什么需要 Offload and Offload 的基本机制: a long context's KV moves out of
+ * HBM into host DRAM), here straight into the pages the attention reads.
+ * k and v point to [n_tokens][n_kv_heads][head_dim] bf16 in logical order,
+ * both HOST memory (ordinary or pinned) or both DEVICE memory (hipMalloc or
+ * managed; then 16-byte aligned):
+ *  - host buffers: host pages are written by the CPU directly, HBM pages
+ *    through a synchronous copy on `stream`;
+ *  - device buffers: one kernel on `stream` scatters the rows into their
+ *    pages, host or HBM, after the work already on `stream`.
+ * Returns when the tokens are in place (it synchronises `stream`). This is
+ * the set-up path (prefill / tests), not part of a decode step. The buffers
+ * stay the caller's. Errors: DKV_E_INVALID_ARG (null, misaligned device
+ * buffers, or one host and one device buffer), DKV_E_CAPACITY (slots beyond
+ * capacity), DKV_E_HIP. */
 dkv_status kv_append(dkv_layout *layout, int32_t layer, int32_t seq,
                      int32_t start_token, int32_t n_tokens,
                      const uint16_t *k, const uint16_t *v, dkv_stream_t stream);

@@ -58,7 +58,7 @@ class Oracle:
         L.oracle_softmax_scale.argtypes = [i64]
         L.oracle_softmax_scale.restype = d
         L.oracle_attention_head.argtypes = [p, i64, p, p, i64, i64, p, p, p]
-        L.oracle_attention_head.restype = None
+        L.oracle_attention_head.restype = ctypes.c_int
         L.oracle_attention_partial.argtypes = [p, i64, p, p, i64, i64, p, p, i64, i64, p, p, p]
         L.oracle_attention_partial.restype = None
         L.oracle_merge_partials.argtypes = [i64, i64, p, p, p, p]
@@ -118,7 +118,8 @@ class Oracle:
         kn = np.ascontiguousarray(k_new, dtype=np.float64)
         vn = np.ascontiguousarray(v_new, dtype=np.float64)
         out = np.empty(d, dtype=np.float64)
-        self.lib.oracle_attention_head(_p(q), d, _p(Kc), _p(Vc), d, L, _p(kn), _p(vn), _p(out))
+        if self.lib.oracle_attention_head(_p(q), d, _p(Kc), _p(Vc), d, L, _p(kn), _p(vn), _p(out)) != 0:
+            raise MemoryError("oracle_attention_head: no memory for %d scores" % (L + 1))
         return out
 
     def attention_partial(self, q, K, V, k_new, v_new, t0: int, t1: int):
@@ -168,7 +169,7 @@ class Oracle:
                                          _p(x), _p(W), _p(ctx), _p(K), _p(V), max(Lmax, 1),
                                          _p(attn), _p(kn), _p(vn), _p(q), threads)
         if rc != 0:
-            raise ValueError("oracle_decode_step rejected its arguments")
+            raise ValueError("oracle_decode_step rejected its arguments or ran out of memory")
         return {"attn_out": attn, "k_new": kn, "v_new": vn, "q": q}
 
     # -- host-operand GEMM (C = A x B^T) ------------------------------------------

@@ -113,16 +113,18 @@ double oracle_softmax_scale(int64_t d)
 }
 
 /* Softmax attention of query q over keys/values 0..L (L cached + the fresh
- * one). Two passes: scores and their maximum, then normalised weights. */
-void oracle_attention_head(const double *q, int64_t d,
-                           const uint16_t *K, const uint16_t *V,
-                           int64_t tok_stride, int64_t L,
-                           const double *k_new, const double *v_new,
-                           double *out)
+ * one). Two passes: scores and their maximum, then normalised weights.
+ * Returns 0, or -1 (out untouched) when the score buffer cannot be had. */
+int oracle_attention_head(const double *q, int64_t d,
+                          const uint16_t *K, const uint16_t *V,
+                          int64_t tok_stride, int64_t L,
+                          const double *k_new, const double *v_new,
+                          double *out)
 {
     const double scale = oracle_softmax_scale(d);
     const int64_t n = L + 1;
     double *s = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    if (!s) return -1;
     double m = -INFINITY;
     for (int64_t j = 0; j < n; ++j) {
         s[j] = score(q, d, K, tok_stride, L, k_new, j, scale);
@@ -142,6 +144,7 @@ void oracle_attention_head(const double *q, int64_t d,
         out[i] = acc / denom;
     }
     free(s);
+    return 0;
 }
 
 /* Unnormalised softmax state of keys/values [t0, t1) of the same sequence of
@@ -229,6 +232,7 @@ int oracle_decode_step(int64_t B, int64_t hidden, int64_t n_q_heads,
         oracle_qkv_projection(x + b * hidden, W, hidden, n_out, y + b * n_out);
 
     const int64_t tok_stride = n_kv_heads * d;
+    int failed = 0;
     #pragma omp parallel for num_threads(n_threads) schedule(dynamic, 1)
     for (int64_t bh = 0; bh < B * n_q_heads; ++bh) {
         const int64_t b = bh / n_q_heads, h = bh % n_q_heads;
@@ -239,8 +243,11 @@ int oracle_decode_step(int64_t B, int64_t hidden, int64_t n_q_heads,
         const double *vn = yb + (n_q_heads + n_kv_heads) * d + g * d;
         const uint16_t *Kb = K + (b * Lmax) * tok_stride + g * d;
         const uint16_t *Vb = V + (b * Lmax) * tok_stride + g * d;
-        oracle_attention_head(q, d, Kb, Vb, tok_stride, ctx_lens[b], kn, vn,
-                              attn_out + b * n_q_heads * d + h * d);
+        if (oracle_attention_head(q, d, Kb, Vb, tok_stride, ctx_lens[b], kn, vn,
+                                  attn_out + b * n_q_heads * d + h * d) != 0) {
+            #pragma omp atomic write
+            failed = 1;
+        }
     }
     for (int64_t b = 0; b < B; ++b) {
         const double *yb = y + b * n_out;
@@ -253,7 +260,7 @@ int oracle_decode_step(int64_t B, int64_t hidden, int64_t n_q_heads,
                    (size_t)(n_kv_heads * d) * sizeof(double));
     }
     free(y);
-    return 0;
+    return failed ? -1 : 0;
 }
 
 /* ---- GEMM entries --------------------------------------------------------

@@ -298,6 +298,42 @@ def test_placement_bit_identity(oracle):
     assert_gates(H.bf16_to_f64(outs[0]), ref, "placements")
 
 
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_kv_append_from_device_buffers(head_dim):
+    """kv_append from device tensors (one scatter kernel) writes the pages a
+    host-array append would: a run that starts off a page boundary and
+    crosses from host pages into HBM pages reads back exactly, and after the
+    original rows are written back the same way the decode step gives the
+    bits it gave before. One host and one device buffer are refused."""
+    import torch
+    wl = configs.LLAMA8B_HOST.replace(batch=3) if head_dim == 128 else \
+        configs.TINY.replace(batch=3, n_kv_heads=4)
+    ctx = np.array([0, 37, 700], np.int32)
+    s = H.Setup(wl, ctx_lens=ctx, hbm_tail=300)          # sequence 2: slots from 400 on are HBM
+    try:
+        assert s.layout.page_tier(2, 24) == 0 and s.layout.page_tier(2, 25) == 1
+        before = bits(s.run())
+        t0, t1 = 389, 431
+        rng = np.random.default_rng(11)
+        shp = (t1 - t0, wl.n_kv_heads, wl.head_dim)
+        k_new = rng.integers(0, 1 << 16, shp, dtype=np.uint16) & 0x7F7F      # finite bf16 patterns
+        v_new = rng.integers(0, 1 << 16, shp, dtype=np.uint16) & 0x7F7F
+        dev = lambda a: torch.from_numpy(a.view(np.int16)).cuda()
+        H.dkv.kv_append(s.layout, 0, 2, t0, dev(k_new), dev(v_new))
+        k_back, v_back = H.dkv.kv_read(s.layout, 0, 2, t0, t1 - t0)
+        assert np.array_equal(k_back, k_new) and np.array_equal(v_back, v_new)
+        k_old, v_old = wl.kv("k", 0, 2, t0, t1), wl.kv("v", 0, 2, t0, t1)
+        k_dev, v_host = dev(k_old), np.ascontiguousarray(v_old)
+        with pytest.raises(H.dkv.DkvError):          # the C ABI refuses one device and one host buffer
+            H.dkv._check(H.dkv.lib().kv_append(s.layout.handle, 0, 2, t0, t1 - t0, k_dev.data_ptr(),
+                                                 v_host.ctypes.data, None))
+        H.dkv.kv_append(s.layout, 0, 2, t0, dev(k_old), dev(v_old))
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(s.run()), before)
+    finally:
+        s.free()
+
+
 @pytest.mark.parametrize("head_dim,n_q_heads,n_kv_heads", [
     (64, 8, 4), (64, 16, 4), (64, 32, 4), (128, 8, 4), (128, 2, 2)],
     ids=["d64-g2", "d64-g4", "d64-g8", "d128-g2", "d128-g1"])
