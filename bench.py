@@ -525,8 +525,7 @@ def projection_facts(wl, ms):
     """The QKV projection of one step (summed over layers): which kernel, its W
     read rate and its matrix-core use against the dense bf16 peak."""
     B = wl.batch
-    kernel = ("qkv_proj_gemv_kernel" if B < 8 else "qkv_proj_stream_kernel" if B < 16 else
-              "qkv_proj_splitk_kernel")
+    kernel = "qkv_proj_gemv_kernel" if B < 8 else "qkv_proj_splitk_kernel"
     w_bytes = wl.n_qkv * wl.hidden * 2 * wl.n_layers
     flop = 2.0 * B * wl.hidden * wl.n_qkv * wl.n_layers
     return {"kernel": kernel, "ms": round(ms, 4), "W_bytes": w_bytes,
@@ -838,7 +837,7 @@ def main(argv=None):
     ap.add_argument("--all-hbm", action="store_true",
                     help="with --profile-run: place every page in HBM instead of the "
                          "workload's own placement")
-    ap.add_argument("--split-kernel", choices=("regs", "lds", "mfma", "naive"),
+    ap.add_argument("--split-kernel", choices=("regs", "lds", "mfma", "ldsmfma", "naive"),
                     help="with --profile-run (and --traffic-record): the split kernel to run instead of "
                          "the layout's default (naive: the per-query-head comparator)")
     ap.add_argument("--calibrate", action="store_true",

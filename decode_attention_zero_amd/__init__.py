@@ -214,7 +214,7 @@ class Layout:
     def split_kernel(self) -> str:
         """'regs' (register double buffer), 'lds' (producer/consumer LDS ring) or
         'naive' (comparator: one work item per query head)."""
-        return {0: "regs", 1: "lds", 2: "naive", 3: "mfma"}[lib().kv_layout_split_kernel(self.handle)]
+        return {0: "regs", 1: "lds", 2: "naive", 3: "mfma", 4: "ldsmfma"}[lib().kv_layout_split_kernel(self.handle)]
 
     @property
     def split_waves(self) -> int:
@@ -223,7 +223,8 @@ class Layout:
 
     @split_kernel.setter
     def split_kernel(self, name: str) -> None:
-        _check(lib().kv_layout_set_split_kernel(self.handle, {"regs": 0, "lds": 1, "naive": 2, "mfma": 3}[name]))
+        _check(lib().kv_layout_set_split_kernel(self.handle, {"regs": 0, "lds": 1, "naive": 2, "mfma": 3,
+                                                              "ldsmfma": 4}[name]))
 
     def page_tier(self, seq: int, page: int) -> int:
         t = ctypes.c_int32()

@@ -389,13 +389,28 @@ struct MfmaState {
         }
         wait_lds();
         asm volatile("" ::: "memory");
+        compute<PARTIAL, false>(lds, lds + STILE, n_valid);
+    }
 
+    // Byte address of 16-byte chunk `chunk` of token row t of a tile in LDS:
+    // padded rows of ROW bytes (the staging above), or with SWZ unpadded rows
+    // of D * 2 bytes whose chunk c sits at chunk position c ^ (t & 15) (the
+    // LDS ring's image, D = 128), which keeps 16 tokens' reads of the same
+    // chunk on 16 different bank groups without padding.
+    template <bool SWZ>
+    __device__ __forceinline__ const char *chunk_at(const char *tile, int t, int chunk) const {
+        if constexpr (SWZ) return tile + t * (D * 2) + ((chunk ^ (t & 15)) << 4);
+        else return tile + t * ROW + (chunk << 4);
+    }
+
+    // One page from its K and V tiles in LDS.
+    template <bool PARTIAL, bool SWZ>
+    __device__ __forceinline__ void compute(const char *ktile, const char *vtile, int n_valid) {
         // S = K Q^T: A = K rows (token = col), B = the query terms.
         f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
-        const char *kt = lds + col * ROW + kq * 16;
 #pragma unroll
         for (int c = 0; c < NKB; ++c) {
-            const uint4 kv = *reinterpret_cast<const uint4 *>(kt + c * 64);
+            const uint4 kv = *reinterpret_cast<const uint4 *>(chunk_at<SWZ>(ktile, col, kq + 4 * c));
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qop[c], sc, 0, 0, 0);
         }
         float sv[4];
@@ -433,14 +448,17 @@ struct MfmaState {
         // i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 (measured on gfx950), so
         // lane j of row group kq addresses dims 16n + 4 (j % 4) .. +3 of token
         // 4kq + j / 4, and lane col gets dim 16n + col of tokens 4kq .. 4kq+3.
-        const char *vtr = lds + STILE + (4 * kq + (col >> 2)) * ROW + (col & 3) * 8;
+        // Lane col's 8-byte piece of block n: token 4kq + col/4, bytes
+        // 32n + 8 (col % 4), i.e. chunk 2n + (col / 2) % 2, half col % 2.
+        const int vt = 4 * kq + (col >> 2);
 #pragma unroll
         for (int n0 = 0; n0 < NDB; n0 += 4) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int n = n0; n < n0 + 4; ++n) {
+                const char *vp = chunk_at<SWZ>(vtile, vt, 2 * n + ((col >> 1) & 1)) + (col & 1) * 8;
                 s16x4 vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4 *)(vtr + n * 32));
+                    (__attribute__((address_space(3))) s16x4 *)vp);
                 if (PARTIAL) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -674,6 +692,100 @@ __global__ __launch_bounds__(64 * (NC + 1)) void attn_split_lds_kernel(StepArgs 
     st.finish(a, b, h0, s, dl);
 }
 
+// Producer/consumer form with a matrix-core consumer (groups of 4 and 8,
+// head_dim 128): the producer/consumer pipeline of the pages (DirectKV
+// digest, 核心方法; "KV Cache 内存层级" overview, 2.1: producer, consumer and
+// storer warp groups) with the register kernel's arithmetic, so that the
+// two streaming schemes compare with the same consumer. One workgroup of two
+// wavefronts per work item: wavefront 0 streams the item's page runs into an
+// NS-slot LDS ring with LDS DMA (global_load_lds_dwordx4), NS - 1 runs in
+// flight; wavefront 1 runs MfmaState::compute on each run straight from its
+// ring slot, so a run is never copied from registers into LDS. The DMA writes
+// lane l's 16 bytes to slot byte 16 l of its 1 KiB load, but each lane picks
+// which 16 bytes of the run it fetches: load j covers token rows 4j .. 4j + 3
+// of the K tile (j < 4) or the V tile, and lane l fetches chunk (l % 16) ^ t
+// of row t = 4 (j % 4) + l / 16, so the slot holds each row's chunk c at
+// position c ^ t, the layout MfmaState::compute<SWZ = true> reads without
+// bank conflicts. Every load still covers one contiguous 1 KiB of the run.
+// Same handoff as attn_split_lds_kernel: one barrier per page. Two ring
+// slots (one run in flight per producer) with four wavefronts per SIMD (123
+// VGPRs, 16 KiB of LDS: eight workgroups per CU) measured fastest, within a
+// few percent of the register kernel with every page in HBM (MI355X, split
+// kernel, all-HBM: config-2 shape 0.165 vs 0.161 ms, config-4 shape 0.62-0.64
+// vs 0.65 ms, 70B layer 1.31 vs 1.30 ms); three or four slots leave the
+// compiler at 176 VGPRs (two wavefronts per SIMD) and run 15-20 % slower.
+template <int G, int NS>
+__global__ __launch_bounds__(128, 4) void attn_split_lds_mfma_kernel(StepArgs a) {
+    constexpr int D = 128;
+    using S = MfmaState<D, G>;
+    constexpr int LPP = S::RUN / 1024;                          // DMA loads per page run
+    static_assert(S::TILE == 4096 && LPP == 8, "the swizzle assumes 16-chunk rows, 4 rows per load");
+    __shared__ __attribute__((aligned(16))) char ring[NS][S::RUN];
+
+    const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+    const int L = a.ctx_lens[b];
+    if (L < 0 || L >= a.capacity[b]) return;
+    const int t0 = s * a.split_tokens;
+    if (t0 >= L) return;
+    const int t1 = min(t0 + a.split_tokens, L);
+    const int p0 = t0 / kPageTokens;
+    const int np = (t1 + kPageTokens - 1) / kPageTokens - p0;   // pages p0 .. p0 + np - 1
+    const int pf = t1 / kPageTokens;                              // pages below pf are full
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+
+    if (wave == 0) {
+        const uint64_t *pt = a.page_table + (size_t)b * a.max_pages + p0;
+        const size_t run_off = (size_t)g * S::RUN;
+        uint64_t window = 0;
+        auto issue = [&](int i) {
+            if ((i & 63) == 0) window = (i + lane < np) ? pt[i + lane] : 0;
+            const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)window, i & 63);
+            const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(window >> 32), i & 63);
+            const char *run = reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo) + run_off;
+            char *dst = ring[i % NS];
+#pragma unroll
+            for (int j = 0; j < LPP; ++j) {
+                // Row t of the tile, chunk position lane % 16: the row's chunk (lane % 16) ^ t.
+                // (Computed here: an array of these offsets captured by the lambda made hipcc
+                // drop the kernel's host-side launch stub.)
+                const int t = 4 * (j % 4) + lane / 16;
+                const char *src = run + (j / 4) * S::TILE + t * (D * 2) + (((lane % 16) ^ t) << 4);
+                __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst + j * 1024), 16, 0,
+                                                 kAuxNontemporal);
+            }
+        };
+        for (int i = 0; i < NS - 1 && i < np; ++i) issue(i);
+        for (int i = 0; i < np; ++i) {
+            if (i + NS - 2 < np) wait_vmcnt<LPP * (NS - 2)>();   // runs i + 1 .. i + NS - 2 may still fly
+            else wait_vmcnt<0>();
+            ring_barrier();
+            if (i + NS - 1 < np) {                                // refills the slot of run i - 1
+                if (a.lds_poison) {
+                    char *dst = ring[(i + NS - 1) % NS] + lane * 16;
+#pragma unroll
+                    for (int j = 0; j < LPP; ++j)
+                        *reinterpret_cast<uint4 *>(dst + j * 1024) = make_uint4(0x7FC07FC0u, 0x7FC07FC0u,
+                                                                               0x7FC07FC0u, 0x7FC07FC0u);
+                    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+                }
+                issue(i + NS - 1);
+            }
+        }
+        return;
+    }
+
+    S st;
+    st.init(a, b, g * G);
+    for (int i = 0; i < np; ++i) {
+        ring_barrier();
+        const char *slot = ring[i % NS];
+        if (p0 + i < pf) st.template compute<false, true>(slot, slot + S::TILE, kPageTokens);
+        else st.template compute<true, true>(slot, slot + S::TILE, t1 - (p0 + i) * kPageTokens);
+    }
+    st.finish(a, b, g * G, s);
+}
+
 // XCD-aware item order of the one-wavefront-per-item launches: the KV head is
 // the fastest grid dimension. Workgroups go to the GPU's 8 XCDs round-robin
 // in linear order, so with 8 KV heads each XCD (its own L2 and a fixed share
@@ -711,10 +823,26 @@ void launch(const StepArgs &a, hipStream_t st) {
     }
 }
 
+// The LDS ring with a matrix-core consumer (head_dim 128, one workgroup per
+// item in the same XCD-aware order).
+template <int G>
+void launch_lds_mfma(const StepArgs &a, hipStream_t st) {
+    const dim3 grid(a.n_kv_heads, a.max_splits, a.batch);
+    if (a.lds_ring == 3) attn_split_lds_mfma_kernel<G, 3><<<grid, 128, 0, st>>>(a);
+    else if (a.lds_ring == 4) attn_split_lds_mfma_kernel<G, 4><<<grid, 128, 0, st>>>(a);
+    else attn_split_lds_mfma_kernel<G, 2><<<grid, 128, 0, st>>>(a);
+}
+
 }  // namespace
 
 hipError_t launch_split(const StepArgs &a, hipStream_t st) {
     const int G = a.n_q_heads / a.n_kv_heads;
+    if (a.split_variant == kSplitLdsMfma) {
+        if (a.head_dim == 128 && G == 4) launch_lds_mfma<4>(a, st);
+        else if (a.head_dim == 128 && G == 8) launch_lds_mfma<8>(a, st);
+        else return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     if (a.head_dim == 128) {
         switch (G) {
             case 1: launch<128, 1>(a, st); break;

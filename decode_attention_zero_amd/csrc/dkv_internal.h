@@ -22,6 +22,9 @@ constexpr int kSplitNaive = 2;
 // matrix cores (the default from groups of kMfmaMinGroup query heads).
 constexpr int kSplitMfma = 3;
 constexpr int kMfmaMinGroup = 4;
+// Producer wavefront streaming page runs into an LDS ring for a matrix-core
+// consumer wavefront (groups of kMfmaMinGroup and more, head_dim 128).
+constexpr int kSplitLdsMfma = 4;
 
 // Everything one decode step's kernels read or write. Built on the host by
 // decode_step from the layout and the caller's pointers; passed by value.
@@ -39,10 +42,13 @@ struct StepArgs {
     int32_t part_slots;     // partial slots per (sequence, query head): max_splits + 1; sequence b's
                             // fresh token takes slot ceil(ctx_lens[b] / split_tokens), after its splits
     float qscale;           // log2(e) / sqrt(head_dim): scores come out in log2 units
-    int32_t split_variant;  // kSplitRegisters, kSplitLds, kSplitNaive or kSplitMfma
+    int32_t split_variant;  // kSplitRegisters, kSplitLds, kSplitNaive, kSplitMfma or kSplitLdsMfma
     int32_t split_waves;    // register kernel: > 0 = that many wavefronts loop over the items
     int32_t proj_mfma_min_batch;  // batches from this size on project on MFMA, below on VALU
-    int32_t lds_ring;       // LDS producer/consumer kernel: ring slots (2, 3 or 4)
+    int32_t proj_splitk_min_batch;  // MFMA batches from this size on split the hidden dimension
+                                    // over workgroups (split-k); below, one workgroup per row block
+    int32_t proj_ranges;          // split-k ranges of the hidden dimension (1, 2, 4, 8; 0 = by size)
+    int32_t lds_ring;       // LDS producer/consumer kernels: ring slots (2, 3 or 4; 0 = the kernel's default)
     int32_t lds_poison;     // LDS producer/consumer kernel: 1 = fill each freed slot with NaN first
     // this layer's page table [batch][max_pages] of device addresses
     const uint64_t *page_table;
@@ -97,15 +103,14 @@ struct AppendArgs {
 
 hipError_t launch_append(const AppendArgs &a, int n_tokens, hipStream_t stream);
 
-// From this batch size the matrix-core projection splits the hidden dimension
-// into at most kProjMaxSplits ranges, each writing its own fp32 slab of
-// StepArgs::proj_part; below it the projection writes one slab. The
+// From this batch size (by default: every batch that projects on the matrix
+// cores) the projection splits the hidden dimension into at most
+// kProjMaxSplits ranges, each writing its own fp32 slab of
+// StepArgs::proj_part; otherwise the projection writes one slab. The
 // fresh-token kernel adds the slabs of its group's rows in range order.
-constexpr int kProjSplitkMinBatch = 16;
+// Scratch always has room for kProjMaxSplits slabs.
+constexpr int kProjSplitkMinBatch = 8;
 constexpr int kProjMaxSplits = 8;
-
-// Projection slabs a batch uses.
-inline int proj_ranges_max(int batch) { return batch >= kProjSplitkMinBatch ? kProjMaxSplits : 1; }
 
 // Scratch bytes of one decode step (each buffer 256-byte aligned in the order
 // proj_part, q, part_o, part_ml, item counter), so that one carve serves the

@@ -33,10 +33,14 @@ namespace {
 constexpr int kFreshWaves = 4;
 constexpr int kFreshThreads = 64 * kFreshWaves;
 
-template <int D, int G>
-__global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a, int ranges) {
+// KS slabs (1, 2, 4 or 8). Each thread owns up to RPT of the group's rows and
+// issues all RPT x KS loads of its slabs before it adds them, each row in
+// range order (the same sums, in the same order, as a plain loop).
+template <int D, int G, int KS>
+__global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a) {
     constexpr int DPL = D / 64;        // dims per lane
     constexpr int NR = (G + 2) * D;    // the group's rows: G query heads, K, V
+    constexpr int RPT = (NR + kFreshThreads - 1) / kFreshThreads;
     const int b = blockIdx.x / a.n_kv_heads;
     const int g = blockIdx.x - b * a.n_kv_heads;
     const int tid = threadIdx.x;
@@ -57,10 +61,23 @@ __global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a, 
     const int krow = a.n_q_heads * D + g * D;
     const int vrow = krow + a.n_kv_heads * D;
     float *qout = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
-    for (int r = tid; r < NR; r += kFreshThreads) {
-        const int n = r < G * D ? g * G * D + r : r < (G + 1) * D ? krow + (r - G * D) : vrow + (r - (G + 1) * D);
-        float y = yb[n];
-        for (int k = 1; k < ranges; ++k) y += yb[(size_t)k * slab + n];
+    float part[RPT][KS];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int r = tid + j * kFreshThreads;
+        if (r < NR) {
+            const int n = r < G * D ? g * G * D + r : r < (G + 1) * D ? krow + (r - G * D) : vrow + (r - (G + 1) * D);
+#pragma unroll
+            for (int k = 0; k < KS; ++k) part[j][k] = yb[(size_t)k * slab + n];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int r = tid + j * kFreshThreads;
+        if (r >= NR) break;
+        float y = part[j][0];
+#pragma unroll
+        for (int k = 1; k < KS; ++k) y += part[j][k];
         if (r < G * D) {
             const float qv = y * a.qscale;
             s_q[r / D][r % D] = qv;
@@ -108,14 +125,20 @@ __global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a, 
 
 template <int D, int G>
 void launch(const StepArgs &a, int ranges, hipStream_t st) {
-    fresh_token_kernel<D, G><<<a.batch * a.n_kv_heads, kFreshThreads, 0, st>>>(a, ranges);
+    const dim3 grid(a.batch * a.n_kv_heads);
+    switch (ranges) {
+        case 1: fresh_token_kernel<D, G, 1><<<grid, kFreshThreads, 0, st>>>(a); break;
+        case 2: fresh_token_kernel<D, G, 2><<<grid, kFreshThreads, 0, st>>>(a); break;
+        case 4: fresh_token_kernel<D, G, 4><<<grid, kFreshThreads, 0, st>>>(a); break;
+        default: fresh_token_kernel<D, G, 8><<<grid, kFreshThreads, 0, st>>>(a); break;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_fresh(const StepArgs &a, int ranges, hipStream_t st) {
     const int G = a.n_q_heads / a.n_kv_heads;
-    if (ranges < 1 || ranges > kProjMaxSplits) return hipErrorInvalidValue;
+    if (ranges != 1 && ranges != 2 && ranges != 4 && ranges != 8) return hipErrorInvalidValue;
     if (a.head_dim == 128) {
         switch (G) {
             case 1: launch<128, 1>(a, ranges, st); break;

@@ -6,8 +6,10 @@
 // decode step, as in the core-method section of the DirectKV digest
 // ("长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）"); the step is bound by
 // reading W from HBM at every batch size here, so each of the three forms
-// (1a VALU GEMV below batch 8, 1b one 16-sequence MFMA tile up to batch 15,
-// 1c split-k MFMA from batch 16) is built to stream W once at full bandwidth.
+// (1a VALU GEMV below batch 8, 1c split-k MFMA from batch 8, and 1b one
+// 16-sequence MFMA tile, which a layout takes up to batch 15 when
+// DKV_PROJ_SPLITK_MIN_BATCH moves the split-k threshold up) is built to
+// stream W once at full bandwidth.
 #include "device_common.h"
 
 namespace dkv {
@@ -123,7 +125,7 @@ __device__ __forceinline__ void load_slice(uint4 (&v)[NK], const uint16_t *row, 
     for (int u = 0; u < NK; ++u) v[u] = *reinterpret_cast<const uint4 *>(row + k0 + 32 * u);
 }
 
-// 1b. Batches of 8 to 15 sequences (one tile of 16): each workgroup owns 16 W
+// 1b. Up to 16 sequences (one tile of 16), below the split-k threshold: each workgroup owns 16 W
 // rows; its KSPLIT wavefronts split the hidden dimension into equal ranges,
 // and each walks its range in KC-wide chunks (128, or 256 for ranges of 2048
 // and more). A wave stages its x chunk (the
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void qkv_proj_stream_kernel(StepArgs a
     }
 }
 
-// 1c. From 16 sequences: W crosses HBM once; what limits a plain tiling is
+// 1c. From 8 sequences: W crosses HBM once; what limits a plain tiling is
 // x. Every 16-row W tile needs the whole batch's x slice, so reading x per
 // wavefront from L2 costs B/16 times the W bytes (measured on MI355X at hidden
 // 4096: 19 -> 41 us from batch 16 to 64, linear in that x traffic; W alone is
@@ -343,14 +345,18 @@ int splitk_ranges(int hidden, int kc, int min_range) {
     return 1;
 }
 
-// 256-wide chunks; ranges of at least 1024 for one 16-sequence tile (4 ranges
-// at hidden 4096, 8 at 8192), 512 for two and four (8 ranges): measured best
-// on MI355X at hidden 4096 and 8192 (128-wide chunks in the one-tile case:
-// 18.3 vs 17.9 us at hidden 4096, 41.5 vs 39.7 us at 8192, batch 16, with
-// the partial sums).
+// 256-wide chunks in up to 8 ranges of at least 256 (8 ranges from hidden
+// 2048): with the fresh-token kernel adding the slabs, 8 ranges measured
+// best or equal at every batch (MI355X, W cycled through copies so that it
+// is read from HBM, decode-step HIP events, hidden 4096 / 8192): batch 8,
+// 14.4 / 36.5 us against 15.1 / 43.1 with 4 ranges and 15.7 / 42.9 for the
+// one-tile streamed kernel; batch 16, 14.7 / 37.0 against 15.7 / 44.3 with
+// 4 ranges; batch 32, 16.7 / 39.4 against 17.6 / 44.4; batch 64, 20.2 /
+// 46.4 against 21.9 / 52.3.
 template <int NBT>
 int launch_splitk(const StepArgs &a, hipStream_t st) {
-    const int ks = splitk_ranges(a.hidden, 256, NBT == 1 ? 1024 : 512);
+    int ks = splitk_ranges(a.hidden, 256, 256);
+    if (a.proj_ranges > 0 && a.hidden % (a.proj_ranges * 256) == 0) ks = a.proj_ranges;
     const dim3 grid(a.n_qkv / (16 * kProjRowBlocks), ks, (a.batch + 16 * NBT - 1) / (16 * NBT));
     qkv_proj_splitk_kernel<NBT, 256><<<grid, 64 * kProjRowBlocks, 0, st>>>(a, a.hidden / ks);
     return ks;
@@ -377,7 +383,7 @@ hipError_t launch_gemv(const StepArgs &a, hipStream_t st) {
 hipError_t launch_projection(const StepArgs &a, int *ranges, hipStream_t st) {
     if (a.hidden % 512 != 0 || a.n_qkv % (16 * kProjRowBlocks) != 0 || !a.proj_part) return hipErrorInvalidValue;
     *ranges = 1;
-    if (a.batch >= a.proj_mfma_min_batch && a.batch < kProjSplitkMinBatch) {
+    if (a.batch >= a.proj_mfma_min_batch && a.batch < a.proj_splitk_min_batch && a.batch <= 16) {
         // One sequence tile: streamed over k by up to 4 wavefronts per row block.
         int ksplit = 4;
         while (ksplit > 1 && a.hidden % (128 * ksplit) != 0) ksplit >>= 1;

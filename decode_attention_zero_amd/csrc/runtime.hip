@@ -146,6 +146,8 @@ struct dkv_layout {
     int32_t split_variant;             // dkv::kSplitRegisters, kSplitLds, kSplitNaive or kSplitMfma
     int32_t split_waves;               // > 0: the register kernel runs on that many looping wavefronts
     int32_t proj_mfma_min_batch;       // batches from this size on project on the matrix cores
+    int32_t proj_splitk_min_batch;     // MFMA batches from this size on use the split-k projection
+    int32_t proj_ranges;               // split-k ranges (0: chosen from the shape)
     int32_t lds_ring;                  // LDS producer/consumer kernel: ring slots
     int32_t lds_poison;                // LDS producer/consumer kernel: NaN-fill freed slots
     dkv_pool *host_pool;
@@ -269,12 +271,17 @@ int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, int32_t max_cap) 
 // at group 8: 1.41 ms vs 2.0 ms); smaller groups keep the VALU form.
 // DKV_SPLIT_KERNEL=regs|lds|mfma overrides it; DKV_SPLIT_KERNEL=naive selects
 // the naive zero-copy comparator (one work item per query head).
-int32_t choose_split_variant(int32_t group) {
+bool lds_mfma_supported(int32_t group, int32_t head_dim) {
+    return group >= dkv::kMfmaMinGroup && head_dim == 128;
+}
+
+int32_t choose_split_variant(int32_t group, int32_t head_dim) {
     if (const char *env = getenv("DKV_SPLIT_KERNEL")) {
         if (!strcmp(env, "lds")) return dkv::kSplitLds;
         if (!strcmp(env, "regs")) return dkv::kSplitRegisters;
         if (!strcmp(env, "naive")) return dkv::kSplitNaive;
         if (!strcmp(env, "mfma") && group >= dkv::kMfmaMinGroup) return dkv::kSplitMfma;
+        if (!strcmp(env, "ldsmfma") && lds_mfma_supported(group, head_dim)) return dkv::kSplitLdsMfma;
     }
     return group >= dkv::kMfmaMinGroup ? dkv::kSplitMfma : dkv::kSplitRegisters;
 }
@@ -312,6 +319,25 @@ int32_t choose_split_waves(int64_t host_pages, int64_t hbm_pages) {
 // 40.1 us; batch 16, 31.8 / 124 vs 20.1 / 48.6 us; batch 32 at 4096, 57 vs
 // 29 us; batch 64, 109 vs 46 us. DKV_PROJ_MFMA_MIN_BATCH=<n> overrides it.
 constexpr int32_t kProjMfmaMinBatch = 8;
+
+// The split-k projection's batch threshold and range count; the defaults
+// are measured choices (proj.hip), the environment variables
+// DKV_PROJ_SPLITK_MIN_BATCH=<n> and DKV_PROJ_RANGES=1|2|4|8 override them.
+int32_t choose_proj_splitk_min_batch() {
+    if (const char *env = getenv("DKV_PROJ_SPLITK_MIN_BATCH")) {
+        const int v = atoi(env);
+        if (v >= 1) return v;
+    }
+    return dkv::kProjSplitkMinBatch;
+}
+
+int32_t choose_proj_ranges() {
+    if (const char *env = getenv("DKV_PROJ_RANGES")) {
+        const int v = atoi(env);
+        if (v == 1 || v == 2 || v == 4 || v == 8) return v;
+    }
+    return 0;
+}
 
 int32_t choose_proj_mfma_min_batch() {
     if (const char *env = getenv("DKV_PROJ_MFMA_MIN_BATCH")) {
@@ -372,7 +398,7 @@ ScratchPlan scratch_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim,
     ScratchPlan p{};
     const size_t B = (size_t)batch, Hq = (size_t)n_q_heads, D = (size_t)head_dim;
     const size_t n_qkv = (Hq + 2 * (size_t)n_kv_heads) * D;
-    p.proj_part = align256((size_t)proj_ranges_max(batch) * B * n_qkv * sizeof(float));
+    p.proj_part = align256((size_t)kProjMaxSplits * B * n_qkv * sizeof(float));
     p.q = align256(B * Hq * D * sizeof(float));
     p.part_o = align256(B * Hq * (size_t)part_slots * D * sizeof(float));
     p.part_ml = align256(B * Hq * (size_t)part_slots * sizeof(float2));
@@ -548,13 +574,14 @@ static dkv_status check_pools(const dkv_shape *shape, int32_t batch, const int32
 // Allocates the layout's device tables and scratch, uploads the page table
 // (and the window tables), and hands the layout out; frees everything on
 // failure.
-// Debug knobs of the LDS producer/consumer split kernel, the race detector
-// of its handoff: DKV_LDS_RING=2|3|4 ring slots (default 4: three runs in
-// flight), DKV_POISON=1 fills every slot with NaN before it is refilled, so a
+// Debug knobs of the LDS producer/consumer split kernels, the race detector
+// of their handoff: DKV_LDS_RING=2|3|4 ring slots (default 4 for the VALU
+// consumers, 2 for the matrix-core consumer: measured fastest, see
+// attn_split.hip), DKV_POISON=1 fills every slot with NaN before it is refilled, so a
 // consumer that read a slot before its loads landed would produce NaN
 // instead of a silently stale result. Neither changes the arithmetic.
 static void choose_lds_ring(dkv_layout *L) {
-    L->lds_ring = 4;
+    L->lds_ring = 0;                   // each ring kernel's own default
     if (const char *env = getenv("DKV_LDS_RING")) {
         const int v = atoi(env);
         if (v >= 2 && v <= 4) L->lds_ring = v;
@@ -568,11 +595,11 @@ static void choose_lds_ring(dkv_layout *L) {
 static void log_plan(const dkv_layout *L, int64_t n_host, int64_t n_hbm) {
     const char *env = getenv("DKV_LOG");
     if (!env || strcmp(env, "1") != 0) return;
-    static const char *const kSplitNames[] = {"regs", "lds", "naive", "mfma"};
+    static const char *const kSplitNames[] = {"regs", "lds", "naive", "mfma", "ldsmfma"};
     const dkv_shape *s = &L->shape;
     const int B = L->batch;
     const char *proj = B < L->proj_mfma_min_batch ? "gemv"
-                       : B < dkv::kProjSplitkMinBatch ? "mfma one-tile streamed"
+                       : B < L->proj_splitk_min_batch ? "mfma one-tile streamed"
                                                       : "mfma split-k (x staged in LDS)";
     fprintf(stderr,
             "[dkv] layout: batch %d, hidden %d, heads %d/%d, head_dim %d, layers %d; pages per layer: "
@@ -596,7 +623,7 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
     L->split_tokens = choose_split_tokens(batch, shape->n_kv_heads, max_cap);
     L->max_splits = std::max(1, (std::max(1, max_cap - 1) + L->split_tokens - 1) / L->split_tokens);
     L->scratch = dkv::scratch_plan(batch, shape->n_q_heads, shape->n_kv_heads, shape->head_dim, L->max_splits + 1);
-    L->split_variant = choose_split_variant(shape->n_q_heads / shape->n_kv_heads);
+    L->split_variant = choose_split_variant(shape->n_q_heads / shape->n_kv_heads, shape->head_dim);
     int64_t n_host = 0, n_hbm = 0;
     for (int b = 0; b < batch; ++b) {
         const int hot = L->windowed ? L->window[b] : L->n_pages[b] - L->first_hbm[b];
@@ -605,6 +632,8 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
     }
     L->split_waves = choose_split_waves(n_host, n_hbm);
     L->proj_mfma_min_batch = choose_proj_mfma_min_batch();
+    L->proj_splitk_min_batch = choose_proj_splitk_min_batch();
+    L->proj_ranges = choose_proj_ranges();
     choose_lds_ring(L);
     log_plan(L, n_host, n_hbm);
     track(L);                          // the last step that can throw
@@ -918,10 +947,13 @@ int32_t kv_layout_split_kernel(const dkv_layout *L) { return L && live(L) ? L->s
 int32_t kv_layout_split_waves(const dkv_layout *L) { return L && live(L) ? L->split_waves : -1; }
 
 dkv_status kv_layout_set_split_kernel(dkv_layout *L, int32_t kernel) {
-    if (!L || !live(L) || (kernel != dkv::kSplitRegisters && kernel != dkv::kSplitLds && kernel != dkv::kSplitNaive &&
-               (kernel != dkv::kSplitMfma || L->shape.n_q_heads / L->shape.n_kv_heads < dkv::kMfmaMinGroup)))
-        return fail(DKV_E_INVALID_ARG, "kv_layout_set_split_kernel: null or freed layout, or unknown kernel %d",
-                    kernel);
+    if (!L || !live(L)) return fail(DKV_E_INVALID_ARG, "kv_layout_set_split_kernel: null or freed layout");
+    const int32_t group = L->shape.n_q_heads / L->shape.n_kv_heads;
+    const bool ok = kernel == dkv::kSplitRegisters || kernel == dkv::kSplitLds || kernel == dkv::kSplitNaive ||
+                    (kernel == dkv::kSplitMfma && group >= dkv::kMfmaMinGroup) ||
+                    (kernel == dkv::kSplitLdsMfma && lds_mfma_supported(group, L->shape.head_dim));
+    if (!ok)
+        return fail(DKV_E_INVALID_ARG, "kv_layout_set_split_kernel: unknown kernel %d, or not for this shape", kernel);
     L->split_variant = kernel;
     return DKV_OK;
 }
@@ -1198,6 +1230,8 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     a.lds_ring = L->lds_ring;
     a.lds_poison = L->lds_poison;
     a.proj_mfma_min_batch = L->proj_mfma_min_batch;
+    a.proj_splitk_min_batch = L->proj_splitk_min_batch;
+    a.proj_ranges = L->proj_ranges;
     a.max_splits = L->max_splits;
     a.part_slots = L->max_splits + 1;
     a.qscale = (float)(1.4426950408889634074 / std::sqrt((double)s->head_dim));

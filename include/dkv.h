@@ -316,8 +316,9 @@ dkv_status kv_layout_check_status(dkv_layout *kv_layout);
  * of 16 fixed at creation, independent of placement. */
 int32_t kv_layout_split_tokens(const dkv_layout *kv_layout);
 
-/* Split-attention kernel the layout's decode steps use. All read each page
- * run once per step for the whole group of query heads:
+/* Split-attention kernel the layout's decode steps use. All but the naive
+ * comparator read each page run once per step for the whole group of query
+ * heads:
  *   0 = one wavefront per work item with a register double buffer, VALU
  *       arithmetic (the default below groups of 4 query heads);
  *   1 = a producer wavefront that streams page runs with LDS DMA into a ring
@@ -329,10 +330,15 @@ int32_t kv_layout_split_tokens(const dkv_layout *kv_layout);
  *   2 = the naive zero-copy comparator (one wavefront per query head, so
  *       each KV head's pages are read once per query head of its group), for
  *       measurement only, with the arithmetic of the group's default kernel
- *       and so the same bits as it.
- * Chosen at creation; the environment variable
- * DKV_SPLIT_KERNEL=regs|lds|naive|mfma, read by kv_layout_create, selects
- * one (mfma only from groups of 4). -1 for a NULL layout. */
+ *       and so the same bits as it;
+ *   4 = a producer wavefront streaming page runs with LDS DMA into a ring for
+ *       a consumer wavefront with the arithmetic of 3 (same bits as 3; groups
+ *       of 4 and 8, head_dim 128).
+ * Chosen at creation (producer/consumer DirectKV digest, 核心方法; the
+ * "KV Cache 内存层级" overview, 2.1); the environment variable
+ * DKV_SPLIT_KERNEL=regs|lds|naive|mfma|ldsmfma, read by kv_layout_create,
+ * selects one (mfma from groups of 4, ldsmfma from groups of 4 at head_dim
+ * 128). -1 for a NULL layout. */
 int32_t kv_layout_split_kernel(const dkv_layout *kv_layout);
 
 /* Wavefronts the register split kernel runs on: 0 = one per work item
@@ -346,9 +352,9 @@ int32_t kv_layout_split_kernel(const dkv_layout *kv_layout);
  * either way. -1 for a NULL layout. */
 int32_t kv_layout_split_waves(const dkv_layout *kv_layout);
 
-/* Switches the layout's split-attention kernel (0 to 3 as above) for the
+/* Switches the layout's split-attention kernel (0 to 4 as above) for the
  * decode steps enqueued after the call. Errors: DKV_E_INVALID_ARG for a NULL
- * layout, an unknown kernel, or 3 below groups of 4. */
+ * layout, an unknown kernel, or 3 / 4 on a shape they do not serve. */
 dkv_status kv_layout_set_split_kernel(dkv_layout *kv_layout, int32_t kernel);
 
 /* Thread-local message of the last failing call on this thread. */

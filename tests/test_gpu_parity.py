@@ -158,25 +158,33 @@ def test_split_and_page_edges(oracle, monkeypatch, split):
 
 
 # --------------------------------------------------------------------------- exactness
-@pytest.mark.parametrize("shape_name,batch,mfma_from", [
-    ("llama8b", 3, None), ("llama8b", 3, 1), ("llama8b", 1, 1), ("llama8b", 8, None), ("llama8b", 16, None),
-    ("llama8b", 17, None), ("llama8b", 32, None), ("llama8b", 40, None), ("llama8b", 64, None),
-    ("llama8b", 70, None), ("llama70b", 16, None), ("llama70b", 33, None)])
-def test_projection_integer_exact(oracle, monkeypatch, shape_name, batch, mfma_from):
+PROJ_KNOBS = ("DKV_PROJ_MFMA_MIN_BATCH", "DKV_PROJ_SPLITK_MIN_BATCH", "DKV_PROJ_RANGES")
+
+
+@pytest.mark.parametrize("shape_name,batch,knobs", [
+    ("llama8b", 3, {}), ("llama8b", 3, {"DKV_PROJ_MFMA_MIN_BATCH": "1"}),
+    ("llama8b", 1, {"DKV_PROJ_MFMA_MIN_BATCH": "1"}), ("llama8b", 8, {}),
+    ("llama8b", 8, {"DKV_PROJ_SPLITK_MIN_BATCH": "16"}), ("llama8b", 16, {}),
+    ("llama8b", 17, {}), ("llama8b", 32, {}), ("llama8b", 40, {}), ("llama8b", 64, {}),
+    ("llama8b", 70, {}), ("llama8b", 12, {"DKV_PROJ_RANGES": "1"}), ("llama8b", 24, {"DKV_PROJ_RANGES": "2"}),
+    ("llama8b", 48, {"DKV_PROJ_RANGES": "4"}), ("llama70b", 16, {}), ("llama70b", 33, {}),
+    ("llama70b", 8, {"DKV_PROJ_SPLITK_MIN_BATCH": "16"})])
+def test_projection_integer_exact(oracle, monkeypatch, shape_name, batch, knobs):
     """Small-integer x and W make every product and fp32 sum exact, so the
     written-back K/V must equal the oracle's fp64 values rounded to bf16, bit
     for bit; with an empty history attn_out is exactly bf16(v_new). Batches
     below 8 take the VALU projection by default (and the streamed one-tile
-    MFMA kernel with DKV_PROJ_MFMA_MIN_BATCH=1), 8 to 15 the one-tile MFMA
-    kernel; from 16 the split-k MFMA kernel stages x in tiles of 16, 32 or 64
-    sequences and a second kernel adds the partial sums (17, 40: a partly
-    filled tile; 70: a second 64-sequence tile). The Llama-3-70B shape
-    (hidden 8192) splits the hidden dimension into 8 ranges."""
+    MFMA kernel with DKV_PROJ_MFMA_MIN_BATCH=1, as do batches 8 to 15 with
+    DKV_PROJ_SPLITK_MIN_BATCH=16); from 8 the split-k MFMA kernel stages x in
+    tiles of 16, 32 or 64 sequences (17, 40: a partly filled tile; 70: a
+    second 64-sequence tile) and writes one slab per range of the hidden
+    dimension (8 by default; 1, 2 and 4 forced), which the fresh-token kernel
+    adds."""
     import synth
-    if mfma_from is None:
-        monkeypatch.delenv("DKV_PROJ_MFMA_MIN_BATCH", raising=False)
-    else:
-        monkeypatch.setenv("DKV_PROJ_MFMA_MIN_BATCH", str(mfma_from))
+    for k in PROJ_KNOBS:
+        monkeypatch.delenv(k, raising=False)
+    for k, v in knobs.items():
+        monkeypatch.setenv(k, v)
     base = configs.LLAMA8B_HOST if shape_name == "llama8b" else configs.LLAMA70B_LONG
     wl = base.replace(batch=batch, n_layers=1)
     ctx = np.array([[0, 5, 16][b % 3] for b in range(batch)], np.int32)
@@ -443,9 +451,10 @@ def test_split_kernel_variants_bit_identical(oracle, monkeypatch, wl_name, ctx):
     VALU kernels compute every head in the same order (identical bits); at
     group 8 the register kernel splits each page's tokens over two
     wavefronts, which changes the order of the fp32 sums. The layout's
-    default is the matrix-core kernel from groups of 4."""
+    default is the matrix-core kernel from groups of 4; the LDS ring with a
+    matrix-core consumer gives its bits exactly."""
     wl = configs.BY_NAME[wl_name].replace(batch=len(ctx), n_layers=1)
-    variants = ("regs", "lds", "mfma") if wl.group >= 4 else ("regs", "lds")
+    variants = ("regs", "lds", "mfma", "ldsmfma") if wl.group >= 4 else ("regs", "lds")
     monkeypatch.delenv("DKV_SPLIT_KERNEL", raising=False)
     s = H.Setup(wl, ctx_lens=ctx[:1], hbm_tail=0)
     try:
@@ -465,6 +474,9 @@ def test_split_kernel_variants_bit_identical(oracle, monkeypatch, wl_name, ctx):
     if wl.group < 8:
         assert np.array_equal(outs["regs"], outs["lds"])
         assert np.array_equal(outs32["regs"].view(np.uint32), outs32["lds"].view(np.uint32))
+    if wl.group >= 4:
+        assert np.array_equal(outs["mfma"], outs["ldsmfma"])
+        assert np.array_equal(outs32["mfma"].view(np.uint32), outs32["ldsmfma"].view(np.uint32))
     ref = H.oracle_full(oracle, wl, 0, np.asarray(ctx, np.int32))["attn_out"]
     tight = tight_reference(oracle, wl, 0, np.asarray(ctx, np.int32))
     for variant in variants:
@@ -518,6 +530,42 @@ def test_lds_ring_depths_and_poison(oracle, monkeypatch, wl_name):
         assert np.array_equal(run({"DKV_SPLIT_KERNEL": "regs"}), base)
     check_tight(base.view(np.float32).astype(np.float64), tight_reference(oracle, wl, 0, np.asarray(ctx, np.int32)),
                 "lds ring %s" % wl_name)
+
+
+@pytest.mark.parametrize("wl_name", ["llama3-8b-b8-ctx32768-host", "llama3-70b-b16-ctx131072-8layers-host"],
+                         ids=["g4", "g8"])
+def test_lds_mfma_ring_depths_poison_and_edges(oracle, monkeypatch, wl_name):
+    """The LDS ring with a matrix-core consumer: ring depths 2, 3 and 4 with
+    every freed slot filled with NaN before its refill (DKV_POISON=1), over
+    splits of 144 tokens (9 pages: ring wrap-around) with partial first,
+    middle and last pages and host and HBM pages mixed, give the bits of the
+    matrix-core register kernel; a consumer reading a slot before its DMA
+    landed, or a wrong swizzle, would show."""
+    wl = configs.BY_NAME[wl_name].replace(n_layers=1)
+    ctx = [1, 15, 16, 17, 145, 300, 1030]
+    wl = wl.replace(batch=len(ctx))
+    tail = [0, 1 << 20, 0, 16, 40, 300, 500]
+
+    def run(env):
+        for k in ("DKV_SPLIT_KERNEL", "DKV_LDS_RING", "DKV_POISON", "DKV_SPLIT_TOKENS"):
+            monkeypatch.delenv(k, raising=False)
+        monkeypatch.setenv("DKV_SPLIT_TOKENS", "144")
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        s = H.Setup(wl, ctx_lens=ctx, hbm_tail=tail)
+        try:
+            assert s.layout.split_kernel == env["DKV_SPLIT_KERNEL"]
+            return s.run(f32=True).cpu().numpy().view(np.uint32)
+        finally:
+            s.free()
+
+    base = run({"DKV_SPLIT_KERNEL": "mfma"})
+    assert np.all(np.isfinite(base.view(np.float32)))
+    for ring in ("2", "3", "4"):
+        got = run({"DKV_SPLIT_KERNEL": "ldsmfma", "DKV_LDS_RING": ring, "DKV_POISON": "1"})
+        assert np.array_equal(got, base), ring
+    check_tight(base.view(np.float32).astype(np.float64), tight_reference(oracle, wl, 0, np.asarray(ctx, np.int32)),
+                "lds-mfma ring %s" % wl_name)
 
 
 # --------------------------------------------------------------------------- comparators

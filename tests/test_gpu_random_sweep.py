@@ -4,7 +4,8 @@ Each case draws a shape (head_dim 64/128, group 1/2/4/8, 1-8 KV heads, hidden
 512-2048), a batch with ragged context lengths (uniform, plus the page and
 split edges 0, 1, 15, 16, 17, T-1, T, T+1), spare capacity, a per-sequence
 HBM window, and the launch knobs the layout reads at creation (split length T,
-split kernel variant, looping wavefront count, projection threshold). It
+split kernel variant, looping wavefront count, projection thresholds and
+split-k range count). It
 checks, through the C ABI:
   * fp32 output against the oracle fed the bf16-rounded fresh K/V:
     rel-L2 <= 1e-4;
@@ -28,7 +29,7 @@ pytestmark = [pytest.mark.gpu,
 
 N_CASES = 24
 KNOBS = ("DKV_SPLIT_TOKENS", "DKV_SPLIT_KERNEL", "DKV_SPLIT_WAVES", "DKV_PROJ_MFMA_MIN_BATCH",
-         "DKV_LDS_RING")
+         "DKV_LDS_RING", "DKV_PROJ_SPLITK_MIN_BATCH", "DKV_PROJ_RANGES")
 
 
 def draw(i):
@@ -45,12 +46,14 @@ def draw(i):
     cap = [c + 1 + s for c, s in zip(ctx, slack)]
     tail = [int(rng.choice([0, 0, 1, 16, 17, 100, 1 << 20])) if rng.random() < 0.8 else int(rng.integers(0, cc + 1))
             for cc in cap]
-    variants = ["regs", "lds"] + (["mfma"] if G >= 4 else [])
+    variants = ["regs", "lds"] + (["mfma"] if G >= 4 else []) + (["ldsmfma"] if G >= 4 and d == 128 else [])
     env = {"DKV_SPLIT_TOKENS": str(T),
            "DKV_SPLIT_KERNEL": str(rng.choice(variants + [None])),
            "DKV_SPLIT_WAVES": str(rng.choice(["", "0", "3", "64", "256"])),
            "DKV_PROJ_MFMA_MIN_BATCH": str(rng.choice(["", "1", "8", "1000"])),
-           "DKV_LDS_RING": str(rng.choice(["", "2", "3", "4"]))}
+           "DKV_LDS_RING": str(rng.choice(["", "2", "3", "4"])),
+           "DKV_PROJ_SPLITK_MIN_BATCH": str(rng.choice(["", "", "1", "16"])),
+           "DKV_PROJ_RANGES": str(rng.choice(["", "", "1", "2", "4", "8"]))}
     env = {k: v for k, v in env.items() if v not in ("", "None")}
     wl = configs.TINY.replace(name="sweep-%d" % i, seed=0x5EED0000 + i, batch=B, hidden=hidden,
                               n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=d)
