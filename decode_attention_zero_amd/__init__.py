@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
             "dkv_host_buffer_free": ([P], I32),
             "dkv_copy": ([P, P, ctypes.c_uint64, P], I32),
             "dkv_gemm_bf16_nt": ([P, P, P, I32, I32, I32, I32, P], I32),
+            "dkv_gemm_bf16_nt_bstationary": ([P, P, P, I32, I32, I32, P, ctypes.c_uint64, P], I32),
+            "dkv_gemm_bstationary_workspace_bytes": ([I32, I32, I32], ctypes.c_uint64),
             "kv_layout_timing_enable": ([P, I32, I32], I32),
             "kv_layout_timing_read": ([P, P, P, P, P, P], I32),
             "dkv_cpu_attention": ([P, I32, P, P, P, P, P, I32, P], I32),
@@ -116,7 +118,8 @@ EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement",
             "kv_layout_create", "kv_layout_create_windowed", "kv_advance", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
             "kv_layout_split_kernel", "kv_layout_set_split_kernel", "kv_layout_split_waves", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
             "decode_step_noalloc", "decode_step_noalloc_scratch_bytes", "dkv_probe_stream_read", "kv_pool_copy", "dkv_host_buffer_alloc", "dkv_host_buffer_free",
-            "dkv_copy", "dkv_gemm_bf16_nt", "kv_layout_timing_enable", "kv_layout_timing_read",
+            "dkv_copy", "dkv_gemm_bf16_nt", "dkv_gemm_bf16_nt_bstationary", "dkv_gemm_bstationary_workspace_bytes",
+            "kv_layout_timing_enable", "kv_layout_timing_read",
             "dkv_cpu_attention", "dkv_cpu_stream_read", "dkv_cpu_attention_pages"]
 
 
@@ -423,6 +426,25 @@ class HostBuffer:
 def copy(dst_ptr: int, src_ptr: int, nbytes: int, stream=None) -> None:
     """Copy-engine copy between device-known addresses (the swap-in of staging)."""
     _check(lib().dkv_copy(dst_ptr, src_ptr, nbytes, _stream_ptr(stream)))
+
+
+def gemm_bstationary_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().dkv_gemm_bstationary_workspace_bytes(M, N, K))
+
+
+def gemm_bf16_nt_bstationary(A, B_ptr: int, C, M: int, N: int, K: int, workspace, stream=None):
+    """C [M][N] fp32 = A [M][K] bf16 x B^T (B [N][K] bf16 at B_ptr, HBM or host),
+    B-stationary: each B tile fetched once; `workspace` a device tensor of at
+    least gemm_bstationary_workspace_bytes(M, N, K) bytes."""
+    import torch
+    if A.dtype != torch.bfloat16 or tuple(A.shape) != (M, K):
+        raise ValueError("A must be a bf16 [M][K] device tensor")
+    if C.dtype != torch.float32 or tuple(C.shape) != (M, N):
+        raise ValueError("C must be an fp32 [M][N] device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().dkv_gemm_bf16_nt_bstationary(_dev_ptr(A, "A"), B_ptr, _dev_ptr(C, "C"), M, N, K,
+                                              _dev_ptr(workspace, "workspace"), nbytes, _stream_ptr(stream)))
+    return C
 
 
 def gemm_bf16_nt(A, B_ptr: int, C, M: int, N: int, K: int, cpu_aware: bool, stream=None):

@@ -147,6 +147,11 @@ hipError_t launch_split(const StepArgs &a, hipStream_t stream);
 hipError_t launch_combine(const StepArgs &a, hipStream_t stream);
 
 // GEMM C = A x B^T (bf16 in, fp32 out) with a row-major or CPU-aware tile order.
+// B-stationary GEMM (each 128 x 512 tile of B fetched once): partial sums of
+// C per 512-wide k tile in `workspace`, then added in k order.
+uint64_t gemm_bstationary_workspace_bytes(int M, int N, int K);
+hipError_t launch_gemm_nt_bstationary(const uint16_t *A, const uint16_t *B, float *C, int M, int N, int K,
+                                      float *workspace, hipStream_t stream);
 hipError_t launch_gemm_nt(const uint16_t *A, const uint16_t *B, float *C, int M, int N, int K,
                           bool cpu_aware, hipStream_t stream);
 

@@ -1370,6 +1370,27 @@ dkv_status dkv_gemm_bf16_nt(const uint16_t *A, const uint16_t *B, float *C, int3
     return DKV_OK;
 }
 
+uint64_t dkv_gemm_bstationary_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return dkv::gemm_bstationary_workspace_bytes(M, N, K);
+}
+
+dkv_status dkv_gemm_bf16_nt_bstationary(const uint16_t *A, const uint16_t *B, float *C, int32_t M, int32_t N,
+                                        int32_t K, float *workspace, uint64_t workspace_bytes,
+                                        dkv_stream_t stream) {
+    if (!A || !B || !C || !workspace || M <= 0 || N <= 0 || K <= 0 || M % 64 || N % 128 || K % 512 ||
+        (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C | (uintptr_t)workspace) & 15u))
+        return fail(DKV_E_INVALID_ARG,
+                    "dkv_gemm_bf16_nt_bstationary: need M a multiple of 64, N of 128, K of 512, aligned pointers");
+    if (workspace_bytes < dkv::gemm_bstationary_workspace_bytes(M, N, K))
+        return fail(DKV_E_CAPACITY, "dkv_gemm_bf16_nt_bstationary: workspace of %llu bytes, %llu needed",
+                    (unsigned long long)workspace_bytes,
+                    (unsigned long long)dkv::gemm_bstationary_workspace_bytes(M, N, K));
+    hipError_t e = dkv::launch_gemm_nt_bstationary(A, B, C, M, N, K, workspace, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "dkv_gemm_bf16_nt_bstationary");
+    return DKV_OK;
+}
+
 static dkv_status dkv_probe_stream_read_body(const void *ptr, uint64_t bytes, int32_t grid, int32_t unroll,
                                              int32_t reps, float *ms_median) {
     // unroll < 0 selects nontemporal loads with |unroll| in flight

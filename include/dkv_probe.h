@@ -93,6 +93,25 @@ dkv_status dkv_copy(void *dst, const void *src, uint64_t bytes, dkv_stream_t str
 dkv_status dkv_gemm_bf16_nt(const uint16_t *A, const uint16_t *B, float *C, int32_t M, int32_t N,
                             int32_t K, int32_t tile_order, dkv_stream_t stream);
 
+/* The B-stationary form of the same product ("KV Cache 内存层级" overview,
+ * 2.1 去搬运：DirectKV: CPU-aware tiling keeps the remote operand's tile
+ * resident so that it crosses the link once, at the price of sending partial
+ * results through HBM): each 128 x 512 tile of B is fetched once into one
+ * workgroup's LDS and all of A streams past it; the fp32 partial C of each
+ * 512-wide k tile goes to `workspace`, and a second kernel adds the k tiles
+ * in order into C. Every entry is one fp32 sum per k tile plus the adds of
+ * the tiles' sums, so its bits can differ from dkv_gemm_bf16_nt's within the
+ * fp32 summation bound (identical when every partial sum is exact).
+ * workspace: device memory of at least
+ * dkv_gemm_bstationary_workspace_bytes(M, N, K) = (K / 512) * M * N * 4
+ * bytes, caller-owned. Requires M a multiple of 64, N of 128, K of 512 and
+ * 16-byte aligned pointers. Errors: DKV_E_INVALID_ARG, DKV_E_CAPACITY (too
+ * small a workspace); both before anything is enqueued. */
+dkv_status dkv_gemm_bf16_nt_bstationary(const uint16_t *A, const uint16_t *B, float *C, int32_t M, int32_t N,
+                                        int32_t K, float *workspace, uint64_t workspace_bytes,
+                                        dkv_stream_t stream);
+uint64_t dkv_gemm_bstationary_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
 /* ---------------------------------------------------------------------------
  * Attention on the host CPU: the comparator for moving decoding attention to
  * where the KV lives instead of moving the KV to the GPU ("KV Cache 内存层级"
