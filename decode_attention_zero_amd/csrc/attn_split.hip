@@ -14,13 +14,17 @@
 // state is the standard flash-decoding decomposition (not on the pages); the
 // split boundaries depend only on token indices, never on where a page lives,
 // so host and HBM placements give bit-identical results.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace dkv {
 namespace {
 
-// VALU split attention. Work item (KV head g, split s, sequence b) = blockIdx
-// (x, y, z) in the one-wavefront-per-item launches (XCD-aware order, see launch).
+// VALU split attention. Work item (KV head g, split s, sequence b): in the
+// one-wavefront-per-item launches g = blockIdx.x and (b, s) is entry
+// blockIdx.y + gridDim.y * blockIdx.z of the step's item list (XCD-aware
+// order, see launch).
 //
 // Lane mapping inside a page run (K tile then V tile, each [16 tok][D] bf16):
 // wave load j reads bytes [j*1024, (j+1)*1024) of a tile, lane l the 16 bytes
@@ -508,20 +512,25 @@ __device__ __forceinline__ void split_item_mfma(const StepArgs &a, char *stage, 
     st.finish(a, b, h0, s);
 }
 
-// Matrix-core split kernels: one wavefront per work item (g, s, b) =
-// blockIdx (x, y, z), or (PER_QUERY_HEAD, G = 1) the naive comparator with
-// one item per query head, (s, h, b) = blockIdx (x, y, z); and the looping form for host-dominated layouts.
+// Matrix-core split kernels: one wavefront per work item (KV head blockIdx.x,
+// item list entry blockIdx.y + gridDim.y * blockIdx.z), or (PER_QUERY_HEAD,
+// G = 1) the naive comparator with one item per query head, (s, h, b) =
+// blockIdx (x, y, z) over every split slot; and the looping form for
+// host-dominated layouts.
 constexpr int kMfmaWavesPerSimd = 3;   // register budget: 168 per lane
 
 template <int D, int G, bool PER_QUERY_HEAD = false>
 __global__ __launch_bounds__(64, kMfmaWavesPerSimd) void attn_split_mfma_kernel(StepArgs a) {
     __shared__ __attribute__((aligned(16))) char stage[MfmaState<D, G>::STAGE];
-    // The naive comparator keeps a plain (split, query head, sequence) order.
-    const int head = PER_QUERY_HEAD ? blockIdx.y : blockIdx.x;
-    const int s = PER_QUERY_HEAD ? blockIdx.x : blockIdx.y;
-    const int g = PER_QUERY_HEAD ? head / (a.n_q_heads / a.n_kv_heads) : head;
-    const int h0 = PER_QUERY_HEAD ? head : head * G;
-    split_item_mfma<D, G>(a, stage, s, g, h0, blockIdx.z);
+    if constexpr (PER_QUERY_HEAD) {
+        // The naive comparator keeps a plain (split, query head, sequence) order.
+        const int h = blockIdx.y;
+        split_item_mfma<D, G>(a, stage, blockIdx.x, h / (a.n_q_heads / a.n_kv_heads), h, blockIdx.z);
+    } else {
+        int b, s;
+        if (!listed_item(a, blockIdx.y + gridDim.y * blockIdx.z, b, s)) return;
+        split_item_mfma<D, G>(a, stage, s, blockIdx.x, blockIdx.x * G, b);
+    }
 }
 
 // The looping form runs a few hundred wavefronts in all (one or two per CU),
@@ -531,33 +540,38 @@ template <int D, int G>
 __global__ __launch_bounds__(64, 1) void attn_split_mfma_persistent_kernel(StepArgs a) {
     __shared__ __attribute__((aligned(16))) char stage[MfmaState<D, G>::STAGE];
     __shared__ int item;
-    const int n_items = a.n_kv_heads * a.max_splits * a.batch;
+    const int n_items = a.n_kv_heads * (int)a.item_list[0];
     for (;;) {
         const int i = take_item(a, &item);
         if (i >= n_items) break;
         const int g = i % a.n_kv_heads;
-        const int rest = i / a.n_kv_heads;
-        split_item_mfma<D, G>(a, stage, rest % a.max_splits, g, g * G, rest / a.max_splits);
+        int b, s;
+        listed_item(a, i / a.n_kv_heads, b, s);
+        split_item_mfma<D, G>(a, stage, s, g, g * G, b);
     }
 }
 
-// One wavefront per work item (g, s, b) = blockIdx (x, y, z).
+// One wavefront per work item (KV head blockIdx.x, item list entry
+// blockIdx.y + gridDim.y * blockIdx.z).
 // PER_QUERY_HEAD (with G = 1) is the naive zero-copy comparator, not the
 // method: one work item per query head (s, h, b) = blockIdx (x, y, z), so each KV head's pages
 // cross the link once per query head of its group (G times per step) instead
 // of once. Each head's arithmetic is the same as in the grouped kernel.
 template <int D, int G, int WPI, bool PER_QUERY_HEAD = false>
 __global__ __launch_bounds__(64 * WPI, WPI) void attn_split_kernel(StepArgs a) {
-    const int head = PER_QUERY_HEAD ? blockIdx.y : blockIdx.x;
-    const int s = PER_QUERY_HEAD ? blockIdx.x : blockIdx.y;
-    const int g = PER_QUERY_HEAD ? head / (a.n_q_heads / a.n_kv_heads) : head;
-    const int h0 = PER_QUERY_HEAD ? head : head * G;
-    split_item<D, G, WPI>(a, s, g, h0, blockIdx.z);
+    if constexpr (PER_QUERY_HEAD) {
+        const int h = blockIdx.y;
+        split_item<D, G, WPI>(a, blockIdx.x, h / (a.n_q_heads / a.n_kv_heads), h, blockIdx.z);
+    } else {
+        int b, s;
+        if (!listed_item(a, blockIdx.y + gridDim.y * blockIdx.z, b, s)) return;
+        split_item<D, G, WPI>(a, s, blockIdx.x, blockIdx.x * G, b);
+    }
 }
 
 // The same work items on a fixed number of workgroups (gridDim.x), each
 // taking the next item from a shared queue (take_item) in the order (KV head
-// fastest, then split, then sequence), so the waves in flight read the runs
+// fastest, then the item list's (sequence, split) pairs), so the waves in flight read the runs
 // of the same pages together. Bounding the waves in flight bounds the
 // requests queued on the host link, where too many outstanding reads lower
 // its bandwidth (the streaming-read probe drops from 57.5 to 56.0 GB/s when
@@ -569,14 +583,13 @@ __global__ __launch_bounds__(64 * WPI, WPI) void attn_split_kernel(StepArgs a) {
 template <int D, int G, int WPI>
 __global__ __launch_bounds__(64 * WPI, WPI) void attn_split_persistent_kernel(StepArgs a) {
     __shared__ int item;
-    const int n_items = a.n_kv_heads * a.max_splits * a.batch;
+    const int n_items = a.n_kv_heads * (int)a.item_list[0];
     for (;;) {
         const int i = take_item(a, &item);
         if (i >= n_items) break;
         const int g = i % a.n_kv_heads;
-        const int rest = i / a.n_kv_heads;
-        const int s = rest % a.max_splits;
-        const int b = rest / a.max_splits;
+        int b, s;
+        listed_item(a, i / a.n_kv_heads, b, s);
         split_item<D, G, WPI>(a, s, g, g * G, b);
     }
 }
@@ -620,7 +633,9 @@ __global__ __launch_bounds__(64 * (NC + 1)) void attn_split_lds_kernel(StepArgs 
     constexpr int LPP = 2 * NLD;               // DMA loads per page run
     __shared__ __attribute__((aligned(16))) char ring[NS][S::RUN];
 
-    const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+    const int g = blockIdx.x;
+    int b, s;
+    if (!listed_item(a, blockIdx.y + gridDim.y * blockIdx.z, b, s)) return;
     const int L = a.ctx_lens[b];
     if (L < 0 || L >= a.capacity[b]) return;
     const int t0 = s * a.split_tokens;
@@ -722,7 +737,9 @@ __global__ __launch_bounds__(128, 4) void attn_split_lds_mfma_kernel(StepArgs a)
     static_assert(S::TILE == 4096 && LPP == 8, "the swizzle assumes 16-chunk rows, 4 rows per load");
     __shared__ __attribute__((aligned(16))) char ring[NS][S::RUN];
 
-    const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+    const int g = blockIdx.x;
+    int b, s;
+    if (!listed_item(a, blockIdx.y + gridDim.y * blockIdx.z, b, s)) return;
     const int L = a.ctx_lens[b];
     if (L < 0 || L >= a.capacity[b]) return;
     const int t0 = s * a.split_tokens;
@@ -795,12 +812,23 @@ __global__ __launch_bounds__(128, 4) void attn_split_lds_mfma_kernel(StepArgs a)
 // split 0 but only the long ones a split 7 or 15, so one XCD streamed 2.3x
 // the bytes of another (MI355X, batch 32, contexts U[8192, 131072], all in
 // HBM, 8192-token splits: 1.87 ms, the busiest XCD's bytes at 1/8 of the
-// chip's bandwidth).
+// chip's bandwidth). The host does not know ctx_lens, so the grid has a
+// workgroup for every split the capacities allow (item_slots per KV head),
+// and the y/z index walks the step's item list: the workgroups with work are
+// dispatched first, those past the list's end return at once. Sizing the grid
+// by the capacities rather than by batch x max_splits matters: 2048 trailing
+// empty workgroups behind 2048 items still cost 5 % (MI355X, batch 32,
+// 65536-token contexts in HBM, 8192-token splits: 1.236 ms vs 1.298 ms).
+dim3 item_grid(const StepArgs &a) {
+    const int ny = std::min(a.item_slots, 65535);
+    return dim3(a.n_kv_heads, ny, (a.item_slots + ny - 1) / ny);
+}
+
 template <int D, int G>
 void launch(const StepArgs &a, hipStream_t st) {
     // Groups of 8 query heads share each work item between two wavefronts.
     constexpr int WPI = G >= 8 ? 2 : 1;
-    dim3 grid(a.n_kv_heads, a.max_splits, a.batch);
+    const dim3 grid = item_grid(a);
     if (a.split_variant == kSplitNaive) {
         // Per query head, with the arithmetic of the layout's grouped kernel.
         const dim3 heads(a.max_splits, a.n_q_heads, a.batch);
@@ -827,7 +855,7 @@ void launch(const StepArgs &a, hipStream_t st) {
 // item in the same XCD-aware order).
 template <int G>
 void launch_lds_mfma(const StepArgs &a, hipStream_t st) {
-    const dim3 grid(a.n_kv_heads, a.max_splits, a.batch);
+    const dim3 grid = item_grid(a);
     if (a.lds_ring == 3) attn_split_lds_mfma_kernel<G, 3><<<grid, 128, 0, st>>>(a);
     else if (a.lds_ring == 4) attn_split_lds_mfma_kernel<G, 4><<<grid, 128, 0, st>>>(a);
     else attn_split_lds_mfma_kernel<G, 2><<<grid, 128, 0, st>>>(a);

@@ -101,6 +101,37 @@ __device__ __forceinline__ void reset_items(const StepArgs &a) {
         __hip_atomic_store(a.item_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// Work items of a step: split s of sequence b covers cached tokens
+// [s T, min((s + 1) T, L)) with T = split_tokens and L = ctx_lens[b]; a
+// sequence has ceil(L / T) of them, none when L is out of range. The
+// fresh-token kernel lists them, sequence-major, in StepArgs::item_list; the
+// split kernels map workgroup (KV head g, list entry j) to entry j, so every
+// workgroup of the launch that has work comes before every one that has none
+// (a grid with empty items interleaved among the real ones streamed 9 % fewer
+// bytes per second on MI355X).
+__device__ __forceinline__ int splits_of(const StepArgs &a, int b) {
+    const int L = a.ctx_lens[b];
+    if (L < 0 || L >= a.capacity[b]) return 0;
+    return (L + a.split_tokens - 1) / a.split_tokens;
+}
+
+// Entry j of the item list: false past its end. The entry is read at an
+// index clamped into the list, so that both loads are in flight together.
+__device__ __forceinline__ bool listed_item(const StepArgs &a, int j, int &b, int &s) {
+    const uint32_t n = a.item_list[0];
+    const uint32_t e = a.item_list[1 + min(j, a.batch * a.max_splits - 1)];
+    if ((uint32_t)j >= n) return false;
+    b = (int)(e >> 16);
+    s = (int)(e & 0xFFFFu);
+    return true;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
 // Sequences whose ctx_lens entry is out of range raise the layout's flag.
 __device__ __forceinline__ void check_context_range(const StepArgs &a, int b) {
     const int L = a.ctx_lens[b];

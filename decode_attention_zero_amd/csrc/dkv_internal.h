@@ -41,6 +41,8 @@ struct StepArgs {
     int32_t max_splits;     // splits of the cached tokens per sequence, at most
     int32_t part_slots;     // partial slots per (sequence, query head): max_splits + 1; sequence b's
                             // fresh token takes slot ceil(ctx_lens[b] / split_tokens), after its splits
+    int32_t item_slots;     // work items the capacities allow: the sum over sequences of
+                            // ceil((capacity[b] - 1) / split_tokens), at least 1
     float qscale;           // log2(e) / sqrt(head_dim): scores come out in log2 units
     int32_t split_variant;  // kSplitRegisters, kSplitLds, kSplitNaive, kSplitMfma or kSplitLdsMfma
     int32_t split_waves;    // register kernel: > 0 = that many wavefronts loop over the items
@@ -68,6 +70,10 @@ struct StepArgs {
     uint32_t *status;         // range flag (bit 0: a ctx_lens entry out of range)
     uint32_t *item_counter;   // looping split kernels: next work item to take (zeroed by the
                               // step's fresh-token kernel before the split kernel runs)
+    uint32_t *item_list;      // [1 + batch * max_splits]: [0] = n, the number of (sequence, split)
+                              // pairs with tokens this step; [1 + j] = (b << 16) | s, sequence-major.
+                              // Written by the fresh-token kernel from ctx_lens; the split kernels
+                              // take their work items from it.
 };
 
 // What kv_advance's kernel reads and writes (see kv_advance in dkv.h).
@@ -113,10 +119,11 @@ constexpr int kProjSplitkMinBatch = 8;
 constexpr int kProjMaxSplits = 8;
 
 // Scratch bytes of one decode step (each buffer 256-byte aligned in the order
-// proj_part, q, part_o, part_ml, item counter), so that one carve serves the
-// layout-owned scratch and the static array of decode_step_noalloc alike.
+// proj_part, q, part_o, part_ml, item counter, item list), so that one carve
+// serves the layout-owned scratch and the static array of decode_step_noalloc
+// alike.
 struct ScratchPlan {
-    size_t proj_part, q, part_o, part_ml, item_counter, total;
+    size_t proj_part, q, part_o, part_ml, item_counter, item_list, total;
 };
 ScratchPlan scratch_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int part_slots);
 // Points a's scratch fields into `base` (an allocation of plan.total bytes).

@@ -24,7 +24,8 @@
 // partial sums, not K/V.
 //
 // The step's other bookkeeping happens here too: the range check of
-// ctx_lens and the reset of the split kernel's work queue.
+// ctx_lens, the list of the split kernel's work items and the reset of its
+// work queue.
 #include "device_common.h"
 
 namespace dkv {
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a) 
     __shared__ float s_q[G][D];
     __shared__ float s_kv[2][D];               // rounded K and V, as fp32 (exact)
     __shared__ __attribute__((aligned(16))) uint16_t s_kvb[2][D];   // their bf16 bits
+    __shared__ int s_before[kFreshWaves];
 
     reset_items(a);
     const int L = a.ctx_lens[b];
@@ -90,6 +92,23 @@ __global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a) 
         }
     }
     __syncthreads();
+
+    // Sequence b's entries of the step's item list, after those of sequences
+    // 0 .. b - 1 (workgroup g = 0 of each sequence; the last one writes the count).
+    if (g == 0) {
+        int n = 0;
+        for (int i = tid; i < b; i += kFreshThreads) n += splits_of(a, i);
+        n = wave_sum_int(n);
+        if (lane == 0) s_before[wave] = n;
+        __syncthreads();
+        int before = 0;
+#pragma unroll
+        for (int w = 0; w < kFreshWaves; ++w) before += s_before[w];
+        const int mine = splits_of(a, b);
+        for (int s = tid; s < mine; s += kFreshThreads)
+            a.item_list[1 + before + s] = ((uint32_t)b << 16) | (uint32_t)s;
+        if (b == a.batch - 1 && tid == 0) a.item_list[0] = (uint32_t)(before + mine);
+    }
     if (!in_range) return;
 
     // One-token state of each query head: m = s_new, l = 1, o = v_new.

@@ -143,6 +143,7 @@ struct dkv_layout {
     int32_t max_pages;
     int32_t split_tokens;
     int32_t max_splits;
+    int32_t item_slots;                // sum over sequences of ceil((capacity - 1) / split_tokens), >= 1
     int32_t split_variant;             // dkv::kSplitRegisters, kSplitLds, kSplitNaive or kSplitMfma
     int32_t split_waves;               // > 0: the register kernel runs on that many looping wavefronts
     int32_t proj_mfma_min_batch;       // batches from this size on project on the matrix cores
@@ -232,34 +233,49 @@ char *host_view(const dkv_layout *L, uint64_t addr) {
     return hp->host_base + (addr - base);
 }
 
-int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, int32_t max_cap) {
+// The split size T: the longest power of two of at most 8192 tokens whose
+// work items both
+//  * spread over the chip: at least 1536 full items (batch x KV heads x
+//    floor(longest cached context / T)); a short tail split, such as decode
+//    headroom past the cached tokens, is not counted), and
+//  * fit one round of the 3072 wavefronts the matrix-core split kernel keeps
+//    resident (3 per SIMD): at most 3072 items in all, tails included (KV
+//    heads x the sum over sequences of ceil((capacity - 1) / T)).
+// Without such a T: the smallest T whose items still fit one round (the most
+// parallel single round), or 8192 when even that takes two rounds (the
+// fewest rounds). A second round leaves waves idling at its end: 32
+// sequences of 57344 tokens, all in HBM: 1792 items of 8192 tokens 1.09 ms
+// (6.9 TB/s), 3584 items of 4096 tokens 1.28 ms. A longer split is a longer
+// contiguous page stream per wavefront, fewer partials to write and
+// combine, and fewer waves starting up; with every page in HBM on MI355X
+// (one wave per item): 1 GiB at batch 8 (2048 items at 1024 tokens),
+// 1024 / 2048 / 4096 tokens: 0.169 / 0.198 / 0.297 ms (too few items);
+// an 8 GiB layer at batch 16, 131072 tokens, group 8: 1024 / 2048 / 8192
+// tokens: 1.415 / 1.348 / 1.252 ms (6.07 -> 6.86 TB/s), group 4: 1.40 /
+// 1.35 / 1.25-1.31 ms. The choice depends on the shape and capacities
+// only, never on placement.
+int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, const int32_t *capacity) {
     if (const char *env = getenv("DKV_SPLIT_TOKENS")) {
         const int v = atoi(env);
         if (v >= DKV_PAGE_TOKENS && v % DKV_PAGE_TOKENS == 0) return v;
     }
-    // The longest split (at most 8192 tokens) that still leaves at least 1536
-    // full work items (splits of T tokens at the longest capacity; a short
-    // tail split is not counted) to spread over 256 CUs. Halving the split
-    // at most doubles
-    // the items, so a uniform batch lands in [1536, 3072) items: never more
-    // than the 3072 wavefronts the matrix-core split kernel keeps resident
-    // (3 per SIMD), which a second round of items would leave idling at the
-    // end (32 sequences of 57344 tokens, all in HBM: 1792 items of 8192
-    // tokens 1.09 ms, 6.9 TB/s; 3584 of 4096 tokens 1.28 ms). A longer split is a longer
-    // contiguous page stream per wavefront, fewer partials to write and
-    // combine, and fewer waves starting up; with every page in HBM on MI355X
-    // (one wave per item): 1 GiB at batch 8 (2048 items at 1024 tokens),
-    // 1024 / 2048 / 4096 tokens: 0.169 / 0.198 / 0.297 ms (too few items);
-    // an 8 GiB layer at batch 16, 131072 tokens, group 8: 1024 / 2048 / 8192
-    // tokens: 1.415 / 1.348 / 1.252 ms (6.07 -> 6.86 TB/s), group 4: 1.40 /
-    // 1.35 / 1.25-1.31 ms. The choice depends on the shape and capacities
-    // only, never on placement.
+    constexpr int64_t kMinFullItems = 1536, kResidentWaves = 3072;
+    int32_t max_cap = 1;
+    for (int b = 0; b < batch; ++b) max_cap = std::max(max_cap, capacity[b]);
     const int64_t max_cached = std::max(1, max_cap - 1);
-    int32_t t = 8192;
-    while (t > DKV_PAGE_TOKENS &&
-           (int64_t)batch * n_kv_heads * (max_cached / t) < 1536)
-        t /= 2;
-    return t;
+    auto items = [&](int64_t t) {
+        int64_t n = 0;
+        for (int b = 0; b < batch; ++b) n += (capacity[b] - 1 + t - 1) / t;
+        return n * n_kv_heads;
+    };
+    int32_t one_round = 0;       // the smallest T whose items fit one round
+    for (int32_t t = 8192; t >= DKV_PAGE_TOKENS; t /= 2) {
+        const int64_t n = items(t);
+        if (n > kResidentWaves) break;          // smaller T only add items
+        if ((int64_t)batch * n_kv_heads * (max_cached / t) >= kMinFullItems) return t;
+        one_round = t;
+    }
+    return one_round ? one_round : 8192;
 }
 
 // Split-attention kernel variant. Every default streams pages through a
@@ -403,7 +419,8 @@ ScratchPlan scratch_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim,
     p.part_o = align256(B * Hq * (size_t)part_slots * D * sizeof(float));
     p.part_ml = align256(B * Hq * (size_t)part_slots * sizeof(float2));
     p.item_counter = 256;
-    p.total = p.proj_part + p.q + p.part_o + p.part_ml + p.item_counter;
+    p.item_list = align256((1 + B * (size_t)(part_slots - 1)) * sizeof(uint32_t));
+    p.total = p.proj_part + p.q + p.part_o + p.part_ml + p.item_counter + p.item_list;
     return p;
 }
 
@@ -418,6 +435,8 @@ void carve_scratch(StepArgs &a, char *base, const ScratchPlan &p) {
     a.part_ml = reinterpret_cast<float2 *>(c);
     c += p.part_ml;
     a.item_counter = reinterpret_cast<uint32_t *>(c);
+    c += p.item_counter;
+    a.item_list = reinterpret_cast<uint32_t *>(c);
 }
 
 hipError_t launch_decode_step(const StepArgs &a, hipStream_t st, hipEvent_t *ev) {
@@ -620,8 +639,11 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
     const int batch = L->batch;
     int32_t max_cap = 0;
     for (int b = 0; b < batch; ++b) max_cap = std::max(max_cap, L->capacity[b]);
-    L->split_tokens = choose_split_tokens(batch, shape->n_kv_heads, max_cap);
+    L->split_tokens = choose_split_tokens(batch, shape->n_kv_heads, L->capacity.data());
     L->max_splits = std::max(1, (std::max(1, max_cap - 1) + L->split_tokens - 1) / L->split_tokens);
+    int64_t item_slots = 0;
+    for (int b = 0; b < batch; ++b) item_slots += (L->capacity[b] - 1 + L->split_tokens - 1) / L->split_tokens;
+    L->item_slots = (int32_t)std::max<int64_t>(1, std::min<int64_t>(item_slots, INT32_MAX));
     L->scratch = dkv::scratch_plan(batch, shape->n_q_heads, shape->n_kv_heads, shape->head_dim, L->max_splits + 1);
     L->split_variant = choose_split_variant(shape->n_q_heads / shape->n_kv_heads, shape->head_dim);
     int64_t n_host = 0, n_hbm = 0;
@@ -650,10 +672,16 @@ static dkv_status finish_layout(dkv_layout *L, const std::vector<uint64_t> &tabl
         return st;
     };
     // The one-wavefront-per-item launches put the splits of a sequence in
-    // grid dimension y (at most 65535).
+    // grid dimension y (at most 65535); the step's item list packs a split
+    // index into 16 bits and indexes its batch * max_splits entries with int.
     if (L->max_splits > 65535) {
         fail(DKV_E_UNSUPPORTED, "kv_layout_create: %d splits per sequence (capacity / split size) exceed 65535",
              L->max_splits);
+        return cleanup(DKV_E_UNSUPPORTED);
+    }
+    if ((int64_t)batch * L->max_splits >= (int64_t)INT32_MAX) {
+        fail(DKV_E_UNSUPPORTED, "kv_layout_create: batch x splits per sequence (%lld) exceeds 2^31 - 1",
+             (long long)batch * L->max_splits);
         return cleanup(DKV_E_UNSUPPORTED);
     }
     const size_t n_entries = table.size();
@@ -1234,6 +1262,7 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     a.proj_ranges = L->proj_ranges;
     a.max_splits = L->max_splits;
     a.part_slots = L->max_splits + 1;
+    a.item_slots = L->item_slots;
     a.qscale = (float)(1.4426950408889634074 / std::sqrt((double)s->head_dim));
     a.page_table = L->d_page_table + (size_t)layer * L->batch * L->max_pages;
     a.capacity = L->d_capacity;

@@ -631,3 +631,59 @@ def test_wave_count_does_not_change_bits(monkeypatch):
         assert s.layout.split_waves == 0          # 1 host page in 110: HBM decides the step
     finally:
         s.free()
+
+
+# --------------------------------------------------------------------------- work-item list
+ITEM_FORMS = [("regs", "0"), ("regs", "5"), ("lds", "0"), ("mfma", "0"), ("mfma", "5"), ("ldsmfma", "0")]
+
+
+def test_item_list_edges(oracle, monkeypatch):
+    """The split kernels take their (sequence, split) work items from a list
+    the fresh-token kernel builds from ctx_lens each step, on a grid sized by
+    the capacities. Sequences of capacity 1 (no split at all) and of empty
+    context, contexts that shrink from one step to the next (the list is
+    rebuilt), and an out-of-range sequence in the middle of the batch (it
+    lists no item, the others keep theirs) give the oracle's outputs on every
+    split kernel form, one wavefront per item or a few looping wavefronts,
+    with identical bits across the forms of one arithmetic."""
+    import torch
+    monkeypatch.setenv("DKV_SPLIT_TOKENS", "64")
+    wl = configs.LLAMA8B_HOST.replace(batch=7)
+    cap = [1, 300, 65, 1000, 1, 2000, 130]
+    # Contexts never grow from one step to the next, so the fresh K/V a step
+    # writes back (slot ctx_lens[b]) is never read by a later one.
+    steps = [[0, 299, 64, 999, 0, 1999, 129],
+             [0, 17, 64, 64, 0, 1499, 1],
+             [0, 300, 0, 5, 0, 7, 1]]            # sequence 1: ctx == capacity, out of range
+    tails = [0, 1 << 20, 0, 500, 0, 1 << 20, 40]
+    outs = {}
+    for variant, waves in ITEM_FORMS:
+        monkeypatch.setenv("DKV_SPLIT_KERNEL", variant)
+        monkeypatch.setenv("DKV_SPLIT_WAVES", waves)
+        s = H.Setup(wl, ctx_lens=steps[0], capacity=cap, hbm_tail=tails)
+        try:
+            assert s.layout.split_kernel == variant and s.layout.split_tokens == 64
+            assert s.layout.split_waves == int(waves)
+            got = []
+            for i, ctx in enumerate(steps):
+                s.ctx_dev = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+                got.append(s.run(f32=True).cpu().numpy())
+                if i < 2:
+                    s.layout.check_status()
+                else:
+                    with pytest.raises(H.dkv.DkvError):
+                        s.layout.check_status()
+            outs[(variant, waves)] = got
+        finally:
+            s.free()
+    for i, ctx in enumerate(steps):
+        c = np.asarray(ctx, np.int32)
+        ok = c < np.asarray(cap)
+        ref = tight_reference(oracle, wl, 0, np.where(ok, c, 0))
+        for form, got in outs.items():
+            assert np.all(np.isnan(got[i][~ok])), (form, i)
+            check_tight(got[i].astype(np.float64), ref, "item list %s step %d" % (form, i), mask=ok)
+        for a, b in (("regs", "lds"), ("mfma", "ldsmfma")):
+            same = [f for f in outs if f[0] in (a, b)]
+            for f in same[1:]:
+                assert np.array_equal(outs[same[0]][i][ok].view(np.uint32), outs[f][i][ok].view(np.uint32)), (f, i)

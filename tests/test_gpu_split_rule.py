@@ -1,8 +1,10 @@
 """The layout's split size: the longest power-of-two split of at most 8192
 tokens that leaves at least 1536 full work items (batch x KV heads x
-floor(longest cached context / T)), so that a uniform batch never has more
-items than the 3072 wavefronts the matrix-core split kernel keeps resident.
-Layouts only (all pages in HBM); no kernel runs."""
+floor(longest cached context / T)) and whose items, tails included (KV heads
+x sum of ceil((capacity - 1) / T)), fit the 3072 wavefronts the matrix-core
+split kernel keeps resident; failing that, the smallest T whose items fit
+one round, or 8192 when none does. Layouts only (all pages in HBM); no
+kernel runs."""
 import numpy as np
 import pytest
 
@@ -18,6 +20,8 @@ pytestmark = [pytest.mark.gpu,
     (192, 8192, 8192),     # exactly 1536 full items
     (192, 8191, 4096),     # one token short of a full 8192 split: 1536 items of 4096
     (8, 32768, 1024),      # 1024 items at 2048 tokens are too few: 2048 of 1024
+    (138, 12288, 8192),    # 4096 would give 3312 full items, past one round; 8192: 2208 items
+    (192, 24575, 8192),    # 4608 items at 8192 (3 per sequence and KV head): the fewest rounds
 ])
 def test_split_size_rule(monkeypatch, batch, cached, want):
     monkeypatch.delenv("DKV_SPLIT_TOKENS", raising=False)
