@@ -497,6 +497,88 @@ def gemm_experiment(dkv, args):
     return 0
 
 
+PROJ_MFMA_MIN_BATCH = 2              # the library's default: split-k MFMA from batch 2, GEMV below
+PROJ_SHAPES = (("llama3-8b", 4096, 32), ("llama3-70b", 8192, 64))
+PROJ_BATCHES = (1, 2, 3, 4, 8, 16, 32, 64)
+PROJ_COLD_BYTES = 640 << 20          # W copies cycled per step: past the 256 MiB last-level cache
+PROJ_READ_PROBES = [(256, -2), (512, -2), (1024, -2), (1024, -4), (2048, -2), (2048, -4), (4096, -2)]
+
+
+def projection_experiment(dkv, args):
+    """The decode step's QKV projection on its own: for the Llama-3 8B and
+    70B shapes (8 KV heads, head_dim 128) at batches 1-64, the projection
+    kernel's and the fresh-token kernel's times from the layout's HIP events,
+    with W cycled through enough copies that every step reads W from HBM;
+    beside them, the best of several grid-stride streaming reads of the same
+    W bytes, also cycled (the read a kernel of this size can reach, launch
+    and ramp included). KV is 16 tokens per sequence, so the step's
+    attention is negligible. One JSON line per (shape, batch)."""
+    import torch
+    dev = torch.device("cuda", 0)
+    steps = max(args.steps, 8)
+    batches = [int(v) for v in args.proj_batches.split(",")]
+    shapes = args.proj_shapes.split(",")
+    for name, hidden, Hq in PROJ_SHAPES:
+        if name not in shapes:
+            continue
+        shape = dkv.Shape.of(hidden, Hq, 8, 128, 1)
+        n_qkv = (Hq + 16) * 128
+        w_elems = n_qkv * hidden
+        w_bytes = w_elems * 2
+        nW = max(4, -(-PROJ_COLD_BYTES // w_bytes))
+        Wall = torch.empty(nW * w_elems, dtype=torch.bfloat16, device=dev)
+        g = torch.Generator(device=dev).manual_seed(1)
+        for i in range(nW):
+            Wall[i * w_elems:(i + 1) * w_elems] = (torch.randn(w_elems, device=dev, generator=g) * 0.02).to(
+                torch.bfloat16)
+        Ws = [Wall[i * w_elems:(i + 1) * w_elems].view(n_qkv, hidden) for i in range(nW)]
+        torch.cuda.synchronize()
+        reads = {}
+        for grid, unroll in PROJ_READ_PROBES:
+            ms = dkv.probe_stream_read_cycled(Wall.data_ptr(), w_bytes, nW, grid, unroll, reps=2 * nW)
+            reads["%dx%d%s" % (grid, abs(unroll), "nt" if unroll < 0 else "")] = round(ms * 1e3, 2)
+        read_us = min(reads.values())
+        log("projection %s: cold read of W (%d B) %.2f us" % (name, w_bytes, read_us))
+        for B in batches:
+            ctx = np.full(B, 16, np.int32)
+            hbm = dkv.kv_alloc_hbm(shape, B * 2)
+            layout = dkv.kv_layout_create(shape, ctx + 1, np.full(B, 1 << 30, np.int32), None, hbm)
+            x = (torch.randn(B, hidden, device=dev, generator=g)).to(torch.bfloat16)
+            c = torch.from_numpy(ctx).to(dev)
+            out = torch.empty(B, Hq * 128, dtype=torch.bfloat16, device=dev)
+            for i in range(nW):
+                dkv.decode_step(layout, 0, x, Ws[i], c, out)
+            torch.cuda.synchronize()
+            layout.timing_enable(True, steps)
+            for i in range(steps):
+                dkv.decode_step(layout, 0, x, Ws[i % nW], c, out)
+            t = layout.timing_read()
+            layout.timing_enable(False)
+            layout.check_status()
+            layout.free()
+            hbm.free()
+            n = t["steps"]
+            proj_us, fresh_us = t["projection"] / n * 1e3, t["fresh"] / n * 1e3
+            mfma = B >= PROJ_MFMA_MIN_BATCH
+            flop = 2.0 * B * hidden * n_qkv
+            line = {"experiment": "qkv_projection", "shape": name, "hidden": hidden, "n_qkv": n_qkv,
+                    "batch": B, "kernel": "qkv_proj_splitk_kernel" if mfma else "qkv_proj_gemv_kernel",
+                    "W_bytes": w_bytes, "W_copies_cycled": nW, "steps": n,
+                    "projection_us": round(proj_us, 2), "fresh_token_us": round(fresh_us, 2),
+                    "W_TBps": round(w_bytes / (proj_us * 1e-6) / 1e12, 3),
+                    "W_frac_of_8TBps": round(w_bytes / (proj_us * 1e-6) / 8e12, 4),
+                    "cold_read_us": read_us, "cold_read_TBps": round(w_bytes / (read_us * 1e-6) / 1e12, 3),
+                    "projection_vs_cold_read": round(read_us / proj_us, 4),
+                    "TFLOPs": round(flop / (proj_us * 1e-6) / 1e12, 2),
+                    "mfma_utilisation": round(flop / (proj_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)
+                    if mfma else None,
+                    "cold_read_probes_us": reads}
+            print(json.dumps(line), flush=True)
+        del Ws, Wall
+        torch.cuda.empty_cache()
+    return 0
+
+
 SWEEP_HOST_FRACTIONS = (0.0, 0.01, 0.03, 0.1, 0.25, 0.5, 0.75, 1.0)
 SWEEP_CTX_LENGTHS = [1024, 4096, 16384, 32768, 65536, 131072]
 
@@ -539,7 +621,7 @@ def projection_facts(wl, ms):
     """The QKV projection of one step (summed over layers): which kernel, its W
     read rate and its matrix-core use against the dense bf16 peak."""
     B = wl.batch
-    kernel = "qkv_proj_gemv_kernel" if B < 8 else "qkv_proj_splitk_kernel"
+    kernel = "qkv_proj_gemv_kernel" if B < PROJ_MFMA_MIN_BATCH else "qkv_proj_splitk_kernel"
     w_bytes = wl.n_qkv * wl.hidden * 2 * wl.n_layers
     flop = 2.0 * B * wl.hidden * wl.n_qkv * wl.n_layers
     return {"kernel": kernel, "ms": round(ms, 4), "W_bytes": w_bytes,
@@ -844,6 +926,14 @@ def main(argv=None):
                     help="with --gemm: run each zero-copy order once and exit (for rocprofv3)")
     ap.add_argument("--gemm-noncoherent", action="store_true",
                     help="with --gemm: allocate B non-coherent (cacheable in the GPU's L2)")
+    ap.add_argument("--projection", action="store_true",
+                    help="QKV projection experiment instead of the bench line: the projection and "
+                         "fresh-token kernels at batches 1-64 (8B and 70B shapes), W read cold, beside "
+                         "a cold streaming read of the same bytes")
+    ap.add_argument("--proj-batches", default=",".join(map(str, PROJ_BATCHES)),
+                    help="with --projection: comma-separated batch sizes")
+    ap.add_argument("--proj-shapes", default=",".join(n for n, _, _ in PROJ_SHAPES),
+                    help="with --projection: comma-separated shapes (llama3-8b, llama3-70b)")
     ap.add_argument("--no-comparators", action="store_true",
                     help="skip the naive zero-copy and staging comparator legs")
     ap.add_argument("--profile-run", action="store_true",
@@ -880,6 +970,8 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.gemm:
         return gemm_experiment(dkv, args)
+    if args.projection:
+        return projection_experiment(dkv, args)
     wl = configs.BY_NAME[args.workload]
     if args.sweep_ctx:
         return sweep_ctx(dkv, wl, args)

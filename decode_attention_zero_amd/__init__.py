@@ -19,7 +19,7 @@ from ._build import LIBRARY, build_library
 __all__ = [
     "DkvError", "Shape", "Pool", "Layout", "build", "lib", "kv_page_bytes", "kv_page_offset",
     "kv_placement", "kv_alloc_host", "kv_alloc_hbm", "kv_layout_create", "kv_append", "kv_read",
-    "decode_step", "decode_step_f32", "probe_stream_read", "PAGE_TOKENS",
+    "decode_step", "decode_step_f32", "probe_stream_read", "probe_stream_read_cycled", "PAGE_TOKENS",
 ]
 
 PAGE_TOKENS = 16
@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
             "decode_step_noalloc": ([P, I32, P, P, P, P, P], I32),
             "decode_step_noalloc_scratch_bytes": ([], ctypes.c_size_t),
             "dkv_probe_stream_read": ([P, ctypes.c_uint64, I32, I32, I32, P], I32),
+            "dkv_probe_stream_read_cycled": ([P, ctypes.c_uint64, I32, I32, I32, I32, P], I32),
             "kv_pool_copy": ([P, P, I64, P], I32),
             "dkv_host_buffer_alloc": ([ctypes.c_uint64, U32, P, P], I32),
             "dkv_host_buffer_free": ([P], I32),
@@ -117,7 +118,7 @@ EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement",
             "kv_alloc_hbm", "kv_pool_free_pages", "kv_pool_info", "kv_pool_free",
             "kv_layout_create", "kv_layout_create_windowed", "kv_advance", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
             "kv_layout_split_kernel", "kv_layout_set_split_kernel", "kv_layout_split_waves", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
-            "decode_step_noalloc", "decode_step_noalloc_scratch_bytes", "dkv_probe_stream_read", "kv_pool_copy", "dkv_host_buffer_alloc", "dkv_host_buffer_free",
+            "decode_step_noalloc", "decode_step_noalloc_scratch_bytes", "dkv_probe_stream_read", "dkv_probe_stream_read_cycled", "kv_pool_copy", "dkv_host_buffer_alloc", "dkv_host_buffer_free",
             "dkv_copy", "dkv_gemm_bf16_nt", "dkv_gemm_bf16_nt_bstationary", "dkv_gemm_bstationary_workspace_bytes",
             "kv_layout_timing_enable", "kv_layout_timing_read",
             "dkv_cpu_attention", "dkv_cpu_stream_read", "dkv_cpu_attention_pages"]
@@ -399,6 +400,16 @@ def probe_stream_read(device_ptr: int, nbytes: int, grid: int = 256, unroll: int
     """Median milliseconds of a kernel streaming-read of nbytes at device_ptr."""
     ms = ctypes.c_float()
     _check(lib().dkv_probe_stream_read(device_ptr, nbytes, grid, unroll, reps, ctypes.byref(ms)))
+    return ms.value
+
+
+def probe_stream_read_cycled(device_ptr: int, nbytes: int, n_regions: int, grid: int = 256,
+                             unroll: int = 2, reps: int = 3) -> float:
+    """Median milliseconds of a cold streaming-read of nbytes: timed run r
+    reads the r mod n_regions-th of n_regions consecutive regions."""
+    ms = ctypes.c_float()
+    _check(lib().dkv_probe_stream_read_cycled(device_ptr, nbytes, n_regions, grid, unroll, reps,
+                                              ctypes.byref(ms)))
     return ms.value
 
 

@@ -328,13 +328,15 @@ int32_t choose_split_waves(int64_t host_pages, int64_t hbm_pages) {
     return t_looping < t_per_item ? kHostSplitWaves : 0;
 }
 
-// Batch size from which the QKV projection runs on the matrix cores; smaller
-// batches take the VALU GEMV. Measured on MI355X (W read once per step, x
-// from L2; hidden 4096 / 8192): batch 1, 12.5 / 28.8 us on VALU vs 14.8 /
-// 34.1 us on MFMA; batch 4, 14.4 vs 16.3 us; batch 8, 21.2 / 53.1 vs 17.5 /
-// 40.1 us; batch 16, 31.8 / 124 vs 20.1 / 48.6 us; batch 32 at 4096, 57 vs
-// 29 us; batch 64, 109 vs 46 us. DKV_PROJ_MFMA_MIN_BATCH=<n> overrides it.
-constexpr int32_t kProjMfmaMinBatch = 8;
+// Batch size from which the QKV projection runs on the matrix cores (the
+// split-k kernel); batch 1 takes the VALU GEMV. Measured on MI355X (W cycled
+// through copies so that every step reads it from HBM, decode-step HIP
+// events, hidden 4096 / 8192, GEMV vs split-k MFMA): batch 1, 13.33 / 33.5
+// vs 13.31 / 35.3 us; batch 2, 14.07 / 35.5 vs 13.48 / 35.6; batch 3, 14.85
+// / 37.0 vs 13.54 / 35.2; batch 4, 15.5 / 38.6 vs 13.38 / 35.6; the GEMV
+// falls further behind from there (batch 8 at hidden 4096: 21.2 vs 13.6
+// us). DKV_PROJ_MFMA_MIN_BATCH=<n> overrides it.
+constexpr int32_t kProjMfmaMinBatch = 2;
 
 // The split-k projection's batch threshold and range count; the defaults
 // are measured choices (proj.hip), the environment variables
@@ -1420,14 +1422,15 @@ dkv_status dkv_gemm_bf16_nt_bstationary(const uint16_t *A, const uint16_t *B, fl
     return DKV_OK;
 }
 
-static dkv_status dkv_probe_stream_read_body(const void *ptr, uint64_t bytes, int32_t grid, int32_t unroll,
-                                             int32_t reps, float *ms_median) {
+static dkv_status dkv_probe_stream_read_body(const void *ptr, uint64_t bytes, int32_t n_regions, int32_t grid,
+                                             int32_t unroll, int32_t reps, float *ms_median) {
     // unroll < 0 selects nontemporal loads with |unroll| in flight
     const bool nt = unroll < 0;
     if (nt) unroll = -unroll;
     if (!ptr || !ms_median || bytes == 0 || bytes % 16 || ((uintptr_t)ptr & 15u) || grid <= 0 || reps <= 0 ||
-        !(unroll == 1 || unroll == 2 || unroll == 4 || unroll == 8))
+        n_regions <= 0 || !(unroll == 1 || unroll == 2 || unroll == 4 || unroll == 8))
         return fail(DKV_E_INVALID_ARG, "dkv_probe_stream_read: bad argument");
+    auto region = [&](int r) { return static_cast<const char *>(ptr) + (size_t)(r % n_regions) * bytes; };
     hipStream_t st;
     HIP_TRY(hipStreamCreate(&st));
     uint32_t *sink = nullptr;
@@ -1436,11 +1439,11 @@ static dkv_status dkv_probe_stream_read_body(const void *ptr, uint64_t bytes, in
     hipError_t e = hipMalloc(&sink, 64);
     if (e == hipSuccess) e = hipEventCreate(&e0);
     if (e == hipSuccess) e = hipEventCreate(&e1);
-    if (e == hipSuccess) e = dkv::launch_stream_read(ptr, bytes, grid, unroll, nt, sink, st);
+    if (e == hipSuccess) e = dkv::launch_stream_read(region(n_regions - 1), bytes, grid, unroll, nt, sink, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     for (int r = 0; r < reps && e == hipSuccess; ++r) {
         e = hipEventRecord(e0, st);
-        if (e == hipSuccess) e = dkv::launch_stream_read(ptr, bytes, grid, unroll, nt, sink, st);
+        if (e == hipSuccess) e = dkv::launch_stream_read(region(r), bytes, grid, unroll, nt, sink, st);
         if (e == hipSuccess) e = hipEventRecord(e1, st);
         if (e == hipSuccess) e = hipEventSynchronize(e1);
         float ms = 0.0f;
@@ -1460,7 +1463,14 @@ static dkv_status dkv_probe_stream_read_body(const void *ptr, uint64_t bytes, in
 dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid, int32_t unroll, int32_t reps,
                                  float *ms_median) {
     return guarded("dkv_probe_stream_read",
-                   [&] { return dkv_probe_stream_read_body(ptr, bytes, grid, unroll, reps, ms_median); });
+                   [&] { return dkv_probe_stream_read_body(ptr, bytes, 1, grid, unroll, reps, ms_median); });
+}
+
+dkv_status dkv_probe_stream_read_cycled(const void *ptr, uint64_t bytes, int32_t n_regions, int32_t grid,
+                                        int32_t unroll, int32_t reps, float *ms_median) {
+    return guarded("dkv_probe_stream_read_cycled", [&] {
+        return dkv_probe_stream_read_body(ptr, bytes, n_regions, grid, unroll, reps, ms_median);
+    });
 }
 
 }  // extern "C"

@@ -35,6 +35,16 @@ dkv_status kv_pool_info(const dkv_pool *pool, void **device_base, int64_t *bytes
 dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid,
                                  int32_t unroll, int32_t reps, float *ms_median);
 
+/* The same read of `bytes` bytes, cold: timed run r reads region
+ * r mod n_regions of n_regions consecutive regions at `ptr` (n_regions x
+ * bytes in all), so that with n_regions x bytes beyond the GPU's caches
+ * (256 MiB of last-level cache on MI355X) every timed run fetches its bytes
+ * from memory, as a kernel that reads a fresh operand once per step does.
+ * The warm-up run reads the last region. Same arguments and errors
+ * otherwise; n_regions >= 1. */
+dkv_status dkv_probe_stream_read_cycled(const void *ptr, uint64_t bytes, int32_t n_regions,
+                                        int32_t grid, int32_t unroll, int32_t reps, float *ms_median);
+
 /* Comparator for measurement: the staging design the pages set against
  * zero-copy (KV Offload wiki, Offload 的基本机制: swap-in copies KV into a GPU
  * buffer before attention runs; KV-hierarchy overview, 2.1: staging costs a

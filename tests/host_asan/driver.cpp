@@ -116,6 +116,9 @@ int main() {
     uint64_t sum = 0;
     EXPECT(dkv_cpu_stream_read(words.data(), words.size() * 8, 3, &sum) == DKV_OK && sum == want);
     EXPECT(dkv_cpu_stream_read(words.data(), 100, 3, &sum) == DKV_E_INVALID_ARG);
+    // The cold-read probe refuses a region count below 1 before touching the device.
+    float ms = -1.0f;
+    EXPECT(dkv_probe_stream_read_cycled(words.data(), 64, 0, 1, 1, 1, &ms) == DKV_E_INVALID_ARG && ms == -1.0f);
     std::printf(failures ? "FAILED %d\n" : "OK\n", failures);
     return failures ? 1 : 0;
 }
