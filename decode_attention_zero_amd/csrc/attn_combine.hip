@@ -18,6 +18,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kChunk = 64 * kWaves;   // slots weighed per pass
+constexpr int kPrefetch = 8;          // slots per wave held in registers on the short path
 
 template <int D>
 __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(StepArgs a) {
@@ -47,44 +48,86 @@ __global__ __launch_bounds__(64 * kWaves) void attn_combine_kernel(StepArgs a) {
         const float2 *ml = a.part_ml + slot0;
         const float *po = a.part_o + slot0 * D + (size_t)lane * DPL;
 
-        // Pass 1: the common max.
-        float mx = kNegInf;
-        for (int s = tid; s < S; s += kChunk) mx = fmaxf(mx, ml[s].x);
-        mx = wave_max(mx);
-        if (lane == 0) s_red[wave] = mx;
-        __syncthreads();
-        float M = s_red[0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_red[w]);
-
-        // Pass 2: weights of a chunk of slots into LDS, then each wave adds
-        // the weighted outputs of the chunk's slots w, w + 4, ...
         float den = 0.0f;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
-        for (int c0 = 0; c0 < S; c0 += kChunk) {
-            const int s = c0 + tid;
+        if (S <= kWaves * kPrefetch) {
+            // Short path (every split count up to 31): each thread's state and
+            // each wave's output vectors are loaded at once, so the merge waits
+            // for memory once. Same sums, in the same order, as the loop below.
+            const float2 st = tid < S ? ml[tid] : make_float2(kNegInf, 0.0f);
+            float ov[kPrefetch][DPL];
+#pragma unroll
+            for (int i = 0; i < kPrefetch; ++i) {
+                const int j = wave + kWaves * i;
+                if constexpr (DPL == 2) {
+                    const float2 v = j < S ? *reinterpret_cast<const float2 *>(po + (size_t)j * D)
+                                           : make_float2(0.0f, 0.0f);
+                    ov[i][0] = v.x;
+                    ov[i][1] = v.y;
+                } else {
+                    for (int e = 0; e < DPL; ++e) ov[i][e] = j < S ? po[(size_t)j * D + e] : 0.0f;
+                }
+            }
+            float mx = wave_max(st.x);
+            if (lane == 0) s_red[wave] = mx;
+            __syncthreads();
+            float M = s_red[0];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_red[w]);
             float c = 0.0f;
-            if (s < S) {
-                const float2 st = ml[s];
+            if (tid < S) {
                 c = fast_exp2(st.x - M);
                 den = fmaf(c, st.y, den);
             }
-            __syncthreads();                  // the previous chunk's weights are consumed
             s_c[tid] = c;
             __syncthreads();
-            const int n = min(kChunk, S - c0);
-#pragma unroll 4
-            for (int j = wave; j < n; j += kWaves) {
-                const float cj = s_c[j];
-                const float *p = po + (size_t)(c0 + j) * D;
-                if constexpr (DPL == 2) {
-                    const float2 v = *reinterpret_cast<const float2 *>(p);
-                    o[0] = fmaf(cj, v.x, o[0]);
-                    o[1] = fmaf(cj, v.y, o[1]);
-                } else {
 #pragma unroll
-                    for (int e = 0; e < DPL; ++e) o[e] = fmaf(cj, p[e], o[e]);
+            for (int i = 0; i < kPrefetch; ++i) {
+                const int j = wave + kWaves * i;
+                if (j < S) {
+                    const float cj = s_c[j];
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) o[e] = fmaf(cj, ov[i][e], o[e]);
+                }
+            }
+        } else {
+            // Pass 1: the common max.
+            float mx = kNegInf;
+            for (int s = tid; s < S; s += kChunk) mx = fmaxf(mx, ml[s].x);
+            mx = wave_max(mx);
+            if (lane == 0) s_red[wave] = mx;
+            __syncthreads();
+            float M = s_red[0];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_red[w]);
+
+            // Pass 2: weights of a chunk of slots into LDS, then each wave adds
+            // the weighted outputs of the chunk's slots w, w + 4, ...
+            for (int c0 = 0; c0 < S; c0 += kChunk) {
+                const int s = c0 + tid;
+                float c = 0.0f;
+                if (s < S) {
+                    const float2 st = ml[s];
+                    c = fast_exp2(st.x - M);
+                    den = fmaf(c, st.y, den);
+                }
+                __syncthreads();                  // the previous chunk's weights are consumed
+                s_c[tid] = c;
+                __syncthreads();
+                const int n = min(kChunk, S - c0);
+#pragma unroll 4
+                for (int j = wave; j < n; j += kWaves) {
+                    const float cj = s_c[j];
+                    const float *p = po + (size_t)(c0 + j) * D;
+                    if constexpr (DPL == 2) {
+                        const float2 v = *reinterpret_cast<const float2 *>(p);
+                        o[0] = fmaf(cj, v.x, o[0]);
+                        o[1] = fmaf(cj, v.y, o[1]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < DPL; ++e) o[e] = fmaf(cj, p[e], o[e]);
+                    }
                 }
             }
         }

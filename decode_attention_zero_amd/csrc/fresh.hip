@@ -54,6 +54,11 @@ __global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a) 
     __shared__ int s_before[kFreshWaves];
 
     reset_items(a);
+    // Splits of the sequences before b, for the item list (workgroup g = 0
+    // only); loaded first, so that their latency overlaps the slabs'.
+    int n_before = 0;
+    if (g == 0)
+        for (int i = tid; i < b; i += kFreshThreads) n_before += splits_of(a, i);
     const int L = a.ctx_lens[b];
     const bool in_range = L >= 0 && L < a.capacity[b];
     if (g == 0 && tid == 0) check_context_range(a, b);
@@ -96,9 +101,7 @@ __global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a) 
     // Sequence b's entries of the step's item list, after those of sequences
     // 0 .. b - 1 (workgroup g = 0 of each sequence; the last one writes the count).
     if (g == 0) {
-        int n = 0;
-        for (int i = tid; i < b; i += kFreshThreads) n += splits_of(a, i);
-        n = wave_sum_int(n);
+        const int n = wave_sum_int(n_before);
         if (lane == 0) s_before[wave] = n;
         __syncthreads();
         int before = 0;
