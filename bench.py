@@ -659,8 +659,17 @@ def window_only_leg(dkv, wl, ctx, tail, kv_source, args):
 
 
 def split_kernel_label(layout) -> str:
-    """Name of the split-attention kernel a layout launches, and its wavefronts."""
-    mfma = layout.split_kernel == "mfma"
+    """Name of the split-attention kernel a layout launches, and its wavefronts
+    (the looping count applies to the register kernels only; the LDS-ring
+    kernels and the naive comparator always run one workgroup per item)."""
+    kind = layout.split_kernel
+    if kind == "lds":
+        return "attn_split_lds_kernel (one workgroup per item)"
+    if kind == "ldsmfma":
+        return "attn_split_lds_mfma_kernel (one workgroup per item)"
+    if kind == "naive":
+        return "per-query-head split kernel (one wavefront per query head and split)"
+    mfma = kind == "mfma"
     if layout.split_waves > 0:
         return "%s (%d wavefronts)" % ("attn_split_mfma_persistent_kernel" if mfma
                                        else "attn_split_persistent_kernel", layout.split_waves)

@@ -216,8 +216,10 @@ class Layout:
 
     @property
     def split_kernel(self) -> str:
-        """'regs' (register double buffer), 'lds' (producer/consumer LDS ring) or
-        'naive' (comparator: one work item per query head)."""
+        """'regs' (register double buffer, VALU), 'lds' (producer/consumer LDS
+        ring, VALU), 'mfma' (register double buffer, matrix cores), 'ldsmfma'
+        (LDS ring, matrix-core consumer) or 'naive' (comparator: one work item
+        per query head)."""
         return {0: "regs", 1: "lds", 2: "naive", 3: "mfma", 4: "ldsmfma"}[lib().kv_layout_split_kernel(self.handle)]
 
     @property
