@@ -84,7 +84,7 @@ __device__ __forceinline__ float rescale(float x, float M) {
 
 // Work queue of the looping split kernels: the workgroup takes the next item
 // index (one atomic per item); every workgroup ends on an index past the last
-// item. The step's projection kernel zeroes the counter first (reset_items),
+// item. The step's fresh-token kernel zeroes the counter first (reset_items),
 // so the queue needs no memset and a captured step replays as it ran. Both
 // use system scope, which makes them go through to memory, so the workgroups
 // on all eight XCDs (each with its own L2) share one counter.
