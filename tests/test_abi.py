@@ -68,20 +68,30 @@ def test_page_layout_is_head_major_and_aligned():
     assert dkv.kv_page_offset(t, 3, 2, 1, 5) == ((2 * 2 + 1) * 16 + 3) * 128 + 10
 
 
+def contiguous_runs(offsets, elem=2):
+    """Number of maximal runs of consecutive elements among byte offsets."""
+    offs = sorted(offsets)
+    return 1 + sum(1 for a, b in zip(offs, offs[1:]) if b != a + elem)
+
+
 def test_fragments_per_head_against_token_major(golden):
     """Beluga's count on the KV Offload wiki: a 16-token GQA block with 8 KV
-    heads is 128 separate fragments when stored token-major; head-major pages
-    make it one contiguous run per (page, head)."""
+    heads is 128 separate fragments when stored token-major. Gathering each
+    head's K rows of one block from a token-major array [t][g][d] yields that
+    count; the library's head-major page yields one contiguous run per
+    (page, head)."""
     fact = golden["fragments_16_token_gqa_block"]
-    s = dkv.Shape.of(5120, 40, fact["kv_heads"], 128)
-    token_major_runs = fact["tokens"] * fact["kv_heads"]
-    assert token_major_runs == fact["fragments"]
-    runs = 0
-    for g in range(fact["kv_heads"]):
-        offs = sorted(dkv.kv_page_offset(s, t, g, 0, i) for t in range(16) for i in range(128))
-        assert offs[-1] - offs[0] == 16 * 128 * 2 - 2       # contiguous
-        runs += 1
-    assert runs == fact["kv_heads"]
+    T, Hkv, d = fact["tokens"], fact["kv_heads"], 128
+    token_major = sum(contiguous_runs([((t * Hkv + g) * d + i) * 2 for t in range(T) for i in range(d)])
+                      for g in range(Hkv))
+    assert token_major == fact["fragments"]
+    s = dkv.Shape.of(5120, 40, Hkv, d)
+    head_major = sum(contiguous_runs([dkv.kv_page_offset(s, t, g, 0, i) for t in range(T) for i in range(d)])
+                     for g in range(Hkv))
+    assert head_major == Hkv
+    # K then V of one head: still one run (8 KiB at d = 128)
+    both = [dkv.kv_page_offset(s, t, 3, c, i) for c in range(2) for t in range(T) for i in range(d)]
+    assert contiguous_runs(both) == 1 and max(both) - min(both) == 2 * T * d * 2 - 2
 
 
 def test_placement_policy():
