@@ -55,9 +55,9 @@ __global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a) 
 
     reset_items(a);
     // Splits of the sequences before b, for the item list (workgroup g = 0
-    // only; b / 256 entries per thread, so the batch's sequences read
-    // B^2 / 2 entries in all, a few microseconds at batches in the
-    // thousands); loaded first, so that their latency overlaps the slabs'.
+    // only: b entries, so the batch reads B^2 / 2 in all, which grows with
+    // the batch squared); loaded first, so that their latency overlaps the
+    // slabs'.
     int n_before = 0;
     if (g == 0)
         for (int i = tid; i < b; i += kFreshThreads) n_before += splits_of(a, i);
