@@ -210,6 +210,33 @@ def probe_region(dkv, base, nbytes, configs_):
     return best, rows, nbytes
 
 
+def probe_page_runs(dkv, pool, wl, max_bytes=8 << 30):
+    """The HBM read ceiling in the split kernel's own access pattern, with no
+    arithmetic: each wavefront streams one KV head's run (K then V rows) of
+    every page of an item of consecutive pages, as the one-wavefront-per-item
+    split kernel does; 2048 and 3072 wavefronts, items starting in step or
+    staggered. Returns (best GB/s, rows)."""
+    base, nbytes, _ = pool.info()
+    shape = dkv.Shape.of(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, 1)
+    page = dkv.kv_page_bytes(shape)
+    runs = wl.n_kv_heads
+    best, rows = 0.0, []
+    for waves in PAGE_PROBE_WAVES:
+        items = waves // runs
+        pages = min(nbytes, max_bytes) // page
+        pages -= pages % items
+        if pages == 0:
+            continue
+        for skew in (False, True):
+            ms = dkv.probe_page_read(base, pages * page, page, runs, waves, skew, reps=3)
+            gbps = pages * page / ms / 1e6
+            rows.append({"waves": waves, "pages_per_item": pages // items, "staggered": skew,
+                         "bytes": pages * page, "GBps": round(gbps, 1)})
+            best = max(best, gbps)
+    return best, rows
+
+
+PAGE_PROBE_WAVES = (2048, 3072)
 HOST_PROBES = [(64, 1), (256, 1), (512, 1), (1024, 2), (256, -1), (1024, -2)]
 HBM_PROBES = [(1024, -2), (2048, -2), (4096, -4), (8192, -8), (2048, 4)]
 
@@ -1135,6 +1162,7 @@ def main(argv=None):
         kt_h = rh.kernel_times(n_hbm_steps)
         ms_h_graph = rh.graph_timed(n_hbm_steps)
         hbm_ceiling, hbm_rows, _ = probe_ceiling(dkv, rh.hbm_pool, HBM_PROBES)
+        page_ceiling, page_rows = probe_page_runs(dkv, rh.hbm_pool, wl)
         out_hbm = rh.out_bits(0)
         hbm_split_gbps = kv_bytes / (kt_h["split"] * 1e-3) / 1e9
         hbm = {
@@ -1154,6 +1182,9 @@ def main(argv=None):
             "projection": projection_facts(wl, kt_h["projection"]),
             "measured_hbm_read_GBps": round(hbm_ceiling, 1),
             "hbm_probe": hbm_rows,
+            "page_run_read_GBps": round(page_ceiling, 1) if page_rows else None,
+            "split_kernel_vs_page_run_read": (round(hbm_split_gbps / page_ceiling, 4) if page_rows else None),
+            "page_run_probe": page_rows,
             "bit_identical_to_own_placement": bool(np.array_equal(out_own, out_hbm)),
         }
         log("HBM leg: %.4f ms/step, split kernel %.1f GB/s" % (ms_h, hbm["split_kernel_GBps"]))

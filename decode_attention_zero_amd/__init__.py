@@ -19,7 +19,8 @@ from ._build import LIBRARY, build_library
 __all__ = [
     "DkvError", "Shape", "Pool", "Layout", "build", "lib", "kv_page_bytes", "kv_page_offset",
     "kv_placement", "kv_alloc_host", "kv_alloc_hbm", "kv_layout_create", "kv_append", "kv_read",
-    "decode_step", "decode_step_f32", "probe_stream_read", "probe_stream_read_cycled", "PAGE_TOKENS",
+    "decode_step", "decode_step_f32", "probe_stream_read", "probe_stream_read_cycled", "probe_page_read",
+    "PAGE_TOKENS",
 ]
 
 PAGE_TOKENS = 16
@@ -93,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "decode_step_noalloc_scratch_bytes": ([], ctypes.c_size_t),
             "dkv_probe_stream_read": ([P, ctypes.c_uint64, I32, I32, I32, P], I32),
             "dkv_probe_stream_read_cycled": ([P, ctypes.c_uint64, I32, I32, I32, I32, P], I32),
+            "dkv_probe_page_read": ([P, ctypes.c_uint64, I32, I32, I32, I32, I32, P], I32),
             "kv_pool_copy": ([P, P, I64, P], I32),
             "dkv_host_buffer_alloc": ([ctypes.c_uint64, U32, P, P], I32),
             "dkv_host_buffer_free": ([P], I32),
@@ -118,7 +120,7 @@ EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement",
             "kv_alloc_hbm", "kv_pool_free_pages", "kv_pool_info", "kv_pool_free",
             "kv_layout_create", "kv_layout_create_windowed", "kv_advance", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
             "kv_layout_split_kernel", "kv_layout_set_split_kernel", "kv_layout_split_waves", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
-            "decode_step_noalloc", "decode_step_noalloc_scratch_bytes", "dkv_probe_stream_read", "dkv_probe_stream_read_cycled", "kv_pool_copy", "dkv_host_buffer_alloc", "dkv_host_buffer_free",
+            "decode_step_noalloc", "decode_step_noalloc_scratch_bytes", "dkv_probe_stream_read", "dkv_probe_stream_read_cycled", "dkv_probe_page_read", "kv_pool_copy", "dkv_host_buffer_alloc", "dkv_host_buffer_free",
             "dkv_copy", "dkv_gemm_bf16_nt", "dkv_gemm_bf16_nt_bstationary", "dkv_gemm_bstationary_workspace_bytes",
             "kv_layout_timing_enable", "kv_layout_timing_read",
             "dkv_cpu_attention", "dkv_cpu_stream_read", "dkv_cpu_attention_pages"]
@@ -412,6 +414,17 @@ def probe_stream_read_cycled(device_ptr: int, nbytes: int, n_regions: int, grid:
     ms = ctypes.c_float()
     _check(lib().dkv_probe_stream_read_cycled(device_ptr, nbytes, n_regions, grid, unroll, reps,
                                               ctypes.byref(ms)))
+    return ms.value
+
+
+def probe_page_read(device_ptr: int, nbytes: int, page_bytes: int, runs: int, waves: int,
+                    skew: bool = False, reps: int = 3) -> float:
+    """Median milliseconds of a read of nbytes in the split kernel's access
+    pattern (waves wavefronts, each streaming one run of every page of its
+    item), with no arithmetic."""
+    ms = ctypes.c_float()
+    _check(lib().dkv_probe_page_read(device_ptr, nbytes, page_bytes, runs, waves, int(skew), reps,
+                                     ctypes.byref(ms)))
     return ms.value
 
 

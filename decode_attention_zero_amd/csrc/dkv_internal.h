@@ -166,5 +166,9 @@ hipError_t launch_gemm_nt(const uint16_t *A, const uint16_t *B, float *C, int M,
 // nontemporal).
 hipError_t launch_stream_read(const void *ptr, uint64_t bytes, int grid, int unroll,
                               bool nontemporal, uint32_t *sink, hipStream_t stream);
+// Page-run read probe: `waves` wavefronts, wave w reading run w mod runs of
+// pages_per_item consecutive pages of page_bytes each (item w / runs).
+hipError_t launch_page_read(const void *ptr, int pages_per_item, int page_bytes, int runs, int waves, int skew,
+                            uint32_t *sink, hipStream_t stream);
 
 }  // namespace dkv

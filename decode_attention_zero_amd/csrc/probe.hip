@@ -37,7 +37,43 @@ hipError_t launch(const uint4 *p, uint64_t nvec, int grid, int unroll, uint32_t 
     return hipGetLastError();
 }
 
+// Page-run read: wave w streams run (w mod runs) of the pages of item
+// w / runs, RUN16 16-byte loads per lane per run (one run in flight).
+template <int RUN16>
+__global__ __launch_bounds__(64) void page_read_kernel(const char *__restrict__ base, int pages_per_item,
+                                                       int page_bytes, int runs, int skew, uint32_t *sink) {
+    const int w = blockIdx.x;
+    const int item = w / runs;
+    const int run = w - item * runs;
+    const int lane = threadIdx.x;
+    const char *p0 = base + (size_t)item * pages_per_item * page_bytes + (size_t)run * RUN16 * 1024 + lane * 16;
+    const int r = skew ? (int)(((int64_t)item * 13) % pages_per_item) : 0;
+    uint32_t x = 0;
+    for (int k = 0; k < pages_per_item; ++k) {
+        int p = k + r;
+        if (p >= pages_per_item) p -= pages_per_item;
+        const char *q = p0 + (size_t)p * page_bytes;
+        uint4 v[RUN16];
+#pragma unroll
+        for (int j = 0; j < RUN16; ++j) v[j] = load_stream(q + j * 1024);
+#pragma unroll
+        for (int j = 0; j < RUN16; ++j) x ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+    if (x == 0x9E3779B9u) sink[0] = x;
+}
+
 }  // namespace
+
+hipError_t launch_page_read(const void *ptr, int pages_per_item, int page_bytes, int runs, int waves, int skew,
+                            uint32_t *sink, hipStream_t st) {
+    const char *p = reinterpret_cast<const char *>(ptr);
+    switch (page_bytes / runs / 1024) {
+        case 4: page_read_kernel<4><<<waves, 64, 0, st>>>(p, pages_per_item, page_bytes, runs, skew, sink); break;
+        case 8: page_read_kernel<8><<<waves, 64, 0, st>>>(p, pages_per_item, page_bytes, runs, skew, sink); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void *ptr, uint64_t bytes, int grid, int unroll, bool nontemporal,
                               uint32_t *sink, hipStream_t st) {

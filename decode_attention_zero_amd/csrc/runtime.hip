@@ -1466,6 +1466,53 @@ dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid, 
                    [&] { return dkv_probe_stream_read_body(ptr, bytes, 1, grid, unroll, reps, ms_median); });
 }
 
+static dkv_status dkv_probe_page_read_body(const void *ptr, uint64_t bytes, int32_t page_bytes, int32_t runs,
+                                          int32_t waves, int32_t skew, int32_t reps, float *ms_median) {
+    if (!ptr || !ms_median || ((uintptr_t)ptr & 15u) || page_bytes <= 0 || runs <= 0 || waves <= 0 ||
+        reps <= 0 || waves % runs || page_bytes % (runs * 1024) || bytes % (uint64_t)page_bytes)
+        return fail(DKV_E_INVALID_ARG, "dkv_probe_page_read: bad argument");
+    const int run16 = page_bytes / runs / 1024;
+    const uint64_t pages = bytes / (uint64_t)page_bytes;
+    const int items = waves / runs;
+    if ((run16 != 4 && run16 != 8) || pages % (uint64_t)items || pages / (uint64_t)items > (uint64_t)INT32_MAX)
+        return fail(DKV_E_INVALID_ARG, "dkv_probe_page_read: runs must be 4 or 8 KiB and the pages divide evenly");
+    const int ppi = (int)(pages / (uint64_t)items);
+    hipStream_t st;
+    HIP_TRY(hipStreamCreate(&st));
+    uint32_t *sink = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    std::vector<float> ts;
+    hipError_t e = hipMalloc(&sink, 64);
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    if (e == hipSuccess) e = dkv::launch_page_read(ptr, ppi, page_bytes, runs, waves, skew, sink, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    for (int r = 0; r < reps && e == hipSuccess; ++r) {
+        e = hipEventRecord(e0, st);
+        if (e == hipSuccess) e = dkv::launch_page_read(ptr, ppi, page_bytes, runs, waves, skew, sink, st);
+        if (e == hipSuccess) e = hipEventRecord(e1, st);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+        ts.push_back(ms);
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipFree(sink);
+    (void)hipStreamDestroy(st);
+    if (e != hipSuccess) return hip_fail(e, "dkv_probe_page_read");
+    std::sort(ts.begin(), ts.end());
+    *ms_median = ts[ts.size() / 2];
+    return DKV_OK;
+}
+
+dkv_status dkv_probe_page_read(const void *ptr, uint64_t bytes, int32_t page_bytes, int32_t runs, int32_t waves,
+                               int32_t skew, int32_t reps, float *ms_median) {
+    return guarded("dkv_probe_page_read", [&] {
+        return dkv_probe_page_read_body(ptr, bytes, page_bytes, runs, waves, skew, reps, ms_median);
+    });
+}
+
 dkv_status dkv_probe_stream_read_cycled(const void *ptr, uint64_t bytes, int32_t n_regions, int32_t grid,
                                         int32_t unroll, int32_t reps, float *ms_median) {
     return guarded("dkv_probe_stream_read_cycled", [&] {

@@ -45,6 +45,20 @@ dkv_status dkv_probe_stream_read(const void *ptr, uint64_t bytes, int32_t grid,
 dkv_status dkv_probe_stream_read_cycled(const void *ptr, uint64_t bytes, int32_t n_regions,
                                         int32_t grid, int32_t unroll, int32_t reps, float *ms_median);
 
+/* The read ceiling in the split-attention kernel's own access pattern, with
+ * no arithmetic: `bytes` at `ptr` are `page_bytes` pages of `runs` runs each
+ * (page_bytes / runs bytes per run, a multiple of 1024); `waves` wavefronts
+ * (a multiple of `runs`) each stream one run of every page of their share
+ * (wave w reads run w mod runs of items w / runs, each item an equal stretch
+ * of consecutive pages), with one run's nontemporal 16-byte loads in flight.
+ * With skew != 0 each item starts at page (item x 13) mod its length and
+ * wraps around. One warm-up run, then `reps` timed runs on a private stream;
+ * *ms_median gets the median. DKV_E_INVALID_ARG when the shapes do not
+ * divide (bytes by page_bytes, page_bytes by runs x 1024, the pages by the
+ * items). */
+dkv_status dkv_probe_page_read(const void *ptr, uint64_t bytes, int32_t page_bytes, int32_t runs,
+                               int32_t waves, int32_t skew, int32_t reps, float *ms_median);
+
 /* Comparator for measurement: the staging design the pages set against
  * zero-copy (KV Offload wiki, Offload 的基本机制: swap-in copies KV into a GPU
  * buffer before attention runs; KV-hierarchy overview, 2.1: staging costs a

@@ -119,6 +119,10 @@ int main() {
     // The cold-read probe refuses a region count below 1 before touching the device.
     float ms = -1.0f;
     EXPECT(dkv_probe_stream_read_cycled(words.data(), 64, 0, 1, 1, 1, &ms) == DKV_E_INVALID_ARG && ms == -1.0f);
+    // The page-run probe refuses shapes that do not divide before touching the device.
+    EXPECT(dkv_probe_page_read(words.data(), 65536, 65536, 8, 12, 0, 1, &ms) == DKV_E_INVALID_ARG);   // 12 % 8
+    EXPECT(dkv_probe_page_read(words.data(), 65536, 65536, 4, 8, 0, 1, &ms) == DKV_E_INVALID_ARG);    // 16 KiB runs
+    EXPECT(dkv_probe_page_read(words.data(), 65536, 65536, 8, 16, 0, 1, &ms) == DKV_E_INVALID_ARG && ms == -1.0f);  // 1 page, 2 items
     std::printf(failures ? "FAILED %d\n" : "OK\n", failures);
     return failures ? 1 : 0;
 }
