@@ -620,7 +620,7 @@ static void log_plan(const dkv_layout *L, int64_t n_host, int64_t n_hbm) {
     const dkv_shape *s = &L->shape;
     const int B = L->batch;
     const char *proj = B < L->proj_mfma_min_batch ? "gemv"
-                       : B < L->proj_splitk_min_batch ? "mfma one-tile streamed"
+                       : B < L->proj_splitk_min_batch && B <= 16 ? "mfma one-tile streamed"
                                                       : "mfma split-k (x staged in LDS)";
     fprintf(stderr,
             "[dkv] layout: batch %d, hidden %d, heads %d/%d, head_dim %d, layers %d; pages per layer: "
