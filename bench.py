@@ -524,7 +524,7 @@ def gemm_experiment(dkv, args):
     return 0
 
 
-PROJ_MFMA_MIN_BATCH = 2              # the library's default: split-k MFMA from batch 2, GEMV below
+PROJ_MFMA_MIN_BATCH = 8              # the library's default: split-k MFMA from batch 8, GEMV below
 PROJ_SHAPES = (("llama3-8b", 4096, 32), ("llama3-70b", 8192, 64))
 PROJ_BATCHES = (1, 2, 3, 4, 8, 16, 32, 64)
 PROJ_COLD_BYTES = 640 << 20          # W copies cycled per step: past the 256 MiB last-level cache

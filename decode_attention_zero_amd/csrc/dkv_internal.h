@@ -115,7 +115,7 @@ hipError_t launch_append(const AppendArgs &a, int n_tokens, hipStream_t stream);
 // StepArgs::proj_part; otherwise the projection writes one slab. The
 // fresh-token kernel adds the slabs of its group's rows in range order.
 // Scratch always has room for kProjMaxSplits slabs.
-constexpr int kProjSplitkMinBatch = 2;
+constexpr int kProjSplitkMinBatch = 8;
 constexpr int kProjMaxSplits = 8;
 
 // Scratch bytes of one decode step (each buffer 256-byte aligned in the order

@@ -6,7 +6,7 @@
 // decode step, as in the core-method section of the DirectKV digest
 // ("长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）"); the step is bound by
 // reading W from HBM at every batch size here, so each of the three forms
-// (1a VALU GEMV at batch 1, 1c split-k MFMA from batch 2, and 1b one
+// (1a VALU GEMV below batch 8, 1c split-k MFMA from batch 8, and 1b one
 // 16-sequence MFMA tile, which a layout takes up to batch 15 when
 // DKV_PROJ_SPLITK_MIN_BATCH moves the split-k threshold up) is built to
 // stream W once at full bandwidth.
@@ -50,7 +50,7 @@ __device__ __forceinline__ float reduce_scatter(float (&v)[N], int lane) {
     return r;
 }
 
-// 1a. One sequence (and, with DKV_PROJ_MFMA_MIN_BATCH, small batches): a GEMV on VALU. A workgroup owns 4 W rows and BT
+// 1a. Small batches (below 8 sequences): a GEMV on VALU. A workgroup owns 4 W rows and BT
 // sequences; its KS wavefronts split the hidden dimension into equal ranges,
 // and each lane reads 16-byte (8 x bf16) chunks, so every W row is read as
 // contiguous 1 KiB wave loads, all of a wave's loads issued before its
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void qkv_proj_stream_kernel(StepArgs a
     }
 }
 
-// 1c. From 2 sequences: W crosses HBM once; what limits a plain tiling is
+// 1c. From 8 sequences: W crosses HBM once; what limits a plain tiling is
 // x. Every 16-row W tile needs the whole batch's x slice, so reading x per
 // wavefront from L2 costs B/16 times the W bytes (measured on MI355X at hidden
 // 4096: 19 -> 41 us from batch 16 to 64, linear in that x traffic; W alone is

@@ -329,14 +329,17 @@ int32_t choose_split_waves(int64_t host_pages, int64_t hbm_pages) {
 }
 
 // Batch size from which the QKV projection runs on the matrix cores (the
-// split-k kernel); batch 1 takes the VALU GEMV. Measured on MI355X (W cycled
-// through copies so that every step reads it from HBM, decode-step HIP
-// events, hidden 4096 / 8192, GEMV vs split-k MFMA): batch 1, 13.33 / 33.5
-// vs 13.31 / 35.3 us; batch 2, 14.07 / 35.5 vs 13.48 / 35.6; batch 3, 14.85
-// / 37.0 vs 13.54 / 35.2; batch 4, 15.5 / 38.6 vs 13.38 / 35.6; the GEMV
-// falls further behind from there (batch 8 at hidden 4096: 21.2 vs 13.6
-// us). DKV_PROJ_MFMA_MIN_BATCH=<n> overrides it.
-constexpr int32_t kProjMfmaMinBatch = 2;
+// split-k kernel), below which it takes the VALU GEMV: from 8 sequences,
+// where x fills half of every 16-column MFMA tile or more, the projection is
+// a real dense contraction. Below that the tiles would be mostly padding,
+// although the matrix cores would still save a little time: measured on
+// MI355X (W cycled through copies so that every step reads it from HBM,
+// decode-step HIP events, hidden 4096 / 8192, GEMV vs split-k MFMA), batch
+// 1, 13.33 / 33.5 vs 13.31 / 35.3 us; batch 2, 14.07 / 35.5 vs 13.48 / 35.6;
+// batch 3, 14.85 / 37.0 vs 13.54 / 35.2; batch 4, 15.5 / 38.6 vs 13.38 /
+// 35.6; at batch 8, 21.2 vs 13.6 us at hidden 4096. DKV_PROJ_MFMA_MIN_BATCH=<n>
+// overrides it.
+constexpr int32_t kProjMfmaMinBatch = 8;
 
 // The split-k projection's batch threshold and range count; the defaults
 // are measured choices (proj.hip), the environment variables

@@ -162,10 +162,10 @@ PROJ_KNOBS = ("DKV_PROJ_MFMA_MIN_BATCH", "DKV_PROJ_SPLITK_MIN_BATCH", "DKV_PROJ_
 
 
 @pytest.mark.parametrize("shape_name,batch,knobs", [
-    ("llama8b", 1, {}), ("llama8b", 2, {}), ("llama8b", 3, {}),
-    ("llama8b", 3, {"DKV_PROJ_MFMA_MIN_BATCH": "64"}), ("llama8b", 6, {"DKV_PROJ_MFMA_MIN_BATCH": "64"}),
-    ("llama8b", 12, {"DKV_PROJ_MFMA_MIN_BATCH": "64"}), ("llama70b", 3, {"DKV_PROJ_MFMA_MIN_BATCH": "64"}),
-    ("llama8b", 3, {"DKV_PROJ_SPLITK_MIN_BATCH": "16"}),
+    ("llama8b", 1, {}), ("llama8b", 3, {}), ("llama8b", 6, {}), ("llama70b", 3, {}),
+    ("llama8b", 12, {"DKV_PROJ_MFMA_MIN_BATCH": "64"}),
+    ("llama8b", 3, {"DKV_PROJ_MFMA_MIN_BATCH": "1", "DKV_PROJ_SPLITK_MIN_BATCH": "1"}),
+    ("llama8b", 3, {"DKV_PROJ_MFMA_MIN_BATCH": "1"}),
     ("llama8b", 1, {"DKV_PROJ_MFMA_MIN_BATCH": "1"}), ("llama8b", 8, {}),
     ("llama8b", 8, {"DKV_PROJ_SPLITK_MIN_BATCH": "16"}), ("llama8b", 16, {}),
     ("llama8b", 17, {}), ("llama8b", 32, {}), ("llama8b", 40, {}), ("llama8b", 64, {}),
@@ -175,12 +175,12 @@ PROJ_KNOBS = ("DKV_PROJ_MFMA_MIN_BATCH", "DKV_PROJ_SPLITK_MIN_BATCH", "DKV_PROJ_
 def test_projection_integer_exact(oracle, monkeypatch, shape_name, batch, knobs):
     """Small-integer x and W make every product and fp32 sum exact, so the
     written-back K/V must equal the oracle's fp64 values rounded to bf16, bit
-    for bit; with an empty history attn_out is exactly bf16(v_new). Batch 1
-    takes the VALU projection by default (as do batches up to 16 with
-    DKV_PROJ_MFMA_MIN_BATCH=64: tiles of 4, 8 and 16 sequences), and the
-    streamed one-tile MFMA kernel with DKV_PROJ_MFMA_MIN_BATCH=1 (as do
-    batches 2 to 15 with DKV_PROJ_SPLITK_MIN_BATCH=16); from 2 the split-k
-    MFMA kernel stages x in tiles of 16, 32 or 64 sequences (2, 3, 17, 40: a
+    for bit; with an empty history attn_out is exactly bf16(v_new). Batches
+    below 8 take the VALU projection by default (tiles of 4 and 8 sequences;
+    16 with DKV_PROJ_MFMA_MIN_BATCH=64), and the streamed one-tile MFMA kernel
+    with DKV_PROJ_MFMA_MIN_BATCH=1 (as do batches 8 to 15 with
+    DKV_PROJ_SPLITK_MIN_BATCH=16); from 8 (or, forced, from 1) the split-k
+    MFMA kernel stages x in tiles of 16, 32 or 64 sequences (3, 17, 40: a
     partly filled tile; 70: a second 64-sequence tile) and writes one slab per
     range of the hidden dimension (8 by default; 1, 2 and 4 forced), which
     the fresh-token kernel adds."""
