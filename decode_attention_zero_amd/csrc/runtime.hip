@@ -284,9 +284,12 @@ int32_t choose_split_tokens(int32_t batch, int32_t n_kv_heads, const int32_t *ca
 // 189 us vs 258 us; group 8: 18.8 ms vs 27.6 ms for 64 GiB) and the same on
 // the host link. From groups of 4 the group's products run on the matrix
 // cores (all-HBM, 1 GiB at group 4: 161 us vs 174 us on VALU; 8 GiB layers
-// at group 8: 1.41 ms vs 2.0 ms); smaller groups keep the VALU form.
-// DKV_SPLIT_KERNEL=regs|lds|mfma overrides it; DKV_SPLIT_KERNEL=naive selects
-// the naive zero-copy comparator (one work item per query head).
+// at group 8: 1.41 ms vs 2.0 ms); smaller groups keep the VALU form. The LDS
+// ring with a matrix-core consumer ties with the register kernel at best
+// (all-HBM: 4 GiB at group 4, 0.617 vs 0.619 ms; 1 GiB, 0.168 vs 0.163 ms;
+// 9.1 GB of ragged contexts, 1.62 vs 1.33 ms). DKV_SPLIT_KERNEL=regs|lds|
+// mfma|ldsmfma overrides it; DKV_SPLIT_KERNEL=naive selects the naive
+// zero-copy comparator (one work item per query head).
 bool lds_mfma_supported(int32_t group, int32_t head_dim) {
     return group >= dkv::kMfmaMinGroup && head_dim == 128;
 }
