@@ -50,7 +50,10 @@ __device__ __forceinline__ float reduce_scatter(float (&v)[N], int lane) {
     return r;
 }
 
-// 1a. Small batches (below 8 sequences): a GEMV on VALU. A workgroup owns 4 W rows and BT
+// 1a. Small batches (below 8 sequences): a GEMV on VALU. W is read with
+// nontemporal loads (W read cold, batches 1-4: 1-5 % faster than plain loads;
+// the MFMA kernels below keep plain loads, with which they measured 2-16 %
+// faster). A workgroup owns 4 W rows and BT
 // sequences; its KS wavefronts split the hidden dimension into equal ranges,
 // and each lane reads 16-byte (8 x bf16) chunks, so every W row is read as
 // contiguous 1 KiB wave loads, all of a wave's loads issued before its
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(64 * KS) void qkv_proj_gemv_kernel(StepArgs a) {
     for (int k = kbeg + lane * 8; k < kbeg + krange; k += 512) {
         float wf[4][8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) unpack8(*reinterpret_cast<const uint4 *>(w0 + (size_t)r * a.hidden + k), wf[r]);
+        for (int r = 0; r < 4; ++r) unpack8(load_stream(w0 + (size_t)r * a.hidden + k), wf[r]);
 #pragma unroll
         for (int bb = 0; bb < BT; ++bb) {
             if (bb < nb) {
