@@ -256,9 +256,10 @@ dkv_status kv_read(const dkv_layout *layout, int32_t layer, int32_t seq,
  * ctx_lens[b] < 0 or ctx_lens[b] >= its capacity writes nothing to the
  * cache, gets attn_out rows of NaN, and raises the flag that
  * kv_layout_check_status reports. A layout's steps share its scratch (the
- * projection's output, the split partials and the work queue of the
- * looping split kernel), so steps of one layout must be ordered (one stream,
- * or events between streams); steps of different layouts may overlap. */
+ * projection's output, the split partials, the step's list of work items
+ * and the work queue of the looping split kernel), so steps of one layout
+ * must be ordered (one stream, or events between streams); steps of
+ * different layouts may overlap. */
 dkv_status decode_step(dkv_layout *kv_layout, int32_t layer,
                        const uint16_t *q_in, const uint16_t *W_qkv,
                        const int32_t *ctx_lens, uint16_t *attn_out,
@@ -274,14 +275,16 @@ dkv_status decode_step_f32(dkv_layout *kv_layout, int32_t layer,
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * step as decode_step, with the same arguments, errors and results (identical
- * bits), whose scratch (projection sums, queries, split partials, work-queue
- * counter) is a file-scope device array of decode_step_noalloc_scratch_bytes()
+ * bits), whose scratch (projection sums, queries, split partials, work-item
+ * list, work-queue counter) is a file-scope device array of
+ * decode_step_noalloc_scratch_bytes()
  * bytes (32 MiB) instead of the layout's. The call allocates nothing; its
  * first call on a device looks the array's address up once. A layout whose
  * step needs more scratch than the array holds gets DKV_E_CAPACITY and
  * nothing is enqueued. Every buffer of the array that a step reads is written
- * earlier in the same step (the work-queue counter is zeroed by the step's
- * own kernel), so no clearing is needed between calls. All calls on one GPU
+ * earlier in the same step (the work-item list and the zeroed work-queue
+ * counter by the step's fresh-token kernel), so no clearing is needed
+ * between calls. All calls on one GPU
  * share its one array: calls that overlap on a GPU (different streams without
  * ordering, other threads) race and give undefined results; order them. */
 dkv_status decode_step_noalloc(dkv_layout *kv_layout, int32_t layer,
