@@ -281,7 +281,7 @@ dkv_status decode_step_f32(dkv_layout *kv_layout, int32_t layer,
  * bytes (32 MiB) instead of the layout's. The call allocates nothing; its
  * first call on a device looks the array's address up once. A layout whose
  * step needs more scratch than the array holds gets DKV_E_CAPACITY and
- * nothing is enqueued. Every buffer of the array that a step reads is written
+ * nothing is enqueued. Every value of the array that a step uses is written
  * earlier in the same step (the work-item list and the zeroed work-queue
  * counter by the step's fresh-token kernel), so no clearing is needed
  * between calls. All calls on one GPU
