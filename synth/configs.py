@@ -131,4 +131,17 @@ LLAMA70B_LONG = Workload("llama3-70b-b16-ctx131072-8layers-host", _seed(5), batc
                          ctx=131072, w_sigma=0.015)
 
 ALL = [TINY, LLAMA8B_HOST, LLAMA8B_HYBRID, LLAMA8B_DENSE, LLAMA70B_LONG]
-BY_NAME = {w.name: w for w in ALL}
+
+# One GPU's share of a workload when 8 GPUs split it (each share runs alone
+# on one GPU here). By sequence, a GPU holds B/8 of the sequences; these
+# shares keep their parent's seed, so their inputs are the parent's first
+# sequences, element for element. By KV head, a GPU holds Hkv/8 KV heads
+# with their query heads and the matching W rows (drawn from the same
+# distribution as the parent's W, not sliced from it).
+SHARE_70B_BY_SEQUENCE = LLAMA70B_LONG.replace(name="llama3-70b-b2-ctx131072-8layers-host", batch=2)
+SHARE_70B_BY_KV_HEAD = LLAMA70B_LONG.replace(name="llama3-70b-b16-ctx131072-8layers-host-1kvhead",
+                                             n_q_heads=8, n_kv_heads=1)
+SHARE_8B_BY_SEQUENCE = LLAMA8B_HOST.replace(name="llama3-8b-b1-ctx32768-host", batch=1)
+SHARES = [SHARE_70B_BY_SEQUENCE, SHARE_70B_BY_KV_HEAD, SHARE_8B_BY_SEQUENCE]
+
+BY_NAME = {w.name: w for w in ALL + SHARES}

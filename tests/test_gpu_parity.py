@@ -347,11 +347,12 @@ def test_kv_append_from_device_buffers(head_dim):
 
 
 @pytest.mark.parametrize("head_dim,n_q_heads,n_kv_heads", [
-    (64, 8, 4), (64, 16, 4), (64, 32, 4), (128, 8, 4), (128, 2, 2)],
-    ids=["d64-g2", "d64-g4", "d64-g8", "d128-g2", "d128-g1"])
+    (64, 8, 4), (64, 16, 4), (64, 32, 4), (128, 8, 4), (128, 2, 2), (128, 8, 1)],
+    ids=["d64-g2", "d64-g4", "d64-g8", "d128-g2", "d128-g1", "d128-g8-one-kv-head"])
 def test_every_head_dim_and_group(oracle, head_dim, n_q_heads, n_kv_heads):
-    """Every supported (head_dim, group) pair that the workloads do not use:
-    the oracle's gates with host and HBM pages mixed, identical bits across
+    """Every supported (head_dim, group) pair that the workloads do not use,
+    and one KV head (the shape of a by-KV-head share of 8 heads): the
+    oracle's gates with host and HBM pages mixed, identical bits across
     placements, and the naive per-query-head comparator identical to the
     grouped kernel."""
     wl = configs.TINY.replace(batch=4, hidden=1024, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
