@@ -108,30 +108,30 @@ class Resident:
             self.dkv.decode_step(self.layout, layer, self.x[layer], self.W[layer], self.ctx,
                                  self.out[layer], self.stream)
 
-    def timed(self, steps, warmup, kernel_events=False):
+    def timed(self, steps, warmup, split_events=False):
         """Milliseconds per step over `steps` steps (HIP events on the step's
         stream around the whole run); per-step median / min / max from an
         event between consecutive steps are kept in self.step_stats. With
-        kernel_events, the library also records events around each kernel of
-        these same steps on their stream, and self.kernel_ms gets the
-        per-step kernel milliseconds of the timed region."""
+        split_events, the library also records two events around the split
+        kernel of each of these same steps on their stream (only those two,
+        so that short steps are barely disturbed), and self.kernel_ms["split"]
+        gets its per-step milliseconds over the timed region."""
         import torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        if kernel_events:
-            self.layout.timing_enable(True, steps * self.n_layers)
+        if split_events:
+            self.layout.timing_enable(True, steps * self.n_layers, split_only=True)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         ev[0].record(self.stream)
         for i in range(steps):
             self.step()
             ev[i + 1].record(self.stream)
         torch.cuda.synchronize()
-        if kernel_events:
+        if split_events:
             t = self.layout.timing_read()
             self.layout.timing_enable(False)
-            n = max(1, t["steps"]) / self.n_layers
-            self.kernel_ms = {k: t[k] / n for k in ("projection", "fresh", "split", "combine")}
+            self.kernel_ms = {"split": t["split"] / (max(1, t["steps"]) / self.n_layers)}
         per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
         self.step_stats = {"median": round(float(np.median(per)), 4), "min": round(per[0], 4),
                            "max": round(per[-1], 4)}
@@ -1069,12 +1069,13 @@ def main(argv=None):
         host_kv_layer += host_tokens * wl.kv_bytes_per_token
     host_kv = host_kv_layer * wl.n_layers
     hbm_kv = kv_bytes - host_kv
-    # The timed steps also carry the library's per-kernel events (on the
-    # step's stream): the split kernel's duration behind `roofline.achieved`
-    # comes from the timed region itself.
-    ms = r.timed(args.steps, args.warmup, kernel_events=True)
+    # The timed steps also carry the library's events around the split kernel
+    # (on the step's stream): its duration behind `roofline.achieved` comes
+    # from the timed region itself. The other kernels' times, reported for
+    # information, come from a few more steps with events around every kernel.
+    ms = r.timed(args.steps, args.warmup, split_events=True)
     step_stats = r.step_stats
-    kt = r.kernel_ms
+    kt = dict(r.kernel_times(max(1, min(args.steps, 2 if multi else 5))), split=r.kernel_ms["split"])
     # The graph replay: every step of a one-layer workload again; a few steps
     # of a multi-layer one (each is 8 layers).
     n_aux = args.steps if not multi else max(1, min(args.steps, 3))

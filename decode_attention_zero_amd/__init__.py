@@ -242,8 +242,9 @@ class Layout:
     def check_status(self) -> None:
         _check(lib().kv_layout_check_status(self.handle))
 
-    def timing_enable(self, enable: bool = True, max_steps: int = 1024) -> None:
-        _check(lib().kv_layout_timing_enable(self.handle, 1 if enable else 0, max_steps))
+    def timing_enable(self, enable: bool = True, max_steps: int = 1024, split_only: bool = False) -> None:
+        mode = 0 if not enable else (2 if split_only else 1)
+        _check(lib().kv_layout_timing_enable(self.handle, mode, max_steps))
 
     def timing_read(self) -> dict:
         """Summed per-kernel milliseconds and the step count since the last read."""

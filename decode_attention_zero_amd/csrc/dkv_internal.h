@@ -143,7 +143,7 @@ dkv_status decode_step_on_scratch(dkv_layout *layout, int32_t layer, const uint1
 // records events[0] before the projection, events[1] after it, events[2]
 // after the fresh-token kernel, events[3] after the split attention and
 // events[4] after the combine.
-hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream, hipEvent_t *events);
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream, hipEvent_t *events, bool split_only);
 
 // The four kernels of a step (each returns hipErrorInvalidValue for a shape
 // outside its compiled variants, before launching anything). The projection

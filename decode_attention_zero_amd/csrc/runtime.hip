@@ -170,6 +170,7 @@ struct dkv_layout {
     // per-kernel timing (measurement mode only)
     std::vector<hipEvent_t> timing_events;   // kTimingEvents per recorded step
     int32_t timing_recorded = 0;
+    int32_t timing_mode = 0;                 // 0 off, 1 every kernel, 2 the split kernel only
 };
 
 namespace {
@@ -447,21 +448,22 @@ void carve_scratch(StepArgs &a, char *base, const ScratchPlan &p) {
     a.item_list = reinterpret_cast<uint32_t *>(c);
 }
 
-hipError_t launch_decode_step(const StepArgs &a, hipStream_t st, hipEvent_t *ev) {
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t st, hipEvent_t *ev, bool split_only) {
     const int G = a.n_q_heads / a.n_kv_heads;
     if (!((a.head_dim == 128 || a.head_dim == 64) && (G == 1 || G == 2 || G == 4 || G == 8)))
         return hipErrorInvalidValue;
     hipError_t e;
     int ranges = 1;
-    if (ev) (void)hipEventRecord(ev[0], st);
+    hipEvent_t *every = split_only ? nullptr : ev;
+    if (every) (void)hipEventRecord(every[0], st);
     if ((e = launch_projection(a, &ranges, st)) != hipSuccess) return e;
-    if (ev) (void)hipEventRecord(ev[1], st);
+    if (every) (void)hipEventRecord(every[1], st);
     if ((e = launch_fresh(a, ranges, st)) != hipSuccess) return e;
     if (ev) (void)hipEventRecord(ev[2], st);
     if ((e = launch_split(a, st)) != hipSuccess) return e;
     if (ev) (void)hipEventRecord(ev[3], st);
     if ((e = launch_combine(a, st)) != hipSuccess) return e;
-    if (ev) (void)hipEventRecord(ev[4], st);
+    if (every) (void)hipEventRecord(every[4], st);
     return hipSuccess;
 }
 
@@ -909,12 +911,14 @@ dkv_status kv_layout_create_windowed(const dkv_shape *shape, int32_t batch, cons
 }
 
 static dkv_status kv_layout_timing_enable_body(dkv_layout *L, int32_t enable, int32_t max_steps) {
-    if (!L || !live(L) || (enable && max_steps <= 0))
-        return fail(DKV_E_INVALID_ARG, "kv_layout_timing_enable: null or freed layout, or max_steps <= 0");
+    if (!L || !live(L) || enable < 0 || enable > 2 || (enable && max_steps <= 0))
+        return fail(DKV_E_INVALID_ARG,
+                    "kv_layout_timing_enable: null or freed layout, enable not 0, 1 or 2, or max_steps <= 0");
     HIP_TRY(hipDeviceSynchronize());
     for (hipEvent_t e : L->timing_events) (void)hipEventDestroy(e);
     L->timing_events.clear();
     L->timing_recorded = 0;
+    L->timing_mode = enable;
     if (!enable) return DKV_OK;
     L->timing_events.resize((size_t)max_steps * kTimingEvents);
     for (auto &e : L->timing_events) HIP_TRY(hipEventCreate(&e));
@@ -934,6 +938,7 @@ dkv_status kv_layout_timing_read(dkv_layout *L, double *ms_proj, double *ms_fres
     for (int32_t i = 0; i < L->timing_recorded; ++i) {
         hipEvent_t *ev = &L->timing_events[(size_t)i * kTimingEvents];
         for (int k = 0; k + 1 < kTimingEvents; ++k) {
+            if (L->timing_mode == 2 && k != 2) continue;   // only the split kernel's pair was recorded
             float ms = 0.0f;
             HIP_TRY(hipEventElapsedTime(&ms, ev[k], ev[k + 1]));
             sum[k] += ms;
@@ -1287,7 +1292,7 @@ static dkv_status step_impl(dkv_layout *L, int32_t layer, const uint16_t *q_in, 
     hipEvent_t *ev = nullptr;
     if (!L->timing_events.empty() && (size_t)(L->timing_recorded + 1) * kTimingEvents <= L->timing_events.size())
         ev = &L->timing_events[(size_t)L->timing_recorded++ * kTimingEvents];
-    hipError_t e = dkv::launch_decode_step(a, reinterpret_cast<hipStream_t>(stream), ev);
+    hipError_t e = dkv::launch_decode_step(a, reinterpret_cast<hipStream_t>(stream), ev, L->timing_mode == 2);
     if (e != hipSuccess) return hip_fail(e, who);
     return DKV_OK;
 }

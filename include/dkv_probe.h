@@ -73,9 +73,13 @@ dkv_status kv_pool_copy(dkv_pool *dst, const dkv_pool *src, int64_t bytes, dkv_s
 
 /* Per-kernel timing of a layout's decode steps. While enabled, decode_step
  * records HIP events on its stream before and after each of its kernels
- * (projection, fresh token, split attention, combine) for up to max_steps
- * steps; enabling creates those events, so do it outside graph capture.
- * Disabling (enable = 0) destroys them. */
+ * (enable = 1: projection, fresh token, split attention, combine) or only
+ * around the split-attention kernel (enable = 2: two events per step, which
+ * disturb short steps less; the other kernels then read as 0 ms), for up to
+ * max_steps steps; enabling creates those events, so do it outside graph
+ * capture. Disabling (enable = 0) destroys them. Errors: DKV_E_INVALID_ARG
+ * (null or freed layout, enable not 0, 1 or 2, max_steps <= 0 when
+ * enabling). */
 dkv_status kv_layout_timing_enable(dkv_layout *layout, int32_t enable, int32_t max_steps);
 
 /* Synchronises, then returns the milliseconds each kernel took summed over

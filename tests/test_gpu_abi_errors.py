@@ -162,3 +162,37 @@ def test_plan_log(monkeypatch, capfd):
         host.free()
     err = capfd.readouterr().err
     assert "[dkv] layout: batch 2" in err and "split kernel mfma" in err, err
+
+
+def test_timing_modes():
+    """kv_layout_timing_enable: mode 1 times every kernel of a step, mode 2
+    only the split kernel (the others read 0 ms), any other mode is refused
+    and leaves timing off; the step's output is the same in every mode."""
+    import torch
+    L = dkv.lib()
+    shape = dkv.Shape.of(512, 8, 4, 64, 1)
+    host = dkv.kv_alloc_host(shape, 8)
+    try:
+        layout = dkv.kv_layout_create(shape, np.array([60, 30], np.int32), None, host, None)
+        k = np.full((40, 4, 64), 0x3F80, np.uint16)
+        dkv.kv_append(layout, 0, 0, 0, k, k)
+        x = torch.ones((2, 512), dtype=torch.bfloat16, device="cuda")
+        W = torch.full(((8 + 8) * 64, 512), 0.01, dtype=torch.bfloat16, device="cuda")
+        ctx = torch.tensor([40, 0], dtype=torch.int32, device="cuda")
+        ref = dkv.decode_step(layout, 0, x, W, ctx).cpu()
+        for split_only in (False, True):
+            layout.timing_enable(True, 3, split_only=split_only)
+            for _ in range(3):
+                assert torch.equal(dkv.decode_step(layout, 0, x, W, ctx).cpu(), ref)
+            t = layout.timing_read()
+            assert t["steps"] == 3 and t["split"] > 0
+            others = [t["projection"], t["fresh"], t["combine"]]
+            assert all(v == 0 for v in others) if split_only else all(v > 0 for v in others), t
+            layout.timing_enable(False)
+        assert L.kv_layout_timing_enable(layout.handle, 3, 4) == E_INVALID_ARG
+        assert L.kv_layout_timing_enable(layout.handle, -1, 4) == E_INVALID_ARG
+        dkv.decode_step(layout, 0, x, W, ctx)
+        assert layout.timing_read()["steps"] == 0
+        layout.free()
+    finally:
+        host.free()
