@@ -27,7 +27,7 @@ from tests.test_gpu_parity import FP32_SLACK, MAX_ABS, REL_L2, TIGHT_REL_L2, bit
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
 
-N_CASES = 24
+N_CASES = 128
 KNOBS = ("DKV_SPLIT_TOKENS", "DKV_SPLIT_KERNEL", "DKV_SPLIT_WAVES", "DKV_PROJ_MFMA_MIN_BATCH",
          "DKV_LDS_RING", "DKV_PROJ_SPLITK_MIN_BATCH", "DKV_PROJ_RANGES")
 
