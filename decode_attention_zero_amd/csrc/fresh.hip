@@ -24,8 +24,8 @@
 // partial sums, not K/V.
 //
 // The step's other bookkeeping happens here too: the range check of
-// ctx_lens, the list of the split kernel's work items and the reset of its
-// work queue.
+// ctx_lens, the list of the split kernel's work items (built by one extra
+// workgroup, the launch's first) and the reset of its work queue.
 #include "device_common.h"
 
 namespace dkv {
@@ -33,6 +33,57 @@ namespace {
 
 constexpr int kFreshWaves = 4;
 constexpr int kFreshThreads = 64 * kFreshWaves;
+
+// The step's item list: (sequence, split) for every split that holds tokens,
+// sequence-major, then the count in entry 0. One workgroup walks the batch
+// in chunks of kFreshThreads sequences: each thread takes one sequence's
+// split count (the next chunk's is loaded while this chunk is scanned), an
+// exclusive scan over the workgroup places each sequence's run of entries,
+// and the chunk's entries are then written by all threads together,
+// contiguously (an entry finds its sequence by a binary search over the
+// chunk's run ends in LDS), so that a sequence with many splits does not
+// serialise them on one thread. The batch is read once: linear in its size.
+__device__ void build_item_list(const StepArgs &a) {
+    __shared__ int s_wave[kFreshWaves];
+    __shared__ int s_end[kFreshThreads];     // end of each sequence's run within the chunk
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int base = 0;
+    int next = tid < a.batch ? splits_of(a, tid) : 0;
+    for (int c0 = 0; c0 < a.batch; c0 += kFreshThreads) {
+        const int mine = next;
+        next = c0 + kFreshThreads + tid < a.batch ? splits_of(a, c0 + kFreshThreads + tid) : 0;
+        int incl = mine;                      // inclusive prefix within the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        const int wave_total = wave_sum_int(mine);
+        if (lane == 0) s_wave[wave] = wave_total;
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kFreshWaves; ++w) {
+            before += w < wave ? s_wave[w] : 0;
+            total += s_wave[w];
+        }
+        s_end[tid] = before + incl;
+        __syncthreads();
+        for (int e = tid; e < total; e += kFreshThreads) {
+            int lo = 0, hi = kFreshThreads - 1;   // the first run whose end is past e
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_end[mid] > e) hi = mid;
+                else lo = mid + 1;
+            }
+            const int s = e - (lo ? s_end[lo - 1] : 0);
+            a.item_list[1 + base + e] = ((uint32_t)(c0 + lo) << 16) | (uint32_t)s;
+        }
+        base += total;
+        __syncthreads();                      // s_wave and s_end are rewritten by the next chunk
+    }
+    if (tid == 0) a.item_list[0] = (uint32_t)base;
+}
 
 // KS slabs (1, 2, 4 or 8). Each thread owns up to RPT of the group's rows and
 // issues all RPT x KS loads of its slabs before it adds them, each row in
@@ -42,8 +93,13 @@ __global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a) 
     constexpr int DPL = D / 64;        // dims per lane
     constexpr int NR = (G + 2) * D;    // the group's rows: G query heads, K, V
     constexpr int RPT = (NR + kFreshThreads - 1) / kFreshThreads;
-    const int b = blockIdx.x / a.n_kv_heads;
-    const int g = blockIdx.x - b * a.n_kv_heads;
+    reset_items(a);
+    if (blockIdx.x == 0) {                    // the extra workgroup: the item list
+        build_item_list(a);
+        return;
+    }
+    const int b = (blockIdx.x - 1) / a.n_kv_heads;
+    const int g = (blockIdx.x - 1) - b * a.n_kv_heads;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -51,16 +107,7 @@ __global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a) 
     __shared__ float s_q[G][D];
     __shared__ float s_kv[2][D];               // rounded K and V, as fp32 (exact)
     __shared__ __attribute__((aligned(16))) uint16_t s_kvb[2][D];   // their bf16 bits
-    __shared__ int s_before[kFreshWaves];
 
-    reset_items(a);
-    // Splits of the sequences before b, for the item list (workgroup g = 0
-    // only: b entries, so the batch reads B^2 / 2 in all, which grows with
-    // the batch squared); loaded first, so that their latency overlaps the
-    // slabs'.
-    int n_before = 0;
-    if (g == 0)
-        for (int i = tid; i < b; i += kFreshThreads) n_before += splits_of(a, i);
     const int L = a.ctx_lens[b];
     const bool in_range = L >= 0 && L < a.capacity[b];
     if (g == 0 && tid == 0) check_context_range(a, b);
@@ -99,21 +146,6 @@ __global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a) 
         }
     }
     __syncthreads();
-
-    // Sequence b's entries of the step's item list, after those of sequences
-    // 0 .. b - 1 (workgroup g = 0 of each sequence; the last one writes the count).
-    if (g == 0) {
-        const int n = wave_sum_int(n_before);
-        if (lane == 0) s_before[wave] = n;
-        __syncthreads();
-        int before = 0;
-#pragma unroll
-        for (int w = 0; w < kFreshWaves; ++w) before += s_before[w];
-        const int mine = splits_of(a, b);
-        for (int s = tid; s < mine; s += kFreshThreads)
-            a.item_list[1 + before + s] = ((uint32_t)b << 16) | (uint32_t)s;
-        if (b == a.batch - 1 && tid == 0) a.item_list[0] = (uint32_t)(before + mine);
-    }
     if (!in_range) return;
 
     // One-token state of each query head: m = s_new, l = 1, o = v_new.
@@ -149,7 +181,7 @@ __global__ __launch_bounds__(kFreshThreads) void fresh_token_kernel(StepArgs a) 
 
 template <int D, int G>
 void launch(const StepArgs &a, int ranges, hipStream_t st) {
-    const dim3 grid(a.batch * a.n_kv_heads);
+    const dim3 grid(1 + a.batch * a.n_kv_heads);     // workgroup 0 builds the item list
     switch (ranges) {
         case 1: fresh_token_kernel<D, G, 1><<<grid, kFreshThreads, 0, st>>>(a); break;
         case 2: fresh_token_kernel<D, G, 2><<<grid, kFreshThreads, 0, st>>>(a); break;
