@@ -349,18 +349,24 @@ int splitk_ranges(int hidden, int kc, int min_range) {
 }
 
 // 256-wide chunks in up to 8 ranges of at least 256 (8 ranges from hidden
-// 2048): with the fresh-token kernel adding the slabs, 8 ranges measured
-// best or equal at every batch (MI355X, W cycled through copies so that it
-// is read from HBM, decode-step HIP events, hidden 4096 / 8192): batch 8,
-// 14.4 / 36.5 us against 15.1 / 43.1 with 4 ranges and 15.7 / 42.9 for the
-// one-tile streamed kernel; batch 16, 14.7 / 37.0 against 15.7 / 44.3 with
-// 4 ranges; batch 32, 16.7 / 39.4 against 17.6 / 44.4; batch 64, 20.2 /
-// 46.4 against 21.9 / 52.3.
+// 2048), and at most 8 (range, batch tile) pairs per row block: every range
+// writes a slab of the whole batch, which the fresh-token kernel reads back,
+// and every batch tile reads W again, so past one 64-sequence tile fewer
+// ranges win. Measured on MI355X (W cycled through copies so that it is read
+// from HBM, decode-step HIP events, projection + fresh-token kernel, hidden
+// 4096 / 8192): up to batch 64, 8 ranges best or equal (batch 8, 14.4 /
+// 36.5 us for the projection against 15.1 / 43.1 with 4 ranges; batch 64,
+// 27.1 / 53.7 against 27.0 / 57.1); batch 128, 4 ranges 34.2 / 82.6 against
+// 38.5 / 87.7 with 8; batch 256, 2 ranges 50.5 / 136.5 against 61.7 /
+// 148.7; batch 512, one range 85.3 / 228.1 against 107.3 / 283.2; batch
+// 1024, one range 145.6 / 425.0 against 199.3 / 542.9.
 template <int NBT>
 int launch_splitk(const StepArgs &a, hipStream_t st) {
+    const int tiles = (a.batch + 16 * NBT - 1) / (16 * NBT);
     int ks = splitk_ranges(a.hidden, 256, 256);
+    while (ks > 1 && ks * tiles > kProjMaxSplits) ks >>= 1;
     if (a.proj_ranges > 0 && a.hidden % (a.proj_ranges * 256) == 0) ks = a.proj_ranges;
-    const dim3 grid(a.n_qkv / (16 * kProjRowBlocks), ks, (a.batch + 16 * NBT - 1) / (16 * NBT));
+    const dim3 grid(a.n_qkv / (16 * kProjRowBlocks), ks, tiles);
     qkv_proj_splitk_kernel<NBT, 256><<<grid, 64 * kProjRowBlocks, 0, st>>>(a, a.hidden / ks);
     return ks;
 }

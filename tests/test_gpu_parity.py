@@ -169,7 +169,7 @@ PROJ_KNOBS = ("DKV_PROJ_MFMA_MIN_BATCH", "DKV_PROJ_SPLITK_MIN_BATCH", "DKV_PROJ_
     ("llama8b", 1, {"DKV_PROJ_MFMA_MIN_BATCH": "1"}), ("llama8b", 8, {}),
     ("llama8b", 8, {"DKV_PROJ_SPLITK_MIN_BATCH": "16"}), ("llama8b", 16, {}),
     ("llama8b", 17, {}), ("llama8b", 32, {}), ("llama8b", 40, {}), ("llama8b", 64, {}),
-    ("llama8b", 70, {}), ("llama8b", 12, {"DKV_PROJ_RANGES": "1"}), ("llama8b", 24, {"DKV_PROJ_RANGES": "2"}),
+    ("llama8b", 70, {}), ("llama8b", 130, {}), ("llama8b", 300, {}), ("llama8b", 12, {"DKV_PROJ_RANGES": "1"}), ("llama8b", 24, {"DKV_PROJ_RANGES": "2"}),
     ("llama8b", 48, {"DKV_PROJ_RANGES": "4"}), ("llama70b", 16, {}), ("llama70b", 33, {}),
     ("llama70b", 8, {"DKV_PROJ_SPLITK_MIN_BATCH": "16"})])
 def test_projection_integer_exact(oracle, monkeypatch, shape_name, batch, knobs):
@@ -181,9 +181,10 @@ def test_projection_integer_exact(oracle, monkeypatch, shape_name, batch, knobs)
     with DKV_PROJ_MFMA_MIN_BATCH=1 (as do batches 8 to 15 with
     DKV_PROJ_SPLITK_MIN_BATCH=16); from 8 (or, forced, from 1) the split-k
     MFMA kernel stages x in tiles of 16, 32 or 64 sequences (3, 17, 40: a
-    partly filled tile; 70: a second 64-sequence tile) and writes one slab per
-    range of the hidden dimension (8 by default; 1, 2 and 4 forced), which
-    the fresh-token kernel adds."""
+    partly filled tile; 70, 130, 300: two, three and five 64-sequence tiles)
+    and writes one slab per range of the hidden dimension (8 by default up
+    to one 64-sequence tile, then 4, 2 and 1 as the tiles grow; 1, 2 and 4
+    forced), which the fresh-token kernel adds."""
     import synth
     for k in PROJ_KNOBS:
         monkeypatch.delenv(k, raising=False)
