@@ -169,7 +169,8 @@ PROJ_KNOBS = ("DKV_PROJ_MFMA_MIN_BATCH", "DKV_PROJ_SPLITK_MIN_BATCH", "DKV_PROJ_
     ("llama8b", 1, {"DKV_PROJ_MFMA_MIN_BATCH": "1"}), ("llama8b", 8, {}),
     ("llama8b", 8, {"DKV_PROJ_SPLITK_MIN_BATCH": "16"}), ("llama8b", 16, {}),
     ("llama8b", 17, {}), ("llama8b", 32, {}), ("llama8b", 40, {}), ("llama8b", 64, {}),
-    ("llama8b", 70, {}), ("llama8b", 130, {}), ("llama8b", 300, {}), ("llama8b", 12, {"DKV_PROJ_RANGES": "1"}), ("llama8b", 24, {"DKV_PROJ_RANGES": "2"}),
+    ("llama8b", 70, {}), ("llama8b", 130, {}), ("llama8b", 300, {}), ("llama8b", 384, {}), ("llama8b", 520, {}),
+    ("llama8b", 520, {"DKV_PROJ_RANGES": "4"}), ("tiny", 2600, {}), ("llama8b", 12, {"DKV_PROJ_RANGES": "1"}), ("llama8b", 24, {"DKV_PROJ_RANGES": "2"}),
     ("llama8b", 48, {"DKV_PROJ_RANGES": "4"}), ("llama70b", 16, {}), ("llama70b", 33, {}),
     ("llama70b", 8, {"DKV_PROJ_SPLITK_MIN_BATCH": "16"})])
 def test_projection_integer_exact(oracle, monkeypatch, shape_name, batch, knobs):
@@ -181,16 +182,21 @@ def test_projection_integer_exact(oracle, monkeypatch, shape_name, batch, knobs)
     with DKV_PROJ_MFMA_MIN_BATCH=1 (as do batches 8 to 15 with
     DKV_PROJ_SPLITK_MIN_BATCH=16); from 8 (or, forced, from 1) the split-k
     MFMA kernel stages x in tiles of 16, 32 or 64 sequences (3, 17, 40: a
-    partly filled tile; 70, 130, 300: two, three and five 64-sequence tiles)
-    and writes one slab per range of the hidden dimension (8 by default up
-    to one 64-sequence tile, then 4, 2 and 1 as the tiles grow; 1, 2 and 4
-    forced), which the fresh-token kernel adds."""
+    partly filled tile; 70, 130: two and three 64-sequence tiles) and writes
+    one slab per range of the hidden dimension (8 by default up to one
+    64-sequence tile, then 4 and 2 as the tiles grow; 1, 2 and 4 forced),
+    which the fresh-token kernel adds; from 192 (when its workgroups fill
+    half the CUs: 300, 384, 520, and the tiny shape at 2600) the tiled MFMA
+    kernel (256-sequence tiles, the last partly filled at 300, 520 and 2600;
+    W tiles dealt to the XCDs at hidden 4096, in plain order for the tiny
+    shape's 12 W tiles; two ranges at 300 and 384, one at 520, four
+    forced)."""
     import synth
     for k in PROJ_KNOBS:
         monkeypatch.delenv(k, raising=False)
     for k, v in knobs.items():
         monkeypatch.setenv(k, v)
-    base = configs.LLAMA8B_HOST if shape_name == "llama8b" else configs.LLAMA70B_LONG
+    base = {"llama8b": configs.LLAMA8B_HOST, "llama70b": configs.LLAMA70B_LONG, "tiny": configs.TINY}[shape_name]
     wl = base.replace(batch=batch, n_layers=1)
     ctx = np.array([[0, 5, 16][b % 3] for b in range(batch)], np.int32)
     xi = synth.int_bf16(99, 20, 0, wl.batch * wl.hidden, -4, 4).reshape(wl.batch, wl.hidden)
