@@ -13,7 +13,7 @@ SOURCES = ["proj.hip", "fresh.hip", "attn_split.hip", "attn_combine.hip", "windo
            "runtime.hip", "noalloc.hip", "append.hip"]
 # Host-only C++ (the CPU attention comparator), built with the system compiler.
 HOST_SOURCES = ["cpu_attention.cpp"]
-HEADERS = [os.path.join(CSRC, "cpu_attention.h"), os.path.join(CSRC, "dkv_internal.h"), os.path.join(CSRC, "device_common.h"), os.path.join(INCLUDE, "dkv.h"),
+HEADERS = [os.path.join(CSRC, "cpu_attention.h"), os.path.join(CSRC, "dkv_internal.h"), os.path.join(CSRC, "device_common.h"), os.path.join(CSRC, "mfma_tile.h"), os.path.join(INCLUDE, "dkv.h"),
            os.path.join(INCLUDE, "dkv_probe.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -8,18 +8,11 @@
 //
 //   C[M][N] (fp32) = A[M][K] (bf16, HBM) x B[N][K]^T (bf16, host or HBM)
 //
-// A workgroup of 2*WM wavefronts (WM along M, 2 along N) computes a
-// (64*WM) x 128 tile of C; each wavefront a 64 x 64 block (4 x 4 MFMA tiles
-// of v_mfma_f32_16x16x32_bf16). The k loop runs in steps of 64: each step's
-// A and B tiles are loaded from memory once per workgroup (16-byte chunks,
-// eight lanes per 128-byte row), staged in LDS (rows padded to 144 bytes, so
-// the MFMA operand reads -- lane l takes row l%16, k chunk l/16 -- are free of
-// bank conflicts) and read from there by every wavefront that needs them.
-// Loads run two steps ahead of the matrix cores: while step s is multiplied
-// out of one LDS buffer, step s+1 (already in registers) is written to the
-// other and step s+2 is in flight; one barrier per step. Every element of C
-// is one fp32 sum over k in the same order whatever the tile order or where B
-// lives, so all variants give identical bits.
+// Each workgroup computes a (64*WM) x 128 tile of C with the LDS-staged
+// matrix-core tile product of mfma_tile.h (both operands staged per 64-wide
+// k step, loads two steps ahead); every element of C is one fp32 sum over k
+// in the same order whatever the tile order or where B lives, so all
+// variants give identical bits.
 //
 // Tile orders (the only difference between the zero-copy variants):
 //   row-major  (naive): workgroup id -> (m block, n block), n fastest; the
@@ -35,84 +28,22 @@
 //              streams past the L2 instead of evicting B (without that, the
 //              10240-square product took 135 ms instead of 15.5 ms with the
 //              earlier register-only kernel).
-#include "device_common.h"
+#include "mfma_tile.h"
 
 namespace dkv {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kTileN = 128;
-constexpr int kStepK = 64;
-constexpr int kRowBytes = kStepK * 2 + 16;   // padded LDS row
+using tile::bf16x8;
+using tile::f32x4;
+using tile::kRowBytes;
+using tile::kStepK;
+constexpr int kTileN = tile::kN;
 constexpr int kXcds = 8;
-
-template <int WM, bool CPU_AWARE>
-struct GemmTile {
-    static constexpr int BM = 64 * WM;
-    static constexpr int NT = 128 * WM;                       // threads
-    static constexpr int ACH = BM * (kStepK / 8) / NT;        // A chunks per thread per step
-    static constexpr int BCH = kTileN * (kStepK / 8) / NT;    // B chunks per thread per step
-    static constexpr int STAGE = (BM + kTileN) * kRowBytes;   // LDS bytes per buffer
-    static_assert(ACH >= 1 && BCH >= 1, "tile too small for its threads");
-
-    uint4 a[ACH], b[BCH];
-
-    __device__ __forceinline__ void load(const uint16_t *A, const uint16_t *B, int K, int m0, int n0, int k0) {
-        const int t = threadIdx.x;
-#pragma unroll
-        for (int c = 0; c < ACH; ++c) {
-            const int chunk = t + c * NT;
-            const uint16_t *p = A + (size_t)(m0 + (chunk >> 3)) * K + k0 + (chunk & 7) * 8;
-            a[c] = CPU_AWARE ? load_stream(p) : *reinterpret_cast<const uint4 *>(p);
-        }
-#pragma unroll
-        for (int c = 0; c < BCH; ++c) {
-            const int chunk = t + c * NT;
-            b[c] = *reinterpret_cast<const uint4 *>(B + (size_t)(n0 + (chunk >> 3)) * K + k0 + (chunk & 7) * 8);
-        }
-    }
-
-    __device__ __forceinline__ void stage(char *buf) const {
-        const int t = threadIdx.x;
-#pragma unroll
-        for (int c = 0; c < ACH; ++c) {
-            const int chunk = t + c * NT;
-            *reinterpret_cast<uint4 *>(buf + (chunk >> 3) * kRowBytes + (chunk & 7) * 16) = a[c];
-        }
-#pragma unroll
-        for (int c = 0; c < BCH; ++c) {
-            const int chunk = t + c * NT;
-            *reinterpret_cast<uint4 *>(buf + (BM + (chunk >> 3)) * kRowBytes + (chunk & 7) * 16) = b[c];
-        }
-    }
-};
-
-// The wavefront's 4 x 4 MFMA tiles over one 64-wide k step from LDS.
-__device__ __forceinline__ void gemm_step(f32x4 (&acc)[4][4], const char *a_rows, const char *b_rows) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        __builtin_amdgcn_sched_barrier(0);     // one half step's operands in registers at a time
-        uint4 af[4], bf[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) af[t] = *reinterpret_cast<const uint4 *>(a_rows + t * 16 * kRowBytes + ks * 64);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) bf[t] = *reinterpret_cast<const uint4 *>(b_rows + t * 16 * kRowBytes + ks * 64);
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn)
-                acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[tm]),
-                                                                      __builtin_bit_cast(bf16x8, bf[tn]),
-                                                                      acc[tm][tn], 0, 0, 0);
-    }
-}
 
 template <int WM, bool CPU_AWARE>
 __global__ __launch_bounds__(128 * WM, WM == 4 ? 2 : 1) void gemm_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *B,
                                                            float *__restrict__ C, int M, int N, int K) {
-    using T = GemmTile<WM, CPU_AWARE>;
+    using T = tile::Shape<WM>;
     __shared__ __attribute__((aligned(16))) char lds[2][T::STAGE];
     const int nmb = M / T::BM, nnb = N / kTileN;
     const int id = blockIdx.x;
@@ -126,49 +57,24 @@ __global__ __launch_bounds__(128 * WM, WM == 4 ? 2 : 1) void gemm_nt_kernel(cons
         nb = id % nnb;
     }
     const int m0 = mb * T::BM, n0 = nb * kTileN;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int i = lane & 15, kq = lane >> 4;
-    const int a_off = (wm * 64 + i) * kRowBytes + kq * 16;
-    const int b_off = (T::BM + wn * 64 + i) * kRowBytes + kq * 16;
 
     f32x4 acc[4][4];
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // K is a multiple of 64; A is read nontemporally in the CPU-aware order.
+    tile::product<WM, CPU_AWARE, false>(acc, lds, A, B, K, m0, M, n0, 0, K / kStepK);
 
-    // K is a multiple of 64. Register sets x and y alternate between the
-    // steps: at step s the other set holds step s + 1, this one receives
-    // step s + 2.
-    const int nk = K / kStepK;
-    T x, y;
-    x.load(A, B, K, m0, n0, 0);
-    x.stage(lds[0]);
-    if (nk > 1) x.load(A, B, K, m0, n0, kStepK);
-    __syncthreads();
-    for (int s = 0; s < nk; s += 2) {
-        // step s from lds[0]; x holds step s + 1
-        if (s + 2 < nk) y.load(A, B, K, m0, n0, (s + 2) * kStepK);
-        gemm_step(acc, lds[0] + a_off, lds[0] + b_off);
-        if (s + 1 < nk) x.stage(lds[1]);
-        __syncthreads();
-        if (s + 1 >= nk) break;
-        // step s + 1 from lds[1]; y holds step s + 2
-        if (s + 3 < nk) x.load(A, B, K, m0, n0, (s + 3) * kStepK);
-        gemm_step(acc, lds[1] + a_off, lds[1] + b_off);
-        if (s + 2 < nk) y.stage(lds[0]);
-        __syncthreads();
-    }
-
+    const tile::Lane ln;
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) {
-            const int col = n0 + wn * 64 + tn * 16 + i;
+            const int col = n0 + ln.wn * 64 + tn * 16 + ln.i;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * 64 + tm * 16 + kq * 4 + r;
+                const int row = m0 + ln.wm * 64 + tm * 16 + ln.kq * 4 + r;
                 C[(size_t)row * N + col] = acc[tm][tn][r];
             }
         }

@@ -10,7 +10,7 @@
 // 16-sequence MFMA tile, which a layout takes up to batch 15 when
 // DKV_PROJ_SPLITK_MIN_BATCH moves the split-k threshold up) is built to
 // stream W once at full bandwidth.
-#include "device_common.h"
+#include "mfma_tile.h"
 
 namespace dkv {
 namespace {
@@ -342,35 +342,21 @@ __global__ __launch_bounds__(64 * kProjRowBlocks) void qkv_proj_splitk_kernel(St
 
 // 1d. From kProjTiledMinBatch sequences the product is no longer bound by
 // reading W but by the matrix cores, and the split-k kernel's 64 x 64
-// (W rows x sequences) workgroup tile re-reads W for every 64 sequences. Here
-// a workgroup of 2 * WM wavefronts computes a (64 WM sequences) x (128 W rows)
-// tile of y over one range of the hidden dimension: each 64-wide k step of
-// x and W is loaded once per workgroup (16-byte chunks, eight lanes per
-// 128-byte row; sequences past the batch load zeros), staged in LDS (rows
-// padded to 144 bytes, so the MFMA operand reads are free of bank
-// conflicts) and read by every wavefront that needs it; each wavefront owns
-// a 64 x 64 block (4 x 4 tiles of v_mfma_f32_16x16x32_bf16). Loads run two
-// steps ahead: step s is multiplied out of one LDS buffer while step s + 1,
-// already in registers, is written to the other and step s + 2 is in flight.
-// When the W tiles divide into the 8 XCDs, all sequence tiles of one W tile
-// go to one XCD (the dispatcher deals workgroups to the XCDs in turn), so
-// each W tile is fetched into one L2 and re-read from there.
+// (W rows x sequences) workgroup tile re-reads W for every 64 sequences.
+// Here a workgroup computes a (64 WM sequences) x (128 W rows) tile of y over
+// one range of the hidden dimension with the LDS-staged matrix-core tile
+// product of mfma_tile.h (x and W staged per 64-wide k step; sequences past
+// the batch load zeros and are not stored). When the W tiles divide into the
+// 8 XCDs, all sequence tiles of one W tile go to one XCD (the dispatcher
+// deals workgroups to the XCDs in turn), so each W tile is fetched into one
+// L2 and re-read from there.
 constexpr int kProjTiledMinBatch = 192;
-constexpr int kTiledRows = 128;                     // W rows per workgroup
-constexpr int kTiledStep = 64;                      // k per step
-constexpr int kTiledRowBytes = kTiledStep * 2 + 16; // staged row, padded
 
 template <int WM>
-__global__ __launch_bounds__(128 * WM, WM == 4 ? 2 : 1) void qkv_proj_tiled_kernel(StepArgs a, int krange, int w_tiles,
-                                                                  int b_tiles) {
-    constexpr int BM = 64 * WM;                                   // sequences per workgroup
-    constexpr int NT = 128 * WM;                                  // threads
-    constexpr int XCH = BM * (kTiledStep / 8) / NT;               // x chunks per thread per step
-    constexpr int WCH = kTiledRows * (kTiledStep / 8) / NT;       // W chunks per thread per step
-    constexpr int STAGE = (BM + kTiledRows) * kTiledRowBytes;
-    static_assert(XCH >= 1 && WCH >= 1, "tile too small for its threads");
-    __shared__ __attribute__((aligned(16))) char lds[2][STAGE];
-
+__global__ __launch_bounds__(128 * WM, WM == 4 ? 2 : 1) void qkv_proj_tiled_kernel(StepArgs a, int krange,
+                                                                                  int w_tiles, int b_tiles) {
+    using T = tile::Shape<WM>;
+    __shared__ __attribute__((aligned(16))) char lds[2][T::STAGE];
     const int id = blockIdx.x;
     int bt, wt;
     if (w_tiles % 8 == 0) {
@@ -381,101 +367,30 @@ __global__ __launch_bounds__(128 * WM, WM == 4 ? 2 : 1) void qkv_proj_tiled_kern
         bt = id % b_tiles;
         wt = id / b_tiles;
     }
-    const int b0 = bt * BM, n0 = wt * kTiledRows;
-    const int ks = blockIdx.y, kb = ks * krange;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int i = lane & 15, kq = lane >> 4;
-    const int x_off = (wm * 64 + i) * kTiledRowBytes + kq * 16;
-    const int w_off = (BM + wn * 64 + i) * kTiledRowBytes + kq * 16;
-
-    struct Step {
-        uint4 x[XCH], w[WCH];
-    };
-    auto load = [&](Step &st, int k0) {
-#pragma unroll
-        for (int c = 0; c < XCH; ++c) {
-            const int chunk = threadIdx.x + c * NT;
-            const int b = b0 + (chunk >> 3);
-            st.x[c] = b < a.batch ? *reinterpret_cast<const uint4 *>(a.x + (size_t)b * a.hidden + k0 + (chunk & 7) * 8)
-                                  : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int c = 0; c < WCH; ++c) {
-            const int chunk = threadIdx.x + c * NT;
-            st.w[c] = *reinterpret_cast<const uint4 *>(a.w + (size_t)(n0 + (chunk >> 3)) * a.hidden + k0 +
-                                                       (chunk & 7) * 8);
-        }
-    };
-    auto stage = [&](const Step &st, char *buf) {
-#pragma unroll
-        for (int c = 0; c < XCH; ++c) {
-            const int chunk = threadIdx.x + c * NT;
-            *reinterpret_cast<uint4 *>(buf + (chunk >> 3) * kTiledRowBytes + (chunk & 7) * 16) = st.x[c];
-        }
-#pragma unroll
-        for (int c = 0; c < WCH; ++c) {
-            const int chunk = threadIdx.x + c * NT;
-            *reinterpret_cast<uint4 *>(buf + (BM + (chunk >> 3)) * kTiledRowBytes + (chunk & 7) * 16) = st.w[c];
-        }
-    };
+    const int b0 = bt * T::BM, n0 = wt * tile::kN;
+    const int ks = blockIdx.y;
 
     f32x4 acc[4][4];
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    auto multiply = [&](const char *buf) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            __builtin_amdgcn_sched_barrier(0);   // one half step's operands in registers at a time
-            uint4 xf[4], wf[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                xf[t] = *reinterpret_cast<const uint4 *>(buf + x_off + t * 16 * kTiledRowBytes + h * 64);
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                wf[t] = *reinterpret_cast<const uint4 *>(buf + w_off + t * 16 * kTiledRowBytes + h * 64);
-#pragma unroll
-            for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-                for (int tn = 0; tn < 4; ++tn)
-                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf[tm]),
-                                                                          __builtin_bit_cast(bf16x8, wf[tn]),
-                                                                          acc[tm][tn], 0, 0, 0);
-        }
-    };
+    // krange is a multiple of 64. Only the last sequence tile can run past the
+    // batch; the others skip the row check (which cost the HBM-operand GEMM
+    // 18 % on MI355X).
+    const int k0 = ks * krange, nk = krange / tile::kStepK;
+    if (b0 + T::BM <= a.batch) tile::product<WM, false, false>(acc, lds, a.x, a.w, a.hidden, b0, a.batch, n0, k0, nk);
+    else tile::product<WM, false, true>(acc, lds, a.x, a.w, a.hidden, b0, a.batch, n0, k0, nk);
 
-    // krange is a multiple of 64. Register sets p and q alternate between
-    // the steps: at step s the other set holds step s + 1, this one
-    // receives step s + 2.
-    const int nk = krange / kTiledStep;
-    Step p, q;
-    load(p, kb);
-    stage(p, lds[0]);
-    if (nk > 1) load(p, kb + kTiledStep);
-    __syncthreads();
-    for (int s = 0; s < nk; s += 2) {
-        if (s + 2 < nk) load(q, kb + (s + 2) * kTiledStep);
-        multiply(lds[0]);
-        if (s + 1 < nk) stage(p, lds[1]);
-        __syncthreads();
-        if (s + 1 >= nk) break;
-        if (s + 3 < nk) load(p, kb + (s + 3) * kTiledStep);
-        multiply(lds[1]);
-        if (s + 2 < nk) stage(q, lds[0]);
-        __syncthreads();
-    }
-
-    // acc[tm][tn][r] is y of sequence b0 + 64 wm + 16 tm + 4 kq + r and W row
-    // n0 + 64 wn + 16 tn + i.
+    // acc[tm][tn][r]: sequence b0 + 64 wm + 16 tm + 4 kq + r, W row n0 + 64 wn + 16 tn + i.
+    const tile::Lane ln;
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int b = b0 + wm * 64 + tm * 16 + kq * 4 + r;
+            const int b = b0 + ln.wm * 64 + tm * 16 + ln.kq * 4 + r;
             if (b >= a.batch) continue;
-            float *row = a.proj_part + ((size_t)ks * a.batch + b) * a.n_qkv + n0 + wn * 64 + i;
+            float *row = a.proj_part + ((size_t)ks * a.batch + b) * a.n_qkv + n0 + ln.wn * 64 + ln.i;
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn) row[tn * 16] = acc[tm][tn][r];
         }
@@ -521,11 +436,11 @@ constexpr int kTiledWM = 4;
 
 int tiled_ranges(const StepArgs &a, int tiles) {
     auto rounds = [](int wgs) { return (wgs + 255) / 256; };
-    return 2 * rounds(tiles) > rounds(2 * tiles) && a.hidden % (2 * kTiledStep) == 0 ? 2 : 1;
+    return 2 * rounds(tiles) > rounds(2 * tiles) && a.hidden % (2 * tile::kStepK) == 0 ? 2 : 1;
 }
 
 int tiled_tiles(const StepArgs &a) {
-    return (a.batch + 64 * kTiledWM - 1) / (64 * kTiledWM) * (a.n_qkv / kTiledRows);
+    return (a.batch + 64 * kTiledWM - 1) / (64 * kTiledWM) * (a.n_qkv / tile::kN);
 }
 
 // The tiled form from 192 sequences, once its workgroups fill half the CUs;
@@ -537,16 +452,16 @@ int tiled_tiles(const StepArgs &a) {
 // 192, 110.9 / 98.4; 256, 134.4 / 105.5; 512, 225.7 / 186.9; 1024, 423.6 /
 // 304.8.
 bool tiled_pays(const StepArgs &a) {
-    if (a.batch < kProjTiledMinBatch || a.n_qkv % kTiledRows != 0) return false;
+    if (a.batch < kProjTiledMinBatch || a.n_qkv % tile::kN != 0) return false;
     const int tiles = tiled_tiles(a);
     return tiles * tiled_ranges(a, tiles) >= 128;
 }
 
 int launch_tiled(const StepArgs &a, hipStream_t st) {
     const int b_tiles = (a.batch + 64 * kTiledWM - 1) / (64 * kTiledWM);
-    const int w_tiles = a.n_qkv / kTiledRows;
+    const int w_tiles = a.n_qkv / tile::kN;
     const int tiles = b_tiles * w_tiles;
-    const int r = a.proj_ranges > 0 && a.hidden % (a.proj_ranges * kTiledStep) == 0 ? a.proj_ranges
+    const int r = a.proj_ranges > 0 && a.hidden % (a.proj_ranges * tile::kStepK) == 0 ? a.proj_ranges
                                                                                     : tiled_ranges(a, tiles);
     const dim3 grid(tiles, r);
     qkv_proj_tiled_kernel<kTiledWM><<<grid, 128 * kTiledWM, 0, st>>>(a, a.hidden / r, w_tiles, b_tiles);
