@@ -112,3 +112,59 @@ def test_random_case(oracle, monkeypatch, i):
         finally:
             s.free()
         assert np.array_equal(again.view(np.uint32), out32.view(np.uint32)), (other_tail, other_waves)
+
+
+N_LARGE = 6
+
+
+def draw_large(i):
+    """Llama-sized rows (hidden 4096 or 8192, head_dim 128, group 4 or 8) at
+    batches of 8 to 300 with short contexts, so that every projection form
+    (split-k with 8 to 2 ranges, the tiled kernel from 192 sequences) meets
+    the attention path; KV and the oracle's projection stay small enough for
+    the CPU (hidden 8192 up to batch 130)."""
+    rng = np.random.default_rng(0x1A76E + 104729 * i)
+    hidden = int(rng.choice([4096, 8192]))
+    G = int(rng.choice([4, 8]))
+    Hkv = int(rng.choice([2, 8]))
+    B = int(rng.choice([8, 40, 64, 130] + ([200, 300] if hidden == 4096 else [])))
+    T = int(rng.choice([16, 64, 256]))
+    ctx = [int(rng.integers(0, 300)) for _ in range(B)]
+    cap = [c + 1 + int(rng.choice([0, 16])) for c in ctx]
+    tail = [int(rng.choice([0, 1 << 20, 32])) for _ in range(B)]
+    env = {"DKV_SPLIT_TOKENS": str(T)}
+    if rng.random() < 0.3:
+        env["DKV_PROJ_RANGES"] = str(rng.choice(["1", "2", "4"]))
+    # W's scale as in the workloads of that width (0.02 at 4096, 0.015 at
+    # 8192), which keeps the projection's outputs, and so the bf16 rounding of
+    # the fresh values, within the absolute gate's range.
+    base = configs.LLAMA8B_HOST if hidden == 4096 else configs.LLAMA70B_LONG
+    wl = base.replace(name="sweep-large-%d" % i, seed=0x1A760000 + i, batch=B, hidden=hidden,
+                      n_q_heads=G * Hkv, n_kv_heads=Hkv, n_layers=1)
+    return wl, np.array(ctx, np.int32), np.array(cap, np.int32), np.array(tail, np.int32), env
+
+
+@pytest.mark.parametrize("i", range(N_LARGE))
+def test_random_large_case(oracle, monkeypatch, i):
+    wl, ctx, cap, tail, env = draw_large(i)
+    H.log("large case %d: Hq %d Hkv %d hidden %d batch %d T %s env %s"
+          % (i, wl.n_q_heads, wl.n_kv_heads, wl.hidden, wl.batch, env["DKV_SPLIT_TOKENS"], env))
+    set_env(monkeypatch, env)
+    s = H.Setup(wl, ctx_lens=ctx, hbm_tail=tail, capacity=cap)
+    try:
+        out32 = s.run(f32=True).cpu().numpy()
+        out = bits(s.run())
+    finally:
+        s.free()
+    assert np.all(np.isfinite(out32))
+    rel = H.rel_l2(out32.astype(np.float64), tight_reference(oracle, wl, 0, ctx))
+    assert rel <= TIGHT_REL_L2, rel
+    ref = H.oracle_full(oracle, wl, 0, ctx)["attn_out"]
+    got = H.bf16_to_f64(out)
+    assert np.abs(got - ref).max() <= MAX_ABS and H.rel_l2(got, ref) <= REL_L2
+    s = H.Setup(wl, ctx_lens=ctx, hbm_tail=0, capacity=cap)
+    try:
+        again = s.run(f32=True).cpu().numpy()
+    finally:
+        s.free()
+    assert np.array_equal(again.view(np.uint32), out32.view(np.uint32))
