@@ -4,12 +4,14 @@
 // which adds them, keeps the query in fp32 and rounds the new token's K and
 // V once. The projection that produces the new token's K/V is part of the
 // decode step, as in the core-method section of the DirectKV digest
-// ("长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）"); the step is bound by
-// reading W from HBM at every batch size here, so each of the three forms
-// (1a VALU GEMV below batch 8, 1c split-k MFMA from batch 8, and 1b one
-// 16-sequence MFMA tile, which a layout takes up to batch 15 when
-// DKV_PROJ_SPLITK_MIN_BATCH moves the split-k threshold up) is built to
-// stream W once at full bandwidth.
+// ("长上下文 LLM 的零拷贝 KV Cache 卸载（OSDI 2026）"); up to a few hundred
+// sequences the step is bound by reading W from HBM, so three forms (1a VALU
+// GEMV below batch 8, 1c split-k MFMA from batch 8, and 1b one 16-sequence
+// MFMA tile, which a layout takes up to batch 15 when
+// DKV_PROJ_SPLITK_MIN_BATCH moves the split-k threshold up) are built to
+// stream W once at full bandwidth; past that the product is bound by the
+// matrix cores, and a fourth form (1d, from 192 sequences) tiles both
+// operands in LDS.
 #include "mfma_tile.h"
 
 namespace dkv {
