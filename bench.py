@@ -534,7 +534,6 @@ def gemm_experiment(dkv, args):
     return 0
 
 
-PROJ_MFMA_MIN_BATCH = 8              # the library's default: split-k MFMA from batch 8, GEMV below
 PROJ_SHAPES = (("llama3-8b", 4096, 32), ("llama3-70b", 8192, 64))
 PROJ_BATCHES = (1, 2, 3, 4, 8, 16, 32, 64)
 PROJ_COLD_BYTES = 640 << 20          # W copies cycled per step: past the 256 MiB last-level cache
@@ -580,6 +579,7 @@ def projection_experiment(dkv, args):
             ctx = np.full(B, 16, np.int32)
             hbm = dkv.kv_alloc_hbm(shape, B * 2)
             layout = dkv.kv_layout_create(shape, ctx + 1, np.full(B, 1 << 30, np.int32), None, hbm)
+            kernel = layout.projection_kernel
             x = (torch.randn(B, hidden, device=dev, generator=g)).to(torch.bfloat16)
             c = torch.from_numpy(ctx).to(dev)
             out = torch.empty(B, Hq * 128, dtype=torch.bfloat16, device=dev)
@@ -596,10 +596,10 @@ def projection_experiment(dkv, args):
             hbm.free()
             n = t["steps"]
             proj_us, fresh_us = t["projection"] / n * 1e3, t["fresh"] / n * 1e3
-            mfma = B >= PROJ_MFMA_MIN_BATCH
+            mfma = kernel != "qkv_proj_gemv_kernel"
             flop = 2.0 * B * hidden * n_qkv
             line = {"experiment": "qkv_projection", "shape": name, "hidden": hidden, "n_qkv": n_qkv,
-                    "batch": B, "kernel": "qkv_proj_splitk_kernel" if mfma else "qkv_proj_gemv_kernel",
+                    "batch": B, "kernel": kernel,
                     "W_bytes": w_bytes, "W_copies_cycled": nW, "steps": n,
                     "projection_us": round(proj_us, 2), "fresh_token_us": round(fresh_us, 2),
                     "W_TBps": round(w_bytes / (proj_us * 1e-6) / 1e12, 3),
@@ -654,11 +654,11 @@ def host_facts() -> dict:
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 
 
-def projection_facts(wl, ms):
-    """The QKV projection of one step (summed over layers): which kernel, its W
-    read rate and its matrix-core use against the dense bf16 peak."""
+def projection_facts(wl, ms, kernel):
+    """The QKV projection of one step (summed over layers): which kernel (as
+    the layout reports it), its W read rate and its matrix-core use against
+    the dense bf16 peak."""
     B = wl.batch
-    kernel = "qkv_proj_gemv_kernel" if B < PROJ_MFMA_MIN_BATCH else "qkv_proj_splitk_kernel"
     w_bytes = wl.n_qkv * wl.hidden * 2 * wl.n_layers
     flop = 2.0 * B * wl.hidden * wl.n_qkv * wl.n_layers
     return {"kernel": kernel, "ms": round(ms, 4), "W_bytes": w_bytes,
@@ -1062,6 +1062,7 @@ def main(argv=None):
     r = Resident(dkv, wl, ctx, tail, kv_source)
     if args.split_kernel:
         r.layout.split_kernel = args.split_kernel
+    proj_kernel = r.layout.projection_kernel
     host_kv_layer = 0
     for b in range(B):
         n, first = dkv.kv_placement(int(ctx[b]) + 1, int(tail[b]))
@@ -1193,7 +1194,7 @@ def main(argv=None):
             "split_kernel_frac_of_8TBps": round(kv_bytes / (kt_h["split"] * 1e-3) / 1e9
                                                 / HBM_PEAK_GBPS, 4),
             "kernel_ms": {k: round(v, 4) for k, v in kt_h.items()},
-            "projection": projection_facts(wl, kt_h["projection"]),
+            "projection": projection_facts(wl, kt_h["projection"], proj_kernel),
             "measured_hbm_read_GBps": round(hbm_ceiling, 1),
             "hbm_probe": hbm_rows,
             "page_run_read_GBps": round(page_ceiling, 1) if page_rows else None,
@@ -1324,7 +1325,7 @@ def main(argv=None):
                               "serial_ms": round(t_serial * 1e3, 4),
                               "frac_of_serial": round(t_serial * 1e3 / ms, 4) if t_serial else None},
         "kernel_ms": {k: round(v, 4) for k, v in kt.items()},
-        "projection": projection_facts(wl, kt["projection"]),
+        "projection": projection_facts(wl, kt["projection"], proj_kernel),
         "host_link_probe": ceiling_rows,
         "hbm_placement": hbm,
         "comparators": comparators,

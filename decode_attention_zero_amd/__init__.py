@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "kv_layout_split_kernel": ([P], I32),
             "kv_layout_set_split_kernel": ([P, I32], I32),
             "kv_layout_split_waves": ([P], I32),
+            "kv_layout_projection_kernel": ([P], I32),
             "kv_layout_check_status": ([P], I32),
             "kv_append": ([P, I32, I32, I32, I32, P, P, P], I32),
             "kv_read": ([P, I32, I32, I32, I32, P, P], I32),
@@ -119,11 +120,15 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ["dkv_last_error", "kv_page_bytes", "kv_page_offset", "kv_placement", "kv_alloc_host",
             "kv_alloc_hbm", "kv_pool_free_pages", "kv_pool_info", "kv_pool_free",
             "kv_layout_create", "kv_layout_create_windowed", "kv_advance", "kv_layout_free", "kv_layout_page_tier", "kv_layout_split_tokens",
-            "kv_layout_split_kernel", "kv_layout_set_split_kernel", "kv_layout_split_waves", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
+            "kv_layout_split_kernel", "kv_layout_set_split_kernel", "kv_layout_split_waves", "kv_layout_projection_kernel", "kv_layout_check_status", "kv_append", "kv_read", "decode_step", "decode_step_f32",
             "decode_step_noalloc", "decode_step_noalloc_scratch_bytes", "dkv_probe_stream_read", "dkv_probe_stream_read_cycled", "dkv_probe_page_read", "kv_pool_copy", "dkv_host_buffer_alloc", "dkv_host_buffer_free",
             "dkv_copy", "dkv_gemm_bf16_nt", "dkv_gemm_bf16_nt_bstationary", "dkv_gemm_bstationary_workspace_bytes",
             "kv_layout_timing_enable", "kv_layout_timing_read",
             "dkv_cpu_attention", "dkv_cpu_stream_read", "dkv_cpu_attention_pages"]
+
+
+PROJECTION_KERNELS = {0: "qkv_proj_gemv_kernel", 1: "qkv_proj_stream_kernel", 2: "qkv_proj_splitk_kernel",
+                      3: "qkv_proj_tiled_kernel"}
 
 
 def _check(status: int) -> None:
@@ -228,6 +233,11 @@ class Layout:
     def split_waves(self) -> int:
         """Wavefronts of the register split kernel (0: one per work item)."""
         return lib().kv_layout_split_waves(self.handle)
+
+    @property
+    def projection_kernel(self) -> str:
+        """The QKV projection kernel this layout's steps run."""
+        return PROJECTION_KERNELS[lib().kv_layout_projection_kernel(self.handle)]
 
     @split_kernel.setter
     def split_kernel(self, name: str) -> None:

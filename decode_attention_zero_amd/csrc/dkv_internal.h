@@ -148,6 +148,11 @@ hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream, hipEvent_t 
 // The four kernels of a step (each returns hipErrorInvalidValue for a shape
 // outside its compiled variants, before launching anything). The projection
 // reports how many slabs of proj_part it wrote.
+// The projection form a step of these arguments runs (only the batch, the
+// shape and the layout's thresholds matter): 0 VALU GEMV, 1 one-tile streamed
+// MFMA, 2 split-k MFMA, 3 tiled MFMA.
+enum ProjectionForm { kProjGemv = 0, kProjStream = 1, kProjSplitk = 2, kProjTiled = 3 };
+int projection_form(const StepArgs &a);
 hipError_t launch_projection(const StepArgs &a, int *ranges, hipStream_t stream);
 hipError_t launch_fresh(const StepArgs &a, int ranges, hipStream_t stream);
 hipError_t launch_split(const StepArgs &a, hipStream_t stream);

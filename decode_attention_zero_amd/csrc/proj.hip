@@ -488,37 +488,47 @@ hipError_t launch_gemv(const StepArgs &a, hipStream_t st) {
 
 }  // namespace
 
+int projection_form(const StepArgs &a) {
+    if (a.batch < a.proj_mfma_min_batch) return kProjGemv;
+    if (a.batch < a.proj_splitk_min_batch && a.batch <= 16) return kProjStream;
+    return tiled_pays(a) ? kProjTiled : kProjSplitk;
+}
+
 hipError_t launch_projection(const StepArgs &a, int *ranges, hipStream_t st) {
     if (a.hidden % 512 != 0 || a.n_qkv % (16 * kProjRowBlocks) != 0 || !a.proj_part) return hipErrorInvalidValue;
     *ranges = 1;
-    if (a.batch >= a.proj_mfma_min_batch && a.batch < a.proj_splitk_min_batch && a.batch <= 16) {
-        // One sequence tile: streamed over k by up to 4 wavefronts per row block.
-        int ksplit = 4;
-        while (ksplit > 1 && a.hidden % (128 * ksplit) != 0) ksplit >>= 1;
-        const dim3 grid(a.n_qkv / 16);
-        // 256-wide chunks once each wave's range reaches 2048 (hidden 8192 at
-        // batch 8: 45.7 -> 42.1 us; at hidden 4096, ranges of 1024, 128-wide
-        // chunks stay ahead: 16.7 vs 18.9 us; decode-step HIP events, W
-        // evicted from the caches).
-        if (ksplit == 4 && a.hidden % 1024 == 0 && a.hidden / 4 >= 2048)
-            qkv_proj_stream_kernel<4, 256><<<grid, 256, 0, st>>>(a);
-        else switch (ksplit) {
-            case 1: qkv_proj_stream_kernel<1><<<grid, 64, 0, st>>>(a); break;
-            case 2: qkv_proj_stream_kernel<2><<<grid, 128, 0, st>>>(a); break;
-            default: qkv_proj_stream_kernel<4><<<grid, 256, 0, st>>>(a); break;
+    switch (projection_form(a)) {
+        case kProjStream: {
+            // One sequence tile: streamed over k by up to 4 wavefronts per row block.
+            int ksplit = 4;
+            while (ksplit > 1 && a.hidden % (128 * ksplit) != 0) ksplit >>= 1;
+            const dim3 grid(a.n_qkv / 16);
+            // 256-wide chunks once each wave's range reaches 2048 (hidden 8192 at
+            // batch 8: 45.7 -> 42.1 us; at hidden 4096, ranges of 1024, 128-wide
+            // chunks stay ahead: 16.7 vs 18.9 us; decode-step HIP events, W
+            // evicted from the caches).
+            if (ksplit == 4 && a.hidden % 1024 == 0 && a.hidden / 4 >= 2048)
+                qkv_proj_stream_kernel<4, 256><<<grid, 256, 0, st>>>(a);
+            else switch (ksplit) {
+                case 1: qkv_proj_stream_kernel<1><<<grid, 64, 0, st>>>(a); break;
+                case 2: qkv_proj_stream_kernel<2><<<grid, 128, 0, st>>>(a); break;
+                default: qkv_proj_stream_kernel<4><<<grid, 256, 0, st>>>(a); break;
+            }
+            break;
         }
-    } else if (a.batch >= a.proj_mfma_min_batch && tiled_pays(a)) {
-        *ranges = launch_tiled(a, st);
-    } else if (a.batch >= a.proj_mfma_min_batch) {
-        if (a.batch <= 16) *ranges = launch_splitk<1>(a, st);
-        else if (a.batch <= 32) *ranges = launch_splitk<2>(a, st);
-        else *ranges = launch_splitk<4>(a, st);
-    } else if (a.batch <= 4) {
-        (void)launch_gemv<4>(a, st);
-    } else if (a.batch <= 8) {
-        (void)launch_gemv<8>(a, st);
-    } else {
-        (void)launch_gemv<16>(a, st);
+        case kProjTiled:
+            *ranges = launch_tiled(a, st);
+            break;
+        case kProjSplitk:
+            if (a.batch <= 16) *ranges = launch_splitk<1>(a, st);
+            else if (a.batch <= 32) *ranges = launch_splitk<2>(a, st);
+            else *ranges = launch_splitk<4>(a, st);
+            break;
+        default:
+            if (a.batch <= 4) (void)launch_gemv<4>(a, st);
+            else if (a.batch <= 8) (void)launch_gemv<8>(a, st);
+            else (void)launch_gemv<16>(a, st);
+            break;
     }
     return hipGetLastError();
 }

@@ -619,6 +619,19 @@ static void choose_lds_ring(dkv_layout *L) {
     L->lds_poison = poison && strcmp(poison, "1") == 0;
 }
 
+// The projection form of the layout's steps (dkv::projection_form reads only
+// the batch, the shape and the thresholds, all fixed at creation).
+static int projection_form_of(const dkv_layout *L) {
+    dkv::StepArgs a{};
+    a.batch = L->batch;
+    a.hidden = L->shape.hidden;
+    a.n_qkv = (L->shape.n_q_heads + 2 * L->shape.n_kv_heads) * L->shape.head_dim;
+    a.proj_mfma_min_batch = L->proj_mfma_min_batch;
+    a.proj_splitk_min_batch = L->proj_splitk_min_batch;
+    a.proj_ranges = L->proj_ranges;
+    return dkv::projection_form(a);
+}
+
 // DKV_LOG=1: one line per layout on stderr with the launch plan its decode
 // steps will use (measurement and debugging aid; nothing else changes).
 static void log_plan(const dkv_layout *L, int64_t n_host, int64_t n_hbm) {
@@ -627,9 +640,9 @@ static void log_plan(const dkv_layout *L, int64_t n_host, int64_t n_hbm) {
     static const char *const kSplitNames[] = {"regs", "lds", "naive", "mfma", "ldsmfma"};
     const dkv_shape *s = &L->shape;
     const int B = L->batch;
-    const char *proj = B < L->proj_mfma_min_batch ? "gemv"
-                       : B < L->proj_splitk_min_batch && B <= 16 ? "mfma one-tile streamed"
-                                                      : "mfma split-k (x staged in LDS)";
+    static const char *const kProjNames[] = {"gemv", "mfma one-tile streamed", "mfma split-k (x staged in LDS)",
+                                             "mfma tiled (x and W staged in LDS)"};
+    const char *proj = kProjNames[projection_form_of(L)];
     fprintf(stderr,
             "[dkv] layout: batch %d, hidden %d, heads %d/%d, head_dim %d, layers %d; pages per layer: "
             "%lld host, %lld HBM%s; split %d tokens (%d per sequence at most), split kernel %s on %s; "
@@ -986,6 +999,8 @@ int32_t kv_layout_split_tokens(const dkv_layout *L) { return L && live(L) ? L->s
 int32_t kv_layout_split_kernel(const dkv_layout *L) { return L && live(L) ? L->split_variant : -1; }
 
 int32_t kv_layout_split_waves(const dkv_layout *L) { return L && live(L) ? L->split_waves : -1; }
+
+int32_t kv_layout_projection_kernel(const dkv_layout *L) { return L && live(L) ? projection_form_of(L) : -1; }
 
 dkv_status kv_layout_set_split_kernel(dkv_layout *L, int32_t kernel) {
     if (!L || !live(L)) return fail(DKV_E_INVALID_ARG, "kv_layout_set_split_kernel: null or freed layout");

@@ -71,6 +71,15 @@ dkv_status dkv_probe_page_read(const void *ptr, uint64_t bytes, int32_t page_byt
  * different page sizes, or bytes < 0 or beyond either pool). */
 dkv_status kv_pool_copy(dkv_pool *dst, const dkv_pool *src, int64_t bytes, dkv_stream_t stream);
 
+/* The QKV projection kernel the layout's decode steps run, fixed at creation
+ * by the batch, the shape and the thresholds (DKV_PROJ_MFMA_MIN_BATCH,
+ * DKV_PROJ_SPLITK_MIN_BATCH): 0 the VALU GEMV (below 8 sequences), 1 the
+ * one-tile streamed MFMA kernel (on request, up to 16), 2 the split-k MFMA
+ * kernel, 3 the tiled MFMA kernel (from 192 sequences, once its workgroups
+ * fill half the CUs). -1 for a NULL or freed layout. Measurement and
+ * reporting only. */
+int32_t kv_layout_projection_kernel(const dkv_layout *layout);
+
 /* Per-kernel timing of a layout's decode steps. While enabled, decode_step
  * records HIP events on its stream before and after each of its kernels
  * (enable = 1: projection, fresh token, split attention, combine) or only

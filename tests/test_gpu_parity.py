@@ -225,6 +225,38 @@ def test_projection_integer_exact(oracle, monkeypatch, shape_name, batch, knobs)
         s.free()
 
 
+@pytest.mark.parametrize("shape_name,batch,knobs,kernel", [
+    ("llama8b", 1, {}, "gemv"), ("llama8b", 7, {}, "gemv"), ("llama8b", 8, {}, "splitk"),
+    ("llama8b", 64, {}, "splitk"), ("llama8b", 256, {}, "splitk"), ("llama8b", 257, {}, "tiled"),
+    ("llama8b", 384, {}, "tiled"), ("llama70b", 191, {}, "splitk"), ("llama70b", 192, {}, "tiled"),
+    ("tiny", 1100, {}, "splitk"), ("tiny", 2600, {}, "tiled"),
+    ("llama8b", 12, {"DKV_PROJ_SPLITK_MIN_BATCH": "16"}, "stream"),
+    ("llama8b", 3, {"DKV_PROJ_MFMA_MIN_BATCH": "1"}, "stream"),
+    ("llama8b", 12, {"DKV_PROJ_MFMA_MIN_BATCH": "64"}, "gemv")])
+def test_projection_kernel_choice(monkeypatch, shape_name, batch, knobs, kernel):
+    """The projection form a layout reports (and its steps run): the GEMV
+    below 8 sequences, the split-k kernel from 8, the tiled kernel from 192
+    sequences once its workgroups fill half the CUs (at hidden 4096, 48 W
+    tiles, from 257: one 256-sequence tile and two ranges give 96; at hidden
+    8192, 80 W tiles x 2 ranges from 192; the tiny shape's 12 W tiles from
+    2600), and the thresholds' overrides."""
+    for k in PROJ_KNOBS:
+        monkeypatch.delenv(k, raising=False)
+    for k, v in knobs.items():
+        monkeypatch.setenv(k, v)
+    base = {"llama8b": configs.LLAMA8B_HOST, "llama70b": configs.LLAMA70B_LONG, "tiny": configs.TINY}[shape_name]
+    wl = base.replace(batch=batch, n_layers=1)
+    shape = H.dkv.Shape.of(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, 1)
+    pool = H.dkv.kv_alloc_hbm(shape, batch)
+    try:
+        layout = H.dkv.kv_layout_create(shape, np.full(batch, 2, np.int32), np.full(batch, 1 << 30, np.int32),
+                                        None, pool)
+        assert layout.projection_kernel == "qkv_proj_%s_kernel" % kernel
+        layout.free()
+    finally:
+        pool.free()
+
+
 def test_write_back_within_one_ulp(oracle):
     wl = configs.LLAMA8B_HOST.replace(batch=2)
     ctx = np.array([40, 7], np.int32)
