@@ -39,7 +39,7 @@ def test_double_free_and_use_after_free_are_refused():
     assert L.kv_layout_free(h_layout) == E_INVALID_ARG      # freed twice
     assert L.kv_layout_check_status(h_layout) == E_INVALID_ARG
     assert L.kv_layout_split_tokens(h_layout) == 0 and L.kv_layout_split_kernel(h_layout) == -1
-    assert L.kv_layout_split_waves(h_layout) == -1
+    assert L.kv_layout_split_waves(h_layout) == -1 and L.kv_layout_projection_kernel(h_layout) == -1
     assert L.kv_layout_set_split_kernel(h_layout, 0) == E_INVALID_ARG
     tier = ctypes.c_int32(-7)
     assert L.kv_layout_page_tier(h_layout, 0, 0, ctypes.byref(tier)) == E_INVALID_ARG and tier.value == -7
