@@ -1,4 +1,5 @@
-"""The decode step at the largest batch a layout takes.
+"""The decode step at the largest batch a layout takes, and one sequence
+longer than 2 GiB of KV.
 
 A layout holds at most 65535 sequences: the step's item list packs the
 sequence index into 16 bits, and the fresh-token kernel's bookkeeping for the
@@ -57,3 +58,35 @@ def test_batch_at_the_layout_maximum(oracle):
             assert np.all(np.abs(have - want) <= ulp), b
     assert np.abs(got - ref).max() <= MAX_ABS
     assert H.rel_l2(got, ref) <= REL_L2
+
+
+def test_one_sequence_past_two_gib(oracle):
+    """One sequence of 600,017 cached tokens at the 8B shape: 2.3 GiB of KV,
+    so page addresses and offsets pass 2^31 bytes inside one pool. Sampled
+    query heads (each KV head's first and last) match the oracle, and the
+    all-host and all-HBM placements give identical bits."""
+    wl = configs.LLAMA8B_HOST.replace(batch=1)
+    L = 600_017
+    ctx = np.array([L], np.int32)
+    outs = []
+    for tail in (0, 1 << 30):
+        s = H.Setup(wl, ctx_lens=ctx, hbm_tail=tail)
+        try:
+            assert s.kv_bytes_read() > (1 << 31)
+            outs.append(bits(s.run()))
+            H.log("one sequence of %d tokens, %s: split %d tokens"
+                  % (L, "host" if tail == 0 else "HBM", s.layout.split_tokens))
+        finally:
+            s.free()
+    assert np.array_equal(outs[0], outs[1])
+    got = H.bf16_to_f64(outs[0][0])
+    assert np.all(np.isfinite(got))
+    d, G = wl.head_dim, wl.group
+    heads = sorted({g * G for g in range(wl.n_kv_heads)} | {g * G + G - 1 for g in range(wl.n_kv_heads)})
+    y = oracle.qkv_projection(wl.x(0)[0], wl.W(0))
+    ref = np.zeros((len(heads), d))
+    for i, h in enumerate(heads):
+        ref[i], y = H.oracle_head(oracle, wl, 0, 0, h, L, y)
+    sel = np.stack([got[h * d:(h + 1) * d] for h in heads])
+    assert np.abs(sel - ref).max() <= MAX_ABS
+    assert H.rel_l2(sel, ref) <= REL_L2
