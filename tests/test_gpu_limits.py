@@ -63,12 +63,14 @@ def test_batch_at_the_layout_maximum(oracle):
 def test_one_sequence_past_two_gib(oracle):
     """One sequence of 600,017 cached tokens at the 8B shape: 2.3 GiB of KV,
     so page addresses and offsets pass 2^31 bytes inside one pool. Sampled
-    query heads (each KV head's first and last) match the oracle, and the
-    all-host and all-HBM placements give identical bits."""
+    query heads (each KV head's first and last) match the oracle, the last
+    cached tokens read back as appended, the fresh slot holds k_new / v_new
+    within one bf16 ulp, and the all-host and all-HBM placements give
+    identical bits (outputs and written-back slot)."""
     wl = configs.LLAMA8B_HOST.replace(batch=1)
     L = 600_017
     ctx = np.array([L], np.int32)
-    outs = []
+    outs, slots = [], []
     for tail in (0, 1 << 30):
         s = H.Setup(wl, ctx_lens=ctx, hbm_tail=tail)
         try:
@@ -76,14 +78,25 @@ def test_one_sequence_past_two_gib(oracle):
             outs.append(bits(s.run()))
             H.log("one sequence of %d tokens, %s: split %d tokens"
                   % (L, "host" if tail == 0 else "HBM", s.layout.split_tokens))
+            # the last cached tokens read back as appended, and the fresh slot
+            k_end, v_end = H.dkv.kv_read(s.layout, 0, 0, L - 3, 3)
+            assert np.array_equal(k_end, wl.kv("k", 0, 0, L - 3, L))
+            assert np.array_equal(v_end, wl.kv("v", 0, 0, L - 3, L))
+            slots.append(H.dkv.kv_read(s.layout, 0, 0, L, 1))
         finally:
             s.free()
     assert np.array_equal(outs[0], outs[1])
+    assert all(np.array_equal(a, b) for a, b in zip(slots[0], slots[1]))
     got = H.bf16_to_f64(outs[0][0])
     assert np.all(np.isfinite(got))
     d, G = wl.head_dim, wl.group
     heads = sorted({g * G for g in range(wl.n_kv_heads)} | {g * G + G - 1 for g in range(wl.n_kv_heads)})
     y = oracle.qkv_projection(wl.x(0)[0], wl.W(0))
+    Hq, Hkv = wl.n_q_heads, wl.n_kv_heads
+    for slot, want in ((slots[0][0][0], y[Hq * d:(Hq + Hkv) * d]), (slots[0][1][0], y[(Hq + Hkv) * d:])):
+        have = H.bf16_to_f64(slot.reshape(-1))
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 1e-30))) - 7) + FP32_SLACK
+        assert np.all(np.abs(have - want) <= ulp)
     ref = np.zeros((len(heads), d))
     for i, h in enumerate(heads):
         ref[i], y = H.oracle_head(oracle, wl, 0, 0, h, L, y)
