@@ -448,11 +448,14 @@ int tiled_tiles(const StepArgs &a) {
 // The tiled form from 192 sequences, once its workgroups fill half the CUs;
 // below that the split-k kernel is faster. Measured on MI355X (W cycled
 // through copies so that it is read from HBM, decode-step HIP events,
-// projection + fresh-token kernel, split-k / tiled): hidden 4096 (48 W
-// tiles), batch 256, 52.0 / 57.9 us; 384, 81.0 / 60.8; 512, 84.1 / 62.9;
-// 1024, 143.9 / 107.2; hidden 8192 (80 W tiles), batch 128, 83.5 / 91.6;
-// 192, 110.9 / 98.4; 256, 134.4 / 105.5; 512, 225.7 / 186.9; 1024, 423.6 /
-// 304.8.
+// projection + fresh-token kernel, split-k / tiled with the row check on
+// every tile): hidden 4096 (48 W tiles), batch 256, 52.0 / 57.9 us; 384,
+// 81.0 / 60.8; 512, 84.1 / 62.9; 1024, 143.9 / 107.2; hidden 8192 (80 W
+// tiles), batch 128, 83.5 / 91.6; 192, 110.9 / 98.4; 256, 134.4 / 105.5;
+// 512, 225.7 / 186.9; 1024, 423.6 / 304.8. With the check on the last tile
+// only, the tiled kernel takes 56.7 / 60.0 / 98.4 us at hidden 4096, batch
+// 384 / 512 / 1024, and 104.7 / 170.6 / 273.4 us at hidden 8192, batch 256 /
+// 512 / 1024.
 bool tiled_pays(const StepArgs &a) {
     if (a.batch < kProjTiledMinBatch || a.n_qkv % tile::kN != 0) return false;
     const int tiles = tiled_tiles(a);
