@@ -248,6 +248,7 @@ def probe_page_runs(dkv, pool, wl, max_bytes=8 << 30):
 
 PAGE_PROBE_WAVES = (2048, 3072)
 HOST_PROBES = [(64, 1), (256, 1), (512, 1), (1024, 2), (256, -1), (1024, -2)]
+SMALL_READ_BYTES = 64 << 20       # layers reading less than this over the link also get a same-size read
 HBM_PROBES = [(1024, -2), (2048, -2), (4096, -4), (8192, -8), (2048, 4)]
 
 
@@ -1102,6 +1103,20 @@ def main(argv=None):
             ceiling, ceiling_rows, probe_bytes = probe_host_link(dkv, HOST_PROBES)
     log("own placement: %.3f ms/step, split kernel %.3f ms; host-link ceiling %.2f GB/s"
         % (ms, kt["split"], ceiling or 0.0))
+    # A launch that reads only a few MiB over the link cannot reach the
+    # ceiling of a long read (the link's latency and ramp weigh): for such
+    # layers, also the best streaming read of the same number of bytes.
+    small_ceiling = None
+    if r.host_pool is not None and 0 < host_kv_layer < SMALL_READ_BYTES:
+        nb = -(-host_kv_layer // (1 << 20)) * (1 << 20)
+        buf = dkv.HostBuffer(nb)
+        try:
+            best = max(nb / dkv.probe_stream_read(buf.device_ptr, nb, grid, unroll, reps=21) / 1e6
+                       for grid, unroll in HOST_PROBES)
+        finally:
+            buf.free()
+        small_ceiling = {"bytes": nb, "GBps": round(best, 2),
+                         "split_kernel_vs": round(host_kv_layer / (kt["split"] / wl.n_layers * 1e-3) / 1e9 / best, 4)}
 
     value = kv_bytes / (ms * 1e-3) / 1e9
     split_gbps = kv_bytes / (kt["split"] * 1e-3) / 1e9
@@ -1317,6 +1332,7 @@ def main(argv=None):
                      "measured_ceiling_GBps": round(ceiling, 3) if ceiling else None,
                      "ceiling_probe_bytes": probe_bytes,
                      "frac_of_measured_ceiling": round(split_gbps / ceiling, 4) if ceiling else None,
+                     "same_size_read_ceiling": small_ceiling,
                      "host_GBps_vs_ceiling": round(host_kv / (kt["split"] * 1e-3) / 1e9 / ceiling, 4)
                      if ceiling else None,
                      "split_kernel_ms": round(kt["split"], 4)},
